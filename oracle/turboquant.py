@@ -237,38 +237,43 @@ def dequantize_values(R, centroids, values: dict) -> np.ndarray:
 
 
 def attend(Q, R, S, centroids, keys: dict, values: dict, scale: float | None = None,
-           n_tokens: int | None = None) -> np.ndarray:
+           n_tokens: int | None = None, value_centroids=None) -> np.ndarray:
     """softmax(scale * est) . V^ over the compressed cache ([superapi]
     常见使用模式: scores from the compressed keys, softmax, then the weighted
     sum of the decompressed values).  The weighted sum is taken in the rotated
     domain and rotated back once: out = R^T sum_t a_t ||v_t|| c[idx_t].
     No causal mask: a decode query sees the whole cache.
 
+    ``centroids`` is the key codebook; ``value_centroids`` the value
+    codebook (defaults to the key codebook: same bit width).
+
     Returns (n_seq, G, d) fp64."""
     d = R.shape[0]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
+    vc = centroids if value_centroids is None else value_centroids
     est = key_scores(Q, R, S, centroids, keys)
     T = est.shape[-1] if n_tokens is None else n_tokens
     logits = scale * est[..., :T]
     logits -= logits.max(axis=-1, keepdims=True)
     a = np.exp(logits)
     a /= a.sum(axis=-1, keepdims=True)
-    vrot = centroids[values["idx"][:, :T]] * values["norm"][:, :T].astype(np.float64)[..., None]
+    vrot = vc[values["idx"][:, :T]] * values["norm"][:, :T].astype(np.float64)[..., None]
     acc = np.einsum("sgt,std->sgd", a, vrot)
     return acc @ R
 
 
 def attend_online(Q, R, S, centroids, keys: dict, values: dict, scale: float | None = None,
-                  chunk: int = 64) -> np.ndarray:
+                  chunk: int = 64, value_centroids=None) -> np.ndarray:
     """The same attention as ``attend`` computed chunk by chunk with a running
     (max, sum, acc) per query head and a final log-sum-exp merge -- the
     streaming form a split-token decode uses.  Equal to ``attend`` up to
     rounding."""
     d = R.shape[0]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
+    vc = centroids if value_centroids is None else value_centroids
     est = scale * key_scores(Q, R, S, centroids, keys)
     n_seq, G, T = est.shape
-    vrot = centroids[values["idx"]] * values["norm"].astype(np.float64)[..., None]
+    vrot = vc[values["idx"]] * values["norm"].astype(np.float64)[..., None]
     mx = np.full((n_seq, G), -np.inf)
     sm = np.zeros((n_seq, G))
     acc = np.zeros((n_seq, G, d))

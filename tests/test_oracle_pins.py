@@ -234,6 +234,30 @@ def test_score_equals_inner_product_with_dequantised_key():
 
 # --------------------------------------------------------------- attention ---
 
+def test_attention_with_different_key_and_value_bits():
+    """P8: with 3-bit keys and 2-bit values, attention dequantises the values
+    with their own (2-bit) codebook: it equals textbook attention over
+    dequantize_values(R, value codebook), in one-shot and online form."""
+    d, m = 128, 64
+    R = synth.haar_rotation(d, 42)
+    S = synth.gaussian_projection(m, d, 43)
+    kbeta, kc = O.lloyd_max_codebook(d, 3)
+    vbeta, vc = O.lloyd_max_codebook(d, 2)
+    K = synth.kv_slot(0, 0, 0, 200, d).astype(np.float64)[None]
+    V = synth.kv_slot(1, 0, 0, 200, d).astype(np.float64)[None]
+    Q = synth.kv_slot(2, 0, 0, 4, d).astype(np.float64)[None] * 3
+    keys = O.compress_keys(K, R, S, kbeta, kc)
+    vals = O.compress_values(V, R, vbeta, vc)
+    out = O.attend(Q, R, S, kc, keys, vals, value_centroids=vc)
+    est = O.key_scores(Q, R, S, kc, keys) / math.sqrt(d)
+    a = np.exp(est - est.max(-1, keepdims=True))
+    a /= a.sum(-1, keepdims=True)
+    ref = np.einsum("sgt,std->sgd", a, O.dequantize_values(R, vc, vals))
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(O.attend_online(Q, R, S, kc, keys, vals, chunk=37, value_centroids=vc), ref,
+                               rtol=1e-11, atol=1e-12)
+
+
 def test_online_softmax_equals_one_shot_and_textbook_attention():
     """P8: chunked online softmax (any chunk) equals the one-shot softmax,
     and both equal textbook attention softmax(scale est) V^ computed from
