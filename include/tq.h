@@ -1,0 +1,212 @@
+/*
+ * tq.h -- TurboQuant KV-cache compression and attention over the packed
+ * cache, for AMD Instinct MI355X (gfx950).  C ABI of libtq.so.
+ *
+ * What is computed (sources: the "turboquant-pytorch" skill pages on
+ * nav.superapi.store -- sections 主要能力, 核心 API, 常见使用模式, 算法细节,
+ * 限制与注意事项 -- and on atskills.one -- "What this skill does": Stage 1,
+ * Stage 2, Why Random Rotation?, Why QJL for Keys but Not Values?):
+ *
+ *   keys   k (d floats): n = ||k||, y = R k / n, idx_j = #{i : beta_i < y_j}
+ *          (Lloyd-Max cell of each rotated coordinate), r = y - c[idx],
+ *          gamma = ||r||, sign bits s = [S r >= 0] (1-bit QJL projection of
+ *          the residual).  Stored: idx, s, n, gamma.
+ *   values v: n = ||v||, y = R v / n, idx as above.  Stored: idx, n.
+ *   score  est(q, k) = n * ( <R q, c[idx]> + gamma * sqrt(pi/2)/m * <S R q, 2s-1> )
+ *          (asymmetric: full-precision query against the packed key; unscaled).
+ *   attend out = R^T sum_t softmax_t(scale * est_t) * n_t^v * c[idx_t^v].
+ *
+ * R (d x d, orthogonal) and S (m x d, Gaussian) are fixed per (dim, seed) and
+ * handed in by the caller; c (2^b centroids) and beta (2^b - 1 boundaries)
+ * are the Lloyd-Max codebook of N(0, 1/d).
+ *
+ * Conventions for every call:
+ *  - Return 0 (TQ_OK) or a negative tq_status.  Nothing throws.  On an
+ *    argument error nothing is launched and no output is written;
+ *    tq_last_error() then holds a message (thread-local).
+ *  - "device" pointers are HIP device memory owned by the caller.  The
+ *    library allocates device memory only in tq_create (its own copies of R,
+ *    S and the codebooks, a few hundred KB) and frees it in tq_destroy.
+ *  - Calls that take a stream enqueue work on it and return at once; they
+ *    are ordered with other work on that stream.  stream == NULL means the
+ *    default stream.  The argument is a hipStream_t passed as void*.
+ *  - A context is read-only after its codebooks are loaded, so calls on
+ *    different streams may run concurrently; tq_codebook_load must not run
+ *    concurrently with calls that use the same context.
+ *  - Device pointers must be 16-byte aligned.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_LAYOUT_VERSION 1
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = -1,       /* bad argument: size, bits, dtype, null/misaligned pointer */
+  TQ_ECAPACITY = -2,    /* pos + n_new exceeds the cache capacity */
+  TQ_ENOCODEBOOK = -3,  /* no codebook loaded for the bits this call needs */
+  TQ_ENOMEM = -4,       /* device allocation failed (tq_create only) */
+  TQ_EDEVICE = -5,      /* a HIP call or kernel launch failed */
+  TQ_EUNSUPPORTED = -6, /* valid but not built: e.g. head_dim other than 128 */
+  TQ_EWORKSPACE = -7    /* workspace smaller than tq_workspace_bytes */
+} tq_status;
+
+typedef enum { TQ_F16 = 1, TQ_F32 = 2 } tq_dtype;
+
+typedef struct tq_ctx tq_ctx;
+
+/* Static shape of a compressed cache.  head_dim d: multiple of 128 up to
+ * 1024; the built kernels cover d = 128 (others give TQ_EUNSUPPORTED).
+ * proj_dim m: multiple of 64 up to 512; built: 64 and 128 (default d/2,
+ * nav.superapi.store 算法细节 / proj_dim 选择).  key_bits, value_bits in
+ * 1..4 (the pages use 2-4; 1 is the 1-bit limit). */
+typedef struct {
+  int32_t head_dim;
+  int32_t proj_dim;
+  int32_t key_bits;
+  int32_t value_bits;
+} tq_config;
+
+/* Caller-owned packed cache of n_seq slots (one slot = one KV head of one
+ * sequence/layer), each holding up to `capacity` tokens (multiple of 128).
+ *
+ * key_records: device, n_seq * capacity * tq_key_record_bytes() bytes.  Slot
+ *   s, token t starts at byte (s * capacity + t) * tq_key_record_bytes().
+ * value_blocks: device, n_seq * (capacity/128) * tq_value_block_bytes()
+ *   bytes; block (s, t/128) starts at byte
+ *   (s * capacity/128 + t/128) * tq_value_block_bytes().
+ * Zero-fill both buffers before first use if tokens will be read before
+ * they are written.
+ *
+ * Record layout v1 (32-bit little-endian words; b = bits, d = 128):
+ *  Code groups.  b consecutive words hold 32 b-bit codes as 8 slots s x 4
+ *  byte lanes i; byte lane i of every word belongs to code (s, i):
+ *    b=1: bit s;  b=2: word s/4, bits 2(s%4)..;  b=4: word s/2, bits 4(s%2)..;
+ *    b=3: s<6: word s/2, bits 3(s%2)..; s=6: code bits 0-1 at bits 6-7 of
+ *         word 0, bit 2 at bit 6 of word 2; s=7: bits 0-1 at bits 6-7 of
+ *         word 1, bit 2 at bit 7 of word 2   (bit numbers within the byte).
+ *  Key record: 4 code groups q = 0..3 (words b q .. b q + b - 1); group q,
+ *    slot s, byte lane i is the code of rotated coordinate 16 s + 4 q + i.
+ *    Then m/32 sign words: projection coordinate 16 t + 4 q + i is bit
+ *    16 (q%2) + 4 (t%4) + i of word 2 (t/4) + q/2 (1 = projection >= 0).
+ *    Then fp32 ||k||, then fp32 gamma.  Size 4 (b d/32 + m/32 + 2) bytes.
+ *  Value block (128 tokens): for w = 0..b-1, q = 0..3, coordinate c =
+ *    0..d-1, word (w * 4 + q) * d + c; the b words (w = 0..b-1) of (q, c)
+ *    form a code group whose slot s, byte lane i is the code of coordinate c
+ *    of block token 16 s + 4 q + i.  Then 128 fp32 norms ||v|| in token
+ *    order.  Size 4 (4 b d + 128) bytes.
+ * Codes are idx = #{i : beta_i < y} of the rotated, normalised coordinate.
+ * Keys are grouped by token and values by coordinate because those are the
+ * contraction orders of the score and the weighted-sum matrix products. */
+typedef struct {
+  void* key_records;
+  void* value_blocks;
+  int64_t capacity;
+  int32_t n_seq;
+} tq_cache_view;
+
+/* ---- host-only helpers (no device work) ---------------------------------- */
+
+/* Lloyd-Max codebook for coordinates ~ N(0, 1/head_dim) with 2^bits levels
+ * (nav.superapi.store 核心 API build_lloyd_max_codebook(dim, bits) ->
+ * (boundaries, centroids); 限制与注意事项: computed once per (dim, bits)).
+ * Writes 2^bits ascending centroids and 2^bits - 1 ascending boundaries
+ * (host arrays owned by the caller).  bits in 1..4, head_dim >= 1.
+ * Returns TQ_EINVAL on bad arguments. */
+int tq_lloyd_max_codebook(int32_t head_dim, int32_t bits, double* centroids, double* boundaries);
+
+/* Bytes of one key record / one 128-token value block / a whole cache of
+ * n_seq slots x capacity tokens, for a configuration.  0 if cfg is NULL or
+ * invalid (the same checks as tq_create) or capacity is not a positive
+ * multiple of 128. */
+size_t tq_key_record_bytes(const tq_config* cfg);
+size_t tq_value_block_bytes(const tq_config* cfg);
+size_t tq_cache_key_bytes(const tq_config* cfg, int32_t n_seq, int64_t capacity);
+size_t tq_cache_value_bytes(const tq_config* cfg, int32_t n_seq, int64_t capacity);
+
+/* Device workspace bytes needed by tq_attention_scores and tq_attend for
+ * this shape (query operands, query norms, per-wave attention partials).
+ * 0 on invalid arguments (cfg NULL/invalid, n_seq < 1, G not in 1..16,
+ * n_tokens < 1). */
+size_t tq_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, int64_t n_tokens);
+
+/* Thread-local message describing the last failure of this thread. */
+const char* tq_last_error(void);
+
+/* ---- context ---------------------------------------------------------------- */
+
+/* Create a context on the current HIP device.  R: host, d x d row-major
+ * (rotation y = R x), S: host, m x d row-major (QJL matrix, applied to the
+ * rotated residual).  Both are copied before return.  R should be orthogonal
+ * (nav.superapi.store 算法细节 / 随机旋转); this is not checked.  Returns
+ * TQ_EINVAL (bad config or null pointers), TQ_EUNSUPPORTED (a valid shape
+ * that is not built), TQ_ENOMEM or TQ_EDEVICE.  Arguments are checked before
+ * any HIP call. */
+int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** out);
+
+/* Free the context's device memory.  NULL is accepted.  Work still queued
+ * that uses the context must have finished. */
+int tq_destroy(tq_ctx* ctx);
+
+/* Load the codebook for `bits` (host arrays, copied): 2^bits strictly
+ * ascending finite centroids and 2^bits - 1 strictly ascending finite
+ * boundaries, each boundary strictly between its two centroids.  Needed for
+ * key_bits and value_bits before any append or attention call.  Host-only:
+ * the codebook travels to the kernels as launch arguments. */
+int tq_codebook_load(tq_ctx* ctx, int32_t bits, const double* centroids, const double* boundaries);
+
+/* ---- hot path ---------------------------------------------------------------- */
+
+/* Compress n_new keys per slot and write them at token positions
+ * [pos, pos + n_new) of every slot (append_key of TurboQuantKVCache,
+ * nav.superapi.store 核心 API; stage 1 + stage 2, atskills.one Stage 2).
+ * k: device, [n_seq][n_new][d] contiguous, dtype TQ_F16 or TQ_F32, finite.
+ * A zero vector is encoded with direction 0 and scores 0.
+ * Errors: TQ_EINVAL, TQ_ECAPACITY (pos < 0 or pos + n_new > capacity),
+ * TQ_ENOCODEBOOK, TQ_EDEVICE.  n_new == 0 is a no-op. */
+int tq_append_key(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_t dtype,
+                  int64_t pos, int64_t n_new, void* stream);
+
+/* Compress n_new values per slot (stage 1 only: TurboQuantCompressorMSE,
+ * nav.superapi.store 核心 API; values need no QJL, 算法细节) into token
+ * positions [pos, pos + n_new).  Codes of other tokens sharing a 128-token
+ * block are preserved.  Same arguments and errors as tq_append_key. */
+int tq_append_value(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int32_t dtype,
+                    int64_t pos, int64_t n_new, void* stream);
+
+/* Asymmetric attention scores straight from the packed keys
+ * (asymmetric_attention_scores / attention_scores, nav.superapi.store
+ * 常见使用模式 and 核心 API): scores[s][h][t] = est(q[s][h], k[s][t]),
+ * unscaled, for t < n_tokens.
+ * q: device [n_seq][G][d] (query head h of slot s uses KV slot s; GQA groups
+ * of G contiguous heads), dtype TQ_F16 or TQ_F32.  1 <= G <= 16.
+ * scores: device fp32 [n_seq][G][n_tokens].
+ * workspace: device, >= tq_workspace_bytes(ctx, n_seq, G, n_tokens).
+ * Errors: TQ_EINVAL (n_tokens <= 0 or > capacity, G out of range, ...),
+ * TQ_ENOCODEBOOK, TQ_EWORKSPACE, TQ_EDEVICE. */
+int tq_attention_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype,
+                        int32_t G, int64_t n_tokens, float* scores, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Attention over the packed cache: softmax over the first n_tokens of
+ * scale * est, then the weighted sum of the dequantised values, rotated
+ * back (nav.superapi.store 常见使用模式: scores from compressed keys,
+ * softmax, weighted sum of the decompressed values).  scale <= 0 means
+ * 1/sqrt(d).  No causal mask.  out: device fp32 [n_seq][G][d].
+ * Same q/workspace rules and errors as tq_attention_scores. */
+int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
+              int64_t n_tokens, float scale, float* out, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

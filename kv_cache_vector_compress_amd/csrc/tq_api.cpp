@@ -1,0 +1,337 @@
+// C ABI of libtq.so: argument checking, context set-up and launch dispatch.
+// Every argument is checked on the host before any HIP call, so errors never
+// reach the device and never leave partial writes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+// Round to the nearest fp16 (ties to even), returned as raw bits.
+static uint16_t to_half_bits(float f) {
+  _Float16 h = (_Float16)f;
+  uint16_t b;
+  std::memcpy(&b, &h, 2);
+  return b;
+}
+static float half_to_float(uint16_t b) {
+  _Float16 h;
+  std::memcpy(&h, &b, 2);
+  return (float)h;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by tq_create and the size queries.  Returns TQ_OK,
+// TQ_EINVAL or TQ_EUNSUPPORTED.
+static int check_config(const tq_config* c) {
+  if (!c) return fail(TQ_EINVAL, "config is NULL");
+  if (c->head_dim < 128 || c->head_dim > 1024 || c->head_dim % 128)
+    return fail(TQ_EINVAL, "head_dim %d: need a multiple of 128 in [128, 1024]", c->head_dim);
+  if (c->proj_dim < 64 || c->proj_dim > 512 || c->proj_dim % 64)
+    return fail(TQ_EINVAL, "proj_dim %d: need a multiple of 64 in [64, 512]", c->proj_dim);
+  if (c->key_bits < 1 || c->key_bits > 4 || c->value_bits < 1 || c->value_bits > 4)
+    return fail(TQ_EINVAL, "key_bits %d / value_bits %d: need 1..4", c->key_bits, c->value_bits);
+  if (c->head_dim != kD) return fail(TQ_EUNSUPPORTED, "head_dim %d is valid but only 128 is built", c->head_dim);
+  if (c->proj_dim != 64 && c->proj_dim != 128)
+    return fail(TQ_EUNSUPPORTED, "proj_dim %d is valid but only 64 and 128 are built", c->proj_dim);
+  return TQ_OK;
+}
+
+static size_t key_rec_bytes(const tq_config& c) { return 4u * (c.key_bits * c.head_dim / 32 + c.proj_dim / 32 + 2); }
+static size_t val_blk_bytes(const tq_config& c) { return 4u * (4 * c.value_bits * c.head_dim + kBlockTokens); }
+
+}  // namespace tq
+
+using namespace tq;
+
+struct tq_ctx {
+  tq_config cfg;
+  int device;
+  void* dev_mem;       // one allocation holding every device image below
+  Matrices mats;
+  CodebookDev cb[5];   // indexed by bits
+  bool loaded[5];
+};
+
+static std::once_flag g_init_flag;
+static int g_init_rc = 0;
+
+extern "C" {
+
+const char* tq_last_error(void) { return g_err; }
+
+size_t tq_key_record_bytes(const tq_config* cfg) {
+  if (check_config(cfg) == TQ_EINVAL) return 0;
+  return key_rec_bytes(*cfg);
+}
+
+size_t tq_value_block_bytes(const tq_config* cfg) {
+  if (check_config(cfg) == TQ_EINVAL) return 0;
+  return val_blk_bytes(*cfg);
+}
+
+size_t tq_cache_key_bytes(const tq_config* cfg, int32_t n_seq, int64_t capacity) {
+  if (check_config(cfg) == TQ_EINVAL || n_seq < 1 || capacity < 1 || capacity % kBlockTokens) return 0;
+  return key_rec_bytes(*cfg) * (size_t)n_seq * (size_t)capacity;
+}
+
+size_t tq_cache_value_bytes(const tq_config* cfg, int32_t n_seq, int64_t capacity) {
+  if (check_config(cfg) == TQ_EINVAL || n_seq < 1 || capacity < 1 || capacity % kBlockTokens) return 0;
+  return val_blk_bytes(*cfg) * (size_t)n_seq * (size_t)(capacity / kBlockTokens);
+}
+
+size_t tq_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, int64_t n_tokens) {
+  if (check_config(cfg) == TQ_EINVAL || n_seq < 1 || G < 1 || G > 16 || n_tokens < 1) return 0;
+  return plan_attention(cfg->proj_dim, n_seq, G, n_tokens).total;
+}
+
+int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** out) {
+  clear_error();
+  if (!out) return fail(TQ_EINVAL, "tq_create: out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc != TQ_OK) return rc;
+  if (!R || !S) return fail(TQ_EINVAL, "tq_create: R or S is NULL");
+  const int d = cfg->head_dim, m = cfg->proj_dim;
+  for (int i = 0; i < d * d; ++i)
+    if (!std::isfinite(R[i])) return fail(TQ_EINVAL, "tq_create: R has a non-finite entry");
+  for (int i = 0; i < m * d; ++i)
+    if (!std::isfinite(S[i])) return fail(TQ_EINVAL, "tq_create: S has a non-finite entry");
+
+  // Host images.  R and S are scaled by 2^8 and split into fp16 high and low
+  // parts (hi = fp16(x), lo = fp16(x - hi)), so hi + lo carries ~22 bits.
+  // S's columns are stored in "slot order": column 32 kb + 8 q + e holds
+  // rotated coordinate 16 (2 kb + e/4) + 4 q + e%4, the order in which a key
+  // lane holds its residual after the rotation.
+  const size_t r_img = (size_t)d * kLdsStride, s_img = (size_t)m * kLdsStride;
+  std::vector<uint16_t> rh(r_img, 0), rl(r_img, 0), sh(s_img, 0), sl(s_img, 0);
+  std::vector<float> r32((size_t)d * d), s32((size_t)m * d);
+  auto split = [](double x, uint16_t& hi, uint16_t& lo) {
+    const double xs = x * (double)kRotScale;
+    hi = to_half_bits((float)xs);
+    lo = to_half_bits((float)(xs - (double)half_to_float(hi)));
+  };
+  for (int i = 0; i < d; ++i)
+    for (int k = 0; k < d; ++k) {
+      split(R[i * d + k], rh[i * kLdsStride + k], rl[i * kLdsStride + k]);
+      r32[(size_t)i * d + k] = (float)R[i * d + k];
+    }
+  for (int i = 0; i < m; ++i) {
+    for (int col = 0; col < d; ++col) {
+      const int kb = col / 32, q = (col % 32) / 8, e = col % 8;
+      const int coord = 16 * (2 * kb + e / 4) + 4 * q + e % 4;
+      split(S[i * d + coord], sh[i * kLdsStride + col], sl[i * kLdsStride + col]);
+    }
+    for (int k = 0; k < d; ++k) s32[(size_t)i * d + k] = (float)S[i * d + k];
+  }
+
+  std::call_once(g_init_flag, [] { g_init_rc = compress_device_init() | attention_device_init(); });
+  if (g_init_rc != 0) return fail(TQ_EDEVICE, "tq_create: HIP device initialisation failed");
+
+  tq_ctx* c = new tq_ctx();
+  c->cfg = *cfg;
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return fail(TQ_EDEVICE, "tq_create: hipGetDevice failed");
+  }
+  const size_t b_rimg = r_img * 2, b_simg = s_img * 2;
+  const size_t off_rl = b_rimg, off_sh = 2 * b_rimg, off_sl = off_sh + b_simg, off_r32 = off_sl + b_simg;
+  const size_t off_s32 = off_r32 + r32.size() * 4, total = off_s32 + s32.size() * 4;
+  if (hipMalloc(&c->dev_mem, total) != hipSuccess) {
+    delete c;
+    return fail(TQ_ENOMEM, "tq_create: hipMalloc of %zu bytes failed", total);
+  }
+  char* base = (char*)c->dev_mem;
+  bool ok = hipMemcpy(base, rh.data(), b_rimg, hipMemcpyHostToDevice) == hipSuccess &&
+            hipMemcpy(base + off_rl, rl.data(), b_rimg, hipMemcpyHostToDevice) == hipSuccess &&
+            hipMemcpy(base + off_sh, sh.data(), b_simg, hipMemcpyHostToDevice) == hipSuccess &&
+            hipMemcpy(base + off_sl, sl.data(), b_simg, hipMemcpyHostToDevice) == hipSuccess &&
+            hipMemcpy(base + off_r32, r32.data(), r32.size() * 4, hipMemcpyHostToDevice) == hipSuccess &&
+            hipMemcpy(base + off_s32, s32.data(), s32.size() * 4, hipMemcpyHostToDevice) == hipSuccess;
+  if (!ok) {
+    (void)hipFree(c->dev_mem);
+    delete c;
+    return fail(TQ_EDEVICE, "tq_create: hipMemcpy failed");
+  }
+  c->mats.r_hi = (const uint16_t*)base;
+  c->mats.r_lo = (const uint16_t*)(base + off_rl);
+  c->mats.s_hi = (const uint16_t*)(base + off_sh);
+  c->mats.s_lo = (const uint16_t*)(base + off_sl);
+  c->mats.r32 = (const float*)(base + off_r32);
+  c->mats.s32 = (const float*)(base + off_s32);
+  for (int b = 0; b < 5; ++b) c->loaded[b] = false;
+  *out = c;
+  return TQ_OK;
+}
+
+int tq_destroy(tq_ctx* ctx) {
+  clear_error();
+  if (!ctx) return TQ_OK;
+  int rc = TQ_OK;
+  if (ctx->dev_mem && hipFree(ctx->dev_mem) != hipSuccess) rc = fail(TQ_EDEVICE, "tq_destroy: hipFree failed");
+  delete ctx;
+  return rc;
+}
+
+int tq_codebook_load(tq_ctx* ctx, int32_t bits, const double* centroids, const double* boundaries) {
+  clear_error();
+  if (!ctx) return fail(TQ_EINVAL, "tq_codebook_load: ctx is NULL");
+  if (bits < 1 || bits > 4) return fail(TQ_EINVAL, "tq_codebook_load: bits %d not in 1..4", bits);
+  if (!centroids || !boundaries) return fail(TQ_EINVAL, "tq_codebook_load: NULL table");
+  const int L = 1 << bits;
+  for (int i = 0; i < L; ++i) {
+    if (!std::isfinite(centroids[i])) return fail(TQ_EINVAL, "tq_codebook_load: non-finite centroid %d", i);
+    if (i && !(centroids[i] > centroids[i - 1])) return fail(TQ_EINVAL, "tq_codebook_load: centroids not ascending");
+    if (std::fabs(centroids[i]) > 60000.0) return fail(TQ_EINVAL, "tq_codebook_load: centroid out of fp16 range");
+  }
+  for (int i = 0; i < L - 1; ++i) {
+    if (!std::isfinite(boundaries[i])) return fail(TQ_EINVAL, "tq_codebook_load: non-finite boundary %d", i);
+    if (!(boundaries[i] > centroids[i] && boundaries[i] < centroids[i + 1]))
+      return fail(TQ_EINVAL, "tq_codebook_load: boundary %d not between its centroids", i);
+  }
+  CodebookDev cb;
+  std::memset(&cb, 0, sizeof(cb));
+  for (int i = 0; i < 16; ++i) {
+    cb.beta[i] = i < L - 1 ? (float)boundaries[i] : INFINITY;
+    cb.cent[i] = i < L ? (float)centroids[i] : 0.f;
+    const uint16_t h = i < L ? to_half_bits((float)centroids[i]) : 0;
+    cb.tlo[i / 4] |= (uint32_t)(h & 0xFF) << (8 * (i % 4));
+    cb.thi[i / 4] |= (uint32_t)(h >> 8) << (8 * (i % 4));
+  }
+  ctx->cb[bits] = cb;
+  ctx->loaded[bits] = true;
+  return TQ_OK;
+}
+
+static int check_cache(const tq_ctx* ctx, const tq_cache_view* cache, const char* fn) {
+  if (!ctx) return fail(TQ_EINVAL, "%s: ctx is NULL", fn);
+  if (!cache) return fail(TQ_EINVAL, "%s: cache is NULL", fn);
+  if (cache->n_seq < 1) return fail(TQ_EINVAL, "%s: n_seq %d < 1", fn, cache->n_seq);
+  if (cache->capacity < kBlockTokens || cache->capacity % kBlockTokens)
+    return fail(TQ_EINVAL, "%s: capacity %lld is not a positive multiple of 128", fn, (long long)cache->capacity);
+  if (!cache->key_records || !cache->value_blocks) return fail(TQ_EINVAL, "%s: NULL cache buffer", fn);
+  if (!aligned16(cache->key_records) || !aligned16(cache->value_blocks))
+    return fail(TQ_EINVAL, "%s: cache buffers must be 16-byte aligned", fn);
+  return TQ_OK;
+}
+
+static int append_common(tq_ctx* ctx, const tq_cache_view* cache, const void* x, int32_t dtype, int64_t pos,
+                         int64_t n_new, int bits, const char* fn) {
+  int rc = check_cache(ctx, cache, fn);
+  if (rc) return rc;
+  if (dtype != TQ_F16 && dtype != TQ_F32) return fail(TQ_EINVAL, "%s: dtype %d", fn, dtype);
+  if (n_new < 0) return fail(TQ_EINVAL, "%s: n_new %lld < 0", fn, (long long)n_new);
+  if (pos < 0 || pos > cache->capacity || n_new > cache->capacity - pos)
+    return fail(TQ_ECAPACITY, "%s: tokens [%lld, %lld) exceed capacity %lld", fn, (long long)pos,
+                (long long)(pos + n_new), (long long)cache->capacity);
+  if (n_new > 0 && !x) return fail(TQ_EINVAL, "%s: input is NULL", fn);
+  if (n_new > 0 && !aligned16(x)) return fail(TQ_EINVAL, "%s: input must be 16-byte aligned", fn);
+  if (!ctx->loaded[bits]) return fail(TQ_ENOCODEBOOK, "%s: no %d-bit codebook loaded", fn, bits);
+  return TQ_OK;
+}
+
+int tq_append_key(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_t dtype, int64_t pos,
+                  int64_t n_new, void* stream) {
+  clear_error();
+  int rc = append_common(ctx, cache, k, dtype, pos, n_new, ctx ? ctx->cfg.key_bits : 1, "tq_append_key");
+  if (rc) return rc;
+  if (n_new == 0) return TQ_OK;
+  AppendShape s{k, dtype, n_new, pos, cache->capacity, cache->n_seq};
+  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_append_key: hipSetDevice failed");
+  rc = launch_compress_keys(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.proj_dim, s,
+                            cache->key_records, stream);
+  return rc ? fail(rc, "tq_append_key: launch failed (%d)", rc) : TQ_OK;
+}
+
+int tq_append_value(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int32_t dtype, int64_t pos,
+                    int64_t n_new, void* stream) {
+  clear_error();
+  int rc = append_common(ctx, cache, v, dtype, pos, n_new, ctx ? ctx->cfg.value_bits : 1, "tq_append_value");
+  if (rc) return rc;
+  if (n_new == 0) return TQ_OK;
+  AppendShape s{v, dtype, n_new, pos, cache->capacity, cache->n_seq};
+  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_append_value: hipSetDevice failed");
+  rc = launch_compress_values(ctx->mats, ctx->cb[ctx->cfg.value_bits], ctx->cfg.value_bits, s,
+                              cache->value_blocks, stream);
+  return rc ? fail(rc, "tq_append_value: launch failed (%d)", rc) : TQ_OK;
+}
+
+static int attn_common(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
+                       int64_t n_tokens, const void* outp, void* ws, size_t ws_bytes, bool need_values,
+                       const char* fn, AttnPlan* plan) {
+  int rc = check_cache(ctx, cache, fn);
+  if (rc) return rc;
+  if (dtype != TQ_F16 && dtype != TQ_F32) return fail(TQ_EINVAL, "%s: dtype %d", fn, dtype);
+  if (G < 1 || G > 16) return fail(TQ_EINVAL, "%s: G %d not in 1..16", fn, G);
+  if (n_tokens < 1 || n_tokens > cache->capacity)
+    return fail(TQ_EINVAL, "%s: n_tokens %lld not in [1, capacity]", fn, (long long)n_tokens);
+  if (!q || !outp || !ws) return fail(TQ_EINVAL, "%s: NULL q, output or workspace", fn);
+  if (!aligned16(q) || !aligned16(outp) || !aligned16(ws))
+    return fail(TQ_EINVAL, "%s: q, output and workspace must be 16-byte aligned", fn);
+  if (!ctx->loaded[ctx->cfg.key_bits])
+    return fail(TQ_ENOCODEBOOK, "%s: no %d-bit key codebook loaded", fn, ctx->cfg.key_bits);
+  if (need_values && !ctx->loaded[ctx->cfg.value_bits])
+    return fail(TQ_ENOCODEBOOK, "%s: no %d-bit value codebook loaded", fn, ctx->cfg.value_bits);
+  *plan = plan_attention(ctx->cfg.proj_dim, cache->n_seq, G, n_tokens);
+  if (ws_bytes < plan->total)
+    return fail(TQ_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, plan->total);
+  return TQ_OK;
+}
+
+int tq_attention_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
+                        int64_t n_tokens, float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  AttnPlan plan;
+  int rc = attn_common(ctx, cache, q, dtype, G, n_tokens, scores, workspace, workspace_bytes, false,
+                       "tq_attention_scores", &plan);
+  if (rc) return rc;
+  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_attention_scores: hipSetDevice");
+  AttnShape s{q, dtype, G, n_tokens, cache->capacity, cache->n_seq};
+  rc = launch_prep_queries(ctx->mats, ctx->cfg.proj_dim, s, workspace, plan, stream);
+  if (!rc)
+    rc = launch_scores(ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.proj_dim, s, cache->key_records,
+                       scores, workspace, plan, stream);
+  return rc ? fail(rc, "tq_attention_scores: launch failed (%d)", rc) : TQ_OK;
+}
+
+int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G, int64_t n_tokens,
+              float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  AttnPlan plan;
+  int rc = attn_common(ctx, cache, q, dtype, G, n_tokens, out, workspace, workspace_bytes, true, "tq_attend",
+                       &plan);
+  if (rc) return rc;
+  if (!std::isfinite(scale)) return fail(TQ_EINVAL, "tq_attend: scale is not finite");
+  if (scale <= 0.f) scale = 1.f / std::sqrt((float)ctx->cfg.head_dim);
+  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_attend: hipSetDevice");
+  AttnShape s{q, dtype, G, n_tokens, cache->capacity, cache->n_seq};
+  rc = launch_prep_queries(ctx->mats, ctx->cfg.proj_dim, s, workspace, plan, stream);
+  if (!rc)
+    rc = launch_attend(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cb[ctx->cfg.value_bits],
+                       ctx->cfg.value_bits, ctx->cfg.proj_dim, s, cache->key_records, cache->value_blocks, scale,
+                       out, workspace, plan, stream);
+  return rc ? fail(rc, "tq_attend: launch failed (%d)", rc) : TQ_OK;
+}
+
+}  // extern "C"

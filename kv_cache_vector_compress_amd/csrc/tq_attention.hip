@@ -1,0 +1,561 @@
+// Attention over the packed cache on gfx950, head_dim 128.
+//
+// Scores (asymmetric_attention_scores, nav.superapi.store "turboquant-pytorch"
+// 常见使用模式; the QJL stage makes the inner-product estimate unbiased,
+// atskills.one Stage 2):
+//     est = ||k|| ( <q~, c[idx]> + gamma sqrt(pi/2)/m <p, 2s-1> ),
+//     q~ = R q, p = S q~.
+// Both inner products run on the matrix cores in one accumulator: the packed
+// key is decoded into an fp16 operand (centroids c[idx] for the first part,
+// +-gamma sqrt(pi/2)/m for the second) and multiplied by the prepared query
+// operand (q~ and p in fp16, scaled to unit query norm).  Decoding is byte
+// permutes from an 8/16-entry fp16 table held in registers.
+//
+// Attend (常见使用模式: softmax of the scores, then the weighted sum of the
+// decompressed values; values are stage-1 only, 算法细节): each wave streams a
+// range of 128-token blocks, keeps a running max / sum / accumulator per
+// query head (online softmax), and accumulates sum_t p_t ||v_t|| c[idx_t] in
+// the rotated domain with the matrix cores.  A second kernel merges the
+// per-wave partials (log-sum-exp) and applies R^T once per query head.
+#include "tq_device.h"
+
+namespace tq {
+
+constexpr int kPartFloats = 4 + kD;  // m, l, pad, pad, acc[d]
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int64_t kTargetWaves = 256 * 16;
+
+// ---------------------------------------------------------------------------
+// query preparation: MFMA B operands of q~/|q| and p/|q|, and |q|
+// ---------------------------------------------------------------------------
+
+struct PrepArgs {
+  const void* q;
+  int dtype, G, n_seq;
+  const float* r32;
+  const float* s32;
+  uint16_t* wq;   // [n_seq][KBT][64 lanes][8] fp16
+  float* wqn;     // [n_seq][16]
+};
+
+template <int M>
+__global__ __launch_bounds__(256) void prep_queries_kernel(const PrepArgs a) {
+  constexpr int KBT = 4 + M / 32;
+  __shared__ float qs[16][kD];
+  __shared__ float qt[16][kD];
+  __shared__ float pp[16][M];
+  __shared__ float qn[16];
+  const int slot = blockIdx.x, tid = threadIdx.x;
+  for (int idx = tid; idx < 16 * kD; idx += blockDim.x) {
+    const int h = idx / kD, k = idx % kD;
+    float v = 0.f;
+    if (h < a.G) {
+      const int64_t off = ((int64_t)slot * a.G + h) * kD + k;
+      v = a.dtype == TQ_F32 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
+    }
+    qs[h][k] = v;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 16 * kD; idx += blockDim.x) {
+    const int h = idx / kD, j = idx % kD;
+    float s = 0.f;
+    if (h < a.G)
+      for (int k = 0; k < kD; ++k) s = fmaf(a.r32[j * kD + k], qs[h][k], s);
+    qt[h][j] = s;
+  }
+  if (tid < 16) {
+    float s = 0.f;
+    for (int k = 0; k < kD; ++k) s = fmaf(qs[tid][k], qs[tid][k], s);
+    qn[tid] = sqrtf(s);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 16 * M; idx += blockDim.x) {
+    const int h = idx / M, i = idx % M;
+    float s = 0.f;
+    if (h < a.G)
+      for (int j = 0; j < kD; ++j) s = fmaf(a.s32[i * kD + j], qt[h][j], s);
+    pp[h][i] = s;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < KBT * 64; idx += blockDim.x) {
+    const int kb = idx / 64, l = idx % 64, h = l % 16, qq = l / 16;
+    const float inv = qn[h] > 0.f ? 1.f / qn[h] : 0.f;
+    h8 v;
+    if (kb < 4) {
+      // centroid part, k slot e <-> coordinate 16 (2 kb + e/4) + 4 qq + e%4
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)(qt[h][16 * (2 * kb + e / 4) + 4 * qq + e % 4] * inv);
+    } else {
+      // sign part, k slot 2e+half <-> sign bit p + 16 half of word 2 (kbp/2) + qq/2,
+      // p = 8 (qq%2) + 4 (kbp%2) + e; that bit holds projection coordinate
+      // 16 t + 4 qs + i with qs = 2 (qq/2) + half, t = 4 (kbp/2) + p/4, i = p%4
+      const int kbp = kb - 4;
+      for (int e = 0; e < 4; ++e)
+        for (int half = 0; half < 2; ++half) {
+          const int p = 8 * (qq % 2) + 4 * (kbp % 2) + e;
+          const int qsg = 2 * (qq / 2) + half;
+          const int t = 4 * (kbp / 2) + p / 4;
+          v[2 * e + half] = (_Float16)(pp[h][16 * t + 4 * qsg + p % 4] * inv);
+        }
+    }
+    *(h8*)(a.wq + (((int64_t)slot * KBT + kb) * 64 + l) * 8) = v;
+  }
+  if (tid < 16) a.wqn[slot * 16 + tid] = qn[tid];
+}
+
+// ---------------------------------------------------------------------------
+// shared pieces of the score computation
+// ---------------------------------------------------------------------------
+
+template <int B, int M>
+struct KeyTile {
+  uint32_t cw[B];
+  uint32_t sw[M / 64];
+  float n, g;
+};
+
+template <int B, int M>
+__device__ __forceinline__ void load_key(KeyTile<B, M>& k, const uint32_t* rp, bool valid, int q, int rec_words) {
+#pragma unroll
+  for (int w = 0; w < B; ++w) k.cw[w] = valid ? rp[q * B + w] : 0u;
+#pragma unroll
+  for (int c = 0; c < M / 64; ++c) k.sw[c] = valid ? rp[4 * B + 2 * c + (q >> 1)] : 0u;
+  k.n = valid ? __uint_as_float(rp[rec_words - 2]) : 0.f;
+  k.g = valid ? __uint_as_float(rp[rec_words - 1]) : 0.f;
+}
+
+// acc[i] = (unscaled, unnormalised) score of token row 4q+i of the tile for
+// query head (lane % 16).  est = acc * ||k|| * ||q||.
+template <int B, int M>
+__device__ __forceinline__ f4 key_tile_scores(const KeyTile<B, M>& k, const h8 (&qb)[4 + M / 32],
+                                              const uint32_t (&tlo)[4], const uint32_t (&thi)[4], float kappa,
+                                              int sh0) {
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  acc = mfma(decode_pair<B, 0>(k.cw, tlo, thi), qb[0], acc);
+  acc = mfma(decode_pair<B, 2>(k.cw, tlo, thi), qb[1], acc);
+  acc = mfma(decode_pair<B, 4>(k.cw, tlo, thi), qb[2], acc);
+  acc = mfma(decode_pair<B, 6>(k.cw, tlo, thi), qb[3], acc);
+  const _Float16 gk = (_Float16)(k.g * kappa);
+  const uint32_t gk2 = (uint32_t)__builtin_bit_cast(uint16_t, gk) * 0x00010001u;
+#pragma unroll
+  for (int kbp = 0; kbp < M / 32; ++kbp) {
+    const uint32_t w = ~k.sw[kbp / 2];
+    u4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t sh = w << (sh0 - 4 * (kbp % 2) - e);  // bits p, p+16 -> 15, 31
+      v[e] = (sh & 0x80008000u) | (gk2 & 0x7FFF7FFFu);
+    }
+    acc = mfma(as_h8(v), qb[4 + kbp], acc);
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// scores
+// ---------------------------------------------------------------------------
+
+struct ScoreArgs {
+  const uint32_t* rec;
+  float* scores;
+  const uint16_t* wq;
+  const float* wqn;
+  int64_t n_tokens, capacity;
+  int n_seq, G, rec_words;
+  int tiles_per_wave, waves_per_slot;
+  float kappa;
+  uint32_t tlo[4], thi[4];
+};
+
+template <int B, int M>
+__global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
+  constexpr int KBT = 4 + M / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  const int slot = (int)(gw / a.waves_per_slot);
+  if (slot >= a.n_seq) return;
+  const int wc = (int)(gw - (int64_t)slot * a.waves_per_slot);
+  h8 qb[KBT];
+#pragma unroll
+  for (int kb = 0; kb < KBT; ++kb) qb[kb] = *(const h8*)(a.wq + (((int64_t)slot * KBT + kb) * 64 + lane) * 8);
+  const float qn = a.wqn[slot * 16 + r16];
+  uint32_t tlo[4], thi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; }
+  const int sh0 = 15 - 8 * (q & 1);
+  const int64_t ntile = (a.n_tokens + 15) / 16;
+  const int64_t t_begin = (int64_t)wc * a.tiles_per_wave;
+  const int64_t t_end = min(ntile, t_begin + a.tiles_per_wave);
+  const uint32_t* base = a.rec + (int64_t)slot * a.capacity * a.rec_words;
+  float* out = a.scores + ((int64_t)slot * a.G + r16) * a.n_tokens;
+
+  KeyTile<B, M> cur;
+  if (t_begin < t_end) {
+    const int64_t t = t_begin * 16 + r16;
+    load_key<B, M>(cur, base + t * a.rec_words, t < a.n_tokens, q, a.rec_words);
+  }
+  for (int64_t tile = t_begin; tile < t_end; ++tile) {
+    KeyTile<B, M> nxt;
+    if (tile + 1 < t_end) {
+      const int64_t t = (tile + 1) * 16 + r16;
+      load_key<B, M>(nxt, base + t * a.rec_words, t < a.n_tokens, q, a.rec_words);
+    }
+    const f4 acc = key_tile_scores<B, M>(cur, qb, tlo, thi, a.kappa, sh0);
+    float nk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nk[i] = __shfl(cur.n, 4 * q + i, 64);  // ||k|| of token row 4q+i
+    if (r16 < a.G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t tok = tile * 16 + 4 * q + i;
+        if (tok < a.n_tokens) out[tok] = acc[i] * nk[i] * qn;
+      }
+    }
+    cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attend: per-wave partials
+// ---------------------------------------------------------------------------
+
+struct AttendArgs {
+  const uint32_t* rec;
+  const uint32_t* vblocks;
+  float* part;        // [n_seq][waves_per_slot][G][kPartFloats]
+  const uint16_t* wq;
+  const float* wqn;
+  int64_t n_tokens, capacity;
+  int n_seq, G, rec_words, block_words;
+  int blocks_per_wave, waves_per_slot;
+  float kappa, scale2;  // scale * log2(e)
+  uint32_t tlo[4], thi[4];    // key centroid tables
+  uint32_t vtlo[4], vthi[4];  // value centroid tables
+};
+
+template <int BK, int BV, int M>
+__global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
+  constexpr int KBT = 4 + M / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  const int slot = (int)(gw / a.waves_per_slot);
+  if (slot >= a.n_seq) return;
+  const int wc = (int)(gw - (int64_t)slot * a.waves_per_slot);
+
+  h8 qb[KBT];
+#pragma unroll
+  for (int kb = 0; kb < KBT; ++kb) qb[kb] = *(const h8*)(a.wq + (((int64_t)slot * KBT + kb) * 64 + lane) * 8);
+  const float qsc = a.wqn[slot * 16 + r16] * a.scale2;
+  uint32_t tlo[4], thi[4], vtlo[4], vthi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; vtlo[i] = a.vtlo[i]; vthi[i] = a.vthi[i];
+  }
+  const int sh0 = 15 - 8 * (q & 1);
+  const int64_t nblk = (a.n_tokens + kBlockTokens - 1) / kBlockTokens;
+  const int64_t b_begin = (int64_t)wc * a.blocks_per_wave;
+  const int64_t b_end = min(nblk, b_begin + a.blocks_per_wave);
+  const int64_t nblk_cap = a.capacity / kBlockTokens;
+  const uint32_t* kbase = a.rec + (int64_t)slot * a.capacity * a.rec_words;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  int ve = -1000;  // running value-norm exponent (wave-uniform)
+  f4 acc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t blk = b_begin; blk < b_end; ++blk) {
+    const int64_t tok0 = blk * kBlockTokens;
+    const uint32_t* vb = a.vblocks + ((int64_t)slot * nblk_cap + blk) * a.block_words;
+    const float* vnorm = (const float*)(vb + 4 * BV * kD);
+    uint32_t vw[8][BV];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int w = 0; w < BV; ++w) vw[nt][w] = vb[(w * 4 + q) * kD + 16 * nt + r16];
+    // block maximum of the value norms (tokens past n_tokens count as 0):
+    // lane l looks at tokens 2l, 2l+1, then a wave-wide max
+    float bmax;
+    {
+      const float2 v2 = *(const float2*)(vnorm + 2 * lane);
+      const bool ok0 = tok0 + 2 * lane < a.n_tokens, ok1 = tok0 + 2 * lane + 1 < a.n_tokens;
+      bmax = fmaxf(ok0 ? v2.x : 0.f, ok1 ? v2.y : 0.f);
+#pragma unroll
+      for (int sh = 1; sh < 64; sh <<= 1) bmax = fmaxf(bmax, shfl_xor(bmax, sh));
+    }
+    int e_blk = 0;
+    frexpf(bmax, &e_blk);
+    if (e_blk > ve) {  // wave-uniform: rescale the accumulator to the new exponent
+      const float f = ldexpf(1.f, ve - e_blk);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[nt] *= f;
+      ve = e_blk;
+    }
+    const float vs = ldexpf(1.f, -ve);
+
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      // scores of the two 16-token tiles of this step
+      f4 sc[2];
+      float nk[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t t = tok0 + 16 * (2 * step + u) + r16;
+        KeyTile<BK, M> kt;
+        load_key<BK, M>(kt, kbase + t * a.rec_words, t < a.n_tokens, q, a.rec_words);
+        sc[u] = key_tile_scores<BK, M>(kt, qb, tlo, thi, a.kappa, sh0);
+        nk[u] = kt.n;
+      }
+      float lg[2][4];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float n = __shfl(nk[u], 4 * q + i, 64);
+          const bool ok = tok0 + 16 * (2 * step + u) + 4 * q + i < a.n_tokens;
+          lg[u][i] = ok ? sc[u][i] * n * qsc : -INFINITY;
+          cmax = fmaxf(cmax, lg[u][i]);
+        }
+      cmax = fmaxf(cmax, shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+      float psum = 0.f;
+      u4 pw;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // value norms of tokens 16 (2 step + u) + 4 q + i, masked past n_tokens
+        const f4 vnv = *(const f4*)(vnorm + 16 * (2 * step + u) + 4 * q);
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          float pv[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int i = 2 * i2 + k;
+            const bool ok = tok0 + 16 * (2 * step + u) + 4 * q + i < a.n_tokens;
+            const float p = m_new == -INFINITY ? 0.f : exp2f(lg[u][i] - m_new);
+            psum += p;
+            pv[k] = ok ? p * (vnv[i] * vs) : 0.f;
+          }
+          const _Float16 h0 = (_Float16)pv[0], h1 = (_Float16)pv[1];
+          pw[2 * u + i2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        }
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      const h8 P = as_h8(pw);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        acc[nt] *= alpha;
+        h8 A;
+        if (step == 0) A = decode_pair<BV, 0>(vw[nt], vtlo, vthi);
+        if (step == 1) A = decode_pair<BV, 2>(vw[nt], vtlo, vthi);
+        if (step == 2) A = decode_pair<BV, 4>(vw[nt], vtlo, vthi);
+        if (step == 3) A = decode_pair<BV, 6>(vw[nt], vtlo, vthi);
+        acc[nt] = mfma(A, P, acc[nt]);
+      }
+    }
+  }
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  if (r16 < a.G) {
+    float* pr = a.part + (((int64_t)slot * a.waves_per_slot + wc) * a.G + r16) * kPartFloats;
+    const float f = ldexpf(1.f, ve);
+    if (q == 0) {
+      pr[0] = m_run;
+      pr[1] = l_run;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) *(f4*)(pr + 4 + 16 * nt + 4 * q) = acc[nt] * f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine partials, rotate back: out = R^T (sum_c w_c acc_c / sum_c w_c l_c)
+// ---------------------------------------------------------------------------
+
+struct CombineArgs {
+  const float* part;
+  float* out;
+  const float* r32;
+  int n_seq, G, waves_per_slot;
+};
+
+__global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
+  __shared__ float y[kD];
+  const int sh = blockIdx.x, slot = sh / a.G, h = sh % a.G, j = threadIdx.x;
+  const float* pr = a.part + ((int64_t)slot * a.waves_per_slot * a.G + h) * kPartFloats;
+  const int64_t stride = (int64_t)a.G * kPartFloats;
+  float M = -INFINITY;
+  for (int c = 0; c < a.waves_per_slot; ++c) M = fmaxf(M, pr[c * stride]);
+  float L = 0.f, acc = 0.f;
+  for (int c = 0; c < a.waves_per_slot; ++c) {
+    const float mc = pr[c * stride];
+    const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
+    L = fmaf(w, pr[c * stride + 1], L);
+    acc = fmaf(w, pr[c * stride + 4 + j], acc);
+  }
+  y[j] = acc / L;
+  __syncthreads();
+  float o = 0.f;
+  for (int i = 0; i < kD; ++i) o = fmaf(a.r32[i * kD + j], y[i], o);
+  a.out[((int64_t)slot * a.G + h) * kD + j] = o;
+}
+
+// ---------------------------------------------------------------------------
+// plans and launchers
+// ---------------------------------------------------------------------------
+
+static int g_cus = 256;
+
+int attention_device_init() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&g_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return 0;
+}
+
+AttnPlan plan_attention(int m, int n_seq, int G, int64_t n_tokens) {
+  AttnPlan p;
+  const int KBT = 4 + m / 32;
+  const int64_t nblk = (n_tokens + kBlockTokens - 1) / kBlockTokens;
+  // about 16 waves per compute unit of a 256-CU MI355X over the whole grid;
+  // fixed so that the workspace size does not depend on the device
+  const int64_t target_waves = kTargetWaves;
+  int64_t bpw = (nblk * n_seq + target_waves - 1) / target_waves;
+  if (bpw < 1) bpw = 1;
+  p.blocks_per_wave = (int)bpw;
+  p.waves_per_slot = (int)((nblk + bpw - 1) / bpw);
+  p.q_bytes = (size_t)n_seq * KBT * 64 * 8 * 2;
+  p.qn_bytes = (size_t)n_seq * 16 * 4;
+  p.part_bytes = (size_t)n_seq * p.waves_per_slot * G * kPartFloats * 4;
+  p.total = ((p.q_bytes + 255) / 256 + (p.qn_bytes + 255) / 256 + (p.part_bytes + 255) / 256) * 256;
+  return p;
+}
+
+struct WsPtrs {
+  uint16_t* wq;
+  float* wqn;
+  float* part;
+};
+static WsPtrs ws_ptrs(void* ws, const AttnPlan& p) {
+  char* b = (char*)ws;
+  WsPtrs w;
+  w.wq = (uint16_t*)b;
+  b += (p.q_bytes + 255) / 256 * 256;
+  w.wqn = (float*)b;
+  b += (p.qn_bytes + 255) / 256 * 256;
+  w.part = (float*)b;
+  return w;
+}
+
+int launch_prep_queries(const Matrices& mats, int m, const AttnShape& s, void* ws, const AttnPlan& p,
+                        void* stream) {
+  PrepArgs a;
+  const WsPtrs w = ws_ptrs(ws, p);
+  a.q = s.q;
+  a.dtype = s.dtype;
+  a.G = s.G;
+  a.n_seq = s.n_seq;
+  a.r32 = mats.r32;
+  a.s32 = mats.s32;
+  a.wq = w.wq;
+  a.wqn = w.wqn;
+  hipStream_t st = (hipStream_t)stream;
+  if (m == 64) hipLaunchKernelGGL(prep_queries_kernel<64>, dim3(s.n_seq), dim3(256), 0, st, a);
+  else if (m == 128) hipLaunchKernelGGL(prep_queries_kernel<128>, dim3(s.n_seq), dim3(256), 0, st, a);
+  else return TQ_EUNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+}
+
+static void fill_tables(const CodebookDev& cb, uint32_t* tlo, uint32_t* thi) {
+  for (int i = 0; i < 4; ++i) { tlo[i] = cb.tlo[i]; thi[i] = cb.thi[i]; }
+}
+
+int launch_scores(const CodebookDev& cbk, int kbits, int m, const AttnShape& s, const void* key_records,
+                  float* scores, void* ws, const AttnPlan& p, void* stream) {
+  ScoreArgs a;
+  const WsPtrs w = ws_ptrs(ws, p);
+  a.rec = (const uint32_t*)key_records;
+  a.scores = scores;
+  a.wq = w.wq;
+  a.wqn = w.wqn;
+  a.n_tokens = s.n_tokens;
+  a.capacity = s.capacity;
+  a.n_seq = s.n_seq;
+  a.G = s.G;
+  a.rec_words = kbits * kD / 32 + m / 32 + 2;
+  const int64_t ntile = (s.n_tokens + 15) / 16;
+  const int64_t target_waves = kTargetWaves;
+  int64_t tpw = (ntile * s.n_seq + target_waves - 1) / target_waves;
+  if (tpw < 1) tpw = 1;
+  a.tiles_per_wave = (int)tpw;
+  a.waves_per_slot = (int)((ntile + tpw - 1) / tpw);
+  a.kappa = (float)(1.2533141373155002512 / m);  // sqrt(pi/2) / m
+  fill_tables(cbk, a.tlo, a.thi);
+  const int64_t waves = (int64_t)a.waves_per_slot * s.n_seq;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  hipStream_t st = (hipStream_t)stream;
+#define TQ_SC(B, M) \
+  if (kbits == B && m == M) { hipLaunchKernelGGL((scores_kernel<B, M>), grid, block, 0, st, a); goto done; }
+  TQ_SC(1, 64) TQ_SC(2, 64) TQ_SC(3, 64) TQ_SC(4, 64)
+  TQ_SC(1, 128) TQ_SC(2, 128) TQ_SC(3, 128) TQ_SC(4, 128)
+#undef TQ_SC
+  return TQ_EUNSUPPORTED;
+done:
+  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+}
+
+int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
+                  int m, const AttnShape& s, const void* key_records, const void* value_blocks, float scale,
+                  float* out, void* ws, const AttnPlan& p, void* stream) {
+  AttendArgs a;
+  const WsPtrs w = ws_ptrs(ws, p);
+  a.rec = (const uint32_t*)key_records;
+  a.vblocks = (const uint32_t*)value_blocks;
+  a.part = w.part;
+  a.wq = w.wq;
+  a.wqn = w.wqn;
+  a.n_tokens = s.n_tokens;
+  a.capacity = s.capacity;
+  a.n_seq = s.n_seq;
+  a.G = s.G;
+  a.rec_words = kbits * kD / 32 + m / 32 + 2;
+  a.block_words = 4 * vbits * kD + kBlockTokens;
+  a.blocks_per_wave = p.blocks_per_wave;
+  a.waves_per_slot = p.waves_per_slot;
+  a.kappa = (float)(1.2533141373155002512 / m);
+  a.scale2 = scale * kLog2e;
+  fill_tables(cbk, a.tlo, a.thi);
+  fill_tables(cbv, a.vtlo, a.vthi);
+  const int64_t waves = (int64_t)a.waves_per_slot * s.n_seq;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  hipStream_t st = (hipStream_t)stream;
+  bool launched = false;
+#define TQ_AT(BK, BV, M)                                                                   \
+  if (!launched && kbits == BK && vbits == BV && m == M) {                                 \
+    hipLaunchKernelGGL((attend_kernel<BK, BV, M>), grid, block, 0, st, a);                 \
+    launched = true;                                                                       \
+  }
+#define TQ_AT_V(BK, M) TQ_AT(BK, 1, M) TQ_AT(BK, 2, M) TQ_AT(BK, 3, M) TQ_AT(BK, 4, M)
+  TQ_AT_V(1, 64) TQ_AT_V(2, 64) TQ_AT_V(3, 64) TQ_AT_V(4, 64)
+  TQ_AT_V(1, 128) TQ_AT_V(2, 128) TQ_AT_V(3, 128) TQ_AT_V(4, 128)
+#undef TQ_AT_V
+#undef TQ_AT
+  if (!launched) return TQ_EUNSUPPORTED;
+  if (hipGetLastError() != hipSuccess) return TQ_EDEVICE;
+  CombineArgs c;
+  c.part = w.part;
+  c.out = out;
+  c.r32 = mats.r32;
+  c.n_seq = s.n_seq;
+  c.G = s.G;
+  c.waves_per_slot = p.waves_per_slot;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(s.n_seq * s.G)), dim3(kD), 0, st, c);
+  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+}
+
+}  // namespace tq

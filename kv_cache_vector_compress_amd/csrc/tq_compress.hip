@@ -1,0 +1,564 @@
+// Compression kernels for gfx950: keys (stage 1 + stage 2) and values
+// (stage 1), head_dim 128.
+//
+// Stage 1 (nav.superapi.store "turboquant-pytorch", 主要能力; atskills.one
+// "turboquant-pytorch", Stage 1): y = R k / ||k||, idx_j = #{i : beta_i < y_j}.
+// Stage 2, keys only (same sections, Stage 2 / 第二阶段; 算法细节: keys need
+// QJL, values do not): r = y - c[idx], gamma = ||r||, s = [S r >= 0].
+//
+// Arithmetic.  The codes must agree with an fp64 evaluation except within
+// ~1e-7 of a boundary, so the rotation cannot run in plain fp16/bf16 on the
+// matrix cores (a 2^-11 operand error moves y by ~2e-5).  R is split as
+// R * 2^8 = R_hi + R_lo with both halves fp16; an fp16 input k is exact, so
+// R k = (R_hi k + R_lo k) / 2^8 is two fp16 MFMAs with fp32 accumulation and
+// an error near 2^-22 relative.  fp32 inputs are split too (k = k_hi + k_lo,
+// three MFMAs).  The QJL projection of the fp32 residual uses the same
+// trick: S_hi r_hi + S_lo r_hi + S_hi r_lo.  Only its sign is stored, so the
+// power-of-two scalings never need undoing.
+//
+// Keys are rotated with output coordinates on the MFMA M axis and tokens on
+// N: a lane then owns one token and 32 of its coordinates (16 t + 4 q + i),
+// and packs them into the token's record without talking to other lanes.
+// Values are rotated with tokens on M: a lane owns one coordinate of 32
+// tokens of a 128-token block, which is the order the attention kernel
+// contracts them in.
+#include "tq_device.h"
+
+namespace tq {
+
+struct KeyArgs {
+  const void* x;
+  uint32_t* rec;
+  const uint16_t* r_hi;
+  const uint16_t* r_lo;
+  const uint16_t* s_hi;
+  const uint16_t* s_lo;
+  int64_t n_new, pos, capacity;
+  int n_seq;
+  int rec_words;
+  CodebookDev cb;
+};
+
+constexpr int kRImg = kD * kLdsStride;  // halves per R image
+
+template <int M>
+constexpr size_t key_lds_bytes() {
+  return (size_t)(2 * kRImg + 2 * M * kLdsStride) * 2 + 16 * sizeof(float);
+}
+
+__device__ __forceinline__ void copy_u4(uint16_t* dst, const uint16_t* src, int n_halves) {
+  const int n = n_halves / 8;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ((u4*)dst)[i] = ((const u4*)src)[i];
+}
+
+template <int B, int M, bool F32>
+__global__ __launch_bounds__(256, 1) void compress_keys_kernel(const KeyArgs a) {
+  constexpr int NT = F32 ? 2 : 4;  // 16-token N tiles per wave iteration
+  constexpr int PT = M / 16;       // projection M tiles
+  constexpr int NCH = M / 64;      // 16-bit sign chunks per lane
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint16_t* Rh = lds;
+  uint16_t* Rl = Rh + kRImg;
+  uint16_t* Sh = Rl + kRImg;
+  uint16_t* Sl = Sh + M * kLdsStride;
+  float* Cs = (float*)(Sl + M * kLdsStride);
+  copy_u4(Rh, a.r_hi, kRImg);
+  copy_u4(Rl, a.r_lo, kRImg);
+  copy_u4(Sh, a.s_hi, M * kLdsStride);
+  copy_u4(Sl, a.s_lo, M * kLdsStride);
+  if (threadIdx.x < 16) Cs[threadIdx.x] = a.cb.cent[threadIdx.x];
+  __syncthreads();
+
+  float beta[15];
+  load_beta(beta, a.cb);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t tps = (a.n_new + 16 * NT - 1) / (16 * NT);
+  const int64_t ntiles = tps * a.n_seq;
+  const int waves = blockDim.x >> 6;
+
+  for (int64_t tile = (int64_t)blockIdx.x * waves + wave; tile < ntiles; tile += (int64_t)gridDim.x * waves) {
+    const int slot = (int)(tile / tps);
+    const int64_t t0 = (tile - (int64_t)slot * tps) * (16 * NT);
+
+    h8 xh[NT][4];
+    h8 xl[F32 ? NT : 1][4];
+    float nrm[NT], inv[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t tok = t0 + 16 * j + r16;
+      const bool valid = tok < a.n_new;
+      float ss = 0.f;
+      if constexpr (F32) {
+        const float* src = (const float*)a.x + ((int64_t)slot * a.n_new + tok) * kD + 8 * q;
+        float v[4][8];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          f4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
+          if (valid) {
+            v0 = *(const f4*)(src + 32 * kb);
+            v1 = *(const f4*)(src + 32 * kb + 4);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { v[kb][e] = v0[e]; v[kb][4 + e] = v1[e]; }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf(v[kb][e], v[kb][e], ss);
+        }
+        ss += shfl_xor(ss, 16);
+        ss += shfl_xor(ss, 32);
+        const float n = sqrtf(ss);
+        int E = 0;
+        frexpf(n, &E);
+        const float sc = n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;  // |k * sc| < 2^13
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float s = v[kb][e] * sc;
+            const _Float16 h = (_Float16)s;
+            xh[j][kb][e] = h;
+            xl[j][kb][e] = (_Float16)(s - (float)h);
+          }
+        nrm[j] = n;
+        inv[j] = n > 0.f ? 1.f / (kRotScale * sc * n) : 0.f;
+      } else {
+        const _Float16* src = (const _Float16*)a.x + ((int64_t)slot * a.n_new + tok) * kD + 8 * q;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          h8 v = {};
+          if (valid) v = *(const h8*)(src + 32 * kb);
+          xh[j][kb] = v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf((float)v[e], (float)v[e], ss);
+        }
+        ss += shfl_xor(ss, 16);
+        ss += shfl_xor(ss, 32);
+        const float n = sqrtf(ss);
+        nrm[j] = n;
+        inv[j] = n > 0.f ? 1.f / (kRotScale * n) : 0.f;
+      }
+    }
+
+    f4 zacc[NT][PT];
+    uint32_t cw[NT][B];
+    float g2[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      g2[j] = 0.f;
+#pragma unroll
+      for (int w = 0; w < B; ++w) cw[j][w] = 0u;
+#pragma unroll
+      for (int p = 0; p < PT; ++p) zacc[j][p] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+
+#pragma unroll 1
+    for (int kb2 = 0; kb2 < 4; ++kb2) {  // output tiles 2 kb2, 2 kb2 + 1 = projection K block kb2
+      f4 yacc[NT][2];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) yacc[j][0] = yacc[j][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        h8 ah[2], al[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int off = (16 * (2 * kb2 + u) + r16) * kLdsStride + 32 * kb + 8 * q;
+          ah[u] = *(const h8*)(Rh + off);
+          al[u] = *(const h8*)(Rl + off);
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            yacc[j][u] = mfma(ah[u], xh[j][kb], yacc[j][u]);
+            yacc[j][u] = mfma(al[u], xh[j][kb], yacc[j][u]);
+            if constexpr (F32) yacc[j][u] = mfma(ah[u], xl[j][kb], yacc[j][u]);
+          }
+      }
+      // bucket, residual, pack; build the residual operand of the projection
+      h8 rh[NT], rl[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          uint32_t x4 = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float y = yacc[j][u][i] * inv[j];
+            const int idx = bucket<B>(y, beta);
+            const float r = y - Cs[idx];
+            g2[j] = fmaf(r, r, g2[j]);
+            x4 |= (uint32_t)idx << (8 * i);
+            const float rs = r * kResScale;
+            const _Float16 h = (_Float16)rs;
+            rh[j][4 * u + i] = h;
+            rl[j][4 * u + i] = (_Float16)(rs - (float)h);
+          }
+          put_sel4_rt<B>(cw[j], 2 * kb2 + u, x4);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < PT; ++p) {
+        const int off = (16 * p + r16) * kLdsStride + 32 * kb2 + 8 * q;
+        const h8 sh = *(const h8*)(Sh + off);
+        const h8 sl = *(const h8*)(Sl + off);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          zacc[j][p] = mfma(sh, rh[j], zacc[j][p]);
+          zacc[j][p] = mfma(sl, rh[j], zacc[j][p]);
+          zacc[j][p] = mfma(sh, rl[j], zacc[j][p]);
+        }
+      }
+    }
+
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      float g = g2[j];
+      g += shfl_xor(g, 16);
+      g += shfl_xor(g, 32);
+      const float gamma = sqrtf(g);
+      uint32_t bits[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v |= (zacc[j][4 * c + pp][i] >= 0.f ? 1u : 0u) << (4 * pp + i);
+        bits[c] = v;
+      }
+      const int64_t tok = t0 + 16 * j + r16;
+      if (tok < a.n_new) {
+        uint32_t* rp = a.rec + ((int64_t)slot * a.capacity + a.pos + tok) * a.rec_words;
+#pragma unroll
+        for (int w = 0; w < B; ++w) rp[q * B + w] = cw[j][w];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) ((uint16_t*)(rp + 4 * B + 2 * c + (q >> 1)))[q & 1] = (uint16_t)bits[c];
+        if (q == 0) rp[a.rec_words - 2] = __float_as_uint(nrm[j]);
+        if (q == 1) rp[a.rec_words - 1] = __float_as_uint(gamma);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// values
+// ---------------------------------------------------------------------------
+
+struct ValArgs {
+  const void* x;
+  uint32_t* blocks;
+  const uint16_t* r_hi;
+  const uint16_t* r_lo;
+  int64_t n_new, pos, capacity;
+  int64_t blk0, nblk;  // first touched block of a slot, blocks touched per slot
+  int n_seq;
+  int block_words;
+  CodebookDev cb;
+};
+
+constexpr size_t kValLds = (size_t)2 * kRImg * 2;
+
+// Field mask of (slot s, word w, byte lane i) for b-bit codes (runtime form).
+__device__ __forceinline__ uint32_t field_mask_rt(int b, int s, int w, int i) {
+  uint32_t m = 0;
+  if (b == 1) {
+    if (w == 0) m = 1u << s;
+  } else if (b == 2) {
+    if (w == s / 4) m = 3u << (2 * (s % 4));
+  } else if (b == 4) {
+    if (w == s / 2) m = 15u << (4 * (s % 2));
+  } else {
+    if (s < 6) {
+      if (w == s / 2) m = 7u << (3 * (s % 2));
+    } else if (s == 6) {
+      if (w == 0) m = 3u << 6;
+      if (w == 2) m = 1u << 6;
+    } else {
+      if (w == 1) m = 3u << 6;
+      if (w == 2) m = 1u << 7;
+    }
+  }
+  return m << (8 * i);
+}
+
+template <int B, bool F32>
+__global__ __launch_bounds__(256, 1) void compress_values_kernel(const ValArgs a) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint16_t* Rh = lds;
+  uint16_t* Rl = Rh + kRImg;
+  copy_u4(Rh, a.r_hi, kRImg);
+  copy_u4(Rl, a.r_lo, kRImg);
+  __syncthreads();
+
+  float beta[15];
+  load_beta(beta, a.cb);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int waves = blockDim.x >> 6;
+  const int64_t nitems = a.nblk * a.n_seq;
+  const int64_t nblk_cap = a.capacity / kBlockTokens;
+
+  for (int64_t item = (int64_t)blockIdx.x * waves + wave; item < nitems; item += (int64_t)gridDim.x * waves) {
+    const int slot = (int)(item / a.nblk);
+    const int64_t blk = a.blk0 + (item - (int64_t)slot * a.nblk);
+    const int64_t tok0 = blk * kBlockTokens;
+    uint32_t* vb = a.blocks + ((int64_t)slot * nblk_cap + blk) * a.block_words;
+    float* vnorm = (float*)(vb + 4 * B * kD);
+
+    uint32_t cw[8][B];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int w = 0; w < B; ++w) cw[nt][w] = 0u;
+
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      h8 xa[4][4];
+      h8 xl[F32 ? 4 : 1][4];
+      float inv_tok[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int tau = 16 * (4 * half + mt) + r16;
+        const int64_t row = tok0 + tau - a.pos;
+        const bool valid = row >= 0 && row < a.n_new;
+        float ss = 0.f;
+        if constexpr (F32) {
+          const float* src = (const float*)a.x + ((int64_t)slot * a.n_new + row) * kD + 8 * q;
+          float v[4][8];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            f4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
+            if (valid) {
+              v0 = *(const f4*)(src + 32 * kb);
+              v1 = *(const f4*)(src + 32 * kb + 4);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { v[kb][e] = v0[e]; v[kb][4 + e] = v1[e]; }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(v[kb][e], v[kb][e], ss);
+          }
+          ss += shfl_xor(ss, 16);
+          ss += shfl_xor(ss, 32);
+          const float n = sqrtf(ss);
+          int E = 0;
+          frexpf(n, &E);
+          const float sc = n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float s = v[kb][e] * sc;
+              const _Float16 h = (_Float16)s;
+              xa[mt][kb][e] = h;
+              xl[mt][kb][e] = (_Float16)(s - (float)h);
+            }
+          inv_tok[mt] = n > 0.f ? 1.f / (kRotScale * sc * n) : 0.f;
+          if (q == 0 && valid) vnorm[tau] = n;
+        } else {
+          const _Float16* src = (const _Float16*)a.x + ((int64_t)slot * a.n_new + row) * kD + 8 * q;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            h8 v = {};
+            if (valid) v = *(const h8*)(src + 32 * kb);
+            xa[mt][kb] = v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf((float)v[e], (float)v[e], ss);
+          }
+          ss += shfl_xor(ss, 16);
+          ss += shfl_xor(ss, 32);
+          const float n = sqrtf(ss);
+          inv_tok[mt] = n > 0.f ? 1.f / (kRotScale * n) : 0.f;
+          if (q == 0 && valid) vnorm[tau] = n;
+        }
+      }
+      // 1/||v|| in the output layout: lane (coordinate, q) holds tokens 4q+i
+      float inv_d[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) inv_d[mt][i] = __shfl(inv_tok[mt], 4 * q + i, 64);
+
+#pragma unroll
+      for (int ntp = 0; ntp < 4; ++ntp) {
+        f4 acc[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt][0] = acc[mt][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          h8 bh[2], bl[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int off = (16 * (2 * ntp + u) + r16) * kLdsStride + 32 * kb + 8 * q;
+            bh[u] = *(const h8*)(Rh + off);
+            bl[u] = *(const h8*)(Rl + off);
+          }
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              acc[mt][u] = mfma(xa[mt][kb], bh[u], acc[mt][u]);
+              acc[mt][u] = mfma(xa[mt][kb], bl[u], acc[mt][u]);
+              if constexpr (F32) acc[mt][u] = mfma(xl[mt][kb], bh[u], acc[mt][u]);
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            uint32_t x4 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float y = acc[mt][u][i] * inv_d[mt][i];
+              x4 |= (uint32_t)bucket<B>(y, beta) << (8 * i);
+            }
+            put_sel4_rt<B>(cw[2 * ntp + u], 4 * half + mt, x4);  // slot of these 16 tokens
+          }
+        // keep the scheduler from hoisting the next coordinate tiles' R loads
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    const bool full = tok0 >= a.pos && tok0 + kBlockTokens <= a.pos + a.n_new;
+    if (full) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int w = 0; w < B; ++w) vb[(w * 4 + q) * kD + 16 * nt + r16] = cw[nt][w];
+    } else {
+      // keep the codes of tokens outside [pos, pos + n_new)
+      uint32_t keep[B];
+#pragma unroll
+      for (int w = 0; w < B; ++w) keep[w] = 0u;
+      for (int s = 0; s < 8; ++s)
+        for (int i = 0; i < 4; ++i) {
+          const int64_t p = tok0 + 16 * s + 4 * q + i;
+          if (p < a.pos || p >= a.pos + a.n_new)
+#pragma unroll
+            for (int w = 0; w < B; ++w) keep[w] |= field_mask_rt(B, s, w, i);
+        }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int w = 0; w < B; ++w) {
+          uint32_t* dst = vb + (w * 4 + q) * kD + 16 * nt + r16;
+          *dst = (*dst & keep[w]) | (cw[nt][w] & ~keep[w]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+static int g_num_cus = 0;
+
+template <int B, int M, bool F32>
+static int set_key_attr() {
+  return hipFuncSetAttribute((const void*)compress_keys_kernel<B, M, F32>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)key_lds_bytes<M>()) == hipSuccess
+             ? 0 : -1;
+}
+
+template <int B, bool F32>
+static int set_val_attr() {
+  return hipFuncSetAttribute((const void*)compress_values_kernel<B, F32>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kValLds) == hipSuccess
+             ? 0 : -1;
+}
+
+int compress_device_init() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&g_num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  int rc = 0;
+#define TQ_KEY_ATTR(B)                                                                   \
+  rc |= set_key_attr<B, 64, false>() | set_key_attr<B, 64, true>() |                     \
+        set_key_attr<B, 128, false>() | set_key_attr<B, 128, true>();
+  TQ_KEY_ATTR(1) TQ_KEY_ATTR(2) TQ_KEY_ATTR(3) TQ_KEY_ATTR(4)
+#undef TQ_KEY_ATTR
+  rc |= set_val_attr<1, false>() | set_val_attr<1, true>() | set_val_attr<2, false>() | set_val_attr<2, true>();
+  rc |= set_val_attr<3, false>() | set_val_attr<3, true>() | set_val_attr<4, false>() | set_val_attr<4, true>();
+  return rc;
+}
+
+template <int B, int M, bool F32>
+static void key_launch(const KeyArgs& a, int64_t ntiles, hipStream_t st) {
+  const int waves = 4;
+  int64_t grid = (ntiles + waves - 1) / waves;
+  const int64_t cap = (int64_t)(g_num_cus > 0 ? g_num_cus : 256);
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL((compress_keys_kernel<B, M, F32>), dim3((unsigned)grid), dim3(64 * waves),
+                     key_lds_bytes<M>(), st, a);
+}
+
+int launch_compress_keys(const Matrices& mats, const CodebookDev& cb, int bits, int m, const AppendShape& s,
+                         void* key_records, void* stream) {
+  KeyArgs a;
+  a.x = s.x;
+  a.rec = (uint32_t*)key_records;
+  a.r_hi = mats.r_hi;
+  a.r_lo = mats.r_lo;
+  a.s_hi = mats.s_hi;
+  a.s_lo = mats.s_lo;
+  a.n_new = s.n_new;
+  a.pos = s.pos;
+  a.capacity = s.capacity;
+  a.n_seq = s.n_seq;
+  a.rec_words = bits * kD / 32 + m / 32 + 2;
+  a.cb = cb;
+  const bool f32 = s.dtype == TQ_F32;
+  const int64_t per = f32 ? 32 : 64;
+  const int64_t ntiles = ((s.n_new + per - 1) / per) * s.n_seq;
+  hipStream_t st = (hipStream_t)stream;
+#define TQ_KEY_CASE(B, M)                                  \
+  if (bits == B && m == M) {                               \
+    if (f32) key_launch<B, M, true>(a, ntiles, st);        \
+    else key_launch<B, M, false>(a, ntiles, st);           \
+    return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE; \
+  }
+  TQ_KEY_CASE(1, 64) TQ_KEY_CASE(2, 64) TQ_KEY_CASE(3, 64) TQ_KEY_CASE(4, 64)
+  TQ_KEY_CASE(1, 128) TQ_KEY_CASE(2, 128) TQ_KEY_CASE(3, 128) TQ_KEY_CASE(4, 128)
+#undef TQ_KEY_CASE
+  return TQ_EUNSUPPORTED;
+}
+
+template <int B, bool F32>
+static void val_launch(const ValArgs& a, int64_t nitems, hipStream_t st) {
+  const int waves = 4;
+  int64_t grid = (nitems + waves - 1) / waves;
+  const int64_t cap = (int64_t)(g_num_cus > 0 ? g_num_cus : 256);
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL((compress_values_kernel<B, F32>), dim3((unsigned)grid), dim3(64 * waves), kValLds, st, a);
+}
+
+int launch_compress_values(const Matrices& mats, const CodebookDev& cb, int bits, const AppendShape& s,
+                           void* value_blocks, void* stream) {
+  ValArgs a;
+  a.x = s.x;
+  a.blocks = (uint32_t*)value_blocks;
+  a.r_hi = mats.r_hi;
+  a.r_lo = mats.r_lo;
+  a.n_new = s.n_new;
+  a.pos = s.pos;
+  a.capacity = s.capacity;
+  a.blk0 = s.pos / kBlockTokens;
+  a.nblk = (s.pos + s.n_new - 1) / kBlockTokens - a.blk0 + 1;
+  a.n_seq = s.n_seq;
+  a.block_words = 4 * bits * kD + kBlockTokens;
+  a.cb = cb;
+  const bool f32 = s.dtype == TQ_F32;
+  const int64_t nitems = a.nblk * s.n_seq;
+  hipStream_t st = (hipStream_t)stream;
+#define TQ_VAL_CASE(B)                                     \
+  if (bits == B) {                                         \
+    if (f32) val_launch<B, true>(a, nitems, st);           \
+    else val_launch<B, false>(a, nitems, st);              \
+    return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE; \
+  }
+  TQ_VAL_CASE(1) TQ_VAL_CASE(2) TQ_VAL_CASE(3) TQ_VAL_CASE(4)
+#undef TQ_VAL_CASE
+  return TQ_EUNSUPPORTED;
+}
+
+}  // namespace tq

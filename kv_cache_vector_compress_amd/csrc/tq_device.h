@@ -1,0 +1,207 @@
+// Device-side helpers for the gfx950 kernels: matrix-core operand types, the
+// code-word layout (record layout v1) and codebook lookups.
+//
+// Operand layouts of v_mfma_f32_16x16x32_f16 (wave64), used everywhere:
+//   A (16 x 32): lane l holds row l%16, k = 8*(l/16) .. +7   (8 fp16)
+//   B (32 x 16): lane l holds column l%16, k = 8*(l/16) .. +7
+//   D (16 x 16): lane l holds column l%16, rows 4*(l/16) + i, i = 0..3
+// Which actual coordinate/token sits in each k slot is a free choice as long
+// as A and B agree; the choices below make every pack and unpack lane-local.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma(const h8& a, const h8& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ h8 as_h8(const u4& v) { return __builtin_bit_cast(h8, v); }
+__device__ __forceinline__ u4 as_u4(const h8& v) { return __builtin_bit_cast(u4, v); }
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// ---- code words ---------------------------------------------------------------
+// A group of b 32-bit words holds the b-bit codes of 8 "slots" s = 0..7 of 4
+// byte lanes i = 0..3 each (32 codes).  The byte lane i of every word belongs
+// to code (s, i).  Within a byte lane:
+//   b = 1: bit s of word 0
+//   b = 2: bits 2(s%4).. of word s/4
+//   b = 4: bits 4(s%2).. of word s/2
+//   b = 3: s < 6: bits 3(s%2).. of word s/2;
+//          s = 6: code bits 0,1 at bits 6,7 of word 0, code bit 2 at bit 6 of word 2
+//          s = 7: code bits 0,1 at bits 6,7 of word 1, code bit 2 at bit 7 of word 2
+// so that the 4 codes of a slot come out as one byte-per-code selector word
+// ("sel4") in one or two ALU operations.
+
+// OR the selector word x (code of byte lane i in byte i) into slot S.
+template <int B, int S>
+__device__ __forceinline__ void put_sel4(uint32_t (&w)[B], uint32_t x) {
+  if constexpr (B == 1) {
+    w[0] |= x << S;
+  } else if constexpr (B == 2) {
+    w[S / 4] |= x << (2 * (S % 4));
+  } else if constexpr (B == 4) {
+    w[S / 2] |= x << (4 * (S % 2));
+  } else {
+    static_assert(B == 3, "bits must be 1..4");
+    if constexpr (S < 6) {
+      w[S / 2] |= x << (3 * (S % 2));
+    } else if constexpr (S == 6) {
+      w[0] |= (x & 0x03030303u) << 6;
+      w[2] |= (x & 0x04040404u) << 4;
+    } else {
+      w[1] |= (x & 0x03030303u) << 6;
+      w[2] |= (x & 0x04040404u) << 5;
+    }
+  }
+}
+
+// Extract the selector word of slot S.
+template <int B, int S>
+__device__ __forceinline__ uint32_t get_sel4(const uint32_t (&w)[B]) {
+  if constexpr (B == 1) {
+    return (w[0] >> S) & 0x01010101u;
+  } else if constexpr (B == 2) {
+    return (w[S / 4] >> (2 * (S % 4))) & 0x03030303u;
+  } else if constexpr (B == 4) {
+    return (w[S / 2] >> (4 * (S % 2))) & 0x0F0F0F0Fu;
+  } else {
+    if constexpr (S < 6) {
+      return (w[S / 2] >> (3 * (S % 2))) & 0x07070707u;
+    } else if constexpr (S == 6) {
+      return ((w[0] >> 6) & 0x03030303u) | ((w[2] >> 4) & 0x04040404u);
+    } else {
+      return ((w[1] >> 6) & 0x03030303u) | ((w[2] >> 5) & 0x04040404u);
+    }
+  }
+}
+
+// Field mask (all bits) of slot S in word W, byte lane I.
+template <int B, int S, int W, int I>
+__device__ __forceinline__ constexpr uint32_t field_mask() {
+  uint32_t m = 0;
+  if constexpr (B == 1) {
+    if (W == 0) m = 1u << S;
+  } else if constexpr (B == 2) {
+    if (W == S / 4) m = 3u << (2 * (S % 4));
+  } else if constexpr (B == 4) {
+    if (W == S / 2) m = 15u << (4 * (S % 2));
+  } else {
+    if (S < 6) {
+      if (W == S / 2) m = 7u << (3 * (S % 2));
+    } else if (S == 6) {
+      if (W == 0) m = 3u << 6;
+      if (W == 2) m = 1u << 6;
+    } else {
+      if (W == 1) m = 3u << 6;
+      if (W == 2) m = 1u << 7;
+    }
+  }
+  return m << (8 * I);
+}
+
+// Decode a selector word into 4 fp16 centroids: two registers holding
+// (c[code0], c[code1]) and (c[code2], c[code3]).  tlo/thi hold the low/high
+// bytes of the fp16 centroid table (entry v at byte v).
+template <int B>
+__device__ __forceinline__ void decode4(uint32_t sel, const uint32_t (&tlo)[4], const uint32_t (&thi)[4],
+                                        uint32_t& p01, uint32_t& p23) {
+  uint32_t lo, hi;
+  if constexpr (B <= 3) {
+    lo = perm(tlo[1], tlo[0], sel);
+    hi = perm(thi[1], thi[0], sel);
+  } else {
+    const uint32_t s7 = sel & 0x07070707u;
+    const uint32_t upper = ((sel >> 3) & 0x01010101u) * 0xFFu;  // byte mask: code >= 8
+    const uint32_t lo_a = perm(tlo[1], tlo[0], s7), lo_b = perm(tlo[3], tlo[2], s7);
+    const uint32_t hi_a = perm(thi[1], thi[0], s7), hi_b = perm(thi[3], thi[2], s7);
+    lo = (lo_b & upper) | (lo_a & ~upper);
+    hi = (hi_b & upper) | (hi_a & ~upper);
+  }
+  p01 = perm(hi, lo, 0x05010400u);
+  p23 = perm(hi, lo, 0x07030602u);
+}
+
+// Decode slots S0 and S1 (= S0 + 1) into one 8-element fp16 operand:
+// elements 0..3 = slot S0 byte lanes 0..3, elements 4..7 = slot S1.
+template <int B, int S0>
+__device__ __forceinline__ h8 decode_pair(const uint32_t (&w)[B], const uint32_t (&tlo)[4],
+                                          const uint32_t (&thi)[4]) {
+  uint32_t r0, r1, r2, r3;
+  decode4<B>(get_sel4<B, S0>(w), tlo, thi, r0, r1);
+  decode4<B>(get_sel4<B, S0 + 1>(w), tlo, thi, r2, r3);
+  return as_h8(u4{r0, r1, r2, r3});
+}
+
+// Lloyd-Max cell of y: idx = #{i : beta_i < y} by binary search over the
+// sorted boundaries (beta in registers / kernel arguments).
+template <int B>
+__device__ __forceinline__ int bucket(float y, const float (&beta)[15]) {
+  if constexpr (B == 1) {
+    return y > beta[0] ? 1 : 0;
+  } else if constexpr (B == 2) {
+    const bool m1 = y > beta[1];
+    const float t = m1 ? beta[2] : beta[0];
+    const bool m0 = y > t;
+    return (m1 ? 2 : 0) + (m0 ? 1 : 0);
+  } else if constexpr (B == 3) {
+    const bool m2 = y > beta[3];
+    const float t1 = m2 ? beta[5] : beta[1];
+    const bool m1 = y > t1;
+    const float t0 = m2 ? (m1 ? beta[6] : beta[4]) : (m1 ? beta[2] : beta[0]);
+    const bool m0 = y > t0;
+    return (m2 ? 4 : 0) + (m1 ? 2 : 0) + (m0 ? 1 : 0);
+  } else {
+    // value selects only (a select of two array addresses would force the
+    // boundary array into scratch memory)
+    const float b0 = beta[0], b1 = beta[1], b2 = beta[2], b3 = beta[3], b4 = beta[4], b5 = beta[5];
+    const float b6 = beta[6], b7 = beta[7], b8 = beta[8], b9 = beta[9], b10 = beta[10], b11 = beta[11];
+    const float b12 = beta[12], b13 = beta[13], b14 = beta[14];
+    const bool m3 = y > b7;
+    const float t2 = m3 ? b11 : b3;
+    const bool m2 = y > t2;
+    const float t1 = m3 ? (m2 ? b13 : b9) : (m2 ? b5 : b1);
+    const bool m1 = y > t1;
+    const float ta = m1 ? b14 : b12, tb = m1 ? b10 : b8;
+    const float tc = m1 ? b6 : b4, te = m1 ? b2 : b0;
+    const float t0 = m3 ? (m2 ? ta : tb) : (m2 ? tc : te);
+    const bool m0 = y > t0;
+    return (m3 ? 8 : 0) + (m2 ? 4 : 0) + (m1 ? 2 : 0) + (m0 ? 1 : 0);
+  }
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Runtime-slot form of put_sel4 (the switch folds away when s is a constant).
+template <int B>
+__device__ __forceinline__ void put_sel4_rt(uint32_t (&w)[B], int s, uint32_t x) {
+  switch (s) {
+    case 0: put_sel4<B, 0>(w, x); break;
+    case 1: put_sel4<B, 1>(w, x); break;
+    case 2: put_sel4<B, 2>(w, x); break;
+    case 3: put_sel4<B, 3>(w, x); break;
+    case 4: put_sel4<B, 4>(w, x); break;
+    case 5: put_sel4<B, 5>(w, x); break;
+    case 6: put_sel4<B, 6>(w, x); break;
+    default: put_sel4<B, 7>(w, x); break;
+  }
+}
+
+// Copy the boundaries out of the kernel-argument block into registers.
+__device__ __forceinline__ void load_beta(float (&beta)[15], const CodebookDev& cb) {
+#pragma unroll
+  for (int i = 0; i < 15; ++i) beta[i] = cb.beta[i];
+}
+
+}  // namespace tq

@@ -1,0 +1,83 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+// Record failure `code` with a printf-style message; returns code.
+int fail(int code, const char* fmt, ...);
+void clear_error();
+
+bool lloyd_max_standard(int bits, double* c, double* beta);
+
+constexpr int kD = 128;          // head_dim of the built fast path
+constexpr int kLdsStride = 136;  // padded fp16 row stride of R / S images (conflict-free b128 reads)
+constexpr int kBlockTokens = 128;
+constexpr float kRotScale = 256.0f;   // R and S images are scaled by 2^8 before the hi/lo fp16 split
+constexpr float kResScale = 4096.0f;  // residual scaled by 2^12 before its hi/lo split
+
+// Per-bits codebook as the kernels consume it.
+struct CodebookDev {
+  float beta[16];   // boundaries, +inf past the last
+  float cent[16];   // centroids fp32
+  uint32_t tlo[4];  // low bytes of fp16(centroid v) at byte v (16 entries)
+  uint32_t thi[4];  // high bytes
+};
+
+struct Matrices {
+  const uint16_t* r_hi;  // [d][kLdsStride] fp16 bits, R * 2^8 high part (row = output coordinate)
+  const uint16_t* r_lo;
+  const uint16_t* s_hi;  // [m][kLdsStride] fp16 bits, S * 2^8 high part, columns in slot order
+  const uint16_t* s_lo;
+  const float* r32;      // [d][d] fp32 R
+  const float* s32;      // [m][d] fp32 S (natural column order)
+};
+
+// ---- launchers (defined in the .hip files) -----------------------------------
+
+struct AppendShape {
+  const void* x;
+  int dtype;         // TQ_F16 / TQ_F32
+  int64_t n_new, pos, capacity;
+  int n_seq;
+};
+
+int launch_compress_keys(const Matrices& mats, const CodebookDev& cb, int bits, int m,
+                         const AppendShape& s, void* key_records, void* stream);
+int launch_compress_values(const Matrices& mats, const CodebookDev& cb, int bits,
+                           const AppendShape& s, void* value_blocks, void* stream);
+
+struct AttnShape {
+  const void* q;
+  int dtype;
+  int G;
+  int64_t n_tokens, capacity;
+  int n_seq;
+};
+
+// Workspace partition for the attention calls.
+struct AttnPlan {
+  int waves_per_slot;      // split of the token axis for tq_attend
+  int blocks_per_wave;
+  size_t q_bytes;          // prepared query operands
+  size_t qn_bytes;         // query norms
+  size_t part_bytes;       // attend partials
+  size_t total;
+};
+AttnPlan plan_attention(int m, int n_seq, int G, int64_t n_tokens);
+int attention_device_init();
+
+int launch_prep_queries(const Matrices& mats, int m, const AttnShape& s, void* ws, const AttnPlan& p,
+                        void* stream);
+int launch_scores(const CodebookDev& cbk, int kbits, int m, const AttnShape& s, const void* key_records,
+                  float* scores, void* ws, const AttnPlan& p, void* stream);
+int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
+                  int m, const AttnShape& s, const void* key_records, const void* value_blocks, float scale,
+                  float* out, void* ws, const AttnPlan& p, void* stream);
+int compress_device_init();
+
+}  // namespace tq

@@ -1,0 +1,273 @@
+"""Thin Python binding of libtq.so (the C ABI in include/tq.h).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels.  PyTorch supplies device memory (tensors) and the current HIP
+stream.  There is no fallback: if libtq.so is missing or fails to load, every
+call raises.
+
+Names follow the C ABI, which mirrors the pages' interface (nav.superapi.store
+"turboquant-pytorch", 核心 API: build_lloyd_max_codebook,
+TurboQuantKVCache.append_key / append_value / attention_scores, and the
+softmax-weighted sum over decompressed values of 常见使用模式).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+TQ_OK = 0
+STATUS = {0: "TQ_OK", -1: "TQ_EINVAL", -2: "TQ_ECAPACITY", -3: "TQ_ENOCODEBOOK", -4: "TQ_ENOMEM",
+          -5: "TQ_EDEVICE", -6: "TQ_EUNSUPPORTED", -7: "TQ_EWORKSPACE"}
+TQ_F16, TQ_F32 = 1, 2
+BLOCK_TOKENS = 128
+
+
+class TQError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("proj_dim", ctypes.c_int32),
+                ("key_bits", ctypes.c_int32), ("value_bits", ctypes.c_int32)]
+
+
+class CacheView(ctypes.Structure):
+    _fields_ = [("key_records", ctypes.c_void_p), ("value_blocks", ctypes.c_void_p),
+                ("capacity", ctypes.c_int64), ("n_seq", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtq.so (built in place by kv_cache_vector_compress_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} not built: run `python -m kv_cache_vector_compress_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double)
+    CFG = ctypes.POINTER(Config)
+    VIEW = ctypes.POINTER(CacheView)
+    sig = {
+        "tq_lloyd_max_codebook": (ctypes.c_int, [I32, I32, D, D]),
+        "tq_key_record_bytes": (SZ, [CFG]),
+        "tq_value_block_bytes": (SZ, [CFG]),
+        "tq_cache_key_bytes": (SZ, [CFG, I32, I64]),
+        "tq_cache_value_bytes": (SZ, [CFG, I32, I64]),
+        "tq_workspace_bytes": (SZ, [CFG, I32, I32, I64]),
+        "tq_last_error": (ctypes.c_char_p, []),
+        "tq_create": (ctypes.c_int, [CFG, D, D, ctypes.POINTER(P)]),
+        "tq_destroy": (ctypes.c_int, [P]),
+        "tq_codebook_load": (ctypes.c_int, [P, I32, D, D]),
+        "tq_append_key": (ctypes.c_int, [P, VIEW, P, I32, I64, I64, P]),
+        "tq_append_value": (ctypes.c_int, [P, VIEW, P, I32, I64, I64, P]),
+        "tq_attention_scores": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, P, P, SZ, P]),
+        "tq_attend": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, ctypes.c_float, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return (lib().tq_last_error() or b"").decode()
+
+
+def _check(rc: int) -> None:
+    if rc != TQ_OK:
+        raise TQError(rc, last_error())
+
+
+def _dptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+# ---- host helpers -------------------------------------------------------------
+
+def lloyd_max_codebook(head_dim: int, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """(centroids, boundaries) of the Lloyd-Max quantiser of N(0, 1/head_dim),
+    computed by the library on the host."""
+    L = 1 << bits
+    c = np.zeros(L)
+    b = np.zeros(max(L - 1, 1))
+    _check(lib().tq_lloyd_max_codebook(head_dim, bits, _dptr(c), _dptr(b)))
+    return c, b[:L - 1]
+
+
+def key_record_bytes(cfg: Config) -> int:
+    return lib().tq_key_record_bytes(ctypes.byref(cfg))
+
+
+def value_block_bytes(cfg: Config) -> int:
+    return lib().tq_value_block_bytes(ctypes.byref(cfg))
+
+
+def cache_key_bytes(cfg: Config, n_seq: int, capacity: int) -> int:
+    return lib().tq_cache_key_bytes(ctypes.byref(cfg), n_seq, capacity)
+
+
+def cache_value_bytes(cfg: Config, n_seq: int, capacity: int) -> int:
+    return lib().tq_cache_value_bytes(ctypes.byref(cfg), n_seq, capacity)
+
+
+def workspace_bytes(cfg: Config, n_seq: int, G: int, n_tokens: int) -> int:
+    return lib().tq_workspace_bytes(ctypes.byref(cfg), n_seq, G, n_tokens)
+
+
+# ---- device side ----------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return TQ_F16
+    if t.dtype == torch.float32:
+        return TQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use float16 or float32")
+
+
+def _dev(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Context:
+    """A tq_ctx: the rotation R, the QJL matrix S and the loaded codebooks on
+    the current device."""
+
+    def __init__(self, head_dim: int, proj_dim: int, key_bits: int, value_bits: int,
+                 R: np.ndarray, S: np.ndarray, load_codebooks: bool = True):
+        self.cfg = Config(head_dim, proj_dim, key_bits, value_bits)
+        R = np.ascontiguousarray(R, dtype=np.float64)
+        S = np.ascontiguousarray(S, dtype=np.float64)
+        if R.shape != (head_dim, head_dim) or S.shape != (proj_dim, head_dim):
+            raise ValueError("R must be (d, d) and S (m, d)")
+        h = ctypes.c_void_p()
+        _check(lib().tq_create(ctypes.byref(self.cfg), _dptr(R), _dptr(S), ctypes.byref(h)))
+        self._h = h
+        if load_codebooks:
+            for b in sorted({key_bits, value_bits}):
+                self.codebook_load(b)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def codebook_load(self, bits: int, centroids: Optional[np.ndarray] = None,
+                      boundaries: Optional[np.ndarray] = None) -> None:
+        """Load a codebook; by default the library's own Lloyd-Max codebook."""
+        if centroids is None:
+            centroids, boundaries = lloyd_max_codebook(self.cfg.head_dim, bits)
+        c = np.ascontiguousarray(centroids, dtype=np.float64)
+        b = np.ascontiguousarray(boundaries, dtype=np.float64)
+        if c.size != 1 << bits or b.size != (1 << bits) - 1:
+            raise ValueError("codebook sizes do not match bits")
+        _check(lib().tq_codebook_load(self._h, bits, _dptr(c), _dptr(b if b.size else np.zeros(1))))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().tq_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class KVCache:
+    """Caller-owned packed cache (tq_cache_view) backed by torch device memory."""
+
+    def __init__(self, ctx: Context, n_seq: int, capacity: int, device="cuda"):
+        torch = _torch()
+        if capacity % BLOCK_TOKENS:
+            raise ValueError("capacity must be a multiple of 128")
+        self.ctx, self.n_seq, self.capacity = ctx, n_seq, capacity
+        kb = cache_key_bytes(ctx.cfg, n_seq, capacity)
+        vb = cache_value_bytes(ctx.cfg, n_seq, capacity)
+        if kb == 0 or vb == 0:
+            raise TQError(-1, last_error())
+        self.key_records = torch.zeros(kb // 4, dtype=torch.int32, device=device)
+        self.value_blocks = torch.zeros(vb // 4, dtype=torch.int32, device=device)
+        self.view = CacheView(self.key_records.data_ptr(), self.value_blocks.data_ptr(), capacity, n_seq)
+        self._ws = None
+
+    def workspace(self, G: int, n_tokens: int):
+        torch = _torch()
+        need = workspace_bytes(self.ctx.cfg, self.n_seq, G, n_tokens)
+        if need == 0:
+            raise TQError(-1, last_error())
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.key_records.device)
+        return self._ws
+
+    # hot path ---------------------------------------------------------------
+    def append_key(self, k, pos: int, stream=None) -> None:
+        """k: (n_seq, n_new, d) fp16/fp32 device tensor."""
+        _check(lib().tq_append_key(self.ctx.handle, ctypes.byref(self.view), _dev(k, "k"), _dtype_code(k),
+                                   pos, k.shape[1], _stream_ptr(stream)))
+
+    def append_value(self, v, pos: int, stream=None) -> None:
+        _check(lib().tq_append_value(self.ctx.handle, ctypes.byref(self.view), _dev(v, "v"), _dtype_code(v),
+                                     pos, v.shape[1], _stream_ptr(stream)))
+
+    def attention_scores(self, q, n_tokens: int, out=None, stream=None):
+        """q: (n_seq, G, d).  Returns fp32 (n_seq, G, n_tokens) unscaled estimates."""
+        torch = _torch()
+        G = q.shape[1]
+        if out is None:
+            out = torch.empty((self.n_seq, G, n_tokens), dtype=torch.float32, device=q.device)
+        ws = self.workspace(G, n_tokens)
+        _check(lib().tq_attention_scores(self.ctx.handle, ctypes.byref(self.view), _dev(q, "q"), _dtype_code(q),
+                                         G, n_tokens, _dev(out, "scores"), ctypes.c_void_p(ws.data_ptr()),
+                                         ws.numel(), _stream_ptr(stream)))
+        return out
+
+    def attend(self, q, n_tokens: int, scale: float = 0.0, out=None, stream=None):
+        """softmax(scale * est) . V^ over the first n_tokens; fp32 (n_seq, G, d)."""
+        torch = _torch()
+        G = q.shape[1]
+        if out is None:
+            out = torch.empty((self.n_seq, G, self.ctx.cfg.head_dim), dtype=torch.float32, device=q.device)
+        ws = self.workspace(G, n_tokens)
+        _check(lib().tq_attend(self.ctx.handle, ctypes.byref(self.view), _dev(q, "q"), _dtype_code(q), G,
+                               n_tokens, float(scale), _dev(out, "out"), ctypes.c_void_p(ws.data_ptr()),
+                               ws.numel(), _stream_ptr(stream)))
+        return out
+
+    # raw views for inspection ------------------------------------------------
+    def key_words(self):
+        """(n_seq, capacity, record_words) uint32 numpy copy of the key records."""
+        w = self.key_records.cpu().numpy().view(np.uint32)
+        return w.reshape(self.n_seq, self.capacity, -1)
+
+    def value_words(self):
+        w = self.value_blocks.cpu().numpy().view(np.uint32)
+        return w.reshape(self.n_seq, self.capacity // BLOCK_TOKENS, -1)

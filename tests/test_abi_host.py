@@ -1,0 +1,112 @@
+"""Host-side checks of libtq.so that need no GPU: it loads, exports every
+function include/tq.h declares, its host Lloyd-Max builder agrees with the
+oracle's numerically integrated codebook, size queries follow the record
+layout, and argument errors are reported before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import turboquant as O
+from kv_cache_vector_compress_amd import tq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tq.lib()
+    names = header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in tq.h but not exported"
+    out = os.popen(f"nm -D --defined-only {tq.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not a defined text symbol"
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [64, 128, 1024])
+def test_host_codebook_matches_oracle(bits, d):
+    c, b = tq.lloyd_max_codebook(d, bits)
+    ob, oc = O.lloyd_max_codebook(d, bits)
+    np.testing.assert_allclose(c, oc, rtol=0, atol=1e-13 / np.sqrt(d))
+    np.testing.assert_allclose(b, ob, rtol=0, atol=1e-13 / np.sqrt(d))
+
+
+def test_codebook_builder_rejects_bad_arguments():
+    c = np.zeros(16)
+    b = np.zeros(16)
+    P = c.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    Q = b.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    lib = tq.lib()
+    assert lib.tq_lloyd_max_codebook(128, 0, P, Q) == -1
+    assert lib.tq_lloyd_max_codebook(128, 5, P, Q) == -1
+    assert lib.tq_lloyd_max_codebook(0, 3, P, Q) == -1
+    assert lib.tq_lloyd_max_codebook(128, 3, None, Q) == -1
+    assert "bits" in tq.last_error()
+
+
+@pytest.mark.parametrize("kb,vb,m", [(3, 3, 64), (2, 4, 128), (1, 1, 64), (4, 2, 512)])
+def test_sizes_follow_record_layout(kb, vb, m):
+    cfg = tq.Config(128, m, kb, vb)
+    assert tq.key_record_bytes(cfg) == 4 * (kb * 128 // 32 + m // 32 + 2) == 4 * O.key_record_words(128, m, kb)
+    assert tq.value_block_bytes(cfg) == 4 * O.value_block_words(128, vb)
+    assert tq.cache_key_bytes(cfg, 3, 256) == 3 * 256 * tq.key_record_bytes(cfg)
+    assert tq.cache_value_bytes(cfg, 3, 256) == 3 * 2 * tq.value_block_bytes(cfg)
+    assert tq.cache_key_bytes(cfg, 3, 100) == 0       # capacity not a multiple of 128
+    assert tq.workspace_bytes(cfg, 4, 4, 1000) > 0
+    assert tq.workspace_bytes(cfg, 4, 17, 1000) == 0  # G out of range
+    assert tq.workspace_bytes(cfg, 4, 4, 0) == 0
+
+
+def test_3bit_record_is_64_bytes_and_block_is_52_bytes_per_token():
+    cfg = tq.Config(128, 64, 3, 3)
+    assert tq.key_record_bytes(cfg) == 64
+    assert tq.value_block_bytes(cfg) == 52 * 128
+
+
+@pytest.mark.parametrize("cfg,code", [
+    ((100, 64, 3, 3), -1), ((128, 48, 3, 3), -1), ((128, 64, 0, 3), -1), ((128, 64, 3, 5), -1),
+    ((2048, 64, 3, 3), -1), ((256, 64, 3, 3), -6), ((128, 192, 3, 3), -6)])
+def test_create_rejects_configs_before_any_device_call(cfg, code):
+    R = np.eye(cfg[0])
+    S = np.ones((max(cfg[1], 1), cfg[0]))
+    h = ctypes.c_void_p()
+    c = tq.Config(*cfg)
+    D = ctypes.POINTER(ctypes.c_double)
+    rc = tq.lib().tq_create(ctypes.byref(c), R.ctypes.data_as(D), S.ctypes.data_as(D), ctypes.byref(h))
+    assert rc == code, tq.last_error()
+    assert not h.value
+
+
+def test_create_rejects_null_and_nonfinite_matrices():
+    c = tq.Config(128, 64, 3, 3)
+    h = ctypes.c_void_p()
+    D = ctypes.POINTER(ctypes.c_double)
+    R = np.eye(128)
+    S = np.ones((64, 128))
+    assert tq.lib().tq_create(ctypes.byref(c), None, S.ctypes.data_as(D), ctypes.byref(h)) == -1
+    R[3, 4] = np.nan
+    assert tq.lib().tq_create(ctypes.byref(c), R.ctypes.data_as(D), S.ctypes.data_as(D), ctypes.byref(h)) == -1
+    assert "non-finite" in tq.last_error()
+
+
+def test_hot_path_entry_points_reject_null_context():
+    lib = tq.lib()
+    view = tq.CacheView(16, 16, 128, 1)
+    assert lib.tq_append_key(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 0, 1, None) == -1
+    assert lib.tq_append_value(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 0, 1, None) == -1
+    assert lib.tq_attention_scores(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 4, 1,
+                                   ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 20, None) == -1
+    assert lib.tq_attend(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 4, 1, 0.0,
+                         ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 20, None) == -1
+    assert lib.tq_codebook_load(None, 3, None, None) == -1
+    assert lib.tq_destroy(None) == 0

@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every case uses seeded synthetic inputs from kv_cache_vector_compress_amd.synth;
+the oracle gets the same arrays.  Acceptance rules: tests/parity_util.py.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import turboquant as O
+from kv_cache_vector_compress_amd import synth, tq
+from tests import parity_util as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[parity]", *a, flush=True)
+
+
+def make_ctx(d=128, m=64, kb=3, vb=3):
+    R = synth.haar_rotation(d, synth.SEED_R)
+    S = synth.gaussian_projection(m, d, synth.SEED_S)
+    return tq.Context(d, m, kb, vb, R, S), R, S
+
+
+def run_case(K, V, Q, kb=3, vb=3, m=64, capacity=None, chunks=None, n_tokens=None, scale=0.0,
+             check_attend=True):
+    """Append K/V (np arrays (n_seq, T, d)) in the given chunks, then score and
+    attend with Q (n_seq, G, d); compare every output with the oracle."""
+    n_seq, T, d = K.shape
+    G = Q.shape[1]
+    cap = capacity or -(-T // 128) * 128
+    ctx, R, S = make_ctx(d, m, kb, vb)
+    cache = tq.KVCache(ctx, n_seq, cap)
+    chunks = chunks or [T]
+    pos = 0
+    for n in chunks:
+        kt = torch.from_numpy(np.ascontiguousarray(K[:, pos:pos + n])).cuda()
+        vt = torch.from_numpy(np.ascontiguousarray(V[:, pos:pos + n])).cuda()
+        cache.append_key(kt, pos)
+        cache.append_value(vt, pos)
+        pos += n
+    assert pos == T
+    torch.cuda.synchronize()
+    nt = n_tokens or T
+
+    kbeta, kc = O.lloyd_max_codebook(d, kb)
+    vbeta, vc = O.lloyd_max_codebook(d, vb)
+    ref_k = O.compress_keys(K, R, S, kbeta, kc)
+    ref_v = O.compress_values(V, R, vbeta, vc)
+    gk = P.unpack_gpu_keys(cache, d, m, kb, T)
+    gv = P.unpack_gpu_values(cache, d, vb, T)
+    st = P.check_keys(gk, ref_k, kbeta)
+    flip_tok = st.pop("flip_tokens")
+    st.update({"v_" + k: v for k, v in P.check_values(gv, ref_v, vbeta).items()})
+
+    qt = torch.from_numpy(np.ascontiguousarray(Q)).cuda()
+    sc = cache.attention_scores(qt, nt).cpu().numpy()
+    qn = np.linalg.norm(Q.astype(np.float64), axis=-1)
+    kn = np.linalg.norm(K.astype(np.float64), axis=-1)[:, :nt]
+    # (a) score kernel against the oracle evaluated on the GPU's own codes
+    gk_nt = {k: v[:, :nt] for k, v in gk.items()}
+    ref_on_gpu_codes = O.key_scores(Q, R, S, kc, gk_nt)
+    st["score_vs_gpu_codes"] = P.check_scores(sc, ref_on_gpu_codes, qn, kn)
+    # (b) end to end against the oracle's own codes
+    ref_k_nt = {k: v[:, :nt] for k, v in ref_k.items()}
+    ref_scores = O.key_scores(Q, R, S, kc, ref_k_nt)
+    st["score_end_to_end"] = P.check_scores(sc, ref_scores, qn, kn, skip_tokens=flip_tok[:, :nt])
+    if check_attend:
+        out = cache.attend(qt, nt, scale=scale).cpu().numpy()
+        sc_ = None if scale <= 0 else scale
+        ref_v_nt = {k: v[:, :nt] for k, v in ref_v.items()}
+        ref_out = O.attend(Q, R, S, kc, ref_k_nt, ref_v_nt, scale=sc_, value_centroids=vc)
+        st["attend_rel"] = P.check_attend(out, ref_out)
+    ctx.close()
+    return st
+
+
+def test_tiny_unit_gaussian_fp32():
+    """Tiny case: 1 slot, d=128, 3-bit, m=64, 1024 unit fp32 keys/values, 4 queries."""
+    w = synth.TINY
+    K, V, Q = synth.workload_keys(w), synth.workload_values(w), synth.workload_queries(w)
+    _say("tiny", K.shape, Q.shape)
+    st = run_case(K, V, Q)
+    _say(st)
+
+
+@pytest.mark.parametrize("kb,vb,m", [(1, 1, 64), (2, 2, 64), (3, 3, 64), (4, 4, 64), (3, 2, 128), (2, 4, 128)])
+def test_bits_and_proj_dim_fp16_ragged(kb, vb, m):
+    """fp16 KV-like inputs, ragged token count (several tiles and a tail)."""
+    d, T, n_seq, G = 128, 1000, 3, 8
+    K = np.stack([synth.kv_slot(synth.SEED_K, s, s, T, d) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(synth.SEED_V, s, s, T, d) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(synth.SEED_Q, s, s, G, d) for s in range(n_seq)])
+    _say("bits", kb, vb, m)
+    _say(run_case(K, V, Q, kb=kb, vb=vb, m=m))
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 16])
+def test_query_group_sizes(G):
+    d, T, n_seq = 128, 515, 2
+    K = np.stack([synth.kv_slot(10, s, s, T, d) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(11, s, s, T, d) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(12, s, s, G, d) for s in range(n_seq)]) * np.float16(3.0)
+    _say("G", G)
+    _say(run_case(K, V, Q))
+
+
+def test_streaming_appends_unaligned():
+    """Prefill 300 tokens, then single-token decode appends, then a ragged
+    chunk: blocks shared by several appends must keep earlier codes."""
+    d, n_seq, G = 128, 2, 4
+    chunks = [300, 1, 1, 1, 1, 1, 77, 130, 1]
+    T = sum(chunks)
+    K = np.stack([synth.kv_slot(20, s, s, T, d) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(21, s, s, T, d) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(22, s, s, G, d) for s in range(n_seq)])
+    _say("streaming", chunks)
+    _say(run_case(K, V, Q, chunks=chunks, capacity=1024))
+
+
+def test_partial_token_window_and_scale():
+    """Attention over the first n_tokens only (not a multiple of 16), custom scale."""
+    d, T, n_seq, G = 128, 700, 2, 8
+    K = np.stack([synth.kv_slot(30, s, s, T, d) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(31, s, s, T, d) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(32, s, s, G, d) for s in range(n_seq)])
+    _say("window")
+    _say(run_case(K, V, Q, n_tokens=509, scale=0.3))
+
+
+def test_zero_and_single_token():
+    """Zero key/value rows are encoded as direction 0 and score 0; a cache of
+    one token attends to exactly that token's dequantised value."""
+    d, T, n_seq, G = 128, 40, 1, 4
+    K = synth.kv_slot(40, 0, 0, T, d)[None].copy()
+    V = synth.kv_slot(41, 0, 0, T, d)[None].copy()
+    K[0, 5] = 0
+    V[0, 7] = 0
+    Q = synth.kv_slot(42, 0, 0, G, d)[None]
+    _say("zeros")
+    _say(run_case(K, V, Q))
+    _say(run_case(K[:, :1], V[:, :1], Q))
+
+
+def test_fp32_inputs_kv_like():
+    d, T, n_seq, G = 128, 333, 2, 4
+    K = np.stack([synth.kv_slot(50, s, s, T, d, dtype=np.float32) for s in range(n_seq)]) * 7.5
+    V = np.stack([synth.kv_slot(51, s, s, T, d, dtype=np.float32) for s in range(n_seq)]) * 0.01
+    Q = np.stack([synth.kv_slot(52, s, s, G, d, dtype=np.float32) for s in range(n_seq)])
+    _say("fp32 kv-like")
+    _say(run_case(K.astype(np.float32), V.astype(np.float32), Q.astype(np.float32)))
+
+
+def test_qwen_decode_shape_full():
+    """Qwen2.5-3B-shaped decode step at full size: 36 layers x 2 KV heads
+    (72 slots) x 8192 fp16 tokens, 16 query heads (GQA 8:1), 3-bit keys
+    (m=64) and values, every output compared with the oracle."""
+    w = synth.QWEN_DECODE
+    K, V, Q = synth.workload_keys(w), synth.workload_values(w), synth.workload_queries(w)
+    _say("qwen full", K.shape, Q.shape)
+    _say(run_case(K, V, Q))
+
+
+# ---------------------------------------------------------------------------
+# argument errors: documented code, nothing written
+# ---------------------------------------------------------------------------
+
+def test_error_paths_leave_buffers_untouched():
+    ctx, R, S = make_ctx()
+    cache = tq.KVCache(ctx, 2, 256)
+    canary = 0x5A5A5A5A
+    cache.key_records.fill_(canary)
+    cache.value_blocks.fill_(canary)
+    k = torch.zeros((2, 10, 128), dtype=torch.float16, device="cuda")
+    q = torch.zeros((2, 4, 128), dtype=torch.float16, device="cuda")
+
+    def expect(code, fn):
+        with pytest.raises(tq.TQError) as e:
+            fn()
+        assert e.value.code == code, str(e.value)
+
+    expect(-2, lambda: cache.append_key(k, 250))                    # capacity
+    expect(-2, lambda: cache.append_value(k, -1))                   # negative position
+    expect(-1, lambda: tq._check(tq.lib().tq_append_key(ctx.handle, tq.ctypes.byref(cache.view),
+                                                       tq.ctypes.c_void_p(k.data_ptr()), 7, 0, 10, None)))  # dtype
+    expect(-1, lambda: cache.attention_scores(q, 0))                # n_tokens
+    expect(-1, lambda: cache.attention_scores(q, 257))              # n_tokens > capacity
+    q17 = torch.zeros((2, 17, 128), dtype=torch.float16, device="cuda")
+    expect(-1, lambda: cache.attention_scores(q17, 10))             # G
+    ws = cache.workspace(4, 10)
+    out = torch.empty((2, 4, 10), dtype=torch.float32, device="cuda")
+    expect(-7, lambda: tq._check(tq.lib().tq_attention_scores(
+        ctx.handle, tq.ctypes.byref(cache.view), tq.ctypes.c_void_p(q.data_ptr()), 1, 4, 10,
+        tq.ctypes.c_void_p(out.data_ptr()), tq.ctypes.c_void_p(ws.data_ptr()), 16, None)))
+    kmis = torch.zeros(2 * 10 * 128 + 4, dtype=torch.float16, device="cuda")[4:]
+    expect(-1, lambda: tq._check(tq.lib().tq_append_key(ctx.handle, tq.ctypes.byref(cache.view),
+                                                       tq.ctypes.c_void_p(kmis.data_ptr()), 1, 0, 10, None)))
+    # no codebook for the requested bits
+    ctx2 = tq.Context(128, 64, 2, 2, R, S, load_codebooks=False)
+    cache2 = tq.KVCache(ctx2, 2, 256)
+    expect(-3, lambda: cache2.append_key(k, 0))
+    expect(-3, lambda: cache2.attend(q, 5))
+    torch.cuda.synchronize()
+    assert bool((cache.key_records == canary).all()) and bool((cache.value_blocks == canary).all())
+    assert bool((cache2.key_records == 0).all())
+    # n_new == 0 is a no-op
+    cache.append_key(k[:, :0].contiguous(), 0)
+    torch.cuda.synchronize()
+    assert bool((cache.key_records == canary).all())
+    ctx.close()
+    ctx2.close()
