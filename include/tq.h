@@ -75,7 +75,8 @@ typedef struct {
 } tq_config;
 
 /* Caller-owned packed cache of n_seq slots (one slot = one KV head of one
- * sequence/layer), each holding up to `capacity` tokens (multiple of 128).
+ * sequence/layer), each holding up to `capacity` tokens (a multiple of 128,
+ * at most 2^24).
  *
  * key_records: device, n_seq * capacity * tq_key_record_bytes() bytes.  Slot
  *   s, token t starts at byte (s * capacity + t) * tq_key_record_bytes().
@@ -157,7 +158,9 @@ int tq_destroy(tq_ctx* ctx);
 
 /* Load the codebook for `bits` (host arrays, copied): 2^bits strictly
  * ascending finite centroids and 2^bits - 1 strictly ascending finite
- * boundaries, each boundary strictly between its two centroids.  Needed for
+ * boundaries, each boundary strictly between its two centroids, and the
+ * codebook symmetric about 0 within 1e-9 of its largest centroid (as every
+ * Lloyd-Max codebook of the centred Gaussian is); TQ_EINVAL otherwise.  Needed for
  * key_bits and value_bits before any append or attention call.  Host-only:
  * the codebook travels to the kernels as launch arguments. */
 int tq_codebook_load(tq_ctx* ctx, int32_t bits, const double* centroids, const double* boundaries);

@@ -210,12 +210,25 @@ int tq_codebook_load(tq_ctx* ctx, int32_t bits, const double* centroids, const d
     if (!(boundaries[i] > centroids[i] && boundaries[i] < centroids[i + 1]))
       return fail(TQ_EINVAL, "tq_codebook_load: boundary %d not between its centroids", i);
   }
+  // The kernels bucket |y| against the positive boundaries, which needs a
+  // codebook symmetric about 0 (every Lloyd-Max codebook of N(0, 1/d) is).
+  double cmax = 0.0;
+  for (int i = 0; i < L; ++i) cmax = std::fmax(cmax, std::fabs(centroids[i]));
+  const double tol = 1e-9 * cmax;
+  for (int i = 0; i < L; ++i)
+    if (std::fabs(centroids[i] + centroids[L - 1 - i]) > tol)
+      return fail(TQ_EINVAL, "tq_codebook_load: centroids not symmetric about 0 (c_i != -c_{L-1-i})");
+  for (int i = 0; i < L - 1; ++i)
+    if (std::fabs(boundaries[i] + boundaries[L - 2 - i]) > tol)
+      return fail(TQ_EINVAL, "tq_codebook_load: boundaries not symmetric about 0");
   CodebookDev cb;
   std::memset(&cb, 0, sizeof(cb));
   for (int i = 0; i < 16; ++i) {
-    cb.beta[i] = i < L - 1 ? (float)boundaries[i] : INFINITY;
-    cb.cent[i] = i < L ? (float)centroids[i] : 0.f;
-    const uint16_t h = i < L ? to_half_bits((float)centroids[i]) : 0;
+    // exact symmetry in fp32 (the middle boundary is 0)
+    cb.beta[i] = i < L - 1 ? (float)(0.5 * (boundaries[i] - boundaries[L - 2 - i])) : INFINITY;
+    const double ci = i < L ? 0.5 * (centroids[i] - centroids[L - 1 - i]) : 0.0;
+    cb.cent[i] = (float)ci;
+    const uint16_t h = i < L ? to_half_bits((float)ci) : 0;
     cb.tlo[i / 4] |= (uint32_t)(h & 0xFF) << (8 * (i % 4));
     cb.thi[i / 4] |= (uint32_t)(h >> 8) << (8 * (i % 4));
   }
@@ -228,8 +241,9 @@ static int check_cache(const tq_ctx* ctx, const tq_cache_view* cache, const char
   if (!ctx) return fail(TQ_EINVAL, "%s: ctx is NULL", fn);
   if (!cache) return fail(TQ_EINVAL, "%s: cache is NULL", fn);
   if (cache->n_seq < 1) return fail(TQ_EINVAL, "%s: n_seq %d < 1", fn, cache->n_seq);
-  if (cache->capacity < kBlockTokens || cache->capacity % kBlockTokens)
-    return fail(TQ_EINVAL, "%s: capacity %lld is not a positive multiple of 128", fn, (long long)cache->capacity);
+  if (cache->capacity < kBlockTokens || cache->capacity % kBlockTokens || cache->capacity > kMaxCapacity)
+    return fail(TQ_EINVAL, "%s: capacity %lld is not a multiple of 128 in [128, 2^24]", fn,
+                (long long)cache->capacity);
   if (!cache->key_records || !cache->value_blocks) return fail(TQ_EINVAL, "%s: NULL cache buffer", fn);
   if (!aligned16(cache->key_records) || !aligned16(cache->value_blocks))
     return fail(TQ_EINVAL, "%s: cache buffers must be 16-byte aligned", fn);

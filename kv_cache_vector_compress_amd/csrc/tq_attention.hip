@@ -167,8 +167,19 @@ struct ScoreArgs {
 };
 
 template <int B, int M>
+constexpr int rec_words() { return B * kD / 32 + M / 32 + 2; }
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 v = {(_Float16)a, (_Float16)b};  // v_cvt_pk_f16_f32 (round to nearest)
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int B, int M>
 __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
   constexpr int KBT = 4 + M / 32;
+  constexpr int RW = rec_words<B, M>();
+  __shared__ float nsh[4][16];  // per wave: ||k|| of the tile's 16 tokens
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
@@ -183,32 +194,45 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; }
   const int sh0 = 15 - 8 * (q & 1);
-  const int64_t ntile = (a.n_tokens + 15) / 16;
-  const int64_t t_begin = (int64_t)wc * a.tiles_per_wave;
-  const int64_t t_end = min(ntile, t_begin + a.tiles_per_wave);
-  const uint32_t* base = a.rec + (int64_t)slot * a.capacity * a.rec_words;
-  float* out = a.scores + ((int64_t)slot * a.G + r16) * a.n_tokens;
+  const int n_tok = (int)a.n_tokens;
+  const int ntile = (n_tok + 15) >> 4;
+  const int t_begin = wc * a.tiles_per_wave;
+  const int t_end = min(ntile, t_begin + a.tiles_per_wave);
+  const uint32_t* base = a.rec + (size_t)slot * (size_t)a.capacity * RW + q * B;
+  const uint32_t* sbase = a.rec + (size_t)slot * (size_t)a.capacity * RW + 4 * B + (q >> 1);
+  float* out = a.scores + ((size_t)slot * a.G + r16) * (size_t)n_tok;
+  const bool head_ok = r16 < a.G;
+  const bool vec_store = (n_tok & 3) == 0;
+
+  auto load = [&](KeyTile<B, M>& k, int tile) {
+    const int t = min(tile * 16 + r16, n_tok - 1);  // rows past the end: any valid row
+    const uint32_t* rp = base + t * RW;
+#pragma unroll
+    for (int w = 0; w < B; ++w) k.cw[w] = rp[w];
+    const uint32_t* sp = sbase + t * RW;
+#pragma unroll
+    for (int c = 0; c < M / 64; ++c) k.sw[c] = sp[2 * c];
+    k.n = __uint_as_float(rp[RW - 2 - q * B]);
+    k.g = __uint_as_float(rp[RW - 1 - q * B]);
+  };
 
   KeyTile<B, M> cur;
-  if (t_begin < t_end) {
-    const int64_t t = t_begin * 16 + r16;
-    load_key<B, M>(cur, base + t * a.rec_words, t < a.n_tokens, q, a.rec_words);
-  }
-  for (int64_t tile = t_begin; tile < t_end; ++tile) {
+  if (t_begin < t_end) load(cur, t_begin);
+  for (int tile = t_begin; tile < t_end; ++tile) {
     KeyTile<B, M> nxt;
-    if (tile + 1 < t_end) {
-      const int64_t t = (tile + 1) * 16 + r16;
-      load_key<B, M>(nxt, base + t * a.rec_words, t < a.n_tokens, q, a.rec_words);
-    }
+    if (tile + 1 < t_end) load(nxt, tile + 1);
     const f4 acc = key_tile_scores<B, M>(cur, qb, tlo, thi, a.kappa, sh0);
-    float nk[4];
+    if (q == 0) nsh[wave][r16] = cur.n;
+    const f4 nk = *(const f4*)&nsh[wave][4 * q];  // ||k|| of token rows 4q..4q+3
+    const int t0 = tile * 16 + 4 * q;
+    if (head_ok) {
+      f4 v = acc * nk * qn;
+      if (vec_store && t0 + 4 <= n_tok) {
+        *(f4*)(out + t0) = v;
+      } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nk[i] = __shfl(cur.n, 4 * q + i, 64);  // ||k|| of token row 4q+i
-    if (r16 < a.G) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t tok = tile * 16 + 4 * q + i;
-        if (tok < a.n_tokens) out[tok] = acc[i] * nk[i] * qn;
+        for (int i = 0; i < 4; ++i)
+          if (t0 + i < n_tok) out[t0 + i] = v[i];
       }
     }
     cur = nxt;
@@ -236,6 +260,9 @@ struct AttendArgs {
 template <int BK, int BV, int M>
 __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   constexpr int KBT = 4 + M / 32;
+  constexpr int RW = rec_words<BK, M>();
+  constexpr int BW = 4 * BV * kD + kBlockTokens;
+  __shared__ float nsh[4][32];  // per wave: ||k|| of the step's 32 tokens
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
@@ -253,40 +280,47 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
     tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; vtlo[i] = a.vtlo[i]; vthi[i] = a.vthi[i];
   }
   const int sh0 = 15 - 8 * (q & 1);
-  const int64_t nblk = (a.n_tokens + kBlockTokens - 1) / kBlockTokens;
-  const int64_t b_begin = (int64_t)wc * a.blocks_per_wave;
-  const int64_t b_end = min(nblk, b_begin + a.blocks_per_wave);
-  const int64_t nblk_cap = a.capacity / kBlockTokens;
-  const uint32_t* kbase = a.rec + (int64_t)slot * a.capacity * a.rec_words;
+  const int n_tok = (int)a.n_tokens;
+  const int nblk = (n_tok + kBlockTokens - 1) / kBlockTokens;
+  const int b_begin = wc * a.blocks_per_wave;
+  const int b_end = min(nblk, b_begin + a.blocks_per_wave);
+  const uint32_t* kbase = a.rec + (size_t)slot * (size_t)a.capacity * RW;
+  const uint32_t* vbase = a.vblocks + (size_t)slot * (size_t)(a.capacity / kBlockTokens) * BW;
 
   float m_run = -INFINITY, l_run = 0.f;
-  int ve = -1000;  // running value-norm exponent (wave-uniform)
+  int ve = -1000;  // running exponent of the value norms (wave-uniform)
   f4 acc[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t blk = b_begin; blk < b_end; ++blk) {
-    const int64_t tok0 = blk * kBlockTokens;
-    const uint32_t* vb = a.vblocks + ((int64_t)slot * nblk_cap + blk) * a.block_words;
+  for (int blk = b_begin; blk < b_end; ++blk) {
+    const int tok0 = blk * kBlockTokens;
+    const bool full = tok0 + kBlockTokens <= n_tok;  // wave-uniform
+    const uint32_t* vb = vbase + blk * BW;
     const float* vnorm = (const float*)(vb + 4 * BV * kD);
     uint32_t vw[8][BV];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
       for (int w = 0; w < BV; ++w) vw[nt][w] = vb[(w * 4 + q) * kD + 16 * nt + r16];
-    // block maximum of the value norms (tokens past n_tokens count as 0):
-    // lane l looks at tokens 2l, 2l+1, then a wave-wide max
+    // Value norms enter P as ||v|| 2^-ve with ve the running maximum
+    // exponent of the norms seen so far, so P stays in fp16 range whatever
+    // the norms' scale; the accumulator is rescaled when ve grows.
     float bmax;
     {
       const float2 v2 = *(const float2*)(vnorm + 2 * lane);
-      const bool ok0 = tok0 + 2 * lane < a.n_tokens, ok1 = tok0 + 2 * lane + 1 < a.n_tokens;
-      bmax = fmaxf(ok0 ? v2.x : 0.f, ok1 ? v2.y : 0.f);
+      float x0 = v2.x, x1 = v2.y;
+      if (!full) {
+        x0 = tok0 + 2 * lane < n_tok ? x0 : 0.f;
+        x1 = tok0 + 2 * lane + 1 < n_tok ? x1 : 0.f;
+      }
+      bmax = fmaxf(x0, x1);
 #pragma unroll
       for (int sh = 1; sh < 64; sh <<= 1) bmax = fmaxf(bmax, shfl_xor(bmax, sh));
     }
     int e_blk = 0;
     frexpf(bmax, &e_blk);
-    if (e_blk > ve) {  // wave-uniform: rescale the accumulator to the new exponent
+    if (e_blk > ve) {
       const float f = ldexpf(1.f, ve - e_blk);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) acc[nt] *= f;
@@ -296,60 +330,68 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 
 #pragma unroll
     for (int step = 0; step < 4; ++step) {
-      // scores of the two 16-token tiles of this step
-      f4 sc[2];
-      float nk[2];
+      f4 sc[2], nk[2], vn[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int64_t t = tok0 + 16 * (2 * step + u) + r16;
+        const int tt = tok0 + 16 * (2 * step + u);
+        const int t = full ? tt + r16 : min(tt + r16, n_tok - 1);
+        const uint32_t* rp = kbase + t * RW;
         KeyTile<BK, M> kt;
-        load_key<BK, M>(kt, kbase + t * a.rec_words, t < a.n_tokens, q, a.rec_words);
+#pragma unroll
+        for (int w = 0; w < BK; ++w) kt.cw[w] = rp[q * BK + w];
+#pragma unroll
+        for (int c = 0; c < M / 64; ++c) kt.sw[c] = rp[4 * BK + 2 * c + (q >> 1)];
+        kt.n = __uint_as_float(rp[RW - 2]);
+        kt.g = __uint_as_float(rp[RW - 1]);
         sc[u] = key_tile_scores<BK, M>(kt, qb, tlo, thi, a.kappa, sh0);
-        nk[u] = kt.n;
+        if (q == 0) nsh[wave][16 * u + r16] = kt.n;
+        vn[u] = *(const f4*)(vnorm + 16 * (2 * step + u) + 4 * q);
       }
+      nk[0] = *(const f4*)&nsh[wave][4 * q];
+      nk[1] = *(const f4*)&nsh[wave][16 + 4 * q];
       float lg[2][4];
       float cmax = -INFINITY;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float n = __shfl(nk[u], 4 * q + i, 64);
-          const bool ok = tok0 + 16 * (2 * step + u) + 4 * q + i < a.n_tokens;
-          lg[u][i] = ok ? sc[u][i] * n * qsc : -INFINITY;
-          cmax = fmaxf(cmax, lg[u][i]);
+          float l = sc[u][i] * nk[u][i] * qsc;
+          float v = vn[u][i] * vs;
+          if (!full) {
+            const bool ok = tok0 + 16 * (2 * step + u) + 4 * q + i < n_tok;
+            l = ok ? l : -INFINITY;
+            v = ok ? v : 0.f;
+          }
+          lg[u][i] = l;
+          vn[u][i] = v;
+          cmax = fmaxf(cmax, l);
         }
       cmax = fmaxf(cmax, shfl_xor(cmax, 16));
       cmax = fmaxf(cmax, shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+      // Online softmax with lazy rescaling: the accumulator is rescaled only
+      // when some head's running maximum grows (rare after the first blocks).
+      if (__any(cmax > m_run)) {
+        const float m_new = fmaxf(m_run, cmax);
+        const float alpha = exp2f(m_run - m_new);  // 0 on the first step
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[nt] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
       float psum = 0.f;
       u4 pw;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        // value norms of tokens 16 (2 step + u) + 4 q + i, masked past n_tokens
-        const f4 vnv = *(const f4*)(vnorm + 16 * (2 * step + u) + 4 * q);
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
-          float pv[2];
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const int i = 2 * i2 + k;
-            const bool ok = tok0 + 16 * (2 * step + u) + 4 * q + i < a.n_tokens;
-            const float p = m_new == -INFINITY ? 0.f : exp2f(lg[u][i] - m_new);
-            psum += p;
-            pv[k] = ok ? p * (vnv[i] * vs) : 0.f;
-          }
-          const _Float16 h0 = (_Float16)pv[0], h1 = (_Float16)pv[1];
-          pw[2 * u + i2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          const float p0 = exp2f(lg[u][2 * i2] - m_run), p1 = exp2f(lg[u][2 * i2 + 1] - m_run);
+          psum += p0 + p1;
+          pw[2 * u + i2] = pack_h2(p0 * vn[u][2 * i2], p1 * vn[u][2 * i2 + 1]);
         }
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      l_run += psum;
       const h8 P = as_h8(pw);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        acc[nt] *= alpha;
         h8 A;
         if (step == 0) A = decode_pair<BV, 0>(vw[nt], vtlo, vthi);
         if (step == 1) A = decode_pair<BV, 2>(vw[nt], vtlo, vthi);

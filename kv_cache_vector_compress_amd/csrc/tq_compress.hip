@@ -51,6 +51,56 @@ __device__ __forceinline__ void copy_u4(uint16_t* dst, const uint16_t* src, int 
   for (int i = threadIdx.x; i < n; i += blockDim.x) ((u4*)dst)[i] = ((const u4*)src)[i];
 }
 
+// Load the 32 input coordinates a lane owns (8 per K block: 32 kb + 8 q ..)
+// of one token as fp16 operands, plus the token's sum of squares (partial,
+// over this lane's coordinates).  fp32 inputs are returned as hi/lo parts
+// after scaling by a power of two sc (|k sc| < 2^13): the caller needs the
+// norm first, so fp32 rows are loaded raw and split in split_f32_row.
+template <bool F32>
+__device__ __forceinline__ float load_row16(const void* x, int64_t row, int q, h8 (&xh)[4]) {
+  const _Float16* src = (const _Float16*)x + row * kD + 8 * q;
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    xh[kb] = *(const h8*)(src + 32 * kb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss[kb] = fmaf((float)xh[kb][e], (float)xh[kb][e], ss[kb]);
+  }
+  return (ss[0] + ss[1]) + (ss[2] + ss[3]);
+}
+
+__device__ __forceinline__ float load_row32(const void* x, int64_t row, int q, f4 (&v)[8]) {
+  const float* src = (const float*)x + row * kD + 8 * q;
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    v[2 * kb] = *(const f4*)(src + 32 * kb);
+    v[2 * kb + 1] = *(const f4*)(src + 32 * kb + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ss[kb] = fmaf(v[2 * kb][e], v[2 * kb][e], ss[kb]);
+      ss[kb] = fmaf(v[2 * kb + 1][e], v[2 * kb + 1][e], ss[kb]);
+    }
+  }
+  return (ss[0] + ss[1]) + (ss[2] + ss[3]);
+}
+
+__device__ __forceinline__ void split_row32(const f4 (&v)[8], float sc, h8 (&xh)[4], h8 (&xl)[4]) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    u4 hi, lo;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const f4& src = v[2 * kb + p / 2];
+      const HiLo t = split2(src[2 * (p % 2)] * sc, src[2 * (p % 2) + 1] * sc);
+      hi[p] = t.hi;
+      lo[p] = t.lo;
+    }
+    xh[kb] = as_h8(hi);
+    xl[kb] = as_h8(lo);
+  }
+}
+
 template <int B, int M, bool F32>
 __global__ __launch_bounds__(256, 1) void compress_keys_kernel(const KeyArgs a) {
   constexpr int NT = F32 ? 2 : 4;  // 16-token N tiles per wave iteration
@@ -61,16 +111,16 @@ __global__ __launch_bounds__(256, 1) void compress_keys_kernel(const KeyArgs a) 
   uint16_t* Rl = Rh + kRImg;
   uint16_t* Sh = Rl + kRImg;
   uint16_t* Sl = Sh + M * kLdsStride;
-  float* Cs = (float*)(Sl + M * kLdsStride);
+  float* Cs = (float*)(Sl + M * kLdsStride);  // centroids * 2^12
   copy_u4(Rh, a.r_hi, kRImg);
   copy_u4(Rl, a.r_lo, kRImg);
   copy_u4(Sh, a.s_hi, M * kLdsStride);
   copy_u4(Sl, a.s_lo, M * kLdsStride);
-  if (threadIdx.x < 16) Cs[threadIdx.x] = a.cb.cent[threadIdx.x];
+  if (threadIdx.x < 16) Cs[threadIdx.x] = a.cb.cent[threadIdx.x] * kResScale;
   __syncthreads();
 
-  float beta[15];
-  load_beta(beta, a.cb);
+  float bp[8];
+  load_pos_beta<B>(bp, a.cb);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t tps = (a.n_new + 16 * NT - 1) / (16 * NT);
@@ -81,56 +131,29 @@ __global__ __launch_bounds__(256, 1) void compress_keys_kernel(const KeyArgs a) 
     const int slot = (int)(tile / tps);
     const int64_t t0 = (tile - (int64_t)slot * tps) * (16 * NT);
 
+    // Inputs.  Rows past n_new are clamped to the last row: their results
+    // are never stored, they only need to be finite.
     h8 xh[NT][4];
     h8 xl[F32 ? NT : 1][4];
     float nrm[NT], inv[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int64_t tok = t0 + 16 * j + r16;
-      const bool valid = tok < a.n_new;
-      float ss = 0.f;
+      const int64_t row = (int64_t)slot * a.n_new + (tok < a.n_new ? tok : a.n_new - 1);
       if constexpr (F32) {
-        const float* src = (const float*)a.x + ((int64_t)slot * a.n_new + tok) * kD + 8 * q;
-        float v[4][8];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          f4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
-          if (valid) {
-            v0 = *(const f4*)(src + 32 * kb);
-            v1 = *(const f4*)(src + 32 * kb + 4);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { v[kb][e] = v0[e]; v[kb][4 + e] = v1[e]; }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(v[kb][e], v[kb][e], ss);
-        }
+        f4 v[8];
+        float ss = load_row32(a.x, row, q, v);
         ss += shfl_xor(ss, 16);
         ss += shfl_xor(ss, 32);
         const float n = sqrtf(ss);
         int E = 0;
         frexpf(n, &E);
-        const float sc = n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;  // |k * sc| < 2^13
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float s = v[kb][e] * sc;
-            const _Float16 h = (_Float16)s;
-            xh[j][kb][e] = h;
-            xl[j][kb][e] = (_Float16)(s - (float)h);
-          }
+        const float sc = n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;  // |k sc| < 2^13
+        split_row32(v, sc, xh[j], xl[j]);
         nrm[j] = n;
         inv[j] = n > 0.f ? 1.f / (kRotScale * sc * n) : 0.f;
       } else {
-        const _Float16* src = (const _Float16*)a.x + ((int64_t)slot * a.n_new + tok) * kD + 8 * q;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          h8 v = {};
-          if (valid) v = *(const h8*)(src + 32 * kb);
-          xh[j][kb] = v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf((float)v[e], (float)v[e], ss);
-        }
+        float ss = load_row16<false>(a.x, row, q, xh[j]);
         ss += shfl_xor(ss, 16);
         ss += shfl_xor(ss, 32);
         const float n = sqrtf(ss);
@@ -151,8 +174,11 @@ __global__ __launch_bounds__(256, 1) void compress_keys_kernel(const KeyArgs a) 
       for (int p = 0; p < PT; ++p) zacc[j][p] = f4{0.f, 0.f, 0.f, 0.f};
     }
 
-#pragma unroll 1
+#pragma unroll
     for (int kb2 = 0; kb2 < 4; ++kb2) {  // output tiles 2 kb2, 2 kb2 + 1 = projection K block kb2
+      // one pass per pair of output tiles; the barrier below keeps the
+      // scheduler from hoisting later passes' LDS loads (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
       f4 yacc[NT][2];
 #pragma unroll
       for (int j = 0; j < NT; ++j) yacc[j][0] = yacc[j][1] = f4{0.f, 0.f, 0.f, 0.f};
@@ -174,38 +200,42 @@ __global__ __launch_bounds__(256, 1) void compress_keys_kernel(const KeyArgs a) 
             if constexpr (F32) yacc[j][u] = mfma(ah[u], xl[j][kb], yacc[j][u]);
           }
       }
-      // bucket, residual, pack; build the residual operand of the projection
-      h8 rh[NT], rl[NT];
+      h8 sh[PT], sl[PT];
+#pragma unroll
+      for (int p = 0; p < PT; ++p) {
+        const int off = (16 * p + r16) * kLdsStride + 32 * kb2 + 8 * q;
+        sh[p] = *(const h8*)(Sh + off);
+        sl[p] = *(const h8*)(Sl + off);
+      }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
+        // bucket, scaled residual rs = 2^12 (y - c[idx]), codes, residual operands
+        u4 rhi, rlo;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
+          float rs[4];
           uint32_t x4 = 0;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float y = yacc[j][u][i] * inv[j];
-            const int idx = bucket<B>(y, beta);
-            const float r = y - Cs[idx];
-            g2[j] = fmaf(r, r, g2[j]);
+            const int idx = bucket_sym<B>(y, bp);
+            rs[i] = fmaf(y, kResScale, -Cs[idx]);
+            g2[j] = fmaf(rs[i], rs[i], g2[j]);
             x4 |= (uint32_t)idx << (8 * i);
-            const float rs = r * kResScale;
-            const _Float16 h = (_Float16)rs;
-            rh[j][4 * u + i] = h;
-            rl[j][4 * u + i] = (_Float16)(rs - (float)h);
           }
+          const HiLo t01 = split2(rs[0], rs[1]), t23 = split2(rs[2], rs[3]);
+          rhi[2 * u] = t01.hi;
+          rlo[2 * u] = t01.lo;
+          rhi[2 * u + 1] = t23.hi;
+          rlo[2 * u + 1] = t23.lo;
           put_sel4_rt<B>(cw[j], 2 * kb2 + u, x4);
         }
-      }
+        const h8 rh = as_h8(rhi), rl = as_h8(rlo);
 #pragma unroll
-      for (int p = 0; p < PT; ++p) {
-        const int off = (16 * p + r16) * kLdsStride + 32 * kb2 + 8 * q;
-        const h8 sh = *(const h8*)(Sh + off);
-        const h8 sl = *(const h8*)(Sl + off);
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          zacc[j][p] = mfma(sh, rh[j], zacc[j][p]);
-          zacc[j][p] = mfma(sl, rh[j], zacc[j][p]);
-          zacc[j][p] = mfma(sh, rl[j], zacc[j][p]);
+        for (int p = 0; p < PT; ++p) {
+          zacc[j][p] = mfma(sh[p], rh, zacc[j][p]);
+          zacc[j][p] = mfma(sl[p], rh, zacc[j][p]);
+          zacc[j][p] = mfma(sh[p], rl, zacc[j][p]);
         }
       }
     }
@@ -215,15 +245,15 @@ __global__ __launch_bounds__(256, 1) void compress_keys_kernel(const KeyArgs a) 
       float g = g2[j];
       g += shfl_xor(g, 16);
       g += shfl_xor(g, 32);
-      const float gamma = sqrtf(g);
+      const float gamma = sqrtf(g) * (1.f / kResScale);
       uint32_t bits[NCH];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         uint32_t v = 0;
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp)
+        for (int pp = 3; pp >= 0; --pp)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v |= (zacc[j][4 * c + pp][i] >= 0.f ? 1u : 0u) << (4 * pp + i);
+          for (int i = 3; i >= 0; --i) v = (v << 1) | (zacc[j][4 * c + pp][i] >= 0.f ? 1u : 0u);
         bits[c] = v;
       }
       const int64_t tok = t0 + 16 * j + r16;
@@ -290,8 +320,8 @@ __global__ __launch_bounds__(256, 1) void compress_values_kernel(const ValArgs a
   copy_u4(Rl, a.r_lo, kRImg);
   __syncthreads();
 
-  float beta[15];
-  load_beta(beta, a.cb);
+  float bp[8];
+  load_pos_beta<B>(bp, a.cb);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int waves = blockDim.x >> 6;
@@ -318,52 +348,27 @@ __global__ __launch_bounds__(256, 1) void compress_values_kernel(const ValArgs a
       float inv_tok[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
+        // block token tau -> input row; rows outside [pos, pos + n_new) are
+        // clamped to a valid row (finite data whose codes are masked out)
         const int tau = 16 * (4 * half + mt) + r16;
-        const int64_t row = tok0 + tau - a.pos;
+        int64_t row = tok0 + tau - a.pos;
         const bool valid = row >= 0 && row < a.n_new;
-        float ss = 0.f;
+        row = (int64_t)slot * a.n_new + (row < 0 ? 0 : (row >= a.n_new ? a.n_new - 1 : row));
+        float ss;
         if constexpr (F32) {
-          const float* src = (const float*)a.x + ((int64_t)slot * a.n_new + row) * kD + 8 * q;
-          float v[4][8];
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            f4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
-            if (valid) {
-              v0 = *(const f4*)(src + 32 * kb);
-              v1 = *(const f4*)(src + 32 * kb + 4);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { v[kb][e] = v0[e]; v[kb][4 + e] = v1[e]; }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(v[kb][e], v[kb][e], ss);
-          }
+          f4 v[8];
+          ss = load_row32(a.x, row, q, v);
           ss += shfl_xor(ss, 16);
           ss += shfl_xor(ss, 32);
           const float n = sqrtf(ss);
           int E = 0;
           frexpf(n, &E);
           const float sc = n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float s = v[kb][e] * sc;
-              const _Float16 h = (_Float16)s;
-              xa[mt][kb][e] = h;
-              xl[mt][kb][e] = (_Float16)(s - (float)h);
-            }
+          split_row32(v, sc, xa[mt], xl[mt]);
           inv_tok[mt] = n > 0.f ? 1.f / (kRotScale * sc * n) : 0.f;
           if (q == 0 && valid) vnorm[tau] = n;
         } else {
-          const _Float16* src = (const _Float16*)a.x + ((int64_t)slot * a.n_new + row) * kD + 8 * q;
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            h8 v = {};
-            if (valid) v = *(const h8*)(src + 32 * kb);
-            xa[mt][kb] = v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf((float)v[e], (float)v[e], ss);
-          }
+          ss = load_row16<false>(a.x, row, q, xa[mt]);
           ss += shfl_xor(ss, 16);
           ss += shfl_xor(ss, 32);
           const float n = sqrtf(ss);
@@ -409,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void compress_values_kernel(const ValArgs a
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float y = acc[mt][u][i] * inv_d[mt][i];
-              x4 |= (uint32_t)bucket<B>(y, beta) << (8 * i);
+              x4 |= (uint32_t)bucket_sym<B>(y, bp) << (8 * i);
             }
             put_sel4_rt<B>(cw[2 * ntp + u], 4 * half + mt, x4);  // slot of these 16 tokens
           }

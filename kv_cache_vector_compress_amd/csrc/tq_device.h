@@ -181,6 +181,33 @@ __device__ __forceinline__ int bucket(float y, const float (&beta)[15]) {
   }
 }
 
+
+// Lloyd-Max cell of y for a codebook symmetric about 0 (c_i = -c_{L-1-i},
+// middle boundary 0): with k = #{j : |y| > beta+_j} over the H-1 positive
+// boundaries (H = L/2), idx = H + k for y > 0 and H - 1 - k otherwise, i.e.
+// idx = k ^ (y > 0 ? H : H-1).  bp[j] = beta_{H + j}.  Compare + add-with-
+// carry per boundary, no selects and no branches.
+template <int B>
+__device__ __forceinline__ int bucket_sym(float y, const float (&bp)[8]) {
+  constexpr int H = 1 << (B - 1);
+  const float a = fabsf(y);
+  int k = 0;
+#pragma unroll
+  for (int j = 0; j < H - 1; ++j) k += a > bp[j] ? 1 : 0;
+  return k ^ (y > 0.f ? H : H - 1);
+}
+
+// Split two fp32 values into fp16 high parts (round toward zero) and fp16
+// low parts (the exact remainders, rounded): x = hi + lo to ~2^-22 relative.
+struct HiLo {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ HiLo split2(float x0, float x1) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+  const auto l = __builtin_amdgcn_cvt_pkrtz(x0 - (float)h[0], x1 - (float)h[1]);
+  return HiLo{__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
+}
+
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
 // Runtime-slot form of put_sel4 (the switch folds away when s is a constant).
@@ -202,6 +229,14 @@ __device__ __forceinline__ void put_sel4_rt(uint32_t (&w)[B], int s, uint32_t x)
 __device__ __forceinline__ void load_beta(float (&beta)[15], const CodebookDev& cb) {
 #pragma unroll
   for (int i = 0; i < 15; ++i) beta[i] = cb.beta[i];
+}
+
+// The positive boundaries beta_{H}, beta_{H+1}, ... of a symmetric codebook.
+template <int B>
+__device__ __forceinline__ void load_pos_beta(float (&bp)[8], const CodebookDev& cb) {
+  constexpr int H = 1 << (B - 1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bp[j] = j < H - 1 ? cb.beta[H + j] : INFINITY;
 }
 
 }  // namespace tq

@@ -17,6 +17,7 @@ bool lloyd_max_standard(int bits, double* c, double* beta);
 constexpr int kD = 128;          // head_dim of the built fast path
 constexpr int kLdsStride = 136;  // padded fp16 row stride of R / S images (conflict-free b128 reads)
 constexpr int kBlockTokens = 128;
+constexpr int64_t kMaxCapacity = int64_t(1) << 24;  // tokens per slot: in-slot word offsets fit 32 bits
 constexpr float kRotScale = 256.0f;   // R and S images are scaled by 2^8 before the hi/lo fp16 split
 constexpr float kResScale = 4096.0f;  // residual scaled by 2^12 before its hi/lo split
 
