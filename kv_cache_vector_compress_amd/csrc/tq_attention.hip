@@ -24,6 +24,7 @@ namespace tq {
 constexpr int kPartFloats = 4 + kD;  // m, l, pad, pad, acc[d]
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int64_t kTargetWaves = 256 * 16;
+constexpr int kMaxPartials = 1024;
 
 // ---------------------------------------------------------------------------
 // query preparation: MFMA B operands of q~/|q| and p/|q|, and |q|
@@ -41,27 +42,36 @@ struct PrepArgs {
 template <int M>
 __global__ __launch_bounds__(256) void prep_queries_kernel(const PrepArgs a) {
   constexpr int KBT = 4 + M / 32;
-  __shared__ float qs[16][kD];
-  __shared__ float qt[16][kD];
+  __shared__ __align__(16) float qs[16][kD];
+  __shared__ __align__(16) float qt[16][kD];
   __shared__ float pp[16][M];
   __shared__ float qn[16];
   const int slot = blockIdx.x, tid = threadIdx.x;
+  const int G = a.G;
   for (int idx = tid; idx < 16 * kD; idx += blockDim.x) {
     const int h = idx / kD, k = idx % kD;
     float v = 0.f;
-    if (h < a.G) {
-      const int64_t off = ((int64_t)slot * a.G + h) * kD + k;
+    if (h < G) {
+      const int64_t off = ((int64_t)slot * G + h) * kD + k;
       v = a.dtype == TQ_F32 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
     }
     qs[h][k] = v;
   }
   __syncthreads();
-  for (int idx = tid; idx < 16 * kD; idx += blockDim.x) {
+  // q~ = R q: thread (j, head group) reads row j of R with 16-byte loads
+  for (int idx = tid; idx < G * kD; idx += blockDim.x) {
     const int h = idx / kD, j = idx % kD;
-    float s = 0.f;
-    if (h < a.G)
-      for (int k = 0; k < kD; ++k) s = fmaf(a.r32[j * kD + k], qs[h][k], s);
-    qt[h][j] = s;
+    const f4* row = (const f4*)(a.r32 + j * kD);
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll 8
+    for (int k4 = 0; k4 < kD / 4; ++k4) {
+      const f4 r = row[k4];
+      s0 = fmaf(r[0], qs[h][4 * k4], s0);
+      s1 = fmaf(r[1], qs[h][4 * k4 + 1], s1);
+      s2 = fmaf(r[2], qs[h][4 * k4 + 2], s2);
+      s3 = fmaf(r[3], qs[h][4 * k4 + 3], s3);
+    }
+    qt[h][j] = (s0 + s1) + (s2 + s3);
   }
   if (tid < 16) {
     float s = 0.f;
@@ -69,21 +79,28 @@ __global__ __launch_bounds__(256) void prep_queries_kernel(const PrepArgs a) {
     qn[tid] = sqrtf(s);
   }
   __syncthreads();
-  for (int idx = tid; idx < 16 * M; idx += blockDim.x) {
+  for (int idx = tid; idx < G * M; idx += blockDim.x) {
     const int h = idx / M, i = idx % M;
-    float s = 0.f;
-    if (h < a.G)
-      for (int j = 0; j < kD; ++j) s = fmaf(a.s32[i * kD + j], qt[h][j], s);
-    pp[h][i] = s;
+    const f4* row = (const f4*)(a.s32 + i * kD);
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll 8
+    for (int k4 = 0; k4 < kD / 4; ++k4) {
+      const f4 r = row[k4];
+      s0 = fmaf(r[0], qt[h][4 * k4], s0);
+      s1 = fmaf(r[1], qt[h][4 * k4 + 1], s1);
+      s2 = fmaf(r[2], qt[h][4 * k4 + 2], s2);
+      s3 = fmaf(r[3], qt[h][4 * k4 + 3], s3);
+    }
+    pp[h][i] = (s0 + s1) + (s2 + s3);
   }
   __syncthreads();
   for (int idx = tid; idx < KBT * 64; idx += blockDim.x) {
     const int kb = idx / 64, l = idx % 64, h = l % 16, qq = l / 16;
-    const float inv = qn[h] > 0.f ? 1.f / qn[h] : 0.f;
+    const float inv = h < G && qn[h] > 0.f ? 1.f / qn[h] : 0.f;
     h8 v;
     if (kb < 4) {
       // centroid part, k slot e <-> coordinate 16 (2 kb + e/4) + 4 qq + e%4
-      for (int e = 0; e < 8; ++e) v[e] = (_Float16)(qt[h][16 * (2 * kb + e / 4) + 4 * qq + e % 4] * inv);
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)(h < G ? qt[h][16 * (2 * kb + e / 4) + 4 * qq + e % 4] * inv : 0.f);
     } else {
       // sign part, k slot 2e+half <-> sign bit p + 16 half of word 2 (kbp/2) + qq/2,
       // p = 8 (qq%2) + 4 (kbp%2) + e; that bit holds projection coordinate
@@ -94,12 +111,12 @@ __global__ __launch_bounds__(256) void prep_queries_kernel(const PrepArgs a) {
           const int p = 8 * (qq % 2) + 4 * (kbp % 2) + e;
           const int qsg = 2 * (qq / 2) + half;
           const int t = 4 * (kbp / 2) + p / 4;
-          v[2 * e + half] = (_Float16)(pp[h][16 * t + 4 * qsg + p % 4] * inv);
+          v[2 * e + half] = (_Float16)(h < G ? pp[h][16 * t + 4 * qsg + p % 4] * inv : 0.f);
         }
     }
     *(h8*)(a.wq + (((int64_t)slot * KBT + kb) * 64 + l) * 8) = v;
   }
-  if (tid < 16) a.wqn[slot * 16 + tid] = qn[tid];
+  if (tid < 16) a.wqn[slot * 16 + tid] = tid < G ? qn[tid] : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -427,24 +444,60 @@ struct CombineArgs {
 };
 
 __global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
-  __shared__ float y[kD];
+  __shared__ float w[kMaxPartials];  // per-partial weights exp2(m_c - M)
+  __shared__ float red[128];
+  __shared__ __align__(16) float y[kD];
   const int sh = blockIdx.x, slot = sh / a.G, h = sh % a.G, j = threadIdx.x;
-  const float* pr = a.part + ((int64_t)slot * a.waves_per_slot * a.G + h) * kPartFloats;
+  const int W = a.waves_per_slot;
+  const float* pr = a.part + ((int64_t)slot * W * a.G + h) * kPartFloats;
   const int64_t stride = (int64_t)a.G * kPartFloats;
+  // maximum of the partial maxima
   float M = -INFINITY;
-  for (int c = 0; c < a.waves_per_slot; ++c) M = fmaxf(M, pr[c * stride]);
-  float L = 0.f, acc = 0.f;
-  for (int c = 0; c < a.waves_per_slot; ++c) {
-    const float mc = pr[c * stride];
-    const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
-    L = fmaf(w, pr[c * stride + 1], L);
-    acc = fmaf(w, pr[c * stride + 4 + j], acc);
-  }
-  y[j] = acc / L;
+  for (int c = j; c < W; c += blockDim.x) M = fmaxf(M, pr[c * stride]);
+  red[j] = M;
   __syncthreads();
-  float o = 0.f;
-  for (int i = 0; i < kD; ++i) o = fmaf(a.r32[i * kD + j], y[i], o);
-  a.out[((int64_t)slot * a.G + h) * kD + j] = o;
+  for (int o = 64; o > 0; o >>= 1) {
+    if (j < o) red[j] = fmaxf(red[j], red[j + o]);
+    __syncthreads();
+  }
+  M = red[0];
+  __syncthreads();
+  // weights and the weighted sum of the partial sums
+  float L = 0.f;
+  for (int c = j; c < W; c += blockDim.x) {
+    const float mc = pr[c * stride];
+    const float wc = mc == -INFINITY ? 0.f : exp2f(mc - M);
+    w[c] = wc;
+    L = fmaf(wc, pr[c * stride + 1], L);
+  }
+  red[j] = L;
+  __syncthreads();
+  for (int o = 64; o > 0; o >>= 1) {
+    if (j < o) red[j] += red[j + o];
+    __syncthreads();
+  }
+  L = red[0];
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  int c = 0;
+  for (; c + 4 <= W; c += 4) {
+    acc0 = fmaf(w[c], pr[c * stride + 4 + j], acc0);
+    acc1 = fmaf(w[c + 1], pr[(c + 1) * stride + 4 + j], acc1);
+    acc2 = fmaf(w[c + 2], pr[(c + 2) * stride + 4 + j], acc2);
+    acc3 = fmaf(w[c + 3], pr[(c + 3) * stride + 4 + j], acc3);
+  }
+  for (; c < W; ++c) acc0 = fmaf(w[c], pr[c * stride + 4 + j], acc0);
+  y[j] = ((acc0 + acc1) + (acc2 + acc3)) / L;
+  __syncthreads();
+  // out = R^T y (column j of R, coalesced across threads)
+  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+#pragma unroll 4
+  for (int i = 0; i < kD; i += 4) {
+    o0 = fmaf(a.r32[i * kD + j], y[i], o0);
+    o1 = fmaf(a.r32[(i + 1) * kD + j], y[i + 1], o1);
+    o2 = fmaf(a.r32[(i + 2) * kD + j], y[i + 2], o2);
+    o3 = fmaf(a.r32[(i + 3) * kD + j], y[i + 3], o3);
+  }
+  a.out[((int64_t)slot * a.G + h) * kD + j] = (o0 + o1) + (o2 + o3);
 }
 
 // ---------------------------------------------------------------------------
@@ -469,6 +522,8 @@ AttnPlan plan_attention(int m, int n_seq, int G, int64_t n_tokens) {
   const int64_t target_waves = kTargetWaves;
   int64_t bpw = (nblk * n_seq + target_waves - 1) / target_waves;
   if (bpw < 1) bpw = 1;
+  // the combine kernel merges at most kMaxPartials partials per query head
+  if ((nblk + bpw - 1) / bpw > kMaxPartials) bpw = (nblk + kMaxPartials - 1) / kMaxPartials;
   p.blocks_per_wave = (int)bpw;
   p.waves_per_slot = (int)((nblk + bpw - 1) / bpw);
   p.q_bytes = (size_t)n_seq * KBT * 64 * 8 * 2;

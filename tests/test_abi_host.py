@@ -110,3 +110,4 @@ def test_hot_path_entry_points_reject_null_context():
                          ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 20, None) == -1
     assert lib.tq_codebook_load(None, 3, None, None) == -1
     assert lib.tq_destroy(None) == 0
+

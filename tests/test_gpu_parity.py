@@ -200,6 +200,12 @@ def test_error_paths_leave_buffers_untouched():
     kmis = torch.zeros(2 * 10 * 128 + 4, dtype=torch.float16, device="cuda")[4:]
     expect(-1, lambda: tq._check(tq.lib().tq_append_key(ctx.handle, tq.ctypes.byref(cache.view),
                                                        tq.ctypes.c_void_p(kmis.data_ptr()), 1, 0, 10, None)))
+    # a codebook that is not symmetric about 0 is rejected
+    D = tq.ctypes.POINTER(tq.ctypes.c_double)
+    c_bad = np.array([-0.2, -0.05, 0.06, 0.2])
+    b_bad = np.array([-0.1, 0.0, 0.1])
+    expect(-1, lambda: tq._check(tq.lib().tq_codebook_load(ctx.handle, 2, c_bad.ctypes.data_as(D),
+                                                          b_bad.ctypes.data_as(D))))
     # no codebook for the requested bits
     ctx2 = tq.Context(128, 64, 2, 2, R, S, load_codebooks=False)
     cache2 = tq.KVCache(ctx2, 2, 256)
