@@ -33,10 +33,16 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-file extra flags.  The attention kernels keep their matrix-core
+# accumulators in ordinary VGPRs (they are rescaled by VALU code), so ask for
+# the VGPR form of MFMA there instead of round-tripping through AGPRs.
+EXTRA = {"tq_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l and "unknown target feature" not in l)

@@ -196,7 +196,8 @@ template <int B, int M>
 __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
   constexpr int KBT = 4 + M / 32;
   constexpr int RW = rec_words<B, M>();
-  __shared__ float nsh[4][16];  // per wave: ||k|| of the tile's 16 tokens
+  constexpr int U = 4;          // 16-token tiles per iteration (next U tiles in flight)
+  __shared__ float nsh[4][16 * U];  // per wave: ||k|| of the iteration's tokens
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
@@ -215,8 +216,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
   const int ntile = (n_tok + 15) >> 4;
   const int t_begin = wc * a.tiles_per_wave;
   const int t_end = min(ntile, t_begin + a.tiles_per_wave);
-  const uint32_t* base = a.rec + (size_t)slot * (size_t)a.capacity * RW + q * B;
-  const uint32_t* sbase = a.rec + (size_t)slot * (size_t)a.capacity * RW + 4 * B + (q >> 1);
+  const uint32_t* base = a.rec + (size_t)slot * (size_t)a.capacity * RW;
   float* out = a.scores + ((size_t)slot * a.G + r16) * (size_t)n_tok;
   const bool head_ok = r16 < a.G;
   const bool vec_store = (n_tok & 3) == 0;
@@ -225,34 +225,45 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
     const int t = min(tile * 16 + r16, n_tok - 1);  // rows past the end: any valid row
     const uint32_t* rp = base + t * RW;
 #pragma unroll
-    for (int w = 0; w < B; ++w) k.cw[w] = rp[w];
-    const uint32_t* sp = sbase + t * RW;
+    for (int w = 0; w < B; ++w) k.cw[w] = rp[q * B + w];
 #pragma unroll
-    for (int c = 0; c < M / 64; ++c) k.sw[c] = sp[2 * c];
-    k.n = __uint_as_float(rp[RW - 2 - q * B]);
-    k.g = __uint_as_float(rp[RW - 1 - q * B]);
+    for (int c = 0; c < M / 64; ++c) k.sw[c] = rp[4 * B + 2 * c + (q >> 1)];
+    k.n = __uint_as_float(rp[RW - 2]);
+    k.g = __uint_as_float(rp[RW - 1]);
   };
 
-  KeyTile<B, M> cur;
-  if (t_begin < t_end) load(cur, t_begin);
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    KeyTile<B, M> nxt;
-    if (tile + 1 < t_end) load(nxt, tile + 1);
-    const f4 acc = key_tile_scores<B, M>(cur, qb, tlo, thi, a.kappa, sh0);
-    if (q == 0) nsh[wave][r16] = cur.n;
-    const f4 nk = *(const f4*)&nsh[wave][4 * q];  // ||k|| of token rows 4q..4q+3
-    const int t0 = tile * 16 + 4 * q;
-    if (head_ok) {
-      f4 v = acc * nk * qn;
-      if (vec_store && t0 + 4 <= n_tok) {
-        *(f4*)(out + t0) = v;
-      } else {
+  KeyTile<B, M> cur[U];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t0 + i < n_tok) out[t0 + i] = v[i];
+  for (int u = 0; u < U; ++u) load(cur[u], t_begin + u);
+  for (int tile = t_begin; tile < t_end; tile += U) {
+    KeyTile<B, M> nxt[U];
+    if (tile + U < t_end) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) load(nxt[u], tile + U + u);
+    }
+    f4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc[u] = key_tile_scores<B, M>(cur[u], qb, tlo, thi, a.kappa, sh0);
+      if (q == 0) nsh[wave][16 * u + r16] = cur[u].n;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const f4 nk = *(const f4*)&nsh[wave][16 * u + 4 * q];  // ||k|| of token rows 4q..4q+3
+      const int t0 = (tile + u) * 16 + 4 * q;
+      if (head_ok && tile + u < t_end) {
+        const f4 v = acc[u] * nk * qn;
+        if (vec_store && t0 + 4 <= n_tok) {
+          *(f4*)(out + t0) = v;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + i < n_tok) out[t0 + i] = v[i];
+        }
       }
     }
-    cur = nxt;
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
   }
 }
 
@@ -275,11 +286,23 @@ struct AttendArgs {
 };
 
 template <int BK, int BV, int M>
+struct StepKeys {  // the two 16-token key tiles of a 32-token step
+  KeyTile<BK, M> t[2];
+};
+
+template <int BV>
+struct BlockValues {  // one 128-token value block as this lane needs it
+  uint32_t vw[8][BV];
+  float2 vn;          // norms of block tokens 2 lane, 2 lane + 1
+};
+
+template <int BK, int BV, int M>
 __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   constexpr int KBT = 4 + M / 32;
   constexpr int RW = rec_words<BK, M>();
   constexpr int BW = 4 * BV * kD + kBlockTokens;
-  __shared__ float nsh[4][32];  // per wave: ||k|| of the step's 32 tokens
+  __shared__ float nsh[4][32];               // per wave: ||k|| of the step's 32 tokens
+  __shared__ __align__(16) float vsh[4][kBlockTokens];  // per wave: the block's ||v||
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
@@ -304,37 +327,57 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   const uint32_t* kbase = a.rec + (size_t)slot * (size_t)a.capacity * RW;
   const uint32_t* vbase = a.vblocks + (size_t)slot * (size_t)(a.capacity / kBlockTokens) * BW;
 
+  auto load_keys = [&](StepKeys<BK, BV, M>& k, int tt) {  // tt: first token of the step
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = min(tt + 16 * u + r16, n_tok - 1);  // rows past the end: any valid row
+      const uint32_t* rp = kbase + t * RW;
+#pragma unroll
+      for (int w = 0; w < BK; ++w) k.t[u].cw[w] = rp[q * BK + w];
+#pragma unroll
+      for (int c = 0; c < M / 64; ++c) k.t[u].sw[c] = rp[4 * BK + 2 * c + (q >> 1)];
+      k.t[u].n = __uint_as_float(rp[RW - 2]);
+      k.t[u].g = __uint_as_float(rp[RW - 1]);
+    }
+  };
+  auto load_values = [&](BlockValues<BV>& v, int blk) {
+    const uint32_t* vb = vbase + blk * BW;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int w = 0; w < BV; ++w) v.vw[nt][w] = vb[(w * 4 + q) * kD + 16 * nt + r16];
+    v.vn = *(const float2*)(vb + 4 * BV * kD + 2 * lane);
+  };
+
   float m_run = -INFINITY, l_run = 0.f;
   int ve = -1000;  // running exponent of the value norms (wave-uniform)
   f4 acc[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
 
+  BlockValues<BV> vcur;
+  StepKeys<BK, BV, M> kcur;
+  if (b_begin < b_end) {
+    load_values(vcur, b_begin);
+    load_keys(kcur, b_begin * kBlockTokens);
+  }
   for (int blk = b_begin; blk < b_end; ++blk) {
     const int tok0 = blk * kBlockTokens;
     const bool full = tok0 + kBlockTokens <= n_tok;  // wave-uniform
-    const uint32_t* vb = vbase + blk * BW;
-    const float* vnorm = (const float*)(vb + 4 * BV * kD);
-    uint32_t vw[8][BV];
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int w = 0; w < BV; ++w) vw[nt][w] = vb[(w * 4 + q) * kD + 16 * nt + r16];
+    const bool more = blk + 1 < b_end;
+    BlockValues<BV> vnext;
+    if (more) load_values(vnext, blk + 1);  // in flight during this block
     // Value norms enter P as ||v|| 2^-ve with ve the running maximum
     // exponent of the norms seen so far, so P stays in fp16 range whatever
     // the norms' scale; the accumulator is rescaled when ve grows.
-    float bmax;
-    {
-      const float2 v2 = *(const float2*)(vnorm + 2 * lane);
-      float x0 = v2.x, x1 = v2.y;
-      if (!full) {
-        x0 = tok0 + 2 * lane < n_tok ? x0 : 0.f;
-        x1 = tok0 + 2 * lane + 1 < n_tok ? x1 : 0.f;
-      }
-      bmax = fmaxf(x0, x1);
-#pragma unroll
-      for (int sh = 1; sh < 64; sh <<= 1) bmax = fmaxf(bmax, shfl_xor(bmax, sh));
+    float x0 = vcur.vn.x, x1 = vcur.vn.y;
+    if (!full) {
+      x0 = tok0 + 2 * lane < n_tok ? x0 : 0.f;
+      x1 = tok0 + 2 * lane + 1 < n_tok ? x1 : 0.f;
     }
+    float bmax = fmaxf(x0, x1);
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) bmax = fmaxf(bmax, shfl_xor(bmax, sh));
     int e_blk = 0;
     frexpf(bmax, &e_blk);
     if (e_blk > ve) {
@@ -344,28 +387,25 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
       ve = e_blk;
     }
     const float vs = ldexpf(1.f, -ve);
+    *(float2*)&vsh[wave][2 * lane] = make_float2(x0 * vs, x1 * vs);
 
 #pragma unroll
     for (int step = 0; step < 4; ++step) {
-      f4 sc[2], nk[2], vn[2];
+      StepKeys<BK, BV, M> knext;
+      if (step < 3) load_keys(knext, tok0 + 32 * (step + 1));
+      else if (more) load_keys(knext, tok0 + kBlockTokens);
+      f4 sc[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int tt = tok0 + 16 * (2 * step + u);
-        const int t = full ? tt + r16 : min(tt + r16, n_tok - 1);
-        const uint32_t* rp = kbase + t * RW;
-        KeyTile<BK, M> kt;
-#pragma unroll
-        for (int w = 0; w < BK; ++w) kt.cw[w] = rp[q * BK + w];
-#pragma unroll
-        for (int c = 0; c < M / 64; ++c) kt.sw[c] = rp[4 * BK + 2 * c + (q >> 1)];
-        kt.n = __uint_as_float(rp[RW - 2]);
-        kt.g = __uint_as_float(rp[RW - 1]);
-        sc[u] = key_tile_scores<BK, M>(kt, qb, tlo, thi, a.kappa, sh0);
-        if (q == 0) nsh[wave][16 * u + r16] = kt.n;
-        vn[u] = *(const f4*)(vnorm + 16 * (2 * step + u) + 4 * q);
+        sc[u] = key_tile_scores<BK, M>(kcur.t[u], qb, tlo, thi, a.kappa, sh0);
+        if (q == 0) nsh[wave][16 * u + r16] = kcur.t[u].n;
       }
-      nk[0] = *(const f4*)&nsh[wave][4 * q];
-      nk[1] = *(const f4*)&nsh[wave][16 + 4 * q];
+      f4 nk[2], vn[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        nk[u] = *(const f4*)&nsh[wave][16 * u + 4 * q];
+        vn[u] = *(const f4*)&vsh[wave][16 * (2 * step + u) + 4 * q];
+      }
       float lg[2][4];
       float cmax = -INFINITY;
 #pragma unroll
@@ -373,14 +413,8 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float l = sc[u][i] * nk[u][i] * qsc;
-          float v = vn[u][i] * vs;
-          if (!full) {
-            const bool ok = tok0 + 16 * (2 * step + u) + 4 * q + i < n_tok;
-            l = ok ? l : -INFINITY;
-            v = ok ? v : 0.f;
-          }
+          if (!full) l = tok0 + 16 * (2 * step + u) + 4 * q + i < n_tok ? l : -INFINITY;
           lg[u][i] = l;
-          vn[u][i] = v;
           cmax = fmaxf(cmax, l);
         }
       cmax = fmaxf(cmax, shfl_xor(cmax, 16));
@@ -410,13 +444,15 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         h8 A;
-        if (step == 0) A = decode_pair<BV, 0>(vw[nt], vtlo, vthi);
-        if (step == 1) A = decode_pair<BV, 2>(vw[nt], vtlo, vthi);
-        if (step == 2) A = decode_pair<BV, 4>(vw[nt], vtlo, vthi);
-        if (step == 3) A = decode_pair<BV, 6>(vw[nt], vtlo, vthi);
+        if (step == 0) A = decode_pair<BV, 0>(vcur.vw[nt], vtlo, vthi);
+        if (step == 1) A = decode_pair<BV, 2>(vcur.vw[nt], vtlo, vthi);
+        if (step == 2) A = decode_pair<BV, 4>(vcur.vw[nt], vtlo, vthi);
+        if (step == 3) A = decode_pair<BV, 6>(vcur.vw[nt], vtlo, vthi);
         acc[nt] = mfma(A, P, acc[nt]);
       }
+      kcur = knext;
     }
+    vcur = vnext;
   }
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
