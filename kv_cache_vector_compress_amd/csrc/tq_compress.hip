@@ -102,8 +102,11 @@ __device__ __forceinline__ void split_row32(const f4 (&v)[8], float sc, h8 (&xh)
 }
 
 template <int B, int M, bool F32>
-__global__ __launch_bounds__(256, 1) void compress_keys_kernel(const KeyArgs a) {
-  constexpr int NT = F32 ? 2 : 4;  // 16-token N tiles per wave iteration
+__global__ __launch_bounds__(512, 1) void compress_keys_kernel(const KeyArgs a) {
+  // 8 waves (2 per SIMD) share the LDS images; 2 (fp32: 1) 16-token tiles per
+  // wave iteration keep a wave within 256 registers, so the two waves of a
+  // SIMD overlap one's matrix-core work with the other's bucketing
+  constexpr int NT = (F32 || M > 64) ? 1 : 2;  // 16-token N tiles per wave iteration
   constexpr int PT = M / 16;       // projection M tiles
   constexpr int NCH = M / 64;      // 16-bit sign chunks per lane
   extern __shared__ __align__(16) uint16_t lds[];
@@ -312,7 +315,7 @@ __device__ __forceinline__ uint32_t field_mask_rt(int b, int s, int w, int i) {
 }
 
 template <int B, bool F32>
-__global__ __launch_bounds__(256, 1) void compress_values_kernel(const ValArgs a) {
+__global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const ValArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   uint16_t* Rh = lds;
   uint16_t* Rl = Rh + kRImg;
@@ -489,7 +492,7 @@ int compress_device_init() {
 
 template <int B, int M, bool F32>
 static void key_launch(const KeyArgs& a, int64_t ntiles, hipStream_t st) {
-  const int waves = 4;
+  const int waves = 8;
   int64_t grid = (ntiles + waves - 1) / waves;
   const int64_t cap = (int64_t)(g_num_cus > 0 ? g_num_cus : 256);
   if (grid > cap) grid = cap;
@@ -513,7 +516,7 @@ int launch_compress_keys(const Matrices& mats, const CodebookDev& cb, int bits, 
   a.rec_words = bits * kD / 32 + m / 32 + 2;
   a.cb = cb;
   const bool f32 = s.dtype == TQ_F32;
-  const int64_t per = f32 ? 32 : 64;
+  const int64_t per = (f32 || m > 64) ? 16 : 32;
   const int64_t ntiles = ((s.n_new + per - 1) / per) * s.n_seq;
   hipStream_t st = (hipStream_t)stream;
 #define TQ_KEY_CASE(B, M)                                  \
@@ -532,7 +535,7 @@ template <int B, bool F32>
 static void val_launch(const ValArgs& a, int64_t nitems, hipStream_t st) {
   const int waves = 4;
   int64_t grid = (nitems + waves - 1) / waves;
-  const int64_t cap = (int64_t)(g_num_cus > 0 ? g_num_cus : 256);
+  const int64_t cap = (int64_t)(g_num_cus > 0 ? g_num_cus : 256) * (F32 ? 1 : 2);
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL((compress_values_kernel<B, F32>), dim3((unsigned)grid), dim3(64 * waves), kValLds, st, a);
 }
