@@ -49,7 +49,7 @@ def gen_inputs(n_seq, n_tok, d, G, heads_cycle, threads=16):
 
 
 def algorithmic_bytes(w):
-    """Bytes each stage must move at minimum."""
+    """Bytes each stage must move at minimum: inputs read once, outputs written once."""
     from kv_cache_vector_compress_amd import tq
     cfg = tq.Config(w["d"], w["m"], w["key_bits"], w["value_bits"])
     rec = tq.key_record_bytes(cfg)                      # 64
@@ -63,7 +63,34 @@ def algorithmic_bytes(w):
     }, units
 
 
-def cpu_baseline(w, slots=2):
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources (kernels and headers), sorted by name."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_vector_compress_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    record (FETCH_SIZE + WRITE_SIZE, calibrated on a plain device copy), or
+    None if the record is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_long_context.txt")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash() or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def cpu_baseline(w, slots=16):
     """The fp64 oracle, untuned, on a bounded sample of the same workload."""
     from oracle import turboquant as O
     from kv_cache_vector_compress_amd import synth
@@ -178,7 +205,8 @@ def main():
     stage_info["compress_keys"]["alg_TFLOPs"] = round(units * 2 * (d * d + m * d) / (stage_ms["compress_keys"] * 1e-3) / 1e12, 1)
     dom = max(stages, key=lambda s: stage_ms[s])
     roof = {"bound": "hbm", "kernel": dom, "achieved": stage_info[dom]["GBps"], "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": stage_info[dom]["frac_hbm_peak"], "traffic": None}
+            "unit": "GB/s", "frac": stage_info[dom]["frac_hbm_peak"], "traffic": counter_traffic(dom),
+            "alg_bytes": int(alg[dom])}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -42,12 +42,29 @@ struct PrepArgs {
 template <int M>
 __global__ __launch_bounds__(256) void prep_queries_kernel(const PrepArgs a) {
   constexpr int KBT = 4 + M / 32;
-  __shared__ __align__(16) float qs[16][kD];
-  __shared__ __align__(16) float qt[16][kD];
-  __shared__ float pp[16][M];
-  __shared__ float qn[16];
+  constexpr int LS = kD + 1;  // padded LDS row (conflict-free column walks)
+  extern __shared__ float sm[];
+  float* Rs = sm;                       // [kD][LS]
+  float* Ss = Rs + kD * LS;             // [M][LS]
+  float* qs = Ss + M * LS;              // [16][kD]
+  float* qt = qs + 16 * kD;             // [16][kD]
+  float* pp = qt + 16 * kD;             // [16][M]
+  float* qn = pp + 16 * M;              // [16]
   const int slot = blockIdx.x, tid = threadIdx.x;
   const int G = a.G;
+  // coalesced fills of R, S (16-byte loads) and of this slot's queries
+  for (int i = tid; i < kD * kD / 4; i += blockDim.x) {
+    const f4 v = ((const f4*)a.r32)[i];
+    const int r = (4 * i) / kD, c = (4 * i) % kD;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Rs[r * LS + c + e] = v[e];
+  }
+  for (int i = tid; i < M * kD / 4; i += blockDim.x) {
+    const f4 v = ((const f4*)a.s32)[i];
+    const int r = (4 * i) / kD, c = (4 * i) % kD;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ss[r * LS + c + e] = v[e];
+  }
   for (int idx = tid; idx < 16 * kD; idx += blockDim.x) {
     const int h = idx / kD, k = idx % kD;
     float v = 0.f;
@@ -55,43 +72,34 @@ __global__ __launch_bounds__(256) void prep_queries_kernel(const PrepArgs a) {
       const int64_t off = ((int64_t)slot * G + h) * kD + k;
       v = a.dtype == TQ_F32 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
     }
-    qs[h][k] = v;
+    qs[h * kD + k] = v;
   }
   __syncthreads();
-  // q~ = R q: thread (j, head group) reads row j of R with 16-byte loads
-  for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+  for (int idx = tid; idx < G * kD; idx += blockDim.x) {  // q~ = R q
     const int h = idx / kD, j = idx % kD;
-    const f4* row = (const f4*)(a.r32 + j * kD);
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll 8
-    for (int k4 = 0; k4 < kD / 4; ++k4) {
-      const f4 r = row[k4];
-      s0 = fmaf(r[0], qs[h][4 * k4], s0);
-      s1 = fmaf(r[1], qs[h][4 * k4 + 1], s1);
-      s2 = fmaf(r[2], qs[h][4 * k4 + 2], s2);
-      s3 = fmaf(r[3], qs[h][4 * k4 + 3], s3);
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll 16
+    for (int k = 0; k < kD; k += 2) {
+      s0 = fmaf(Rs[j * LS + k], qs[h * kD + k], s0);
+      s1 = fmaf(Rs[j * LS + k + 1], qs[h * kD + k + 1], s1);
     }
-    qt[h][j] = (s0 + s1) + (s2 + s3);
+    qt[h * kD + j] = s0 + s1;
   }
   if (tid < 16) {
     float s = 0.f;
-    for (int k = 0; k < kD; ++k) s = fmaf(qs[tid][k], qs[tid][k], s);
+    for (int k = 0; k < kD; ++k) s = fmaf(qs[tid * kD + k], qs[tid * kD + k], s);
     qn[tid] = sqrtf(s);
   }
   __syncthreads();
-  for (int idx = tid; idx < G * M; idx += blockDim.x) {
+  for (int idx = tid; idx < G * M; idx += blockDim.x) {  // p = S q~
     const int h = idx / M, i = idx % M;
-    const f4* row = (const f4*)(a.s32 + i * kD);
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll 8
-    for (int k4 = 0; k4 < kD / 4; ++k4) {
-      const f4 r = row[k4];
-      s0 = fmaf(r[0], qt[h][4 * k4], s0);
-      s1 = fmaf(r[1], qt[h][4 * k4 + 1], s1);
-      s2 = fmaf(r[2], qt[h][4 * k4 + 2], s2);
-      s3 = fmaf(r[3], qt[h][4 * k4 + 3], s3);
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll 16
+    for (int k = 0; k < kD; k += 2) {
+      s0 = fmaf(Ss[i * LS + k], qt[h * kD + k], s0);
+      s1 = fmaf(Ss[i * LS + k + 1], qt[h * kD + k + 1], s1);
     }
-    pp[h][i] = (s0 + s1) + (s2 + s3);
+    pp[h * M + i] = s0 + s1;
   }
   __syncthreads();
   for (int idx = tid; idx < KBT * 64; idx += blockDim.x) {
@@ -100,7 +108,8 @@ __global__ __launch_bounds__(256) void prep_queries_kernel(const PrepArgs a) {
     h8 v;
     if (kb < 4) {
       // centroid part, k slot e <-> coordinate 16 (2 kb + e/4) + 4 qq + e%4
-      for (int e = 0; e < 8; ++e) v[e] = (_Float16)(h < G ? qt[h][16 * (2 * kb + e / 4) + 4 * qq + e % 4] * inv : 0.f);
+      for (int e = 0; e < 8; ++e)
+        v[e] = (_Float16)(h < G ? qt[h * kD + 16 * (2 * kb + e / 4) + 4 * qq + e % 4] * inv : 0.f);
     } else {
       // sign part, k slot 2e+half <-> sign bit p + 16 half of word 2 (kbp/2) + qq/2,
       // p = 8 (qq%2) + 4 (kbp%2) + e; that bit holds projection coordinate
@@ -111,12 +120,17 @@ __global__ __launch_bounds__(256) void prep_queries_kernel(const PrepArgs a) {
           const int p = 8 * (qq % 2) + 4 * (kbp % 2) + e;
           const int qsg = 2 * (qq / 2) + half;
           const int t = 4 * (kbp / 2) + p / 4;
-          v[2 * e + half] = (_Float16)(h < G ? pp[h][16 * t + 4 * qsg + p % 4] * inv : 0.f);
+          v[2 * e + half] = (_Float16)(h < G ? pp[h * M + 16 * t + 4 * qsg + p % 4] * inv : 0.f);
         }
     }
     *(h8*)(a.wq + (((int64_t)slot * KBT + kb) * 64 + l) * 8) = v;
   }
   if (tid < 16) a.wqn[slot * 16 + tid] = tid < G ? qn[tid] : 0.f;
+}
+
+template <int M>
+constexpr size_t prep_lds_bytes() {
+  return sizeof(float) * ((size_t)(kD + 1) * (kD + M) + 16 * kD * 2 + 16 * M + 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -513,27 +527,31 @@ __global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
     __syncthreads();
   }
   L = red[0];
-  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  // 16 partial loads in flight per thread
+  float acc[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) acc[u] = 0.f;
   int c = 0;
-  for (; c + 4 <= W; c += 4) {
-    acc0 = fmaf(w[c], pr[c * stride + 4 + j], acc0);
-    acc1 = fmaf(w[c + 1], pr[(c + 1) * stride + 4 + j], acc1);
-    acc2 = fmaf(w[c + 2], pr[(c + 2) * stride + 4 + j], acc2);
-    acc3 = fmaf(w[c + 3], pr[(c + 3) * stride + 4 + j], acc3);
+  for (; c + 16 <= W; c += 16) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc[u] = fmaf(w[c + u], pr[(c + u) * stride + 4 + j], acc[u]);
   }
-  for (; c < W; ++c) acc0 = fmaf(w[c], pr[c * stride + 4 + j], acc0);
-  y[j] = ((acc0 + acc1) + (acc2 + acc3)) / L;
+  for (; c < W; ++c) acc[0] = fmaf(w[c], pr[c * stride + 4 + j], acc[0]);
+#pragma unroll
+  for (int u = 1; u < 16; ++u) acc[0] += acc[u];
+  y[j] = acc[0] / L;
   __syncthreads();
-  // out = R^T y (column j of R, coalesced across threads)
-  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-#pragma unroll 4
-  for (int i = 0; i < kD; i += 4) {
-    o0 = fmaf(a.r32[i * kD + j], y[i], o0);
-    o1 = fmaf(a.r32[(i + 1) * kD + j], y[i + 1], o1);
-    o2 = fmaf(a.r32[(i + 2) * kD + j], y[i + 2], o2);
-    o3 = fmaf(a.r32[(i + 3) * kD + j], y[i + 3], o3);
+  // out = R^T y (column j of R, coalesced across threads), 16 loads in flight
+  float o[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) o[u] = 0.f;
+  for (int i = 0; i < kD; i += 16) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) o[u] = fmaf(a.r32[(i + u) * kD + j], y[i + u], o[u]);
   }
-  a.out[((int64_t)slot * a.G + h) * kD + j] = (o0 + o1) + (o2 + o3);
+#pragma unroll
+  for (int u = 1; u < 16; ++u) o[0] += o[u];
+  a.out[((int64_t)slot * a.G + h) * kD + j] = o[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -546,6 +564,12 @@ int attention_device_init() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   if (hipDeviceGetAttribute(&g_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (hipFuncSetAttribute((const void*)prep_queries_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)prep_lds_bytes<64>()) != hipSuccess)
+    return -1;
+  if (hipFuncSetAttribute((const void*)prep_queries_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)prep_lds_bytes<128>()) != hipSuccess)
+    return -1;
   return 0;
 }
 
@@ -598,8 +622,8 @@ int launch_prep_queries(const Matrices& mats, int m, const AttnShape& s, void* w
   a.wq = w.wq;
   a.wqn = w.wqn;
   hipStream_t st = (hipStream_t)stream;
-  if (m == 64) hipLaunchKernelGGL(prep_queries_kernel<64>, dim3(s.n_seq), dim3(256), 0, st, a);
-  else if (m == 128) hipLaunchKernelGGL(prep_queries_kernel<128>, dim3(s.n_seq), dim3(256), 0, st, a);
+  if (m == 64) hipLaunchKernelGGL(prep_queries_kernel<64>, dim3(s.n_seq), dim3(256), prep_lds_bytes<64>(), st, a);
+  else if (m == 128) hipLaunchKernelGGL(prep_queries_kernel<128>, dim3(s.n_seq), dim3(256), prep_lds_bytes<128>(), st, a);
   else return TQ_EUNSUPPORTED;
   return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
 }

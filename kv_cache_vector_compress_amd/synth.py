@@ -112,7 +112,7 @@ class Workload:
         return slot % self.heads_per_slot_cycle
 
 
-# The five workloads (shapes only; see the DESIGN notes for the recipe).
+# Standard workload shapes (the per-slot recipes are in kv_slot and unit_gaussian).
 TINY = Workload("tiny_d128_b3_T1024", 1, 1024, 128, 64, 3, 3, 4, "f32", 1)
 QWEN_DECODE = Workload("qwen2.5-3b_decode_36x2x8192", 72, 8192, 128, 64, 3, 3, 8, "f16", 72)
 LONG_CONTEXT = Workload("long_context_8x8x131072", 64, 131072, 128, 64, 3, 3, 4, "f16", 8)

@@ -26,7 +26,7 @@ Notation: d = head_dim, b = bits, L = 2**b levels, m = proj_dim,
 c[0..L-1] ascending centroids, beta[0..L-2] ascending boundaries,
 R (d x d) the rotation, S (m x d) the QJL matrix.
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
   * rotation is y = R x with R row-major;
   * the QJL matrix acts on the rotated residual r = R x - c[idx];
   * idx_j = #{i : beta_i < y_j}, so a value equal to a boundary goes to the
