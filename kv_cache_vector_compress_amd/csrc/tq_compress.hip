@@ -36,6 +36,7 @@ struct KeyArgs {
   int64_t n_new, pos, capacity;
   int n_seq;
   int rec_words;
+  _Float16 m1;  // -1 (a run-time value: see split2m)
   CodebookDev cb;
 };
 
@@ -43,7 +44,7 @@ constexpr int kRImg = kD * kLdsStride;  // halves per R image
 
 template <int M>
 constexpr size_t key_lds_bytes() {
-  return (size_t)(2 * kRImg + 2 * M * kLdsStride) * 2 + 16 * sizeof(float);
+  return (size_t)(2 * kRImg + 2 * M * kLdsStride) * 2;
 }
 
 __device__ __forceinline__ void copy_u4(uint16_t* dst, const uint16_t* src, int n_halves) {
@@ -104,26 +105,26 @@ __device__ __forceinline__ void split_row32(const f4 (&v)[8], float sc, h8 (&xh)
 template <int B, int M, bool F32>
 __global__ __launch_bounds__(512, 1) void compress_keys_kernel(const KeyArgs a) {
   // 8 waves (2 per SIMD) share the LDS images; 2 (fp32: 1) 16-token tiles per
-  // wave iteration keep a wave within 256 registers, so the two waves of a
-  // SIMD overlap one's matrix-core work with the other's bucketing
+  // wave iteration keep a wave within 256 registers
+  constexpr int H = 1 << (B - 1);
   constexpr int NT = (F32 || M > 64) ? 1 : 2;  // 16-token N tiles per wave iteration
   constexpr int PT = M / 16;       // projection M tiles
   constexpr int NCH = M / 64;      // 16-bit sign chunks per lane
   extern __shared__ __align__(16) uint16_t lds[];
+  __shared__ float ctab[16];       // 2^12 c_i
   uint16_t* Rh = lds;
   uint16_t* Rl = Rh + kRImg;
   uint16_t* Sh = Rl + kRImg;
   uint16_t* Sl = Sh + M * kLdsStride;
-  float* Cs = (float*)(Sl + M * kLdsStride);  // centroids * 2^12
   copy_u4(Rh, a.r_hi, kRImg);
   copy_u4(Rl, a.r_lo, kRImg);
   copy_u4(Sh, a.s_hi, M * kLdsStride);
   copy_u4(Sl, a.s_lo, M * kLdsStride);
-  if (threadIdx.x < 16) Cs[threadIdx.x] = a.cb.cent[threadIdx.x] * kResScale;
+  if (threadIdx.x < 16) ctab[threadIdx.x] = a.cb.cent[threadIdx.x] * kResScale;
   __syncthreads();
 
-  float bp[8];
-  load_pos_beta<B>(bp, a.cb);
+  float bpos[8];
+  load_pos_beta<B>(bpos, a.cb);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t tps = (a.n_new + 16 * NT - 1) / (16 * NT);
@@ -135,34 +136,42 @@ __global__ __launch_bounds__(512, 1) void compress_keys_kernel(const KeyArgs a) 
     const int64_t t0 = (tile - (int64_t)slot * tps) * (16 * NT);
 
     // Inputs.  Rows past n_new are clamped to the last row: their results
-    // are never stored, they only need to be finite.
+    // are never stored, they only need to be finite.  Per token: the norm,
+    // the boundaries scaled to the accumulator (sigma = 2^8 sc ||k||, sc the
+    // fp32 pre-scale) and s16 = 2^12 / sigma.
     h8 xh[NT][4];
     h8 xl[F32 ? NT : 1][4];
-    float nrm[NT], inv[NT];
+    float nrm[NT], s16[NT], bs[NT][8];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int64_t tok = t0 + 16 * j + r16;
       const int64_t row = (int64_t)slot * a.n_new + (tok < a.n_new ? tok : a.n_new - 1);
+      float n, sigma;
       if constexpr (F32) {
         f4 v[8];
         float ss = load_row32(a.x, row, q, v);
         ss += shfl_xor(ss, 16);
         ss += shfl_xor(ss, 32);
-        const float n = sqrtf(ss);
+        n = sqrtf(ss);
         int E = 0;
         frexpf(n, &E);
         const float sc = n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;  // |k sc| < 2^13
         split_row32(v, sc, xh[j], xl[j]);
-        nrm[j] = n;
-        inv[j] = n > 0.f ? 1.f / (kRotScale * sc * n) : 0.f;
+        sigma = kRotScale * sc * n;
       } else {
-        float ss = load_row16<false>(a.x, row, q, xh[j]);
+        const _Float16* src = (const _Float16*)a.x + row * kD + 8 * q;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) xh[j][kb] = *(const h8*)(src + 32 * kb);
+        float ss = sq_norm16(xh[j]);
         ss += shfl_xor(ss, 16);
         ss += shfl_xor(ss, 32);
-        const float n = sqrtf(ss);
-        nrm[j] = n;
-        inv[j] = n > 0.f ? 1.f / (kRotScale * n) : 0.f;
+        n = sqrtf(ss);
+        sigma = kRotScale * n;
       }
+      nrm[j] = n;
+      s16[j] = n > 0.f ? kResScale / sigma : 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) bs[j][t] = t < H - 1 ? bpos[t] * sigma : 0.f;
     }
 
     f4 zacc[NT][PT];
@@ -212,21 +221,13 @@ __global__ __launch_bounds__(512, 1) void compress_keys_kernel(const KeyArgs a) 
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        // bucket, scaled residual rs = 2^12 (y - c[idx]), codes, residual operands
+        // cells, scaled residual 2^12 (y - c[idx]), codes, residual operands
         u4 rhi, rlo;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           float rs[4];
-          uint32_t x4 = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float y = yacc[j][u][i] * inv[j];
-            const int idx = bucket_sym<B>(y, bp);
-            rs[i] = fmaf(y, kResScale, -Cs[idx]);
-            g2[j] = fmaf(rs[i], rs[i], g2[j]);
-            x4 |= (uint32_t)idx << (8 * i);
-          }
-          const HiLo t01 = split2(rs[0], rs[1]), t23 = split2(rs[2], rs[3]);
+          const uint32_t x4 = quantize4<B>(yacc[j][u], bs[j], s16[j], ctab, rs, g2[j]);
+          const HiLo t01 = split2m(rs[0], rs[1], a.m1), t23 = split2m(rs[2], rs[3], a.m1);
           rhi[2 * u] = t01.hi;
           rlo[2 * u] = t01.lo;
           rhi[2 * u + 1] = t23.hi;
@@ -251,14 +252,8 @@ __global__ __launch_bounds__(512, 1) void compress_keys_kernel(const KeyArgs a) 
       const float gamma = sqrtf(g) * (1.f / kResScale);
       uint32_t bits[NCH];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int pp = 3; pp >= 0; --pp)
-#pragma unroll
-          for (int i = 3; i >= 0; --i) v = (v << 1) | (zacc[j][4 * c + pp][i] >= 0.f ? 1u : 0u);
-        bits[c] = v;
-      }
+      for (int c = 0; c < NCH; ++c)
+        bits[c] = sign_bits16(zacc[j][4 * c], zacc[j][4 * c + 1], zacc[j][4 * c + 2], zacc[j][4 * c + 3]);
       const int64_t tok = t0 + 16 * j + r16;
       if (tok < a.n_new) {
         uint32_t* rp = a.rec + ((int64_t)slot * a.capacity + a.pos + tok) * a.rec_words;
@@ -514,6 +509,7 @@ int launch_compress_keys(const Matrices& mats, const CodebookDev& cb, int bits, 
   a.capacity = s.capacity;
   a.n_seq = s.n_seq;
   a.rec_words = bits * kD / 32 + m / 32 + 2;
+  a.m1 = (_Float16)-1.0f;
   a.cb = cb;
   const bool f32 = s.dtype == TQ_F32;
   const int64_t per = (f32 || m > 64) ? 16 : 32;

@@ -225,6 +225,87 @@ __device__ __forceinline__ void put_sel4_rt(uint32_t (&w)[B], int s, uint32_t x)
   }
 }
 
+// ---- quantisation helpers -----------------------------------------------------
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// Partial sum of squares of 32 fp16 coordinates (dot2 with fp32 accumulation;
+// the fp16 x fp16 products are exact).
+__device__ __forceinline__ float sq_norm16(const h8 (&x)[4]) {
+  float s[2] = {0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const h2 v = {x[kb][e], x[kb][e + 1]};
+      s[kb & 1] = __builtin_amdgcn_fdot2(v, v, s[kb & 1], false);
+    }
+  return s[0] + s[1];
+}
+
+// Lloyd-Max cells of 4 coordinates of one token, with the residual, for a
+// codebook symmetric about 0 (H = L/2 cells per side, middle boundary 0).
+//   a     scaled rotated coordinates, a = sigma y with sigma = 2^8 ||k|| (> 0)
+//   bs    the positive boundaries beta_{H+t} scaled by sigma (t < H-1)
+//   s16   2^12 / sigma, so that a s16 = 2^12 y (0 for a zero vector)
+//   ctab  LDS table of 2^12 c_i at byte offset 4 i
+// With k = #{t : |a| > bs_t}, the cell is H + k for a > 0 and H - 1 - k for
+// a <= 0 (the same count as #{i : beta_i < y}).  Both come out of one select
+// chain on the byte address 4 (H + k), reflected to 4 (H - 1 - k) for
+// a <= 0 by an XOR with all ones (a - 1 as an integer is negative exactly
+// for a <= 0, since a = -0 cannot come out of an accumulation from +0).
+// r_i = 2^12 (y_i - c[idx_i]); g2 += sum r_i^2.  Returns the selector word
+// (cell of coordinate i in byte i).
+template <int B>
+__device__ __forceinline__ uint32_t quantize4(const f4& a, const float (&bs)[8], float s16, const float* ctab,
+                                              float (&r)[4], float& g2) {
+  constexpr uint32_t H = 1u << (B - 1);
+  constexpr uint32_t kMask = 4u * (2u * H - 1u);
+  uint32_t ia[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float m = fabsf(a[i]);
+    uint32_t ad = 4u * H;
+#pragma unroll
+    for (uint32_t t = 0; t + 1 < H; ++t) ad = m > bs[t] ? 4u * (H + 1u + t) : ad;
+    const uint32_t neg = (uint32_t)((int32_t)(__float_as_uint(a[i]) - 1u) >> 31);
+    ia[i] = (ad ^ neg) & kMask;
+    const float c = *(const float*)((const char*)ctab + ia[i]);
+    r[i] = fmaf(a[i], s16, -c);
+    g2 = fmaf(r[i], r[i], g2);
+  }
+  return (perm(ia[1], ia[0], 0x0C0C0400u) | perm(ia[3], ia[2], 0x04000C0Cu)) >> 2;
+}
+
+// Split x0, x1 into fp16 high parts (round toward zero) and fp16 low parts
+// (the remainders, rounded): x = hi + lo to ~2^-22 relative.  m1 must be the
+// fp16 value -1 passed in at run time: with a constant the compiler turns
+// the remainder into a subtract plus conversions instead of one mixed FMA.
+__device__ __forceinline__ HiLo split2m(float x0, float x1, _Float16 m1) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+  h2 l;
+  l[0] = (_Float16)fmaf((float)h[0], (float)m1, x0);
+  l[1] = (_Float16)fmaf((float)h[1], (float)m1, x1);
+  return HiLo{__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
+}
+
+// QJL sign bits [z >= 0] of 16 projections, bit 4 p + i for z[p][i]:
+// v_perm's sign-replicating selectors turn 4 sign bits into byte masks,
+// each byte keeps one distinct bit, and a sum of bytes (v_sad_u8 against 0)
+// gathers them.  (z = -0 cannot come out of an accumulation from +0.)
+__device__ __forceinline__ uint32_t sign_bits16(const f4& z0, const f4& z1, const f4& z2, const f4& z3) {
+  auto keep = [](const f4& z, uint32_t bits) {
+    const uint32_t m = perm(__float_as_uint(z[1]), __float_as_uint(z[0]), 0x0C0C0B09u) |
+                       perm(__float_as_uint(z[3]), __float_as_uint(z[2]), 0x0B090C0Cu);
+    return ~m & bits;
+  };
+  const uint32_t lo =
+      __builtin_amdgcn_sad_u8(keep(z1, 0x80402010u), 0u, __builtin_amdgcn_sad_u8(keep(z0, 0x08040201u), 0u, 0u));
+  const uint32_t hi =
+      __builtin_amdgcn_sad_u8(keep(z3, 0x80402010u), 0u, __builtin_amdgcn_sad_u8(keep(z2, 0x08040201u), 0u, 0u));
+  return lo | (hi << 8);
+}
+
 // Copy the boundaries out of the kernel-argument block into registers.
 __device__ __forceinline__ void load_beta(float (&beta)[15], const CodebookDev& cb) {
 #pragma unroll
