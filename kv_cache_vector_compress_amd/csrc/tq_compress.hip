@@ -53,23 +53,9 @@ __device__ __forceinline__ void copy_u4(uint16_t* dst, const uint16_t* src, int 
 }
 
 // Load the 32 input coordinates a lane owns (8 per K block: 32 kb + 8 q ..)
-// of one token as fp16 operands, plus the token's sum of squares (partial,
-// over this lane's coordinates).  fp32 inputs are returned as hi/lo parts
-// after scaling by a power of two sc (|k sc| < 2^13): the caller needs the
-// norm first, so fp32 rows are loaded raw and split in split_f32_row.
-template <bool F32>
-__device__ __forceinline__ float load_row16(const void* x, int64_t row, int q, h8 (&xh)[4]) {
-  const _Float16* src = (const _Float16*)x + row * kD + 8 * q;
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    xh[kb] = *(const h8*)(src + 32 * kb);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss[kb] = fmaf((float)xh[kb][e], (float)xh[kb][e], ss[kb]);
-  }
-  return (ss[0] + ss[1]) + (ss[2] + ss[3]);
-}
-
+// of one fp32 token, plus the token's partial sum of squares (over this
+// lane's coordinates).  The caller needs the norm before it can split the
+// row into fp16 hi/lo operands (split_row32), so the row comes back raw.
 __device__ __forceinline__ float load_row32(const void* x, int64_t row, int q, f4 (&v)[8]) {
   const float* src = (const float*)x + row * kD + 8 * q;
   float ss[4] = {0.f, 0.f, 0.f, 0.f};
@@ -343,7 +329,7 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
     for (int half = 0; half < 2; ++half) {
       h8 xa[4][4];
       h8 xl[F32 ? 4 : 1][4];
-      float inv_tok[4];
+      float tok_sc[4];  // per token: sigma = 2^8 sc ||v|| (4-bit codes: 1 / sigma)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         // block token tau -> input row; rows outside [pos, pos + n_new) are
@@ -363,23 +349,40 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
           frexpf(n, &E);
           const float sc = n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;
           split_row32(v, sc, xa[mt], xl[mt]);
-          inv_tok[mt] = n > 0.f ? 1.f / (kRotScale * sc * n) : 0.f;
+          tok_sc[mt] = B <= 3 ? kRotScale * sc * n : (n > 0.f ? 1.f / (kRotScale * sc * n) : 0.f);
           if (q == 0 && valid) vnorm[tau] = n;
         } else {
-          ss = load_row16<false>(a.x, row, q, xa[mt]);
+          const _Float16* src = (const _Float16*)a.x + row * kD + 8 * q;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) xa[mt][kb] = *(const h8*)(src + 32 * kb);
+          ss = sq_norm16(xa[mt]);
           ss += shfl_xor(ss, 16);
           ss += shfl_xor(ss, 32);
           const float n = sqrtf(ss);
-          inv_tok[mt] = n > 0.f ? 1.f / (kRotScale * n) : 0.f;
+          tok_sc[mt] = B <= 3 ? kRotScale * n : (n > 0.f ? 1.f / (kRotScale * n) : 0.f);
           if (q == 0 && valid) vnorm[tau] = n;
         }
       }
-      // 1/||v|| in the output layout: lane (coordinate, q) holds tokens 4q+i
+      // Per token in the output layout (lane (coordinate, q) holds tokens
+      // 4q+i): the boundaries scaled to the accumulator, bs = beta sigma with
+      // sigma = 2^8 sc ||v||; for 4-bit codes (7 boundaries a token) the
+      // coordinates are normalised instead, y = a / sigma, against the
+      // unscaled boundaries
+      constexpr bool kScaled = B <= 3;
       float inv_d[4][4];
+      float bsd[4][4][kScaled ? 8 : 1];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) inv_d[mt][i] = __shfl(inv_tok[mt], 4 * q + i, 64);
+        for (int i = 0; i < 4; ++i) {
+          const float v = __shfl(tok_sc[mt], 4 * q + i, 64);
+          if constexpr (kScaled) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) bsd[mt][i][t] = t < (1 << (B - 1)) - 1 ? bp[t] * v : 0.f;
+          } else {
+            inv_d[mt][i] = v;
+          }
+        }
 
 #pragma unroll
       for (int ntp = 0; ntp < 4; ++ntp) {
@@ -408,12 +411,20 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            uint32_t x4 = 0;
+            f4 v = acc[mt][u];
+            float bsx[4][8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float y = acc[mt][u][i] * inv_d[mt][i];
-              x4 |= (uint32_t)bucket_sym<B>(y, bp) << (8 * i);
-            }
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int t = 0; t < 8; ++t) {
+                if constexpr (kScaled) {
+                  bsx[i][t] = bsd[mt][i][t];
+                } else {
+                  bsx[i][t] = bp[t];
+                  if (t == 0) v[i] *= inv_d[mt][i];
+                }
+              }
+            const uint32_t x4 = cells4<B>(v, bsx);
             put_sel4_rt<B>(cw[2 * ntp + u], 4 * half + mt, x4);  // slot of these 16 tokens
           }
         // keep the scheduler from hoisting the next coordinate tiles' R loads

@@ -277,6 +277,26 @@ __device__ __forceinline__ uint32_t quantize4(const f4& a, const float (&bs)[8],
   return (perm(ia[1], ia[0], 0x0C0C0400u) | perm(ia[3], ia[2], 0x04000C0Cu)) >> 2;
 }
 
+// Cells of 4 coordinates without the residual (the value path): a_i are
+// scaled rotated coordinates sigma_i y_i and bs[i][t] = beta_{H+t} sigma_i
+// the matching scaled positive boundaries (one token per i).  Same select
+// chain and reflection as quantize4; returns the selector word.
+template <int B>
+__device__ __forceinline__ uint32_t cells4(const f4& a, const float (&bs)[4][8]) {
+  constexpr uint32_t H = 1u << (B - 1);
+  uint32_t ia[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float m = fabsf(a[i]);
+    uint32_t ad = H;
+#pragma unroll
+    for (uint32_t t = 0; t + 1 < H; ++t) ad = m > bs[i][t] ? H + 1u + t : ad;
+    const uint32_t neg = (uint32_t)((int32_t)(__float_as_uint(a[i]) - 1u) >> 31);
+    ia[i] = (ad ^ neg) & (2u * H - 1u);
+  }
+  return perm(ia[1], ia[0], 0x0C0C0400u) | perm(ia[3], ia[2], 0x04000C0Cu);
+}
+
 // Split x0, x1 into fp16 high parts (round toward zero) and fp16 low parts
 // (the remainders, rounded): x = hi + lo to ~2^-22 relative.  m1 must be the
 // fp16 value -1 passed in at run time: with a constant the compiler turns
