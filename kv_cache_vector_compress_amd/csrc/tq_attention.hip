@@ -246,11 +246,9 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
     k.g = __uint_as_float(rp[RW - 1]);
   };
 
-  KeyTile<B, M> cur[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) load(cur[u], t_begin + u);
-  for (int tile = t_begin; tile < t_end; tile += U) {
-    KeyTile<B, M> nxt[U];
+  // One iteration: scores of U tiles from `cur` while the next U tiles load
+  // into `nxt`.  Iterations alternate the two buffers (no register copies).
+  auto iteration = [&](KeyTile<B, M> (&cur)[U], KeyTile<B, M> (&nxt)[U], int tile) {
     if (tile + U < t_end) {
 #pragma unroll
       for (int u = 0; u < U; ++u) load(nxt[u], tile + U + u);
@@ -276,8 +274,14 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
         }
       }
     }
+  };
+
+  KeyTile<B, M> ta[U], tb[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+  for (int u = 0; u < U; ++u) load(ta[u], t_begin + u);
+  for (int tile = t_begin; tile < t_end; tile += 2 * U) {
+    iteration(ta, tb, tile);
+    if (tile + U < t_end) iteration(tb, ta, tile + U);
   }
 }
 
