@@ -144,14 +144,28 @@ struct KeyTile {
   float n, g;
 };
 
+// Raw buffer resource over one slot's region of the cache: dword loads with
+// 32-bit byte offsets (no 64-bit address arithmetic per lane), reads past
+// `bytes` return 0.  Word 3 selects the 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t bld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// The words of one key record this lane needs (record at byte offset `ro`).
 template <int B, int M>
-__device__ __forceinline__ void load_key(KeyTile<B, M>& k, const uint32_t* rp, bool valid, int q, int rec_words) {
+__device__ __forceinline__ void load_key(KeyTile<B, M>& k, __amdgpu_buffer_rsrc_t r, uint32_t ro, int q) {
+  constexpr int RW = B * kD / 32 + M / 32 + 2;
+  const uint32_t oc = ro + 4u * (uint32_t)(q * B), os = ro + 4u * (uint32_t)(4 * B + (q >> 1));
 #pragma unroll
-  for (int w = 0; w < B; ++w) k.cw[w] = valid ? rp[q * B + w] : 0u;
+  for (int w = 0; w < B; ++w) k.cw[w] = bld(r, oc + 4u * w);
 #pragma unroll
-  for (int c = 0; c < M / 64; ++c) k.sw[c] = valid ? rp[4 * B + 2 * c + (q >> 1)] : 0u;
-  k.n = valid ? __uint_as_float(rp[rec_words - 2]) : 0.f;
-  k.g = valid ? __uint_as_float(rp[rec_words - 1]) : 0.f;
+  for (int c = 0; c < M / 64; ++c) k.sw[c] = bld(r, os + 8u * c);
+  k.n = __uint_as_float(bld(r, ro + 4u * (RW - 2)));
+  k.g = __uint_as_float(bld(r, ro + 4u * (RW - 1)));
 }
 
 // acc[i] = (unscaled, unnormalised) score of token row 4q+i of the tile for
@@ -212,7 +226,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
   constexpr int RW = rec_words<B, M>();
   constexpr int U = 4;          // 16-token tiles per iteration (next U tiles in flight)
   __shared__ float nsh[4][16 * U];  // per wave: ||k|| of the iteration's tokens
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
   const int slot = (int)(gw / a.waves_per_slot);
@@ -231,19 +245,16 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
   const int t_begin = wc * a.tiles_per_wave;
   const int t_end = min(ntile, t_begin + a.tiles_per_wave);
   const uint32_t* base = a.rec + (size_t)slot * (size_t)a.capacity * RW;
-  float* out = a.scores + ((size_t)slot * a.G + r16) * (size_t)n_tok;
-  const bool head_ok = r16 < a.G;
-  const bool vec_store = (n_tok & 3) == 0;
+  // scores of this slot: row h (query head) at byte offset 4 h n_tok; lanes
+  // of heads >= G store past the end of the resource and are dropped
+  const __amdgpu_buffer_rsrc_t ors =
+      slot_rsrc(a.scores + (size_t)slot * a.G * (size_t)n_tok, (uint32_t)a.G * (uint32_t)n_tok * 4u);
+  const uint32_t orow = (uint32_t)r16 * (uint32_t)n_tok;
 
+  const __amdgpu_buffer_rsrc_t krs = slot_rsrc(base, (uint32_t)a.capacity * (uint32_t)(RW * 4));
   auto load = [&](KeyTile<B, M>& k, int tile) {
     const int t = min(tile * 16 + r16, n_tok - 1);  // rows past the end: any valid row
-    const uint32_t* rp = base + t * RW;
-#pragma unroll
-    for (int w = 0; w < B; ++w) k.cw[w] = rp[q * B + w];
-#pragma unroll
-    for (int c = 0; c < M / 64; ++c) k.sw[c] = rp[4 * B + 2 * c + (q >> 1)];
-    k.n = __uint_as_float(rp[RW - 2]);
-    k.g = __uint_as_float(rp[RW - 1]);
+    load_key<B, M>(k, krs, (uint32_t)t * (uint32_t)(RW * 4), q);
   };
 
   // One iteration: scores of U tiles from `cur` while the next U tiles load
@@ -263,14 +274,15 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
     for (int u = 0; u < U; ++u) {
       const f4 nk = *(const f4*)&nsh[wave][16 * u + 4 * q];  // ||k|| of token rows 4q..4q+3
       const int t0 = (tile + u) * 16 + 4 * q;
-      if (head_ok && tile + u < t_end) {
+      if (tile + u < t_end) {
         const f4 v = acc[u] * nk * qn;
-        if (vec_store && t0 + 4 <= n_tok) {
-          *(f4*)(out + t0) = v;
+        const uint32_t ob = (orow + (uint32_t)t0) * 4u;
+        if (t0 + 4 <= n_tok) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), ors, ob, 0, 0);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (t0 + i < n_tok) out[t0 + i] = v[i];
+            if (t0 + i < n_tok) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i]), ors, ob + 4u * i, 0, 0);
         }
       }
     }
@@ -321,7 +333,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   constexpr int BW = 4 * BV * kD + kBlockTokens;
   __shared__ float nsh[4][32];               // per wave: ||k|| of the step's 32 tokens
   __shared__ __align__(16) float vsh[4][kBlockTokens];  // per wave: the block's ||v||
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
   const int slot = (int)(gw / a.waves_per_slot);
@@ -345,26 +357,24 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   const uint32_t* kbase = a.rec + (size_t)slot * (size_t)a.capacity * RW;
   const uint32_t* vbase = a.vblocks + (size_t)slot * (size_t)(a.capacity / kBlockTokens) * BW;
 
+  const __amdgpu_buffer_rsrc_t krs = slot_rsrc(kbase, (uint32_t)a.capacity * (uint32_t)(RW * 4));
+  const __amdgpu_buffer_rsrc_t vrs = slot_rsrc(vbase, (uint32_t)(a.capacity / kBlockTokens) * (uint32_t)(BW * 4));
+  const uint32_t vlane = 4u * (uint32_t)(q * kD + r16);
   auto load_keys = [&](StepKeys<BK, BV, M>& k, int tt) {  // tt: first token of the step
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int t = min(tt + 16 * u + r16, n_tok - 1);  // rows past the end: any valid row
-      const uint32_t* rp = kbase + t * RW;
-#pragma unroll
-      for (int w = 0; w < BK; ++w) k.t[u].cw[w] = rp[q * BK + w];
-#pragma unroll
-      for (int c = 0; c < M / 64; ++c) k.t[u].sw[c] = rp[4 * BK + 2 * c + (q >> 1)];
-      k.t[u].n = __uint_as_float(rp[RW - 2]);
-      k.t[u].g = __uint_as_float(rp[RW - 1]);
+      load_key<BK, M>(k.t[u], krs, (uint32_t)t * (uint32_t)(RW * 4), q);
     }
   };
   auto load_values = [&](BlockValues<BV>& v, int blk) {
-    const uint32_t* vb = vbase + blk * BW;
+    const uint32_t ob = (uint32_t)blk * (uint32_t)(BW * 4);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-      for (int w = 0; w < BV; ++w) v.vw[nt][w] = vb[(w * 4 + q) * kD + 16 * nt + r16];
-    v.vn = *(const float2*)(vb + 4 * BV * kD + 2 * lane);
+      for (int w = 0; w < BV; ++w) v.vw[nt][w] = bld(vrs, ob + vlane + 4u * (uint32_t)(w * 4 * kD + 16 * nt));
+    const uint32_t on = ob + 4u * (uint32_t)(4 * BV * kD + 2 * lane);
+    v.vn = make_float2(__uint_as_float(bld(vrs, on)), __uint_as_float(bld(vrs, on + 4u)));
   };
 
   float m_run = -INFINITY, l_run = 0.f;
