@@ -166,6 +166,60 @@ def test_qwen_decode_shape_full():
     _say(run_case(K, V, Q))
 
 
+def test_long_context_full_size_sampled():
+    """The benchmark workload at full size, in the launch configuration
+    bench.py times: 8 sequences x 8 KV heads (64 slots) x 131072 fp16 tokens,
+    3-bit keys (m=64) and values, 4 query heads per KV head, one
+    tq_append_key / tq_append_value / tq_attention_scores / tq_attend call
+    each over the whole cache.  The oracle recomputes sampled tokens of four
+    slots one by one (codes, signs, norms, gamma, scores) and the full
+    attention of one slot."""
+    from concurrent.futures import ThreadPoolExecutor
+    w = synth.LONG_CONTEXT
+    n_seq, T, d, m, G = w.n_seq, w.n_tok, w.d, w.m, w.G
+    _say("long context: generating", (n_seq, T, d))
+    with ThreadPoolExecutor(8) as ex:
+        K = np.stack(list(ex.map(lambda s: synth.kv_slot(synth.SEED_K, s, w.head_of_slot(s), T, d), range(n_seq))))
+        V = np.stack(list(ex.map(lambda s: synth.kv_slot(synth.SEED_V, s, w.head_of_slot(s), T, d), range(n_seq))))
+    Q = synth.workload_queries(w)
+    ctx, R, S = make_ctx(d, m, 3, 3)
+    cache = tq.KVCache(ctx, n_seq, T)
+    kd, vd, qd = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), torch.from_numpy(Q).cuda()
+    cache.append_key(kd, 0)
+    cache.append_value(vd, 0)
+    sc = cache.attention_scores(qd, T).cpu().numpy()
+    out = cache.attend(qd, T).cpu().numpy()
+    torch.cuda.synchronize()
+    del kd, vd
+    kw_all, vw_all = cache.key_words(), cache.value_words()
+    _say("long context: GPU pass done")
+    beta, c = O.lloyd_max_codebook(d, 3)
+    rng = np.random.default_rng(2024)
+    for slot in (0, 21, 42, 63):
+        toks = np.unique(np.concatenate([rng.choice(T, 1024, replace=False), np.arange(T - 16, T)]))
+        ks, vs = K[slot:slot + 1, toks], V[slot:slot + 1, toks]
+        ref_k = O.compress_keys(ks, R, S, beta, c)
+        ref_v = O.compress_values(vs, R, beta, c)
+        gk = O.unpack_keys(kw_all[slot:slot + 1, toks], d, m, 3)
+        gv_all = O.unpack_values(vw_all[slot:slot + 1], d, 3, n_tokens=T)
+        gv = {k: v[:, toks] for k, v in gv_all.items()}
+        st = P.check_keys(gk, ref_k, beta)
+        flips = st.pop("flip_tokens")
+        st.update({"v_" + k: v for k, v in P.check_values(gv, ref_v, beta).items()})
+        qn = np.linalg.norm(Q[slot:slot + 1].astype(np.float64), axis=-1)
+        kn = np.linalg.norm(ks.astype(np.float64), axis=-1)
+        g_sc = sc[slot:slot + 1][:, :, toks]
+        st["score"] = P.check_scores(g_sc, O.key_scores(Q[slot:slot + 1], R, S, c, ref_k), qn, kn,
+                                     skip_tokens=flips)
+        _say("long context slot", slot, st)
+    slot = 42
+    ref_k = O.compress_keys(K[slot:slot + 1], R, S, beta, c)
+    ref_v = O.compress_values(V[slot:slot + 1], R, beta, c)
+    ref_out = O.attend(Q[slot:slot + 1], R, S, c, ref_k, ref_v, value_centroids=c)
+    _say("long context attend slot", slot, P.check_attend(out[slot:slot + 1], ref_out))
+    ctx.close()
+
+
 # ---------------------------------------------------------------------------
 # argument errors: documented code, nothing written
 # ---------------------------------------------------------------------------
