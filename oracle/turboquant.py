@@ -183,12 +183,19 @@ def compress_keys(K, R, S, boundaries, centroids) -> dict:
     n, x = normalise(K)
     y = rotate(x, R)
     idx = bucketize(y, boundaries)
-    r = y - centroids[idx]
-    gamma = np.linalg.norm(r, axis=-1)
-    z = r @ S.T
-    signs = (z >= 0).astype(np.uint8)
-    return dict(idx=idx, signs=signs, norm=n.astype(np.float32), gamma=gamma.astype(np.float32),
-                y=y, z=z)
+    q = qjl_stage(y, idx, S, centroids)
+    return dict(idx=idx, signs=q["signs"], norm=n.astype(np.float32), gamma=q["gamma"], y=y, z=q["z"])
+
+
+def qjl_stage(y, idx, S, centroids) -> dict:
+    """Stage 2 of the key compressor on given cells ([atskills] Stage 2;
+    [superapi] 主要能力): residual r = y - c[idx], gamma = ||r||, projection
+    z = S r and its sign bits [z >= 0].  Used by compress_keys, and to
+    re-evaluate a token whose cell index legitimately differs (a coordinate
+    within floating-point error of a boundary) on those other cells."""
+    r = _as64(y) - np.asarray(centroids, dtype=np.float64)[idx]
+    z = r @ _as64(S).T
+    return dict(z=z, signs=(z >= 0).astype(np.uint8), gamma=np.linalg.norm(r, axis=-1).astype(np.float32))
 
 
 def compress_values(V, R, boundaries, centroids) -> dict:

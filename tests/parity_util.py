@@ -3,11 +3,13 @@
 The acceptance rules (stated once here, used by every parity test):
   * codes: bit-exact, except an index may differ by one cell where the
     oracle's rotated coordinate lies within FLIP_EPS = 1e-5 of a boundary,
-    and a sign bit may differ where |S r| < FLIP_EPS or where the same token
-    has an allowed index flip; allowed flips must stay under 0.01% of the
-    compared coordinates (indices and signs counted separately);
-  * ||k||, ||v||, gamma: 1e-6 relative (gamma of a token with an index flip
-    is exempt: its residual legitimately differs);
+    and a sign bit may differ where |S r| < FLIP_EPS; allowed flips must stay
+    under 0.01% of the compared coordinates (indices and signs counted
+    separately).  A token with an allowed index flip has a legitimately
+    different residual: its signs and gamma are judged against the oracle's
+    stage 2 re-run on the GPU's cells (oracle.qjl_stage), the same way its
+    scores are judged on the GPU's codes;
+  * ||k||, ||v||, gamma: 1e-6 relative;
   * scores: |est_gpu - est_oracle| <= 2e-3 ||q|| ||k||;
   * attention output: ||out_gpu - out_oracle|| / ||out_oracle|| <= 5e-3 per
     (slot, query head).
@@ -45,17 +47,19 @@ def check_codes(gpu_idx, ref_idx, ref_y, beta, what="idx"):
     return n, diff.any(axis=-1)
 
 
-def check_keys(gpu: dict, ref: dict, beta: np.ndarray) -> dict:
+def check_keys(gpu: dict, ref: dict, beta: np.ndarray, S: np.ndarray, centroids: np.ndarray) -> dict:
     n_idx, tok_flip = check_codes(gpu["idx"], ref["idx"], ref["y"], beta, "key idx")
-    sdiff = gpu["signs"] != ref["signs"]
-    allowed = (np.abs(ref["z"]) < FLIP_EPS) | tok_flip[..., None]
-    bad = sdiff & ~allowed
+    z, signs, gamma = ref["z"].copy(), ref["signs"].copy(), ref["gamma"].copy()
+    if tok_flip.any():
+        alt = O.qjl_stage(ref["y"][tok_flip], gpu["idx"][tok_flip], S, centroids)
+        z[tok_flip], signs[tok_flip], gamma[tok_flip] = alt["z"], alt["signs"], alt["gamma"]
+    sdiff = gpu["signs"] != signs
+    bad = sdiff & ~(np.abs(z) < FLIP_EPS)
     assert not bad.any(), f"sign mismatches away from 0: {int(bad.sum())}, first {np.argwhere(bad)[:5].tolist()}"
     n_sign = int(sdiff.sum())
     assert n_sign <= max(1, FLIP_FRAC * sdiff.size), f"{n_sign} sign flips > 0.01%"
     np.testing.assert_allclose(gpu["norm"], ref["norm"], rtol=NORM_RTOL, atol=1e-30)
-    g_ok = ~tok_flip
-    np.testing.assert_allclose(gpu["gamma"][g_ok], ref["gamma"][g_ok], rtol=NORM_RTOL, atol=1e-7)
+    np.testing.assert_allclose(gpu["gamma"], gamma, rtol=NORM_RTOL, atol=1e-7)
     return dict(idx_flips=n_idx, sign_flips=n_sign, flip_tokens=tok_flip | sdiff.any(axis=-1))
 
 
