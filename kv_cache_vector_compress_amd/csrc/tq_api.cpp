@@ -52,11 +52,15 @@ static int check_config(const tq_config* c) {
     return fail(TQ_EINVAL, "proj_dim %d: need a multiple of 64 in [64, 512]", c->proj_dim);
   if (c->key_bits < 1 || c->key_bits > 4 || c->value_bits < 1 || c->value_bits > 4)
     return fail(TQ_EINVAL, "key_bits %d / value_bits %d: need 1..4", c->key_bits, c->value_bits);
-  if (c->head_dim != kD) return fail(TQ_EUNSUPPORTED, "head_dim %d is valid but only 128 is built", c->head_dim);
-  if (c->proj_dim != 64 && c->proj_dim != 128)
-    return fail(TQ_EUNSUPPORTED, "proj_dim %d is valid but only 64 and 128 are built", c->proj_dim);
   return TQ_OK;
 }
+
+// Shapes with the single-kernel compress / attention path; every other valid
+// shape runs on the general path (tq_general.hip).
+static bool fast_keys(const tq_config& c) { return c.head_dim == kD && (c.proj_dim == 64 || c.proj_dim == 128); }
+static bool fast_values(const tq_config& c) { return c.head_dim == kD; }
+static bool fast_attn(const tq_config& c, int G) { return fast_keys(c) && G <= 16; }
+constexpr int64_t kScratchRows = 32768;  // general-path rows per launch
 
 static size_t key_rec_bytes(const tq_config& c) { return 4u * (c.key_bits * c.head_dim / 32 + c.proj_dim / 32 + 2); }
 static size_t val_blk_bytes(const tq_config& c) { return 4u * (4 * c.value_bits * c.head_dim + kBlockTokens); }
@@ -68,8 +72,9 @@ using namespace tq;
 struct tq_ctx {
   tq_config cfg;
   int device;
-  void* dev_mem;       // one allocation holding every device image below
+  void* dev_mem;       // one allocation holding every device image below (and the general-path scratch)
   Matrices mats;
+  GenMats gen;         // general path: the same images plus scratch
   CodebookDev cb[5];   // indexed by bits
   bool loaded[5];
 };
@@ -102,8 +107,9 @@ size_t tq_cache_value_bytes(const tq_config* cfg, int32_t n_seq, int64_t capacit
 }
 
 size_t tq_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, int64_t n_tokens) {
-  if (check_config(cfg) == TQ_EINVAL || n_seq < 1 || G < 1 || G > 16 || n_tokens < 1) return 0;
-  return plan_attention(cfg->proj_dim, n_seq, G, n_tokens).total;
+  if (check_config(cfg) == TQ_EINVAL || n_seq < 1 || G < 1 || G > kMaxGeneralHeads || n_tokens < 1) return 0;
+  if (fast_attn(*cfg, G)) return plan_attention(cfg->proj_dim, n_seq, G, n_tokens).total;
+  return general_scores_workspace(cfg->head_dim, cfg->proj_dim, n_seq, G);
 }
 
 int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** out) {
@@ -114,17 +120,19 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   if (rc != TQ_OK) return rc;
   if (!R || !S) return fail(TQ_EINVAL, "tq_create: R or S is NULL");
   const int d = cfg->head_dim, m = cfg->proj_dim;
-  for (int i = 0; i < d * d; ++i)
+  for (size_t i = 0; i < (size_t)d * d; ++i)
     if (!std::isfinite(R[i])) return fail(TQ_EINVAL, "tq_create: R has a non-finite entry");
-  for (int i = 0; i < m * d; ++i)
+  for (size_t i = 0; i < (size_t)m * d; ++i)
     if (!std::isfinite(S[i])) return fail(TQ_EINVAL, "tq_create: S has a non-finite entry");
 
   // Host images.  R and S are scaled by 2^8 and split into fp16 high and low
   // parts (hi = fp16(x), lo = fp16(x - hi)), so hi + lo carries ~22 bits.
-  // S's columns are stored in "slot order": column 32 kb + 8 q + e holds
-  // rotated coordinate 16 (2 kb + e/4) + 4 q + e%4, the order in which a key
-  // lane holds its residual after the rotation.
-  const size_t r_img = (size_t)d * kLdsStride, s_img = (size_t)m * kLdsStride;
+  // Rows are padded to ld = d + 8 halves.  S's columns are stored in "slot
+  // order" per 128-coordinate chunk: column 128 u + 32 kb + 8 q + e holds
+  // rotated coordinate 128 u + 16 (2 kb + e/4) + 4 q + e%4, the order in which
+  // a key lane holds its residual after the rotation.
+  const int ld = d + 8;
+  const size_t r_img = (size_t)d * ld, s_img = (size_t)m * ld;
   std::vector<uint16_t> rh(r_img, 0), rl(r_img, 0), sh(s_img, 0), sl(s_img, 0);
   std::vector<float> r32((size_t)d * d), s32((size_t)m * d);
   auto split = [](double x, uint16_t& hi, uint16_t& lo) {
@@ -134,16 +142,16 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   };
   for (int i = 0; i < d; ++i)
     for (int k = 0; k < d; ++k) {
-      split(R[i * d + k], rh[i * kLdsStride + k], rl[i * kLdsStride + k]);
-      r32[(size_t)i * d + k] = (float)R[i * d + k];
+      split(R[(size_t)i * d + k], rh[(size_t)i * ld + k], rl[(size_t)i * ld + k]);
+      r32[(size_t)i * d + k] = (float)R[(size_t)i * d + k];
     }
   for (int i = 0; i < m; ++i) {
     for (int col = 0; col < d; ++col) {
-      const int kb = col / 32, q = (col % 32) / 8, e = col % 8;
-      const int coord = 16 * (2 * kb + e / 4) + 4 * q + e % 4;
-      split(S[i * d + coord], sh[i * kLdsStride + col], sl[i * kLdsStride + col]);
+      const int u = col / 128, c = col % 128, kb = c / 32, q = (c % 32) / 8, e = c % 8;
+      const int coord = 128 * u + 16 * (2 * kb + e / 4) + 4 * q + e % 4;
+      split(S[(size_t)i * d + coord], sh[(size_t)i * ld + col], sl[(size_t)i * ld + col]);
     }
-    for (int k = 0; k < d; ++k) s32[(size_t)i * d + k] = (float)S[i * d + k];
+    for (int k = 0; k < d; ++k) s32[(size_t)i * d + k] = (float)S[(size_t)i * d + k];
   }
 
   std::call_once(g_init_flag, [] { g_init_rc = compress_device_init() | attention_device_init(); });
@@ -157,7 +165,14 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   }
   const size_t b_rimg = r_img * 2, b_simg = s_img * 2;
   const size_t off_rl = b_rimg, off_sh = 2 * b_rimg, off_sl = off_sh + b_simg, off_r32 = off_sl + b_simg;
-  const size_t off_s32 = off_r32 + r32.size() * 4, total = off_s32 + s32.size() * 4;
+  const size_t off_s32 = off_r32 + r32.size() * 4, end_imgs = off_s32 + s32.size() * 4;
+  // general-path scratch (row norms, key residual hi/lo, residual square sums)
+  const bool gen = !fast_keys(*cfg) || !fast_values(*cfg);
+  const int64_t srows = gen ? kScratchRows : 0;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t off_nrm = up(end_imgs), off_rh = off_nrm + up((size_t)srows * 4);
+  const size_t off_rlo = off_rh + up((size_t)srows * d * 2), off_g2 = off_rlo + up((size_t)srows * d * 2);
+  const size_t total = off_g2 + up((size_t)srows * (d / 128) * 4);
   if (hipMalloc(&c->dev_mem, total) != hipSuccess) {
     delete c;
     return fail(TQ_ENOMEM, "tq_create: hipMalloc of %zu bytes failed", total);
@@ -180,6 +195,13 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   c->mats.s_lo = (const uint16_t*)(base + off_sl);
   c->mats.r32 = (const float*)(base + off_r32);
   c->mats.s32 = (const float*)(base + off_s32);
+  c->gen.mats = c->mats;
+  c->gen.ld = ld;
+  c->gen.scratch_rows = srows;
+  c->gen.nrm = gen ? (float*)(base + off_nrm) : nullptr;
+  c->gen.res_hi = gen ? (uint16_t*)(base + off_rh) : nullptr;
+  c->gen.res_lo = gen ? (uint16_t*)(base + off_rlo) : nullptr;
+  c->gen.g2p = gen ? (float*)(base + off_g2) : nullptr;
   for (int b = 0; b < 5; ++b) c->loaded[b] = false;
   *out = c;
   return TQ_OK;
@@ -273,8 +295,12 @@ int tq_append_key(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_
   if (n_new == 0) return TQ_OK;
   AppendShape s{k, dtype, n_new, pos, cache->capacity, cache->n_seq};
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_append_key: hipSetDevice failed");
-  rc = launch_compress_keys(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.proj_dim, s,
-                            cache->key_records, stream);
+  if (fast_keys(ctx->cfg))
+    rc = launch_compress_keys(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.proj_dim, s,
+                              cache->key_records, stream);
+  else
+    rc = launch_general_keys(ctx->gen, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.head_dim,
+                             ctx->cfg.proj_dim, s, cache->key_records, stream);
   return rc ? fail(rc, "tq_append_key: launch failed (%d)", rc) : TQ_OK;
 }
 
@@ -286,8 +312,12 @@ int tq_append_value(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int3
   if (n_new == 0) return TQ_OK;
   AppendShape s{v, dtype, n_new, pos, cache->capacity, cache->n_seq};
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_append_value: hipSetDevice failed");
-  rc = launch_compress_values(ctx->mats, ctx->cb[ctx->cfg.value_bits], ctx->cfg.value_bits, s,
-                              cache->value_blocks, stream);
+  if (fast_values(ctx->cfg))
+    rc = launch_compress_values(ctx->mats, ctx->cb[ctx->cfg.value_bits], ctx->cfg.value_bits, s,
+                                cache->value_blocks, stream);
+  else
+    rc = launch_general_values(ctx->gen, ctx->cb[ctx->cfg.value_bits], ctx->cfg.value_bits, ctx->cfg.head_dim, s,
+                               cache->value_blocks, stream);
   return rc ? fail(rc, "tq_append_value: launch failed (%d)", rc) : TQ_OK;
 }
 
@@ -297,7 +327,11 @@ static int attn_common(tq_ctx* ctx, const tq_cache_view* cache, const void* q, i
   int rc = check_cache(ctx, cache, fn);
   if (rc) return rc;
   if (dtype != TQ_F16 && dtype != TQ_F32) return fail(TQ_EINVAL, "%s: dtype %d", fn, dtype);
-  if (G < 1 || G > 16) return fail(TQ_EINVAL, "%s: G %d not in 1..16", fn, G);
+  const int gmax = need_values ? 16 : kMaxGeneralHeads;
+  if (G < 1 || G > gmax) return fail(TQ_EINVAL, "%s: G %d not in 1..%d", fn, G, gmax);
+  if (need_values && !fast_attn(ctx->cfg, G))
+    return fail(TQ_EUNSUPPORTED, "%s: built for head_dim 128 with proj_dim 64 or 128 (have %d, %d)", fn,
+                ctx->cfg.head_dim, ctx->cfg.proj_dim);
   if (n_tokens < 1 || n_tokens > cache->capacity)
     return fail(TQ_EINVAL, "%s: n_tokens %lld not in [1, capacity]", fn, (long long)n_tokens);
   if (!q || !outp || !ws) return fail(TQ_EINVAL, "%s: NULL q, output or workspace", fn);
@@ -307,9 +341,10 @@ static int attn_common(tq_ctx* ctx, const tq_cache_view* cache, const void* q, i
     return fail(TQ_ENOCODEBOOK, "%s: no %d-bit key codebook loaded", fn, ctx->cfg.key_bits);
   if (need_values && !ctx->loaded[ctx->cfg.value_bits])
     return fail(TQ_ENOCODEBOOK, "%s: no %d-bit value codebook loaded", fn, ctx->cfg.value_bits);
-  *plan = plan_attention(ctx->cfg.proj_dim, cache->n_seq, G, n_tokens);
-  if (ws_bytes < plan->total)
-    return fail(TQ_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, plan->total);
+  const size_t need = fast_attn(ctx->cfg, G) ? (*plan = plan_attention(ctx->cfg.proj_dim, cache->n_seq, G, n_tokens)).total
+                                             : general_scores_workspace(ctx->cfg.head_dim, ctx->cfg.proj_dim,
+                                                                        cache->n_seq, G);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   return TQ_OK;
 }
 
@@ -322,10 +357,15 @@ int tq_attention_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, 
   if (rc) return rc;
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_attention_scores: hipSetDevice");
   AttnShape s{q, dtype, G, n_tokens, cache->capacity, cache->n_seq};
-  rc = launch_prep_queries(ctx->mats, ctx->cfg.proj_dim, s, workspace, plan, stream);
-  if (!rc)
-    rc = launch_scores(ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.proj_dim, s, cache->key_records,
-                       scores, workspace, plan, stream);
+  if (fast_attn(ctx->cfg, G)) {
+    rc = launch_prep_queries(ctx->mats, ctx->cfg.proj_dim, s, workspace, plan, stream);
+    if (!rc)
+      rc = launch_scores(ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.proj_dim, s, cache->key_records,
+                         scores, workspace, plan, stream);
+  } else {
+    rc = launch_general_scores(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.head_dim,
+                               ctx->cfg.proj_dim, s, cache->key_records, scores, workspace, stream);
+  }
   return rc ? fail(rc, "tq_attention_scores: launch failed (%d)", rc) : TQ_OK;
 }
 

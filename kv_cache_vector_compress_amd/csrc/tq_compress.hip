@@ -272,29 +272,6 @@ struct ValArgs {
 
 constexpr size_t kValLds = (size_t)2 * kRImg * 2;
 
-// Field mask of (slot s, word w, byte lane i) for b-bit codes (runtime form).
-__device__ __forceinline__ uint32_t field_mask_rt(int b, int s, int w, int i) {
-  uint32_t m = 0;
-  if (b == 1) {
-    if (w == 0) m = 1u << s;
-  } else if (b == 2) {
-    if (w == s / 4) m = 3u << (2 * (s % 4));
-  } else if (b == 4) {
-    if (w == s / 2) m = 15u << (4 * (s % 2));
-  } else {
-    if (s < 6) {
-      if (w == s / 2) m = 7u << (3 * (s % 2));
-    } else if (s == 6) {
-      if (w == 0) m = 3u << 6;
-      if (w == 2) m = 1u << 6;
-    } else {
-      if (w == 1) m = 3u << 6;
-      if (w == 2) m = 1u << 7;
-    }
-  }
-  return m << (8 * i);
-}
-
 template <int B, bool F32>
 __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const ValArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];

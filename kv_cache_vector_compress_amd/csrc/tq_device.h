@@ -111,6 +111,29 @@ __device__ __forceinline__ constexpr uint32_t field_mask() {
   return m << (8 * I);
 }
 
+// Field mask of (slot s, word w, byte lane i) for b-bit codes (runtime form).
+__device__ __forceinline__ uint32_t field_mask_rt(int b, int s, int w, int i) {
+  uint32_t m = 0;
+  if (b == 1) {
+    if (w == 0) m = 1u << s;
+  } else if (b == 2) {
+    if (w == s / 4) m = 3u << (2 * (s % 4));
+  } else if (b == 4) {
+    if (w == s / 2) m = 15u << (4 * (s % 2));
+  } else {
+    if (s < 6) {
+      if (w == s / 2) m = 7u << (3 * (s % 2));
+    } else if (s == 6) {
+      if (w == 0) m = 3u << 6;
+      if (w == 2) m = 1u << 6;
+    } else {
+      if (w == 1) m = 3u << 6;
+      if (w == 2) m = 1u << 7;
+    }
+  }
+  return m << (8 * i);
+}
+
 // Decode a selector word into 4 fp16 centroids: two registers holding
 // (c[code0], c[code1]) and (c[code2], c[code3]).  tlo/thi hold the low/high
 // bytes of the fp16 centroid table (entry v at byte v).

@@ -1,0 +1,724 @@
+// General-shape path on gfx950: head_dim d a multiple of 128 up to 1024,
+// proj_dim m a multiple of 64 up to 512 (the d = 128, m <= 128 shapes have
+// their own single-kernel path in tq_compress.hip / tq_attention.hip).
+//
+// The computation is the same as on the fast path (nav.superapi.store
+// "turboquant-pytorch", 主要能力 / 算法细节; atskills.one Stage 1 / Stage 2):
+//   keys:   y = R k / ||k||, idx = #{i : beta_i < y}, r = y - c[idx],
+//           gamma = ||r||, s = [S r >= 0]
+//   values: y = R v / ||v||, idx
+//   scores: est = ||k|| (<R q, c[idx]> + gamma sqrt(pi/2)/m <S R q, 2s - 1>)
+// with the same split-fp16 arithmetic (R, S scaled by 2^8 and split into fp16
+// hi + lo; fp16 inputs exact, fp32 inputs split after a power-of-two scale)
+// and the same record layout, which is defined for any d multiple of 128 and
+// m multiple of 64.  What changes is the blocking: R (up to 4 MB as hi/lo
+// fp16) no longer fits in LDS, so the rotation and the projection are tiled
+// GEMMs that stream 32-column slices of R and S through LDS, and the key
+// residual goes through a scratch buffer between the two.
+//
+//   gen_row_norms     ||x|| of every row of the launch
+//   gen_keys_rotate   y for a 128-token x 128-coordinate tile; cells, codes,
+//                     residual (to scratch, fp16 hi/lo in slot order), and
+//                     the tile's share of gamma^2
+//   gen_keys_project  z = S r for a 64-token x 64-projection tile; sign bits,
+//                     and gamma from the shares
+//   gen_values        y for one 128-token block x 128 coordinates; codes
+//   gen_prep_queries  q~ = R q and p = S q~ per query head, as MFMA operands
+//   gen_scores        scores of 16 tokens for every query head
+#include "tq_device.h"
+
+namespace tq {
+
+constexpr int kSliceLS = 40;  // LDS row stride (halves) of a 32-column slice: conflict-free b128 reads
+
+struct GenArgs {
+  const void* x;
+  int64_t n_new;      // tokens per slot in x (the call's n_new)
+  int64_t pos;        // the call's first token position
+  int64_t tok_off;    // first token of this launch, relative to x
+  int64_t n_sub;      // tokens per slot in this launch
+  int64_t capacity;
+  int n_seq, d, m, n_oct, ld, rec_words, block_words;
+  const uint16_t* r_hi;
+  const uint16_t* r_lo;
+  const uint16_t* s_hi;
+  const uint16_t* s_lo;
+  float* nrm;         // [n_seq * n_sub] norms of this launch's rows
+  uint16_t* res_hi;   // [n_seq * n_sub][d] residual 2^12 (y - c), slot order, fp16 high part
+  uint16_t* res_lo;
+  float* g2p;         // [n_seq * n_sub][n_oct] partial sums of the squared residual
+  uint32_t* out;      // key records or value blocks
+  _Float16 m1;        // -1 (a run-time value: see split2m)
+  CodebookDev cb;
+};
+
+// Input row of launch row r (slot-major over the launch's tokens).
+__device__ __forceinline__ int64_t gen_in_row(const GenArgs& a, int64_t r) {
+  const int64_t slot = r / a.n_sub;
+  return slot * a.n_new + a.tok_off + (r - slot * a.n_sub);
+}
+
+// Stage rows [row0, row0 + nrows) x columns [k0, k0 + 32) of an fp16 image
+// pair (hi, lo; row stride ld halves) into LDS (row stride kSliceLS).
+__device__ __forceinline__ void stage_slice(uint16_t* lds_hi, uint16_t* lds_lo, const uint16_t* hi,
+                                            const uint16_t* lo, int ld, int row0, int nrows, int k0) {
+  for (int i = threadIdx.x; i < 2 * nrows * 4; i += blockDim.x) {
+    const int img = i / (nrows * 4), rr = (i / 4) % nrows, cc = (i % 4) * 8;
+    const uint16_t* src = (img ? lo : hi) + (size_t)(row0 + rr) * ld + k0 + cc;
+    *(u4*)((img ? lds_lo : lds_hi) + rr * kSliceLS + cc) = *(const u4*)src;
+  }
+}
+
+// 8 inputs of a row as an MFMA operand: fp16 rows as they are; fp32 rows
+// scaled by sc (|x sc| < 2^13) and split into fp16 hi + lo.
+template <bool F32>
+__device__ __forceinline__ void load_x8(const void* x, int64_t row, int d, int k, float sc, h8& xh, h8& xl) {
+  if constexpr (F32) {
+    const float* p = (const float*)x + row * d + k;
+    const f4 v0 = *(const f4*)p, v1 = *(const f4*)(p + 4);
+    u4 hi, lo;
+    HiLo t = split2(v0[0] * sc, v0[1] * sc);
+    hi[0] = t.hi; lo[0] = t.lo;
+    t = split2(v0[2] * sc, v0[3] * sc);
+    hi[1] = t.hi; lo[1] = t.lo;
+    t = split2(v1[0] * sc, v1[1] * sc);
+    hi[2] = t.hi; lo[2] = t.lo;
+    t = split2(v1[2] * sc, v1[3] * sc);
+    hi[3] = t.hi; lo[3] = t.lo;
+    xh = as_h8(hi);
+    xl = as_h8(lo);
+  } else {
+    xh = *(const h8*)((const _Float16*)x + row * d + k);
+  }
+}
+
+// Power-of-two pre-scale of an fp32 row of norm n: |x sc| < 2^13.
+__device__ __forceinline__ float row_scale(float n) {
+  int E = 0;
+  frexpf(n, &E);
+  return n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;
+}
+
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void gen_row_norms(const GenArgs a, int dtype) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= (int64_t)a.n_seq * a.n_sub) return;
+  const int64_t row = gen_in_row(a, r);
+  float s = 0.f;
+  if (dtype == TQ_F32) {
+    const float* p = (const float*)a.x + row * a.d;
+    for (int c = 4 * lane; c < a.d; c += 256) {
+      const f4 v = *(const f4*)(p + c);
+      s = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], s))));
+    }
+  } else {
+    const _Float16* p = (const _Float16*)a.x + row * a.d;
+    for (int c = 8 * lane; c < a.d; c += 512) {
+      const h8 v = *(const h8*)(p + c);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) s = __builtin_amdgcn_fdot2(h2{v[e], v[e + 1]}, h2{v[e], v[e + 1]}, s, false);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += shfl_xor(s, o);
+  if (lane == 0) a.nrm[r] = sqrtf(s);
+}
+
+// ---------------------------------------------------------------------------
+// keys, part 1: rotation of a 128-row x 128-coordinate tile (4 waves x 2
+// 16-row tiles; coordinates on the MFMA M axis, so a lane ends up with 32
+// coordinates of one row: one code group), then cells, codes and residual.
+// ---------------------------------------------------------------------------
+
+template <int B, bool F32>
+__global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
+  constexpr int H = 1 << (B - 1);
+  __shared__ __align__(16) uint16_t Rs[2][128 * kSliceLS];
+  __shared__ float ctab[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int u = blockIdx.y;  // coordinate chunk
+  const int64_t rows = (int64_t)a.n_seq * a.n_sub;
+  if (tid < 16) ctab[tid] = a.cb.cent[tid] * kResScale;
+
+  int64_t row[2], in_row[2];
+  float n[2], sc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    row[j] = (int64_t)blockIdx.x * 128 + wave * 32 + 16 * j + r16;
+    const int64_t rr = row[j] < rows ? row[j] : rows - 1;  // rows past the end: any valid row, not stored
+    in_row[j] = gen_in_row(a, rr);
+    n[j] = a.nrm[rr];
+    sc[j] = F32 ? row_scale(n[j]) : 1.f;
+  }
+  f4 acc[2][8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc[j][s] = f4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < a.d; k0 += 32) {
+    __syncthreads();
+    stage_slice(Rs[0], Rs[1], a.r_hi, a.r_lo, a.ld, 128 * u, 128, k0);
+    __syncthreads();
+    h8 xh[2], xl[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_x8<F32>(a.x, in_row[j], a.d, k0 + 8 * q, sc[j], xh[j], xl[j]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const h8 ah = *(const h8*)(Rs[0] + (16 * s + r16) * kSliceLS + 8 * q);
+      const h8 al = *(const h8*)(Rs[1] + (16 * s + r16) * kSliceLS + 8 * q);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[j][s] = mfma(ah, xh[j], acc[j][s]);
+        acc[j][s] = mfma(al, xh[j], acc[j][s]);
+        if constexpr (F32) acc[j][s] = mfma(ah, xl[j], acc[j][s]);
+      }
+    }
+  }
+
+  float bpos[8];
+  load_pos_beta<B>(bpos, a.cb);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bool valid = row[j] < rows;
+    const float sigma = kRotScale * sc[j] * n[j];
+    const float s16 = n[j] > 0.f ? kResScale / sigma : 0.f;
+    float bs[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) bs[t] = t < H - 1 ? bpos[t] * sigma : 0.f;
+    uint32_t cw[B];
+#pragma unroll
+    for (int w = 0; w < B; ++w) cw[w] = 0u;
+    float g2 = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2) {
+      u4 rhi, rlo;
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        float rs[4];
+        const uint32_t x4 = quantize4<B>(acc[j][2 * kb2 + uu], bs, s16, ctab, rs, g2);
+        const HiLo t01 = split2m(rs[0], rs[1], a.m1), t23 = split2m(rs[2], rs[3], a.m1);
+        rhi[2 * uu] = t01.hi;
+        rlo[2 * uu] = t01.lo;
+        rhi[2 * uu + 1] = t23.hi;
+        rlo[2 * uu + 1] = t23.lo;
+        put_sel4_rt<B>(cw, 2 * kb2 + uu, x4);
+      }
+      if (valid) {
+        const size_t o = (size_t)row[j] * a.d + 128 * u + 32 * kb2 + 8 * q;
+        *(u4*)(a.res_hi + o) = rhi;
+        *(u4*)(a.res_lo + o) = rlo;
+      }
+    }
+    g2 += shfl_xor(g2, 16);
+    g2 += shfl_xor(g2, 32);
+    if (valid) {
+      const int64_t slot = row[j] / a.n_sub, t = row[j] - slot * a.n_sub;
+      uint32_t* rp = a.out + (slot * a.capacity + a.pos + a.tok_off + t) * a.rec_words;
+#pragma unroll
+      for (int w = 0; w < B; ++w) rp[(q * a.n_oct + u) * B + w] = cw[w];
+      if (q == 0) a.g2p[row[j] * a.n_oct + u] = g2;
+      if (q == 0 && u == 0) rp[a.rec_words - 2] = __float_as_uint(n[j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// keys, part 2: z = S r for a 64-row x 64-projection tile (4 waves x 16
+// rows; projection coordinates on M), sign bits, and gamma.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void gen_keys_project(const GenArgs a, int bits) {
+  __shared__ __align__(16) uint16_t Ss[2][64 * kSliceLS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int u = blockIdx.y;  // 64-projection chunk
+  const int64_t rows = (int64_t)a.n_seq * a.n_sub;
+  const int64_t row = (int64_t)blockIdx.x * 64 + wave * 16 + r16;
+  const int64_t rr = row < rows ? row : rows - 1;
+  f4 z[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) z[p] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.d; k0 += 32) {
+    __syncthreads();
+    stage_slice(Ss[0], Ss[1], a.s_hi, a.s_lo, a.ld, 64 * u, 64, k0);
+    __syncthreads();
+    const h8 rh = *(const h8*)(a.res_hi + (size_t)rr * a.d + k0 + 8 * q);
+    const h8 rl = *(const h8*)(a.res_lo + (size_t)rr * a.d + k0 + 8 * q);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const h8 sh = *(const h8*)(Ss[0] + (16 * p + r16) * kSliceLS + 8 * q);
+      const h8 sl = *(const h8*)(Ss[1] + (16 * p + r16) * kSliceLS + 8 * q);
+      z[p] = mfma(sh, rh, z[p]);
+      z[p] = mfma(sl, rh, z[p]);
+      z[p] = mfma(sh, rl, z[p]);
+    }
+  }
+  const uint32_t bits16 = sign_bits16(z[0], z[1], z[2], z[3]);
+  if (row < rows) {
+    const int64_t slot = row / a.n_sub, t = row - slot * a.n_sub;
+    uint32_t* rp = a.out + (slot * a.capacity + a.pos + a.tok_off + t) * a.rec_words;
+    const int sw0 = bits * a.d / 32;
+    ((uint16_t*)(rp + sw0 + 2 * u + (q >> 1)))[q & 1] = (uint16_t)bits16;
+    if (u == 0 && q == 1) {
+      float g = 0.f;
+      for (int c = 0; c < a.n_oct; ++c) g += a.g2p[row * a.n_oct + c];
+      rp[a.rec_words - 1] = __float_as_uint(sqrtf(g) * (1.f / kResScale));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// values: one 128-token block of one slot x one 128-coordinate chunk.  Tokens
+// on M (so a lane ends up with one coordinate of 4 tokens per tile, the
+// order of the value block); wave w owns coordinate tiles 2w and 2w + 1 of
+// the chunk for all 8 token tiles, i.e. whole code words.
+// ---------------------------------------------------------------------------
+
+template <int B, bool F32>
+__global__ __launch_bounds__(256) void gen_values(const GenArgs a) {
+  __shared__ __align__(16) uint16_t Rs[2][128 * kSliceLS];
+  __shared__ float inv_sh[kBlockTokens];  // 1 / sigma per block token (0: not in this launch or zero row)
+  __shared__ float nrm_sh[kBlockTokens];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int u = blockIdx.y;
+  const int64_t P0 = a.pos + a.tok_off, P1 = P0 + a.n_sub;  // token positions of this launch
+  const int64_t blk0 = P0 / kBlockTokens, nblk = (P1 - 1) / kBlockTokens - blk0 + 1;
+  const int64_t slot = blockIdx.x / nblk, blk = blk0 + (blockIdx.x - slot * nblk);
+  const int64_t tok0 = blk * kBlockTokens;
+  if (tid < kBlockTokens) {
+    const int64_t p = tok0 + tid;
+    const bool valid = p >= P0 && p < P1;
+    const float nn = valid ? a.nrm[slot * a.n_sub + (p - P0)] : 0.f;
+    const float sigma = kRotScale * (F32 ? row_scale(nn) : 1.f) * nn;
+    inv_sh[tid] = sigma > 0.f ? 1.f / sigma : 0.f;
+    nrm_sh[tid] = nn;
+  }
+  // A operand rows: block token 16 mt + r16
+  int64_t in_row[8];
+  float sc[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    int64_t p = tok0 + 16 * mt + r16;
+    p = p < P0 ? P0 : (p >= P1 ? P1 - 1 : p);  // clamp to a row of this launch (codes masked later)
+    const int64_t r = slot * a.n_sub + (p - P0);
+    in_row[mt] = gen_in_row(a, r);
+    sc[mt] = F32 ? row_scale(a.nrm[r]) : 1.f;
+  }
+  f4 acc[8][2];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) acc[mt][0] = acc[mt][1] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.d; k0 += 32) {
+    __syncthreads();
+    stage_slice(Rs[0], Rs[1], a.r_hi, a.r_lo, a.ld, 128 * u, 128, k0);
+    __syncthreads();
+    h8 bh[2], bl[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bh[t] = *(const h8*)(Rs[0] + (16 * (2 * wave + t) + r16) * kSliceLS + 8 * q);
+      bl[t] = *(const h8*)(Rs[1] + (16 * (2 * wave + t) + r16) * kSliceLS + 8 * q);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      h8 xh, xl;
+      load_x8<F32>(a.x, in_row[mt], a.d, k0 + 8 * q, sc[mt], xh, xl);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        acc[mt][t] = mfma(xh, bh[t], acc[mt][t]);
+        acc[mt][t] = mfma(xh, bl[t], acc[mt][t]);
+        if constexpr (F32) acc[mt][t] = mfma(xl, bh[t], acc[mt][t]);
+      }
+    }
+  }
+
+  float bpos[8];
+  load_pos_beta<B>(bpos, a.cb);
+  float bsx[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) bsx[i][t] = bpos[t];
+  uint32_t cw[2][B];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int w = 0; w < B; ++w) cw[t][w] = 0u;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const f4 inv = *(const f4*)&inv_sh[16 * mt + 4 * q];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f4 y = acc[mt][t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] *= inv[i];
+      put_sel4_rt<B>(cw[t], mt, cells4<B>(y, bsx));
+    }
+  }
+  uint32_t* vb = a.out + (slot * (a.capacity / kBlockTokens) + blk) * a.block_words;
+  const bool full = tok0 >= P0 && tok0 + kBlockTokens <= P1;
+  uint32_t keep[B];  // bits of tokens outside this launch: left as they are
+#pragma unroll
+  for (int w = 0; w < B; ++w) keep[w] = 0u;
+  if (!full)
+    for (int s = 0; s < 8; ++s)
+      for (int i = 0; i < 4; ++i) {
+        const int64_t p = tok0 + 16 * s + 4 * q + i;
+        if (p < P0 || p >= P1)
+#pragma unroll
+          for (int w = 0; w < B; ++w) keep[w] |= field_mask_rt(B, s, w, i);
+      }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int c = 128 * u + 16 * (2 * wave + t) + r16;
+#pragma unroll
+    for (int w = 0; w < B; ++w) {
+      uint32_t* wp = vb + (size_t)(w * 4 + q) * a.d + c;
+      *wp = full ? cw[t][w] : ((*wp & keep[w]) | (cw[t][w] & ~keep[w]));
+    }
+  }
+  if (u == 0 && tid < kBlockTokens) {
+    const int64_t p = tok0 + tid;
+    if (p >= P0 && p < P1) ((float*)(vb + 4 * B * a.d))[tid] = nrm_sh[tid];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// query preparation: one workgroup per (slot, query head) of the padded head
+// range; q~ = R q and p = S q~ in fp32, then the fp16 MFMA B operands
+// (divided by ||q||) in the lanes of this head.
+// ---------------------------------------------------------------------------
+
+struct GenPrepArgs {
+  const void* q;
+  int dtype, G, HG, n_seq, d, m, n_oct;
+  const float* r32;
+  const float* s32;
+  uint16_t* wq;   // [n_seq][HG][KBT][64][8] fp16, KBT = d/32 + m/32
+  float* wqn;     // [n_seq][16 HG]
+};
+
+__global__ __launch_bounds__(256) void gen_prep_queries(const GenPrepArgs a) {
+  extern __shared__ float gsm[];
+  float* qs = gsm;          // [d]
+  float* qt = qs + a.d;     // [d]
+  float* pp = qt + a.d;     // [m]
+  __shared__ float red[4];
+  const int H16 = 16 * a.HG;
+  const int slot = blockIdx.x / H16, h = blockIdx.x % H16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool live = h < a.G;
+  float s = 0.f;
+  for (int k = tid; k < a.d; k += blockDim.x) {
+    float v = 0.f;
+    if (live) {
+      const int64_t off = ((int64_t)slot * a.G + h) * a.d + k;
+      v = a.dtype == TQ_F32 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
+    }
+    qs[k] = v;
+    s = fmaf(v, v, s);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += shfl_xor(s, o);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  const float qn = sqrtf((red[0] + red[1]) + (red[2] + red[3]));
+  for (int j = wave; j < a.d; j += 4) {  // q~ = R q, one row per wave step
+    float t = 0.f;
+    for (int k = lane; k < a.d; k += 64) t = fmaf(a.r32[(size_t)j * a.d + k], qs[k], t);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) t += shfl_xor(t, o);
+    if (lane == 0) qt[j] = t;
+  }
+  __syncthreads();
+  for (int i = wave; i < a.m; i += 4) {  // p = S q~
+    float t = 0.f;
+    for (int k = lane; k < a.d; k += 64) t = fmaf(a.s32[(size_t)i * a.d + k], qt[k], t);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) t += shfl_xor(t, o);
+    if (lane == 0) pp[i] = t;
+  }
+  __syncthreads();
+  const float inv = live && qn > 0.f ? 1.f / qn : 0.f;
+  const int KBT = a.d / 32 + a.m / 32;
+  const int hg = h / 16, h16 = h % 16;
+  for (int idx = tid; idx < KBT * 4; idx += blockDim.x) {
+    const int kb = idx / 4, qq = idx % 4;
+    h8 v;
+    if (kb < a.d / 32) {
+      // centroid part of chunk kb/4: k slot e <-> coordinate 128 (kb/4) + 16 (2 (kb%4) + e/4) + 4 qq + e%4
+      const int base = 128 * (kb / 4) + 32 * (kb % 4);
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)(qt[base + 16 * (e / 4) + 4 * qq + e % 4] * inv);
+    } else {
+      // sign part: k slot 2e+half <-> bit p + 16 half of sign word 2 (kbp/2) + qq/2,
+      // p = 8 (qq%2) + 4 (kbp%2) + e, which holds projection coordinate 16 t + 4 qs + p%4
+      // with qs = 2 (qq/2) + half, t = 4 (kbp/2) + p/4
+      const int kbp = kb - a.d / 32;
+      for (int e = 0; e < 4; ++e)
+        for (int half = 0; half < 2; ++half) {
+          const int p = 8 * (qq % 2) + 4 * (kbp % 2) + e;
+          const int qsg = 2 * (qq / 2) + half;
+          const int t = 4 * (kbp / 2) + p / 4;
+          v[2 * e + half] = (_Float16)(pp[16 * t + 4 * qsg + p % 4] * inv);
+        }
+    }
+    const int l = 16 * qq + h16;
+    *(h8*)(a.wq + ((((int64_t)slot * a.HG + hg) * KBT + kb) * 64 + l) * 8) = v;
+  }
+  if (tid == 0) a.wqn[(int64_t)slot * H16 + h] = live ? qn : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// scores: one wave per 16-token tile; every chunk of a key record is decoded
+// once and multiplied by the query operands of all HG head groups.
+// ---------------------------------------------------------------------------
+
+struct GenScoreArgs {
+  const uint32_t* rec;
+  float* scores;
+  const uint16_t* wq;
+  const float* wqn;
+  int64_t n_tokens, capacity;
+  int n_seq, G, HG, d, m, n_oct, rec_words;
+  int64_t tiles_per_slot;
+  float kappa;
+  uint32_t tlo[4], thi[4];
+};
+
+template <int B, int HG>
+__global__ __launch_bounds__(256) void gen_scores(const GenScoreArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (gw >= a.tiles_per_slot * a.n_seq) return;
+  const int slot = (int)(gw / a.tiles_per_slot);
+  const int64_t tile = gw - (int64_t)slot * a.tiles_per_slot;
+  const int n_tok = (int)a.n_tokens;
+  const int t = min((int)(tile * 16) + r16, n_tok - 1);
+  const uint32_t* rp = a.rec + ((int64_t)slot * a.capacity + t) * a.rec_words;
+  const int KBT = a.d / 32 + a.m / 32;
+  const uint16_t* wq = a.wq + (int64_t)slot * HG * KBT * 64 * 8 + lane * 8;
+  uint32_t tlo[4], thi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; }
+  f4 acc[HG];
+#pragma unroll
+  for (int g = 0; g < HG; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < a.n_oct; ++c) {
+    uint32_t cw[B];
+#pragma unroll
+    for (int w = 0; w < B; ++w) cw[w] = rp[(q * a.n_oct + c) * B + w];
+    const h8 A0 = decode_pair<B, 0>(cw, tlo, thi), A1 = decode_pair<B, 2>(cw, tlo, thi);
+    const h8 A2 = decode_pair<B, 4>(cw, tlo, thi), A3 = decode_pair<B, 6>(cw, tlo, thi);
+#pragma unroll
+    for (int g = 0; g < HG; ++g) {
+      const uint16_t* wg = wq + ((int64_t)g * KBT + 4 * c) * 64 * 8;
+      acc[g] = mfma(A0, *(const h8*)(wg), acc[g]);
+      acc[g] = mfma(A1, *(const h8*)(wg + 64 * 8), acc[g]);
+      acc[g] = mfma(A2, *(const h8*)(wg + 2 * 64 * 8), acc[g]);
+      acc[g] = mfma(A3, *(const h8*)(wg + 3 * 64 * 8), acc[g]);
+    }
+  }
+  const float gamma = __uint_as_float(rp[a.rec_words - 1]);
+  const _Float16 gk = (_Float16)(gamma * a.kappa);
+  const uint32_t gk2 = (uint32_t)__builtin_bit_cast(uint16_t, gk) * 0x00010001u;
+  const int sh0 = 15 - 8 * (q & 1);
+  const int sw0 = B * a.d / 32;
+  for (int kbp = 0; kbp < a.m / 32; ++kbp) {
+    const uint32_t w = ~rp[sw0 + 2 * (kbp / 2) + (q >> 1)];
+    u4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t sh = w << (sh0 - 4 * (kbp % 2) - e);  // bits p, p+16 -> 15, 31
+      v[e] = (sh & 0x80008000u) | (gk2 & 0x7FFF7FFFu);
+    }
+    const h8 A = as_h8(v);
+#pragma unroll
+    for (int g = 0; g < HG; ++g)
+      acc[g] = mfma(A, *(const h8*)(wq + ((int64_t)g * KBT + a.d / 32 + kbp) * 64 * 8), acc[g]);
+  }
+  // acc[g][i]: token row 4q+i of the tile, query head 16 g + r16; ||k|| of
+  // token row 4q+i comes from the lanes that loaded that record
+  const float kn = __uint_as_float(rp[a.rec_words - 2]);
+  f4 nk;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nk[i] = __shfl(kn, 4 * q + i, 64);
+  const int t0 = (int)(tile * 16) + 4 * q;
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+    const int h = 16 * g + r16;
+    if (h >= a.G) continue;
+    const float qn = a.wqn[(int64_t)slot * 16 * HG + h];
+    float* out = a.scores + ((int64_t)slot * a.G + h) * (int64_t)n_tok;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (t0 + i < n_tok) out[t0 + i] = acc[g][i] * nk[i] * qn;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+static GenArgs gen_args(const GenMats& g, const CodebookDev& cb, int bits, const AppendShape& s, int d, int m,
+                        int64_t tok_off, int64_t n_sub, void* out) {
+  GenArgs a;
+  a.x = s.x;
+  a.n_new = s.n_new;
+  a.pos = s.pos;
+  a.tok_off = tok_off;
+  a.n_sub = n_sub;
+  a.capacity = s.capacity;
+  a.n_seq = s.n_seq;
+  a.d = d;
+  a.m = m;
+  a.n_oct = d / 128;
+  a.ld = g.ld;
+  a.rec_words = bits * d / 32 + m / 32 + 2;
+  a.block_words = 4 * bits * d + kBlockTokens;
+  a.r_hi = g.mats.r_hi;
+  a.r_lo = g.mats.r_lo;
+  a.s_hi = g.mats.s_hi;
+  a.s_lo = g.mats.s_lo;
+  a.nrm = g.nrm;
+  a.res_hi = g.res_hi;
+  a.res_lo = g.res_lo;
+  a.g2p = g.g2p;
+  a.out = (uint32_t*)out;
+  a.m1 = (_Float16)-1.0f;
+  a.cb = cb;
+  return a;
+}
+
+// Tokens per slot of one launch: the scratch holds scratch_rows rows, and for
+// values the split points must fall on block boundaries.
+static int64_t gen_sub_tokens(const GenMats& g, int n_seq) {
+  int64_t t = g.scratch_rows / n_seq;
+  t -= t % kBlockTokens;
+  return t < kBlockTokens ? kBlockTokens : t;
+}
+
+int launch_general_keys(const GenMats& g, const CodebookDev& cb, int bits, int d, int m, const AppendShape& s,
+                        void* key_records, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t sub = gen_sub_tokens(g, s.n_seq);
+  if (sub * s.n_seq > g.scratch_rows) return TQ_EUNSUPPORTED;
+  for (int64_t off = 0; off < s.n_new; off += sub) {
+    const int64_t n_sub = s.n_new - off < sub ? s.n_new - off : sub;
+    const GenArgs a = gen_args(g, cb, bits, s, d, m, off, n_sub, key_records);
+    const int64_t rows = n_sub * s.n_seq;
+    hipLaunchKernelGGL(gen_row_norms, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, s.dtype);
+    const dim3 g1((unsigned)((rows + 127) / 128), (unsigned)(d / 128)), g2((unsigned)((rows + 63) / 64),
+                                                                             (unsigned)(m / 64));
+    const bool f32 = s.dtype == TQ_F32;
+#define TQ_GK(B)                                                                              \
+  if (bits == B) {                                                                            \
+    if (f32) hipLaunchKernelGGL((gen_keys_rotate<B, true>), g1, dim3(256), 0, st, a);        \
+    else hipLaunchKernelGGL((gen_keys_rotate<B, false>), g1, dim3(256), 0, st, a);           \
+  }
+    TQ_GK(1) TQ_GK(2) TQ_GK(3) TQ_GK(4)
+#undef TQ_GK
+    hipLaunchKernelGGL(gen_keys_project, g2, dim3(256), 0, st, a, bits);
+    if (hipGetLastError() != hipSuccess) return TQ_EDEVICE;
+  }
+  return 0;
+}
+
+int launch_general_values(const GenMats& g, const CodebookDev& cb, int bits, int d, const AppendShape& s,
+                          void* value_blocks, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t sub = gen_sub_tokens(g, s.n_seq);
+  // launch boundaries at absolute multiples of sub (a multiple of 128): no
+  // value block is touched by two launches
+  int64_t off = 0;
+  while (off < s.n_new) {
+    const int64_t p = s.pos + off;
+    const int64_t end_abs = (p / sub + 1) * sub;
+    int64_t n_sub = end_abs - p;
+    if (n_sub > s.n_new - off) n_sub = s.n_new - off;
+    const GenArgs a = gen_args(g, cb, bits, s, d, 64, off, n_sub, value_blocks);
+    const int64_t rows = n_sub * s.n_seq;
+    hipLaunchKernelGGL(gen_row_norms, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, s.dtype);
+    const int64_t nblk = (p + n_sub - 1) / kBlockTokens - p / kBlockTokens + 1;
+    const dim3 g1((unsigned)(nblk * s.n_seq), (unsigned)(d / 128));
+    const bool f32 = s.dtype == TQ_F32;
+#define TQ_GV(B)                                                                   \
+  if (bits == B) {                                                                 \
+    if (f32) hipLaunchKernelGGL((gen_values<B, true>), g1, dim3(256), 0, st, a);  \
+    else hipLaunchKernelGGL((gen_values<B, false>), g1, dim3(256), 0, st, a);     \
+  }
+    TQ_GV(1) TQ_GV(2) TQ_GV(3) TQ_GV(4)
+#undef TQ_GV
+    if (hipGetLastError() != hipSuccess) return TQ_EDEVICE;
+    off += n_sub;
+  }
+  return 0;
+}
+
+static int head_groups_bucket(int G) {
+  const int HG = (G + 15) / 16;
+  int b = 1;
+  while (b < HG) b *= 2;
+  return b;
+}
+
+size_t general_scores_workspace(int d, int m, int n_seq, int G) {
+  const int HG = head_groups_bucket(G);
+  const size_t q_bytes = (size_t)n_seq * HG * (d / 32 + m / 32) * 64 * 8 * 2;
+  const size_t qn_bytes = (size_t)n_seq * HG * 16 * 4;
+  return ((q_bytes + 255) / 256 + (qn_bytes + 255) / 256) * 256;
+}
+
+int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, int m,
+                          const AttnShape& s, const void* key_records, float* scores, void* ws, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int HG = head_groups_bucket(s.G);
+  if (HG > 32) return TQ_EUNSUPPORTED;
+  GenPrepArgs p;
+  p.q = s.q;
+  p.dtype = s.dtype;
+  p.G = s.G;
+  p.HG = HG;
+  p.n_seq = s.n_seq;
+  p.d = d;
+  p.m = m;
+  p.n_oct = d / 128;
+  p.r32 = mats.r32;
+  p.s32 = mats.s32;
+  const size_t q_bytes = (size_t)s.n_seq * HG * (d / 32 + m / 32) * 64 * 8 * 2;
+  p.wq = (uint16_t*)ws;
+  p.wqn = (float*)((char*)ws + (q_bytes + 255) / 256 * 256);
+  const size_t lds = sizeof(float) * (2 * d + m);
+  hipLaunchKernelGGL(gen_prep_queries, dim3((unsigned)(s.n_seq * 16 * HG)), dim3(256), lds, st, p);
+  GenScoreArgs a;
+  a.rec = (const uint32_t*)key_records;
+  a.scores = scores;
+  a.wq = p.wq;
+  a.wqn = p.wqn;
+  a.n_tokens = s.n_tokens;
+  a.capacity = s.capacity;
+  a.n_seq = s.n_seq;
+  a.G = s.G;
+  a.HG = HG;
+  a.d = d;
+  a.m = m;
+  a.n_oct = d / 128;
+  a.rec_words = kbits * d / 32 + m / 32 + 2;
+  a.tiles_per_slot = (s.n_tokens + 15) / 16;
+  a.kappa = (float)(1.2533141373155002512 / m);  // sqrt(pi/2) / m
+  for (int i = 0; i < 4; ++i) { a.tlo[i] = cbk.tlo[i]; a.thi[i] = cbk.thi[i]; }
+  const int64_t waves = a.tiles_per_slot * s.n_seq;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+#define TQ_GS(B, H) \
+  if (kbits == B && HG == H) hipLaunchKernelGGL((gen_scores<B, H>), grid, block, 0, st, a);
+#define TQ_GSB(B) TQ_GS(B, 1) TQ_GS(B, 2) TQ_GS(B, 4) TQ_GS(B, 8) TQ_GS(B, 16) TQ_GS(B, 32)
+  TQ_GSB(1) TQ_GSB(2) TQ_GSB(3) TQ_GSB(4)
+#undef TQ_GSB
+#undef TQ_GS
+  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+}
+
+}  // namespace tq

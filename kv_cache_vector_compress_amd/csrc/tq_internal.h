@@ -81,4 +81,24 @@ int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const
                   float* out, void* ws, const AttnPlan& p, void* stream);
 int compress_device_init();
 
+// General-shape path (tq_general.hip): head_dim a multiple of 128 up to 1024,
+// proj_dim a multiple of 64 up to 512.
+constexpr int kMaxGeneralHeads = 512;   // query heads per KV slot for general scores
+struct GenMats {
+  Matrices mats;         // R / S images (row stride ld halves) and fp32 copies
+  int ld;                // d + 8
+  float* nrm;            // scratch: [scratch_rows] row norms
+  uint16_t* res_hi;      // scratch: [scratch_rows][d] key residual, fp16 high part
+  uint16_t* res_lo;      //          and low part
+  float* g2p;            // scratch: [scratch_rows][d/128] residual square sums
+  int64_t scratch_rows;
+};
+int launch_general_keys(const GenMats& g, const CodebookDev& cb, int bits, int d, int m, const AppendShape& s,
+                        void* key_records, void* stream);
+int launch_general_values(const GenMats& g, const CodebookDev& cb, int bits, int d, const AppendShape& s,
+                          void* value_blocks, void* stream);
+size_t general_scores_workspace(int d, int m, int n_seq, int G);
+int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, int m,
+                          const AttnShape& s, const void* key_records, float* scores, void* ws, void* stream);
+
 }  // namespace tq

@@ -63,8 +63,25 @@ def test_sizes_follow_record_layout(kb, vb, m):
     assert tq.cache_value_bytes(cfg, 3, 256) == 3 * 2 * tq.value_block_bytes(cfg)
     assert tq.cache_key_bytes(cfg, 3, 100) == 0       # capacity not a multiple of 128
     assert tq.workspace_bytes(cfg, 4, 4, 1000) > 0
-    assert tq.workspace_bytes(cfg, 4, 17, 1000) == 0  # G out of range
+    assert tq.workspace_bytes(cfg, 4, 17, 1000) > 0   # scores only (general kernel)
+    assert tq.workspace_bytes(cfg, 4, 513, 1000) == 0  # G out of range
     assert tq.workspace_bytes(cfg, 4, 4, 0) == 0
+
+
+@pytest.mark.parametrize("d,m,kb,vb", [(256, 128, 3, 3), (1024, 512, 4, 4), (128, 256, 2, 2), (512, 64, 1, 4)])
+def test_general_shape_sizes_follow_record_layout(d, m, kb, vb):
+    """head_dim a multiple of 128 up to 1024, proj_dim a multiple of 64 up to
+    512: the same record layout, sized from the oracle's word counts."""
+    cfg = tq.Config(d, m, kb, vb)
+    assert tq.key_record_bytes(cfg) == 4 * O.key_record_words(d, m, kb)
+    assert tq.value_block_bytes(cfg) == 4 * O.value_block_words(d, vb)
+    assert tq.workspace_bytes(cfg, 2, 512, 4096) > 0
+    assert tq.workspace_bytes(cfg, 2, 513, 4096) == 0
+
+
+def test_vector_search_record_is_584_bytes():
+    # 4-bit codes of 1024 coordinates (512 B), 512 sign bits (64 B), two fp32 norms
+    assert tq.key_record_bytes(tq.Config(1024, 512, 4, 4)) == 584
 
 
 def test_3bit_record_is_64_bytes_and_block_is_52_bytes_per_token():
@@ -75,7 +92,8 @@ def test_3bit_record_is_64_bytes_and_block_is_52_bytes_per_token():
 
 @pytest.mark.parametrize("cfg,code", [
     ((100, 64, 3, 3), -1), ((128, 48, 3, 3), -1), ((128, 64, 0, 3), -1), ((128, 64, 3, 5), -1),
-    ((2048, 64, 3, 3), -1), ((256, 64, 3, 3), -6), ((128, 192, 3, 3), -6)])
+    ((2048, 64, 3, 3), -1), ((1152, 64, 3, 3), -1), ((192, 64, 3, 3), -1), ((128, 576, 3, 3), -1),
+    ((128, 96, 3, 3), -1)])
 def test_create_rejects_configs_before_any_device_call(cfg, code):
     R = np.eye(cfg[0])
     S = np.ones((max(cfg[1], 1), cfg[0]))

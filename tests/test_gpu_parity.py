@@ -54,7 +54,7 @@ def run_case(K, V, Q, kb=3, vb=3, m=64, capacity=None, chunks=None, n_tokens=Non
     ref_v = O.compress_values(V, R, vbeta, vc)
     gk = P.unpack_gpu_keys(cache, d, m, kb, T)
     gv = P.unpack_gpu_values(cache, d, vb, T)
-    st = P.check_keys(gk, ref_k, kbeta)
+    st = P.check_keys(gk, ref_k, kbeta, S, kc)
     flip_tok = st.pop("flip_tokens")
     st.update({"v_" + k: v for k, v in P.check_values(gv, ref_v, vbeta).items()})
 
@@ -203,7 +203,7 @@ def test_long_context_full_size_sampled():
         gk = O.unpack_keys(kw_all[slot:slot + 1, toks], d, m, 3)
         gv_all = O.unpack_values(vw_all[slot:slot + 1], d, 3, n_tokens=T)
         gv = {k: v[:, toks] for k, v in gv_all.items()}
-        st = P.check_keys(gk, ref_k, beta)
+        st = P.check_keys(gk, ref_k, beta, S, c)
         flips = st.pop("flip_tokens")
         st.update({"v_" + k: v for k, v in P.check_values(gv, ref_v, beta).items()})
         qn = np.linalg.norm(Q[slot:slot + 1].astype(np.float64), axis=-1)
@@ -217,6 +217,65 @@ def test_long_context_full_size_sampled():
     ref_v = O.compress_values(V[slot:slot + 1], R, beta, c)
     ref_out = O.attend(Q[slot:slot + 1], R, S, c, ref_k, ref_v, value_centroids=c)
     _say("long context attend slot", slot, P.check_attend(out[slot:slot + 1], ref_out))
+    ctx.close()
+
+
+# ---------------------------------------------------------------------------
+# general shapes: head_dim a multiple of 128 up to 1024, proj_dim a multiple
+# of 64 up to 512 (tiled rotation / projection kernels)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,m,kb,vb,dtype,G", [
+    (256, 128, 3, 3, np.float16, 4),
+    (128, 256, 2, 4, np.float16, 8),
+    (512, 192, 1, 2, np.float32, 3),
+    (384, 64, 4, 3, np.float16, 40),
+    (1024, 512, 4, 4, np.float32, 16),
+])
+def test_general_shapes_ragged_chunks(d, m, kb, vb, dtype, G):
+    """Codes, signs, norms, gamma of keys and values, and scores, on the
+    general path; appended in unaligned chunks (partial value blocks)."""
+    n_seq, T = 2, 700
+    K = np.stack([synth.kv_slot(60 + d, s, s, T, d, dtype=dtype) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(61 + d, s, s, T, d, dtype=dtype) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(62 + d, s, s, G, d, dtype=dtype) for s in range(n_seq)])
+    _say("general", (d, m, kb, vb, dtype.__name__, G))
+    _say(run_case(K, V, Q, kb=kb, vb=vb, m=m, chunks=[130, 1, 300, 269], check_attend=False))
+
+
+def test_vector_search_shape():
+    """The vector-search configuration's shape at a reduced count: unit-norm
+    fp32 database rows (Gaussian plus cluster mixture) at d = 1024, 4-bit keys
+    with proj_dim 512, scored against 64 and against 512 queries."""
+    d, m, b = 1024, 512, 4
+    N = 3000
+    X = synth.vector_database(N, d, seed=5)[None]
+    Qd = synth.vector_database(512, d, seed=6)[None]
+    ctx, R, S = make_ctx(d, m, b, b)
+    cache = tq.KVCache(ctx, 1, -(-N // 128) * 128)
+    cache.append_key(torch.from_numpy(X).cuda(), 0)
+    beta, c = O.lloyd_max_codebook(d, b)
+    ref = O.compress_keys(X, R, S, beta, c)
+    gk = P.unpack_gpu_keys(cache, d, m, b, N)
+    st = P.check_keys(gk, ref, beta, S, c)
+    flips = st.pop("flip_tokens")
+    kn = np.linalg.norm(X.astype(np.float64), axis=-1)
+    for G in (64, 512):
+        Q = Qd[:, :G]
+        sc = cache.attention_scores(torch.from_numpy(np.ascontiguousarray(Q)).cuda(), N).cpu().numpy()
+        qn = np.linalg.norm(Q.astype(np.float64), axis=-1)
+        st[f"score_G{G}"] = P.check_scores(sc, O.key_scores(Q, R, S, c, ref), qn, kn, skip_tokens=flips)
+    _say("vector search shape", st)
+    ctx.close()
+
+
+def test_attend_reports_unsupported_off_the_fast_shape():
+    ctx, R, S = make_ctx(256, 64, 3, 3)
+    cache = tq.KVCache(ctx, 1, 128)
+    q = torch.zeros((1, 4, 256), dtype=torch.float16, device="cuda")
+    with pytest.raises(tq.TQError) as e:
+        cache.attend(q, 16)
+    assert e.value.code == -6
     ctx.close()
 
 
@@ -245,7 +304,9 @@ def test_error_paths_leave_buffers_untouched():
     expect(-1, lambda: cache.attention_scores(q, 0))                # n_tokens
     expect(-1, lambda: cache.attention_scores(q, 257))              # n_tokens > capacity
     q17 = torch.zeros((2, 17, 128), dtype=torch.float16, device="cuda")
-    expect(-1, lambda: cache.attention_scores(q17, 10))             # G
+    expect(-1, lambda: cache.attend(q17, 10))                       # G above 16 (attend)
+    q513 = torch.zeros((2, 513, 128), dtype=torch.float16, device="cuda")
+    expect(-1, lambda: cache.attention_scores(q513, 10))            # G above 512 (scores)
     ws = cache.workspace(4, 10)
     out = torch.empty((2, 4, 10), dtype=torch.float32, device="cuda")
     expect(-7, lambda: tq._check(tq.lib().tq_attention_scores(
