@@ -58,16 +58,32 @@ __device__ __forceinline__ int64_t gen_in_row(const GenArgs& a, int64_t r) {
   return slot * a.n_new + a.tok_off + (r - slot * a.n_sub);
 }
 
-// Stage rows [row0, row0 + nrows) x columns [k0, k0 + 32) of an fp16 image
-// pair (hi, lo; row stride ld halves) into LDS (row stride kSliceLS).
-__device__ __forceinline__ void stage_slice(uint16_t* lds_hi, uint16_t* lds_lo, const uint16_t* hi,
-                                            const uint16_t* lo, int ld, int row0, int nrows, int k0) {
-  for (int i = threadIdx.x; i < 2 * nrows * 4; i += blockDim.x) {
-    const int img = i / (nrows * 4), rr = (i / 4) % nrows, cc = (i % 4) * 8;
-    const uint16_t* src = (img ? lo : hi) + (size_t)(row0 + rr) * ld + k0 + cc;
-    *(u4*)((img ? lds_lo : lds_hi) + rr * kSliceLS + cc) = *(const u4*)src;
+// A slice of an fp16 image pair (hi, lo; row stride ld halves): rows
+// [row0, row0 + NR) x columns [k0, k0 + 32), 2 NR 16-byte pieces, fetched
+// into registers by a 256-thread workgroup (NR / 32 pieces a thread) and then
+// stored into LDS (row stride kSliceLS).  The fetch of the next slice is
+// issued before the current one is multiplied, so its latency is hidden.
+template <int NR>
+struct Slice {
+  static constexpr int kPer = 2 * NR * 4 / 256;
+  u4 v[kPer];
+  __device__ __forceinline__ void fetch(const uint16_t* hi, const uint16_t* lo, int ld, int row0, int k0) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      const int img = i / (NR * 4), rr = (i / 4) % NR, cc = (i % 4) * 8;
+      v[j] = *(const u4*)((img ? lo : hi) + (size_t)(row0 + rr) * ld + k0 + cc);
+    }
   }
-}
+  __device__ __forceinline__ void store(uint16_t* lds) const {  // lds: [2][NR * kSliceLS]
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      const int img = i / (NR * 4), rr = (i / 4) % NR, cc = (i % 4) * 8;
+      *(u4*)(lds + img * NR * kSliceLS + rr * kSliceLS + cc) = v[j];
+    }
+  }
+};
 
 // 8 inputs of a row as an MFMA operand: fp16 rows as they are; fp32 rows
 // scaled by sc (|x sc| < 2^13) and split into fp16 hi + lo.
@@ -89,6 +105,24 @@ __device__ __forceinline__ void load_x8(const void* x, int64_t row, int d, int k
     xl = as_h8(lo);
   } else {
     xh = *(const h8*)((const _Float16*)x + row * d + k);
+  }
+}
+
+// Workgroup -> (row tile, chunk) for a 1-D grid of ntiles x nchunk
+// workgroups.  Consecutive workgroups go to the 8 XCDs in turn, each with its
+// own L2; this order sends all chunks of a row tile to the same XCD, close
+// together in time, so the tile's rows come from HBM once and then from that
+// L2.
+__device__ __forceinline__ void xcd_tile_chunk(int64_t b, int64_t ntiles, int nchunk, int64_t& tile, int& chunk) {
+  const int64_t full = ntiles / 8 * 8;      // row tiles in complete groups of 8
+  if (b < full * nchunk) {
+    const int64_t grp = b / (8 * nchunk), rem = b % (8 * nchunk);
+    chunk = (int)(rem / 8);
+    tile = grp * 8 + rem % 8;
+  } else {
+    const int64_t r = b - full * nchunk, tail = ntiles - full;
+    chunk = (int)(r / tail);
+    tile = full + r % tail;
   }
 }
 
@@ -135,19 +169,21 @@ __global__ __launch_bounds__(256) void gen_row_norms(const GenArgs a, int dtype)
 template <int B, bool F32>
 __global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
   constexpr int H = 1 << (B - 1);
-  __shared__ __align__(16) uint16_t Rs[2][128 * kSliceLS];
+  __shared__ __align__(16) uint16_t Rs[2][2 * 128 * kSliceLS];  // [buffer][hi, lo][128 rows]
   __shared__ float ctab[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q = lane >> 4;
-  const int u = blockIdx.y;  // coordinate chunk
   const int64_t rows = (int64_t)a.n_seq * a.n_sub;
+  int64_t rtile;
+  int u;  // coordinate chunk
+  xcd_tile_chunk(blockIdx.x, (rows + 127) / 128, a.n_oct, rtile, u);
   if (tid < 16) ctab[tid] = a.cb.cent[tid] * kResScale;
 
   int64_t row[2], in_row[2];
   float n[2], sc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    row[j] = (int64_t)blockIdx.x * 128 + wave * 32 + 16 * j + r16;
+    row[j] = rtile * 128 + wave * 32 + 16 * j + r16;
     const int64_t rr = row[j] < rows ? row[j] : rows - 1;  // rows past the end: any valid row, not stored
     in_row[j] = gen_in_row(a, rr);
     n[j] = a.nrm[rr];
@@ -159,17 +195,27 @@ __global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc[j][s] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < a.d; k0 += 32) {
-    __syncthreads();
-    stage_slice(Rs[0], Rs[1], a.r_hi, a.r_lo, a.ld, 128 * u, 128, k0);
-    __syncthreads();
-    h8 xh[2], xl[2];
+  Slice<128> sl;
+  sl.fetch(a.r_hi, a.r_lo, a.ld, 128 * u, 0);
+  h8 xh[2], xl[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) load_x8<F32>(a.x, in_row[j], a.d, k0 + 8 * q, sc[j], xh[j], xl[j]);
+  for (int j = 0; j < 2; ++j) load_x8<F32>(a.x, in_row[j], a.d, 8 * q, sc[j], xh[j], xl[j]);
+  sl.store(Rs[0]);
+  __syncthreads();
+  for (int k0 = 0, buf = 0; k0 < a.d; k0 += 32, buf ^= 1) {
+    const bool more = k0 + 32 < a.d;
+    h8 nh[2], nl[2];
+    if (more) {
+      sl.fetch(a.r_hi, a.r_lo, a.ld, 128 * u, k0 + 32);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) load_x8<F32>(a.x, in_row[j], a.d, k0 + 32 + 8 * q, sc[j], nh[j], nl[j]);
+    }
+    const uint16_t* Rh = Rs[buf];
+    const uint16_t* Rl = Rs[buf] + 128 * kSliceLS;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const h8 ah = *(const h8*)(Rs[0] + (16 * s + r16) * kSliceLS + 8 * q);
-      const h8 al = *(const h8*)(Rs[1] + (16 * s + r16) * kSliceLS + 8 * q);
+      const h8 ah = *(const h8*)(Rh + (16 * s + r16) * kSliceLS + 8 * q);
+      const h8 al = *(const h8*)(Rl + (16 * s + r16) * kSliceLS + 8 * q);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         acc[j][s] = mfma(ah, xh[j], acc[j][s]);
@@ -177,6 +223,15 @@ __global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
         if constexpr (F32) acc[j][s] = mfma(ah, xl[j], acc[j][s]);
       }
     }
+    if (more) {
+      sl.store(Rs[buf ^ 1]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        xh[j] = nh[j];
+        xl[j] = nl[j];
+      }
+    }
+    __syncthreads();
   }
 
   float bpos[8];
@@ -232,30 +287,49 @@ __global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void gen_keys_project(const GenArgs a, int bits) {
-  __shared__ __align__(16) uint16_t Ss[2][64 * kSliceLS];
+  __shared__ __align__(16) uint16_t Ss[2][2 * 64 * kSliceLS];  // [buffer][hi, lo][64 rows]
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q = lane >> 4;
-  const int u = blockIdx.y;  // 64-projection chunk
   const int64_t rows = (int64_t)a.n_seq * a.n_sub;
-  const int64_t row = (int64_t)blockIdx.x * 64 + wave * 16 + r16;
+  int64_t rtile;
+  int u;  // 64-projection chunk
+  xcd_tile_chunk(blockIdx.x, (rows + 63) / 64, a.m / 64, rtile, u);
+  const int64_t row = rtile * 64 + wave * 16 + r16;
   const int64_t rr = row < rows ? row : rows - 1;
   f4 z[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) z[p] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.d; k0 += 32) {
-    __syncthreads();
-    stage_slice(Ss[0], Ss[1], a.s_hi, a.s_lo, a.ld, 64 * u, 64, k0);
-    __syncthreads();
-    const h8 rh = *(const h8*)(a.res_hi + (size_t)rr * a.d + k0 + 8 * q);
-    const h8 rl = *(const h8*)(a.res_lo + (size_t)rr * a.d + k0 + 8 * q);
+  const uint16_t* rhp = a.res_hi + (size_t)rr * a.d + 8 * q;
+  const uint16_t* rlp = a.res_lo + (size_t)rr * a.d + 8 * q;
+  Slice<64> sv;
+  sv.fetch(a.s_hi, a.s_lo, a.ld, 64 * u, 0);
+  h8 rh = *(const h8*)rhp, rl = *(const h8*)rlp;
+  sv.store(Ss[0]);
+  __syncthreads();
+  for (int k0 = 0, buf = 0; k0 < a.d; k0 += 32, buf ^= 1) {
+    const bool more = k0 + 32 < a.d;
+    h8 nh, nl;
+    if (more) {
+      sv.fetch(a.s_hi, a.s_lo, a.ld, 64 * u, k0 + 32);
+      nh = *(const h8*)(rhp + k0 + 32);
+      nl = *(const h8*)(rlp + k0 + 32);
+    }
+    const uint16_t* Sh = Ss[buf];
+    const uint16_t* Sl = Ss[buf] + 64 * kSliceLS;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const h8 sh = *(const h8*)(Ss[0] + (16 * p + r16) * kSliceLS + 8 * q);
-      const h8 sl = *(const h8*)(Ss[1] + (16 * p + r16) * kSliceLS + 8 * q);
+      const h8 sh = *(const h8*)(Sh + (16 * p + r16) * kSliceLS + 8 * q);
+      const h8 sl = *(const h8*)(Sl + (16 * p + r16) * kSliceLS + 8 * q);
       z[p] = mfma(sh, rh, z[p]);
       z[p] = mfma(sl, rh, z[p]);
       z[p] = mfma(sh, rl, z[p]);
     }
+    if (more) {
+      sv.store(Ss[buf ^ 1]);
+      rh = nh;
+      rl = nl;
+    }
+    __syncthreads();
   }
   const uint32_t bits16 = sign_bits16(z[0], z[1], z[2], z[3]);
   if (row < rows) {
@@ -280,15 +354,17 @@ __global__ __launch_bounds__(256) void gen_keys_project(const GenArgs a, int bit
 
 template <int B, bool F32>
 __global__ __launch_bounds__(256) void gen_values(const GenArgs a) {
-  __shared__ __align__(16) uint16_t Rs[2][128 * kSliceLS];
+  __shared__ __align__(16) uint16_t Rs[2][2 * 128 * kSliceLS];  // [buffer][hi, lo][128 rows]
   __shared__ float inv_sh[kBlockTokens];  // 1 / sigma per block token (0: not in this launch or zero row)
   __shared__ float nrm_sh[kBlockTokens];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q = lane >> 4;
-  const int u = blockIdx.y;
   const int64_t P0 = a.pos + a.tok_off, P1 = P0 + a.n_sub;  // token positions of this launch
   const int64_t blk0 = P0 / kBlockTokens, nblk = (P1 - 1) / kBlockTokens - blk0 + 1;
-  const int64_t slot = blockIdx.x / nblk, blk = blk0 + (blockIdx.x - slot * nblk);
+  int64_t item;
+  int u;
+  xcd_tile_chunk(blockIdx.x, nblk * a.n_seq, a.n_oct, item, u);
+  const int64_t slot = item / nblk, blk = blk0 + (item - slot * nblk);
   const int64_t tok0 = blk * kBlockTokens;
   if (tid < kBlockTokens) {
     const int64_t p = tok0 + tid;
@@ -312,15 +388,20 @@ __global__ __launch_bounds__(256) void gen_values(const GenArgs a) {
   f4 acc[8][2];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt][0] = acc[mt][1] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.d; k0 += 32) {
-    __syncthreads();
-    stage_slice(Rs[0], Rs[1], a.r_hi, a.r_lo, a.ld, 128 * u, 128, k0);
-    __syncthreads();
+  Slice<128> sl;
+  sl.fetch(a.r_hi, a.r_lo, a.ld, 128 * u, 0);
+  sl.store(Rs[0]);
+  __syncthreads();
+  for (int k0 = 0, buf = 0; k0 < a.d; k0 += 32, buf ^= 1) {
+    const bool more = k0 + 32 < a.d;
+    if (more) sl.fetch(a.r_hi, a.r_lo, a.ld, 128 * u, k0 + 32);
+    const uint16_t* Rh = Rs[buf];
+    const uint16_t* Rl = Rs[buf] + 128 * kSliceLS;
     h8 bh[2], bl[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      bh[t] = *(const h8*)(Rs[0] + (16 * (2 * wave + t) + r16) * kSliceLS + 8 * q);
-      bl[t] = *(const h8*)(Rs[1] + (16 * (2 * wave + t) + r16) * kSliceLS + 8 * q);
+      bh[t] = *(const h8*)(Rh + (16 * (2 * wave + t) + r16) * kSliceLS + 8 * q);
+      bl[t] = *(const h8*)(Rl + (16 * (2 * wave + t) + r16) * kSliceLS + 8 * q);
     }
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
@@ -333,6 +414,8 @@ __global__ __launch_bounds__(256) void gen_values(const GenArgs a) {
         if constexpr (F32) acc[mt][t] = mfma(xl, bh[t], acc[mt][t]);
       }
     }
+    if (more) sl.store(Rs[buf ^ 1]);
+    __syncthreads();
   }
 
   float bpos[8];
@@ -611,8 +694,7 @@ int launch_general_keys(const GenMats& g, const CodebookDev& cb, int bits, int d
     const GenArgs a = gen_args(g, cb, bits, s, d, m, off, n_sub, key_records);
     const int64_t rows = n_sub * s.n_seq;
     hipLaunchKernelGGL(gen_row_norms, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, s.dtype);
-    const dim3 g1((unsigned)((rows + 127) / 128), (unsigned)(d / 128)), g2((unsigned)((rows + 63) / 64),
-                                                                             (unsigned)(m / 64));
+    const dim3 g1((unsigned)((rows + 127) / 128 * (d / 128))), g2((unsigned)((rows + 63) / 64 * (m / 64)));
     const bool f32 = s.dtype == TQ_F32;
 #define TQ_GK(B)                                                                              \
   if (bits == B) {                                                                            \
@@ -643,7 +725,7 @@ int launch_general_values(const GenMats& g, const CodebookDev& cb, int bits, int
     const int64_t rows = n_sub * s.n_seq;
     hipLaunchKernelGGL(gen_row_norms, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, s.dtype);
     const int64_t nblk = (p + n_sub - 1) / kBlockTokens - p / kBlockTokens + 1;
-    const dim3 g1((unsigned)(nblk * s.n_seq), (unsigned)(d / 128));
+    const dim3 g1((unsigned)(nblk * s.n_seq * (d / 128)));
     const bool f32 = s.dtype == TQ_F32;
 #define TQ_GV(B)                                                                   \
   if (bits == B) {                                                                 \
