@@ -26,13 +26,25 @@
  *    tq_last_error() then holds a message (thread-local).
  *  - "device" pointers are HIP device memory owned by the caller.  The
  *    library allocates device memory only in tq_create (its own copies of R,
- *    S and the codebooks, a few hundred KB) and frees it in tq_destroy.
+ *    S and the codebooks: d^2 + m d fp32 plus the same again as fp16 halves;
+ *    for shapes on the general path, see below, also a scratch buffer of
+ *    32768 rows x (4 d + 4 + d/32) bytes, 128 MB at d = 1024) and frees it
+ *    in tq_destroy.
  *  - Calls that take a stream enqueue work on it and return at once; they
  *    are ordered with other work on that stream.  stream == NULL means the
  *    default stream.  The argument is a hipStream_t passed as void*.
  *  - A context is read-only after its codebooks are loaded, so calls on
  *    different streams may run concurrently; tq_codebook_load must not run
- *    concurrently with calls that use the same context.
+ *    concurrently with calls that use the same context.  Exception: on the
+ *    general path the appends of one context share its scratch buffer, so
+ *    its tq_append_key / tq_append_value calls must be ordered (one stream,
+ *    or one context per stream).
+ *  - Shapes.  head_dim 128 with proj_dim 64 or 128 runs single-kernel
+ *    compress and attention paths; every other valid shape (head_dim a
+ *    multiple of 128 up to 1024, proj_dim a multiple of 64 up to 512) runs
+ *    the general path: tiled rotation / projection kernels for the appends
+ *    and a chunked score kernel.  tq_attend is built for the first group of
+ *    shapes only.
  *  - Device pointers must be 16-byte aligned.
  */
 #ifndef TQ_H
@@ -54,7 +66,7 @@ typedef enum {
   TQ_ENOCODEBOOK = -3,  /* no codebook loaded for the bits this call needs */
   TQ_ENOMEM = -4,       /* device allocation failed (tq_create only) */
   TQ_EDEVICE = -5,      /* a HIP call or kernel launch failed */
-  TQ_EUNSUPPORTED = -6, /* valid but not built: e.g. head_dim other than 128 */
+  TQ_EUNSUPPORTED = -6, /* valid but not built: tq_attend off head_dim 128 / proj_dim 64, 128 */
   TQ_EWORKSPACE = -7    /* workspace smaller than tq_workspace_bytes */
 } tq_status;
 
@@ -63,8 +75,7 @@ typedef enum { TQ_F16 = 1, TQ_F32 = 2 } tq_dtype;
 typedef struct tq_ctx tq_ctx;
 
 /* Static shape of a compressed cache.  head_dim d: multiple of 128 up to
- * 1024; the built kernels cover d = 128 (others give TQ_EUNSUPPORTED).
- * proj_dim m: multiple of 64 up to 512; built: 64 and 128 (default d/2,
+ * 1024.  proj_dim m: multiple of 64 up to 512 (default d/2,
  * nav.superapi.store 算法细节 / proj_dim 选择).  key_bits, value_bits in
  * 1..4 (the pages use 2-4; 1 is the 1-bit limit). */
 typedef struct {
@@ -86,15 +97,16 @@ typedef struct {
  * Zero-fill both buffers before first use if tokens will be read before
  * they are written.
  *
- * Record layout v1 (32-bit little-endian words; b = bits, d = 128):
+ * Record layout v1 (32-bit little-endian words; b = bits, d = head_dim):
  *  Code groups.  b consecutive words hold 32 b-bit codes as 8 slots s x 4
  *  byte lanes i; byte lane i of every word belongs to code (s, i):
  *    b=1: bit s;  b=2: word s/4, bits 2(s%4)..;  b=4: word s/2, bits 4(s%2)..;
  *    b=3: s<6: word s/2, bits 3(s%2)..; s=6: code bits 0-1 at bits 6-7 of
  *         word 0, bit 2 at bit 6 of word 2; s=7: bits 0-1 at bits 6-7 of
  *         word 1, bit 2 at bit 7 of word 2   (bit numbers within the byte).
- *  Key record: 4 code groups q = 0..3 (words b q .. b q + b - 1); group q,
- *    slot s, byte lane i is the code of rotated coordinate 16 s + 4 q + i.
+ *  Key record: 4 d/128 code groups (q, g), q = 0..3, g = 0..d/128 - 1, at
+ *    words b (q d/128 + g) .. + b - 1; group (q, g), slot s, byte lane i is
+ *    the code of rotated coordinate 128 g + 16 s + 4 q + i.
  *    Then m/32 sign words: projection coordinate 16 t + 4 q + i is bit
  *    16 (q%2) + 4 (t%4) + i of word 2 (t/4) + q/2 (1 = projection >= 0).
  *    Then fp32 ||k||, then fp32 gamma.  Size 4 (b d/32 + m/32 + 2) bytes.
@@ -134,7 +146,7 @@ size_t tq_cache_value_bytes(const tq_config* cfg, int32_t n_seq, int64_t capacit
 
 /* Device workspace bytes needed by tq_attention_scores and tq_attend for
  * this shape (query operands, query norms, per-wave attention partials).
- * 0 on invalid arguments (cfg NULL/invalid, n_seq < 1, G not in 1..16,
+ * 0 on invalid arguments (cfg NULL/invalid, n_seq < 1, G not in 1..512,
  * n_tokens < 1). */
 size_t tq_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, int64_t n_tokens);
 
@@ -147,9 +159,8 @@ const char* tq_last_error(void);
  * (rotation y = R x), S: host, m x d row-major (QJL matrix, applied to the
  * rotated residual).  Both are copied before return.  R should be orthogonal
  * (nav.superapi.store 算法细节 / 随机旋转); this is not checked.  Returns
- * TQ_EINVAL (bad config or null pointers), TQ_EUNSUPPORTED (a valid shape
- * that is not built), TQ_ENOMEM or TQ_EDEVICE.  Arguments are checked before
- * any HIP call. */
+ * TQ_EINVAL (bad config or null pointers), TQ_ENOMEM or TQ_EDEVICE.
+ * Arguments are checked before any HIP call. */
 int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** out);
 
 /* Free the context's device memory.  NULL is accepted.  Work still queued
@@ -189,7 +200,8 @@ int tq_append_value(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int3
  * 常见使用模式 and 核心 API): scores[s][h][t] = est(q[s][h], k[s][t]),
  * unscaled, for t < n_tokens.
  * q: device [n_seq][G][d] (query head h of slot s uses KV slot s; GQA groups
- * of G contiguous heads), dtype TQ_F16 or TQ_F32.  1 <= G <= 16.
+ * of G contiguous heads), dtype TQ_F16 or TQ_F32.  1 <= G <= 512 (a
+ * vector-search batch of queries against one slot is G queries, n_seq = 1).
  * scores: device fp32 [n_seq][G][n_tokens].
  * workspace: device, >= tq_workspace_bytes(ctx, n_seq, G, n_tokens).
  * Errors: TQ_EINVAL (n_tokens <= 0 or > capacity, G out of range, ...),
@@ -203,7 +215,9 @@ int tq_attention_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, 
  * back (nav.superapi.store 常见使用模式: scores from compressed keys,
  * softmax, weighted sum of the decompressed values).  scale <= 0 means
  * 1/sqrt(d).  No causal mask.  out: device fp32 [n_seq][G][d].
- * Same q/workspace rules and errors as tq_attention_scores. */
+ * Same q/workspace rules and errors as tq_attention_scores, with
+ * 1 <= G <= 16; TQ_EUNSUPPORTED unless head_dim is 128 and proj_dim is 64
+ * or 128. */
 int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
               int64_t n_tokens, float scale, float* out, void* workspace, size_t workspace_bytes,
               void* stream);
