@@ -116,6 +116,191 @@ def cpu_baseline(w, slots=16):
                       f"scores and attend, numpy fp64; {dt:.1f} s"}
 
 
+def _timed(torch, fn, reps):
+    """Average ms of fn() over reps calls, HIP events on the current stream."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _kv_device(torch, n_seq, T, d, seed, heads_cycle, dev):
+    """KV-like fp16 slots generated on the host (synth.kv_slot) and moved to the device."""
+    from kv_cache_vector_compress_amd import synth
+    with ThreadPoolExecutor(16) as ex:
+        X = np.stack(list(ex.map(lambda s: synth.kv_slot(seed, s, s % heads_cycle, T, d), range(n_seq))))
+    return torch.from_numpy(X).to(dev)
+
+
+def bench_qwen_decode(args):
+    """Qwen2.5-3B-shaped decode (36 layers x 2 KV heads x 8192 tokens, 16
+    query heads = GQA 8:1, 3-bit keys m=64 and values): (i) per-layer latency
+    of appending one token's K and V and attending over 8192 tokens; (ii) all
+    36 layers' scores and attend in one call each, cache-resident (warm) and
+    rotating over 8 cache copies (cold)."""
+    import torch
+    from kv_cache_vector_compress_amd import synth, tq
+    w = synth.QWEN_DECODE
+    d, m, T, G, n_seq = w.d, w.m, w.n_tok, w.G, w.n_seq
+    dev = torch.device("cuda:0")
+    R, S = synth.haar_rotation(d), synth.gaussian_projection(m, d)
+    ctx = tq.Context(d, m, 3, 3, R, S)
+    K = _kv_device(torch, n_seq, T, d, synth.SEED_K, n_seq, dev)
+    V = _kv_device(torch, n_seq, T, d, synth.SEED_V, n_seq, dev)
+    Q = torch.from_numpy(synth.workload_queries(w)).to(dev)
+    copies = 8
+    caches = [tq.KVCache(ctx, n_seq, T) for _ in range(copies)]
+    for c in caches:
+        c.append_key(K, 0)
+        c.append_value(V, 0)
+    sc = torch.empty((n_seq, G, T), dtype=torch.float32, device=dev)
+    out = torch.empty((n_seq, G, d), dtype=torch.float32, device=dev)
+    caches[0].workspace(G, T)
+    reps = max(args.steps, 20)
+    warm_s = _timed(torch, lambda: caches[0].attention_scores(Q, T, out=sc), reps)
+    warm_a = _timed(torch, lambda: caches[0].attend(Q, T, out=out), reps)
+    it = iter(range(10 ** 9))
+    cold_s = _timed(torch, lambda: caches[next(it) % copies].attention_scores(Q, T, out=sc), reps)
+    cold_a = _timed(torch, lambda: caches[next(it) % copies].attend(Q, T, out=out), reps)
+    # one layer: 2 KV slots, 8191 cached tokens, append token 8191 and attend over 8192
+    layer = tq.KVCache(ctx, 2, T)
+    layer.append_key(K[:2, :T - 1].contiguous(), 0)
+    layer.append_value(V[:2, :T - 1].contiguous(), 0)
+    k1, v1, q1 = K[:2, T - 1:].contiguous(), V[:2, T - 1:].contiguous(), Q[:2].contiguous()
+    o1 = torch.empty((2, G, d), dtype=torch.float32, device=dev)
+    layer.workspace(G, T)
+
+    def one_layer():
+        layer.append_key(k1, T - 1)
+        layer.append_value(v1, T - 1)
+        layer.attend(q1, T, out=o1)
+    lat = _timed(torch, one_layer, reps)
+    b_sc = n_seq * T * (tq.key_record_bytes(ctx.cfg) + 4 * G)
+    b_at = n_seq * T * (tq.key_record_bytes(ctx.cfg) + tq.value_block_bytes(ctx.cfg) / 128)
+    gb = lambda b, ms: round(b / (ms * 1e-3) / 1e9, 1)
+    line = {"metric": "per-layer decode latency (append 1 token K+V, attend 8192) and 36-layer score/attend HBM GB/s",
+            "value": round(lat * 1e3, 2), "unit": "us/layer", "higher_is_better": False, "n_gpus": 1,
+            "data": "synthetic", "dtype": "f16",
+            "config": {"workload": w.name, "n_seq": n_seq, "tokens_per_slot": T, "head_dim": d, "proj_dim": m,
+                       "key_bits": 3, "value_bits": 3, "query_heads_per_kv": G},
+            "all_layers": {"scores_warm": {"ms": round(warm_s, 4), "GBps": gb(b_sc, warm_s)},
+                           "attend_warm": {"ms": round(warm_a, 4), "GBps": gb(b_at, warm_a)},
+                           "scores_cold": {"ms": round(cold_s, 4), "GBps": gb(b_sc, cold_s)},
+                           "attend_cold": {"ms": round(cold_a, 4), "GBps": gb(b_at, cold_a)},
+                           "alg_bytes": {"scores": int(b_sc), "attend": int(b_at)},
+                           "cold_copies": copies, "hbm_peak_GBps": HBM_PEAK_GBPS}}
+    print(json.dumps(line))
+    ctx.close()
+
+
+def bench_bit_sweep(args):
+    """Bit-width sweep on the Qwen decode shape (72 slots x 8192 tokens): for
+    2-, 3- and 4-bit keys (m=64) and values, bulk compression rate, score
+    GB/s, and fidelity of the attention weights against exact fp16 attention
+    (cosine of the softmax rows and top-1 match, evaluated with torch on the
+    GPU), with the plain queries and with queries rescaled to a logit
+    standard deviation of 2 (a diagnostic: plain queries give nearly uniform
+    attention)."""
+    import torch
+    from kv_cache_vector_compress_amd import synth, tq
+    w = synth.QWEN_DECODE
+    d, m, T, G, n_seq = w.d, w.m, w.n_tok, w.G, w.n_seq
+    dev = torch.device("cuda:0")
+    R, S = synth.haar_rotation(d), synth.gaussian_projection(m, d)
+    K = _kv_device(torch, n_seq, T, d, synth.SEED_K, n_seq, dev)
+    V = _kv_device(torch, n_seq, T, d, synth.SEED_V, n_seq, dev)
+    Q = torch.from_numpy(synth.workload_queries(w)).to(dev)
+    exact = torch.matmul(Q.float(), K.float().transpose(1, 2).contiguous())   # (n_seq, G, T)
+    scale = 1.0 / d ** 0.5
+    rescale = 2.0 / float((exact * scale).std())
+    reps = max(args.steps, 10)
+    res = {}
+    for b in (2, 3, 4):
+        ctx = tq.Context(d, m, b, b, R, S)
+        cache = tq.KVCache(ctx, n_seq, T)
+        sc = torch.empty((n_seq, G, T), dtype=torch.float32, device=dev)
+        cache.workspace(G, T)
+        ck = _timed(torch, lambda: cache.append_key(K, 0), reps)
+        cv = _timed(torch, lambda: cache.append_value(V, 0), reps)
+        ts = _timed(torch, lambda: cache.attention_scores(Q, T, out=sc), reps)
+        fid = {}
+        for tag, f in (("plain", 1.0), ("logit_std_2", rescale)):
+            pe = torch.softmax(exact * (scale * f), dim=-1)
+            pq = torch.softmax(sc * (scale * f), dim=-1)
+            cos = torch.nn.functional.cosine_similarity(pe, pq, dim=-1)
+            top1 = (pe.argmax(-1) == pq.argmax(-1)).float().mean()
+            fid[tag] = {"cosine_mean": round(float(cos.mean()), 5), "cosine_min": round(float(cos.min()), 5),
+                        "top1": round(float(top1), 4)}
+        b_sc = n_seq * T * (tq.key_record_bytes(ctx.cfg) + 4 * G)
+        res[f"{b}bit"] = {"compress_keys_per_s": round(n_seq * T / (ck * 1e-3), 1),
+                          "compress_values_per_s": round(n_seq * T / (cv * 1e-3), 1),
+                          "scores_ms": round(ts, 4), "scores_GBps": round(b_sc / (ts * 1e-3) / 1e9, 1),
+                          "fidelity": fid}
+        ctx.close()
+    line = {"metric": "bit-width sweep: compress keys/s, score GB/s, attention cosine and top-1 vs fp16",
+            "value": res["3bit"]["compress_keys_per_s"], "unit": "keys/s (3-bit)", "higher_is_better": True,
+            "n_gpus": 1, "data": "synthetic", "dtype": "f16",
+            "config": {"workload": "bit_sweep_" + w.name, "n_seq": n_seq, "tokens_per_slot": T, "head_dim": d,
+                       "proj_dim": m, "query_heads_per_kv": G, "logit_rescale": round(rescale, 3)},
+            "sweep": res}
+    print(json.dumps(line))
+
+
+def bench_vector_search(args):
+    """Vector search: 2,000,000 unit-norm fp32 vectors at d = 1024 (half
+    isotropic Gaussian, half a 64-cluster mixture normalise(mu_c + 0.3 g /
+    sqrt(d)), generated on the device with a seeded torch generator), 4-bit
+    keys with proj_dim 512, 512 unit-norm queries: compress rate, score rate
+    for all 512 queries, and recall@10 of the estimated inner products
+    against brute-force fp32 (top-10 taken with torch.topk, evaluation only)."""
+    import torch
+    from kv_cache_vector_compress_amd import synth, tq
+    d, m, b, N, G = 1024, 512, 4, 2_000_000, 512
+    dev = torch.device("cuda:0")
+    R, S = synth.haar_rotation(d), synth.gaussian_projection(m, d)
+    ctx = tq.Context(d, m, b, b, R, S)
+    g = torch.Generator(device=dev).manual_seed(4)
+    cent = torch.randn((64, d), device=dev, generator=g)
+    cent /= cent.norm(dim=1, keepdim=True)
+    X = torch.randn((1, N, d), device=dev, generator=g)
+    odd = torch.arange(N, device=dev) % 2 == 1
+    cl = torch.randint(0, 64, (N,), device=dev, generator=g)
+    X[0, odd] = cent[cl[odd]] + 0.3 * X[0, odd] / d ** 0.5
+    X /= X.norm(dim=-1, keepdim=True)
+    Q = torch.randn((1, G, d), device=dev, generator=g)
+    Q /= Q.norm(dim=-1, keepdim=True)
+    cache = tq.KVCache(ctx, 1, -(-N // 128) * 128)
+    sc = torch.empty((1, G, N), dtype=torch.float32, device=dev)
+    cache.workspace(G, N)
+    reps = 3
+    cache.append_key(X, 0)
+    cache.attention_scores(Q, N, out=sc)
+    tc = _timed(torch, lambda: cache.append_key(X, 0), reps)
+    ts = _timed(torch, lambda: cache.attention_scores(Q, N, out=sc), reps)
+    rec = []
+    for q0 in range(0, G, 64):
+        ex = torch.matmul(Q[0, q0:q0 + 64], X[0].T)
+        t_true = ex.topk(10, dim=1).indices
+        t_est = sc[0, q0:q0 + 64].topk(10, dim=1).indices
+        rec.append(float((t_true[:, :, None] == t_est[:, None, :]).any(-1).float().mean()))
+    executed = N * (2 * d * d * 3 + 2 * m * d * 3)   # split-fp16 MFMA flops actually issued (fp32 inputs)
+    line = {"metric": "vector search: vectors compressed/s, score rate for 512 queries, recall@10 vs fp32",
+            "value": round(N / (tc * 1e-3), 1), "unit": "vectors/s", "higher_is_better": True, "n_gpus": 1,
+            "data": "synthetic", "dtype": "f32",
+            "config": {"workload": "vector_search_2M_d1024", "n_vectors": N, "head_dim": d, "proj_dim": m,
+                       "key_bits": b, "queries": G},
+            "compress_ms": round(tc, 3), "scores_ms": round(ts, 3),
+            "compress_mfma": {"achieved_TFLOPs": round(executed / (tc * 1e-3) / 1e12, 1), "peak_TFLOPs": FP16_MFMA_PEAK_TFLOPS,
+                              "frac": round(executed / (tc * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4)},
+            "scores_alg_TFLOPs": round(N * G * 2 * (d + m) / (ts * 1e-3) / 1e12, 1),
+            "recall_at_10": round(float(np.mean(rec)), 4)}
+    print(json.dumps(line))
+    ctx.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,11 +309,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--workload", default="long_context",
+                    choices=["long_context", "qwen_decode", "bit_sweep", "vector_search"],
+                    help="long_context (default): the full hot-path step; the others print one extra "
+                         "JSON line for the decode, bit-width sweep and vector-search configurations")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the hot path is single-GPU); --gpus {args.gpus} is not "
               f"supported", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "long_context":
+        {"qwen_decode": bench_qwen_decode, "bit_sweep": bench_bit_sweep,
+         "vector_search": bench_vector_search}[args.workload](args)
+        return
 
     import torch
     from kv_cache_vector_compress_amd import synth, tq
