@@ -42,9 +42,9 @@
  *  - Shapes.  head_dim 128 with proj_dim 64 or 128 runs single-kernel
  *    compress and attention paths; every other valid shape (head_dim a
  *    multiple of 128 up to 1024, proj_dim a multiple of 64 up to 512) runs
- *    the general path: tiled rotation / projection kernels for the appends
- *    and a chunked score kernel.  tq_attend is built for the first group of
- *    shapes only.
+ *    the general path: tiled rotation / projection kernels for the appends,
+ *    a chunked score kernel, and an attend that materialises the scores in
+ *    the workspace and merges per-range softmax partials.
  *  - Device pointers must be 16-byte aligned.
  */
 #ifndef TQ_H
@@ -66,7 +66,7 @@ typedef enum {
   TQ_ENOCODEBOOK = -3,  /* no codebook loaded for the bits this call needs */
   TQ_ENOMEM = -4,       /* device allocation failed (tq_create only) */
   TQ_EDEVICE = -5,      /* a HIP call or kernel launch failed */
-  TQ_EUNSUPPORTED = -6, /* valid but not built: tq_attend off head_dim 128 / proj_dim 64, 128 */
+  TQ_EUNSUPPORTED = -6, /* valid but not built (reserved; every valid shape is built) */
   TQ_EWORKSPACE = -7    /* workspace smaller than tq_workspace_bytes */
 } tq_status;
 
@@ -216,8 +216,7 @@ int tq_attention_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, 
  * softmax, weighted sum of the decompressed values).  scale <= 0 means
  * 1/sqrt(d).  No causal mask.  out: device fp32 [n_seq][G][d].
  * Same q/workspace rules and errors as tq_attention_scores, with
- * 1 <= G <= 16; TQ_EUNSUPPORTED unless head_dim is 128 and proj_dim is 64
- * or 128. */
+ * 1 <= G <= 16. */
 int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
               int64_t n_tokens, float scale, float* out, void* workspace, size_t workspace_bytes,
               void* stream);

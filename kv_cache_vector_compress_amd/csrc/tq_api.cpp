@@ -109,6 +109,7 @@ size_t tq_cache_value_bytes(const tq_config* cfg, int32_t n_seq, int64_t capacit
 size_t tq_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, int64_t n_tokens) {
   if (check_config(cfg) == TQ_EINVAL || n_seq < 1 || G < 1 || G > kMaxGeneralHeads || n_tokens < 1) return 0;
   if (fast_attn(*cfg, G)) return plan_attention(cfg->proj_dim, n_seq, G, n_tokens).total;
+  if (G <= 16) return general_attend_plan(cfg->head_dim, cfg->proj_dim, n_seq, G, n_tokens).total;
   return general_scores_workspace(cfg->head_dim, cfg->proj_dim, n_seq, G);
 }
 
@@ -329,9 +330,6 @@ static int attn_common(tq_ctx* ctx, const tq_cache_view* cache, const void* q, i
   if (dtype != TQ_F16 && dtype != TQ_F32) return fail(TQ_EINVAL, "%s: dtype %d", fn, dtype);
   const int gmax = need_values ? 16 : kMaxGeneralHeads;
   if (G < 1 || G > gmax) return fail(TQ_EINVAL, "%s: G %d not in 1..%d", fn, G, gmax);
-  if (need_values && !fast_attn(ctx->cfg, G))
-    return fail(TQ_EUNSUPPORTED, "%s: built for head_dim 128 with proj_dim 64 or 128 (have %d, %d)", fn,
-                ctx->cfg.head_dim, ctx->cfg.proj_dim);
   if (n_tokens < 1 || n_tokens > cache->capacity)
     return fail(TQ_EINVAL, "%s: n_tokens %lld not in [1, capacity]", fn, (long long)n_tokens);
   if (!q || !outp || !ws) return fail(TQ_EINVAL, "%s: NULL q, output or workspace", fn);
@@ -341,9 +339,13 @@ static int attn_common(tq_ctx* ctx, const tq_cache_view* cache, const void* q, i
     return fail(TQ_ENOCODEBOOK, "%s: no %d-bit key codebook loaded", fn, ctx->cfg.key_bits);
   if (need_values && !ctx->loaded[ctx->cfg.value_bits])
     return fail(TQ_ENOCODEBOOK, "%s: no %d-bit value codebook loaded", fn, ctx->cfg.value_bits);
-  const size_t need = fast_attn(ctx->cfg, G) ? (*plan = plan_attention(ctx->cfg.proj_dim, cache->n_seq, G, n_tokens)).total
-                                             : general_scores_workspace(ctx->cfg.head_dim, ctx->cfg.proj_dim,
-                                                                        cache->n_seq, G);
+  size_t need;
+  if (fast_attn(ctx->cfg, G))
+    need = (*plan = plan_attention(ctx->cfg.proj_dim, cache->n_seq, G, n_tokens)).total;
+  else if (need_values)
+    need = general_attend_plan(ctx->cfg.head_dim, ctx->cfg.proj_dim, cache->n_seq, G, n_tokens).total;
+  else
+    need = general_scores_workspace(ctx->cfg.head_dim, ctx->cfg.proj_dim, cache->n_seq, G);
   if (ws_bytes < need) return fail(TQ_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   return TQ_OK;
 }
@@ -380,11 +382,18 @@ int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dt
   if (scale <= 0.f) scale = 1.f / std::sqrt((float)ctx->cfg.head_dim);
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_attend: hipSetDevice");
   AttnShape s{q, dtype, G, n_tokens, cache->capacity, cache->n_seq};
-  rc = launch_prep_queries(ctx->mats, ctx->cfg.proj_dim, s, workspace, plan, stream);
-  if (!rc)
-    rc = launch_attend(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cb[ctx->cfg.value_bits],
-                       ctx->cfg.value_bits, ctx->cfg.proj_dim, s, cache->key_records, cache->value_blocks, scale,
-                       out, workspace, plan, stream);
+  if (fast_attn(ctx->cfg, G)) {
+    rc = launch_prep_queries(ctx->mats, ctx->cfg.proj_dim, s, workspace, plan, stream);
+    if (!rc)
+      rc = launch_attend(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cb[ctx->cfg.value_bits],
+                         ctx->cfg.value_bits, ctx->cfg.proj_dim, s, cache->key_records, cache->value_blocks, scale,
+                         out, workspace, plan, stream);
+  } else {
+    rc = launch_general_attend(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits,
+                               ctx->cb[ctx->cfg.value_bits], ctx->cfg.value_bits, ctx->cfg.head_dim,
+                               ctx->cfg.proj_dim, s, cache->key_records, cache->value_blocks, scale, out,
+                               workspace, stream);
+  }
   return rc ? fail(rc, "tq_attend: launch failed (%d)", rc) : TQ_OK;
 }
 

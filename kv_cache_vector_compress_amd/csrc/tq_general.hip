@@ -643,6 +643,201 @@ __global__ __launch_bounds__(256) void gen_scores(const GenScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// attend (general shapes): the scores come from gen_scores (materialised in
+// the workspace); each wave runs the online softmax over a range of 128-token
+// blocks of one slot and accumulates sum_t p_t ||v_t|| c[idx_t] for one
+// 128-coordinate chunk of the output (the P V product of the single-kernel
+// path, with the value words of that chunk), and gen_combine merges the
+// ranges (log-sum-exp) and applies R^T.
+// ---------------------------------------------------------------------------
+
+constexpr int kGenPart = 4 + 128;  // m, l, pad, pad, acc[128] per (slot, range, chunk, head)
+
+struct GenAttendArgs {
+  const float* scores;   // [n_seq][G][n_tokens] unscaled estimates
+  const uint32_t* vblocks;
+  float* part;           // [n_seq][ranges][n_oct][G][kGenPart]
+  int64_t n_tokens, capacity;
+  int n_seq, G, d, n_oct, block_words;
+  int blocks_per_wave, ranges;
+  float scale2;          // scale * log2(e)
+  uint32_t vtlo[4], vthi[4];
+};
+
+__device__ __forceinline__ uint32_t pack_h2f(float x0, float x1) {
+  const h2 v = {(_Float16)x0, (_Float16)x1};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int BV>
+__global__ __launch_bounds__(256) void gen_attend_kernel(const GenAttendArgs a) {
+  __shared__ __align__(16) float vsh[4][kBlockTokens];  // per wave: ||v|| 2^-ve of the block's tokens
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+  if (gw >= (int64_t)a.n_seq * a.ranges * a.n_oct) return;
+  const int u = (int)(gw % a.n_oct);  // chunk fastest: the chunk waves of a range read the same scores
+  const int64_t sr = gw / a.n_oct;
+  const int slot = (int)(sr / a.ranges), rg = (int)(sr % a.ranges);
+  const int n_tok = (int)a.n_tokens;
+  const int nblk = (n_tok + kBlockTokens - 1) / kBlockTokens;
+  const int b_begin = rg * a.blocks_per_wave, b_end = min(nblk, b_begin + a.blocks_per_wave);
+  const int h = r16;
+  const bool head_ok = h < a.G;
+  const float* srow = a.scores + ((int64_t)slot * a.G + (head_ok ? h : 0)) * (int64_t)n_tok;
+  const uint32_t* vbase = a.vblocks + (int64_t)slot * (a.capacity / kBlockTokens) * a.block_words;
+  uint32_t vtlo[4], vthi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { vtlo[i] = a.vtlo[i]; vthi[i] = a.vthi[i]; }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  int ve = -1000;  // running exponent of the value norms (wave-uniform)
+  f4 acc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int blk = b_begin; blk < b_end; ++blk) {
+    const int tok0 = blk * kBlockTokens;
+    const uint32_t* vb = vbase + (int64_t)blk * a.block_words;
+    uint32_t vw[8][BV];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int w = 0; w < BV; ++w) vw[nt][w] = vb[(w * 4 + q) * a.d + 128 * u + 16 * nt + r16];
+    const float2 vn2 = *(const float2*)(vb + 4 * BV * a.d + 2 * lane);
+    const float x0 = tok0 + 2 * lane < n_tok ? vn2.x : 0.f, x1 = tok0 + 2 * lane + 1 < n_tok ? vn2.y : 0.f;
+    float bmax = fmaxf(x0, x1);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) bmax = fmaxf(bmax, shfl_xor(bmax, o));
+    int e_blk = 0;
+    frexpf(bmax, &e_blk);
+    if (e_blk > ve) {
+      const float f = ldexpf(1.f, ve - e_blk);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[nt] *= f;
+      ve = e_blk;
+    }
+    const float vs = ldexpf(1.f, -ve);
+    *(float2*)&vsh[wave][2 * lane] = make_float2(x0 * vs, x1 * vs);
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      float lg[2][4];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int t0 = tok0 + 16 * (2 * step + uu) + 4 * q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float l = (head_ok && t0 + i < n_tok) ? srow[t0 + i] * a.scale2 : -INFINITY;
+          lg[uu][i] = l;
+          cmax = fmaxf(cmax, l);
+        }
+      }
+      cmax = fmaxf(cmax, shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, shfl_xor(cmax, 32));
+      if (__any(cmax > m_run)) {
+        const float m_new = fmaxf(m_run, cmax);
+        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[nt] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      u4 pw;
+      float psum = 0.f;
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const f4 vn = *(const f4*)&vsh[wave][16 * (2 * step + uu) + 4 * q];
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const float p0 = m_run == -INFINITY ? 0.f : exp2f(lg[uu][2 * i2] - m_run);
+          const float p1 = m_run == -INFINITY ? 0.f : exp2f(lg[uu][2 * i2 + 1] - m_run);
+          psum += p0 + p1;
+          pw[2 * uu + i2] = pack_h2f(p0 * vn[2 * i2], p1 * vn[2 * i2 + 1]);
+        }
+      }
+      l_run += psum;
+      const h8 P = as_h8(pw);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        h8 A;
+        if (step == 0) A = decode_pair<BV, 0>(vw[nt], vtlo, vthi);
+        if (step == 1) A = decode_pair<BV, 2>(vw[nt], vtlo, vthi);
+        if (step == 2) A = decode_pair<BV, 4>(vw[nt], vtlo, vthi);
+        if (step == 3) A = decode_pair<BV, 6>(vw[nt], vtlo, vthi);
+        acc[nt] = mfma(A, P, acc[nt]);
+      }
+    }
+  }
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  if (head_ok) {
+    float* pr = a.part + ((((int64_t)slot * a.ranges + rg) * a.n_oct + u) * a.G + h) * kGenPart;
+    const float f = ldexpf(1.f, ve);
+    if (q == 0) {
+      pr[0] = m_run;
+      pr[1] = l_run;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) *(f4*)(pr + 4 + 16 * nt + 4 * q) = acc[nt] * f;
+  }
+}
+
+struct GenCombineArgs {
+  const float* part;
+  float* out;   // [n_seq][G][d]
+  const float* r32;
+  int n_seq, G, d, n_oct, ranges;
+};
+
+// One workgroup per (slot, query head): out = R^T (sum_r w_r acc_r) / sum_r w_r l_r,
+// w_r = exp2(m_r - max_r m_r).
+__global__ __launch_bounds__(256) void gen_combine(const GenCombineArgs a) {
+  extern __shared__ float ysh[];  // [d] combined rotated-domain accumulator, then [ranges] weights
+  float* wsh = ysh + a.d;
+  __shared__ float red[4];
+  __shared__ float Msh, Lsh;
+  const int sh = blockIdx.x, slot = sh / a.G, h = sh % a.G, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  auto P = [&](int r, int u) { return a.part + ((((int64_t)slot * a.ranges + r) * a.n_oct + u) * a.G + h) * kGenPart; };
+  float mx = -INFINITY;
+  for (int r = tid; r < a.ranges; r += blockDim.x) mx = fmaxf(mx, P(r, 0)[0]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  if (tid == 0) Msh = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  const float M = Msh;
+  float L = 0.f;
+  for (int r = tid; r < a.ranges; r += blockDim.x) {
+    const float mr = P(r, 0)[0];
+    const float w = (mr == -INFINITY || M == -INFINITY) ? 0.f : exp2f(mr - M);
+    wsh[r] = w;
+    L += w * P(r, 0)[1];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += shfl_xor(L, o);
+  __syncthreads();
+  if (lane == 0) red[wave] = L;
+  __syncthreads();
+  if (tid == 0) Lsh = (red[0] + red[1]) + (red[2] + red[3]);
+  for (int c = tid; c < a.d; c += blockDim.x) {
+    const int u = c / 128, cc = c % 128;
+    float y = 0.f;
+    for (int r = 0; r < a.ranges; ++r) y = fmaf(wsh[r], P(r, u)[4 + cc], y);
+    ysh[c] = y;
+  }
+  __syncthreads();
+  const float inv = Lsh > 0.f ? 1.f / Lsh : 0.f;
+  float* out = a.out + ((int64_t)slot * a.G + h) * a.d;
+  for (int j = tid; j < a.d; j += blockDim.x) {
+    float t = 0.f;
+    for (int i = 0; i < a.d; ++i) t = fmaf(a.r32[(size_t)i * a.d + j], ysh[i], t);
+    out[j] = t * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -800,6 +995,70 @@ int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbit
   TQ_GSB(1) TQ_GSB(2) TQ_GSB(3) TQ_GSB(4)
 #undef TQ_GSB
 #undef TQ_GS
+  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+}
+
+
+GenAttnPlan general_attend_plan(int d, int m, int n_seq, int G, int64_t n_tokens) {
+  GenAttnPlan p;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const int HG = head_groups_bucket(G);
+  const size_t q_bytes = (size_t)n_seq * HG * (d / 32 + m / 32) * 64 * 8 * 2;
+  const size_t qn_bytes = (size_t)n_seq * HG * 16 * 4;
+  const int n_oct = d / 128;
+  const int64_t nblk = (n_tokens + kBlockTokens - 1) / kBlockTokens;
+  int64_t R = (4096 + (int64_t)n_seq * n_oct - 1) / ((int64_t)n_seq * n_oct);  // ~16 waves per CU in all
+  if (R > nblk) R = nblk;
+  if (R > 1024) R = 1024;
+  if (R < 1) R = 1;
+  const int64_t bpw = (nblk + R - 1) / R;
+  p.blocks_per_wave = (int)bpw;
+  p.ranges = (int)((nblk + bpw - 1) / bpw);
+  p.off_scores = up(q_bytes) + up(qn_bytes);
+  p.off_part = p.off_scores + up((size_t)n_seq * G * n_tokens * 4);
+  p.total = p.off_part + up((size_t)n_seq * p.ranges * n_oct * G * kGenPart * 4);
+  return p;
+}
+
+int launch_general_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
+                          int d, int m, const AttnShape& s, const void* key_records, const void* value_blocks,
+                          float scale, float* out, void* ws, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const GenAttnPlan p = general_attend_plan(d, m, s.n_seq, s.G, s.n_tokens);
+  float* scores = (float*)((char*)ws + p.off_scores);
+  int rc = launch_general_scores(mats, cbk, kbits, d, m, s, key_records, scores, ws, stream);
+  if (rc) return rc;
+  GenAttendArgs a;
+  a.scores = scores;
+  a.vblocks = (const uint32_t*)value_blocks;
+  a.part = (float*)((char*)ws + p.off_part);
+  a.n_tokens = s.n_tokens;
+  a.capacity = s.capacity;
+  a.n_seq = s.n_seq;
+  a.G = s.G;
+  a.d = d;
+  a.n_oct = d / 128;
+  a.block_words = 4 * vbits * d + kBlockTokens;
+  a.blocks_per_wave = p.blocks_per_wave;
+  a.ranges = p.ranges;
+  a.scale2 = scale * 1.4426950408889634f;
+  for (int i = 0; i < 4; ++i) { a.vtlo[i] = cbv.tlo[i]; a.vthi[i] = cbv.thi[i]; }
+  const int64_t waves = (int64_t)s.n_seq * p.ranges * (d / 128);
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  if (vbits == 1) hipLaunchKernelGGL(gen_attend_kernel<1>, grid, block, 0, st, a);
+  if (vbits == 2) hipLaunchKernelGGL(gen_attend_kernel<2>, grid, block, 0, st, a);
+  if (vbits == 3) hipLaunchKernelGGL(gen_attend_kernel<3>, grid, block, 0, st, a);
+  if (vbits == 4) hipLaunchKernelGGL(gen_attend_kernel<4>, grid, block, 0, st, a);
+  GenCombineArgs c;
+  c.part = a.part;
+  c.out = out;
+  c.r32 = mats.r32;
+  c.n_seq = s.n_seq;
+  c.G = s.G;
+  c.d = d;
+  c.n_oct = d / 128;
+  c.ranges = p.ranges;
+  hipLaunchKernelGGL(gen_combine, dim3((unsigned)(s.n_seq * s.G)), dim3(256), sizeof(float) * (d + p.ranges), st, c);
   return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
 }
 

@@ -98,6 +98,16 @@ int launch_general_keys(const GenMats& g, const CodebookDev& cb, int bits, int d
 int launch_general_values(const GenMats& g, const CodebookDev& cb, int bits, int d, const AppendShape& s,
                           void* value_blocks, void* stream);
 size_t general_scores_workspace(int d, int m, int n_seq, int G);
+struct GenAttnPlan {
+  int blocks_per_wave, ranges;  // split of each slot's token axis for the value accumulation
+  size_t off_scores;            // materialised scores [n_seq][G][n_tokens] fp32
+  size_t off_part;              // partials [n_seq][ranges][d/128][G][132] fp32
+  size_t total;
+};
+GenAttnPlan general_attend_plan(int d, int m, int n_seq, int G, int64_t n_tokens);
+int launch_general_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
+                          int d, int m, const AttnShape& s, const void* key_records, const void* value_blocks,
+                          float scale, float* out, void* ws, void* stream);
 int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, int m,
                           const AttnShape& s, const void* key_records, float* scores, void* ws, void* stream);
 

@@ -233,14 +233,15 @@ def test_long_context_full_size_sampled():
     (1024, 512, 4, 4, np.float32, 16),
 ])
 def test_general_shapes_ragged_chunks(d, m, kb, vb, dtype, G):
-    """Codes, signs, norms, gamma of keys and values, and scores, on the
-    general path; appended in unaligned chunks (partial value blocks)."""
+    """Codes, signs, norms, gamma of keys and values, scores and (G <= 16)
+    attention on the general path; appended in unaligned chunks (partial
+    value blocks)."""
     n_seq, T = 2, 700
     K = np.stack([synth.kv_slot(60 + d, s, s, T, d, dtype=dtype) for s in range(n_seq)])
     V = np.stack([synth.kv_slot(61 + d, s, s, T, d, dtype=dtype) for s in range(n_seq)])
     Q = np.stack([synth.kv_slot(62 + d, s, s, G, d, dtype=dtype) for s in range(n_seq)])
     _say("general", (d, m, kb, vb, dtype.__name__, G))
-    _say(run_case(K, V, Q, kb=kb, vb=vb, m=m, chunks=[130, 1, 300, 269], check_attend=False))
+    _say(run_case(K, V, Q, kb=kb, vb=vb, m=m, chunks=[130, 1, 300, 269], check_attend=G <= 16))
 
 
 def test_vector_search_shape():
@@ -269,14 +270,15 @@ def test_vector_search_shape():
     ctx.close()
 
 
-def test_attend_reports_unsupported_off_the_fast_shape():
-    ctx, R, S = make_ctx(256, 64, 3, 3)
-    cache = tq.KVCache(ctx, 1, 128)
-    q = torch.zeros((1, 4, 256), dtype=torch.float16, device="cuda")
-    with pytest.raises(tq.TQError) as e:
-        cache.attend(q, 16)
-    assert e.value.code == -6
-    ctx.close()
+def test_general_attend_long_range_scale():
+    """General-shape attention over several 128-token ranges per slot (the
+    split-and-merge path) with a non-default scale, d = 256, m = 128."""
+    d, m, T, n_seq, G = 256, 128, 3000, 2, 8
+    K = np.stack([synth.kv_slot(70, s, s, T, d) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(71, s, s, T, d) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(72, s, s, G, d) for s in range(n_seq)])
+    _say("general attend", (d, m, T))
+    _say(run_case(K, V, Q, m=m, n_tokens=2900, scale=0.11))
 
 
 # ---------------------------------------------------------------------------
