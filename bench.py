@@ -63,15 +63,19 @@ def algorithmic_bytes(w):
     }, units
 
 
+# Sources the long-context step's kernels are built from (the counter record
+# in profiles/ is valid only for these exact files).
+STEP_SOURCES = ("tq_attention.hip", "tq_compress.hip", "tq_device.h", "tq_internal.h")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources (kernels and headers), sorted by name."""
-    import glob
+    """sha256 over the sources of the long-context step's kernels, in name order."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_vector_compress_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+    for name in STEP_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
 
