@@ -27,113 +27,6 @@ constexpr int64_t kTargetWaves = 256 * 16;
 constexpr int kMaxPartials = 1024;
 
 // ---------------------------------------------------------------------------
-// query preparation: MFMA B operands of q~/|q| and p/|q|, and |q|
-// ---------------------------------------------------------------------------
-
-struct PrepArgs {
-  const void* q;
-  int dtype, G, n_seq;
-  const float* r32;
-  const float* s32;
-  uint16_t* wq;   // [n_seq][KBT][64 lanes][8] fp16
-  float* wqn;     // [n_seq][16]
-};
-
-template <int M>
-__global__ __launch_bounds__(256) void prep_queries_kernel(const PrepArgs a) {
-  constexpr int KBT = 4 + M / 32;
-  constexpr int LS = kD + 1;  // padded LDS row (conflict-free column walks)
-  extern __shared__ float sm[];
-  float* Rs = sm;                       // [kD][LS]
-  float* Ss = Rs + kD * LS;             // [M][LS]
-  float* qs = Ss + M * LS;              // [16][kD]
-  float* qt = qs + 16 * kD;             // [16][kD]
-  float* pp = qt + 16 * kD;             // [16][M]
-  float* qn = pp + 16 * M;              // [16]
-  const int slot = blockIdx.x, tid = threadIdx.x;
-  const int G = a.G;
-  // coalesced fills of R, S (16-byte loads) and of this slot's queries
-  for (int i = tid; i < kD * kD / 4; i += blockDim.x) {
-    const f4 v = ((const f4*)a.r32)[i];
-    const int r = (4 * i) / kD, c = (4 * i) % kD;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Rs[r * LS + c + e] = v[e];
-  }
-  for (int i = tid; i < M * kD / 4; i += blockDim.x) {
-    const f4 v = ((const f4*)a.s32)[i];
-    const int r = (4 * i) / kD, c = (4 * i) % kD;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Ss[r * LS + c + e] = v[e];
-  }
-  for (int idx = tid; idx < 16 * kD; idx += blockDim.x) {
-    const int h = idx / kD, k = idx % kD;
-    float v = 0.f;
-    if (h < G) {
-      const int64_t off = ((int64_t)slot * G + h) * kD + k;
-      v = a.dtype == TQ_F32 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
-    }
-    qs[h * kD + k] = v;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * kD; idx += blockDim.x) {  // q~ = R q
-    const int h = idx / kD, j = idx % kD;
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll 16
-    for (int k = 0; k < kD; k += 2) {
-      s0 = fmaf(Rs[j * LS + k], qs[h * kD + k], s0);
-      s1 = fmaf(Rs[j * LS + k + 1], qs[h * kD + k + 1], s1);
-    }
-    qt[h * kD + j] = s0 + s1;
-  }
-  if (tid < 16) {
-    float s = 0.f;
-    for (int k = 0; k < kD; ++k) s = fmaf(qs[tid * kD + k], qs[tid * kD + k], s);
-    qn[tid] = sqrtf(s);
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * M; idx += blockDim.x) {  // p = S q~
-    const int h = idx / M, i = idx % M;
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll 16
-    for (int k = 0; k < kD; k += 2) {
-      s0 = fmaf(Ss[i * LS + k], qt[h * kD + k], s0);
-      s1 = fmaf(Ss[i * LS + k + 1], qt[h * kD + k + 1], s1);
-    }
-    pp[h * M + i] = s0 + s1;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < KBT * 64; idx += blockDim.x) {
-    const int kb = idx / 64, l = idx % 64, h = l % 16, qq = l / 16;
-    const float inv = h < G && qn[h] > 0.f ? 1.f / qn[h] : 0.f;
-    h8 v;
-    if (kb < 4) {
-      // centroid part, k slot e <-> coordinate 16 (2 kb + e/4) + 4 qq + e%4
-      for (int e = 0; e < 8; ++e)
-        v[e] = (_Float16)(h < G ? qt[h * kD + 16 * (2 * kb + e / 4) + 4 * qq + e % 4] * inv : 0.f);
-    } else {
-      // sign part, k slot 2e+half <-> sign bit p + 16 half of word 2 (kbp/2) + qq/2,
-      // p = 8 (qq%2) + 4 (kbp%2) + e; that bit holds projection coordinate
-      // 16 t + 4 qs + i with qs = 2 (qq/2) + half, t = 4 (kbp/2) + p/4, i = p%4
-      const int kbp = kb - 4;
-      for (int e = 0; e < 4; ++e)
-        for (int half = 0; half < 2; ++half) {
-          const int p = 8 * (qq % 2) + 4 * (kbp % 2) + e;
-          const int qsg = 2 * (qq / 2) + half;
-          const int t = 4 * (kbp / 2) + p / 4;
-          v[2 * e + half] = (_Float16)(h < G ? pp[h * M + 16 * t + 4 * qsg + p % 4] * inv : 0.f);
-        }
-    }
-    *(h8*)(a.wq + (((int64_t)slot * KBT + kb) * 64 + l) * 8) = v;
-  }
-  if (tid < 16) a.wqn[slot * 16 + tid] = tid < G ? qn[tid] : 0.f;
-}
-
-template <int M>
-constexpr size_t prep_lds_bytes() {
-  return sizeof(float) * ((size_t)(kD + 1) * (kD + M) + 16 * kD * 2 + 16 * M + 16);
-}
-
-// ---------------------------------------------------------------------------
 // shared pieces of the score computation
 // ---------------------------------------------------------------------------
 
@@ -578,12 +471,6 @@ int attention_device_init() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   if (hipDeviceGetAttribute(&g_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  if (hipFuncSetAttribute((const void*)prep_queries_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)prep_lds_bytes<64>()) != hipSuccess)
-    return -1;
-  if (hipFuncSetAttribute((const void*)prep_queries_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)prep_lds_bytes<128>()) != hipSuccess)
-    return -1;
   return 0;
 }
 
@@ -625,21 +512,10 @@ static WsPtrs ws_ptrs(void* ws, const AttnPlan& p) {
 
 int launch_prep_queries(const Matrices& mats, int m, const AttnShape& s, void* ws, const AttnPlan& p,
                         void* stream) {
-  PrepArgs a;
+  // one workgroup per (slot, head), wave-parallel dot products (tq_general.hip);
+  // with a single head group its operands have the layout read here
   const WsPtrs w = ws_ptrs(ws, p);
-  a.q = s.q;
-  a.dtype = s.dtype;
-  a.G = s.G;
-  a.n_seq = s.n_seq;
-  a.r32 = mats.r32;
-  a.s32 = mats.s32;
-  a.wq = w.wq;
-  a.wqn = w.wqn;
-  hipStream_t st = (hipStream_t)stream;
-  if (m == 64) hipLaunchKernelGGL(prep_queries_kernel<64>, dim3(s.n_seq), dim3(256), prep_lds_bytes<64>(), st, a);
-  else if (m == 128) hipLaunchKernelGGL(prep_queries_kernel<128>, dim3(s.n_seq), dim3(256), prep_lds_bytes<128>(), st, a);
-  else return TQ_EUNSUPPORTED;
-  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+  return launch_gen_prep(mats, kD, m, s, 1, w.wq, w.wqn, stream);
 }
 
 static void fill_tables(const CodebookDev& cb, uint32_t* tlo, uint32_t* thi) {

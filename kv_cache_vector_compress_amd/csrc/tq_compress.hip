@@ -304,6 +304,10 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
 
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
+      // a half with no token of [pos, pos + n_new) keeps all its codes (a
+      // short append, e.g. one decode token, touches one half)
+      const int64_t h0 = tok0 + 64 * half;
+      if (h0 + 64 <= a.pos || h0 >= a.pos + a.n_new) continue;
       h8 xa[4][4];
       h8 xl[F32 ? 4 : 1][4];
       float tok_sc[4];  // per token: sigma = 2^8 sc ||v|| (4-bit codes: 1 / sigma)

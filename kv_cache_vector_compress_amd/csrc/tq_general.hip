@@ -509,20 +509,30 @@ __global__ __launch_bounds__(256) void gen_prep_queries(const GenPrepArgs a) {
   if (lane == 0) red[wave] = s;
   __syncthreads();
   const float qn = sqrtf((red[0] + red[1]) + (red[2] + red[3]));
-  for (int j = wave; j < a.d; j += 4) {  // q~ = R q, one row per wave step
-    float t = 0.f;
-    for (int k = lane; k < a.d; k += 64) t = fmaf(a.r32[(size_t)j * a.d + k], qs[k], t);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) t += shfl_xor(t, o);
-    if (lane == 0) qt[j] = t;
+  // q~ = R q and p = S q~: one output row per thread, its row of R (S) read
+  // as float4 runs so that many loads are in flight at once
+  for (int j = tid; j < a.d; j += blockDim.x) {
+    const f4* rr = (const f4*)(a.r32 + (size_t)j * a.d);
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll 8
+    for (int k4 = 0; k4 < a.d / 4; k4 += 2) {
+      const f4 x = rr[k4], y = rr[k4 + 1];
+      t0 = fmaf(x[0], qs[4 * k4], fmaf(x[1], qs[4 * k4 + 1], fmaf(x[2], qs[4 * k4 + 2], fmaf(x[3], qs[4 * k4 + 3], t0))));
+      t1 = fmaf(y[0], qs[4 * k4 + 4], fmaf(y[1], qs[4 * k4 + 5], fmaf(y[2], qs[4 * k4 + 6], fmaf(y[3], qs[4 * k4 + 7], t1))));
+    }
+    qt[j] = t0 + t1;
   }
   __syncthreads();
-  for (int i = wave; i < a.m; i += 4) {  // p = S q~
-    float t = 0.f;
-    for (int k = lane; k < a.d; k += 64) t = fmaf(a.s32[(size_t)i * a.d + k], qt[k], t);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) t += shfl_xor(t, o);
-    if (lane == 0) pp[i] = t;
+  for (int i = tid; i < a.m; i += blockDim.x) {
+    const f4* sr = (const f4*)(a.s32 + (size_t)i * a.d);
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll 8
+    for (int k4 = 0; k4 < a.d / 4; k4 += 2) {
+      const f4 x = sr[k4], y = sr[k4 + 1];
+      t0 = fmaf(x[0], qt[4 * k4], fmaf(x[1], qt[4 * k4 + 1], fmaf(x[2], qt[4 * k4 + 2], fmaf(x[3], qt[4 * k4 + 3], t0))));
+      t1 = fmaf(y[0], qt[4 * k4 + 4], fmaf(y[1], qt[4 * k4 + 5], fmaf(y[2], qt[4 * k4 + 6], fmaf(y[3], qt[4 * k4 + 7], t1))));
+    }
+    pp[i] = t0 + t1;
   }
   __syncthreads();
   const float inv = live && qn > 0.f ? 1.f / qn : 0.f;
@@ -949,11 +959,8 @@ size_t general_scores_workspace(int d, int m, int n_seq, int G) {
   return ((q_bytes + 255) / 256 + (qn_bytes + 255) / 256) * 256;
 }
 
-int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, int m,
-                          const AttnShape& s, const void* key_records, float* scores, void* ws, void* stream) {
-  hipStream_t st = (hipStream_t)stream;
-  const int HG = head_groups_bucket(s.G);
-  if (HG > 32) return TQ_EUNSUPPORTED;
+int launch_gen_prep(const Matrices& mats, int d, int m, const AttnShape& s, int HG, uint16_t* wq, float* wqn,
+                    void* stream) {
   GenPrepArgs p;
   p.q = s.q;
   p.dtype = s.dtype;
@@ -965,16 +972,28 @@ int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbit
   p.n_oct = d / 128;
   p.r32 = mats.r32;
   p.s32 = mats.s32;
-  const size_t q_bytes = (size_t)s.n_seq * HG * (d / 32 + m / 32) * 64 * 8 * 2;
-  p.wq = (uint16_t*)ws;
-  p.wqn = (float*)((char*)ws + (q_bytes + 255) / 256 * 256);
+  p.wq = wq;
+  p.wqn = wqn;
   const size_t lds = sizeof(float) * (2 * d + m);
-  hipLaunchKernelGGL(gen_prep_queries, dim3((unsigned)(s.n_seq * 16 * HG)), dim3(256), lds, st, p);
+  hipLaunchKernelGGL(gen_prep_queries, dim3((unsigned)(s.n_seq * 16 * HG)), dim3(256), lds, (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+}
+
+int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, int m,
+                          const AttnShape& s, const void* key_records, float* scores, void* ws, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int HG = head_groups_bucket(s.G);
+  if (HG > 32) return TQ_EUNSUPPORTED;
+  const size_t q_bytes = (size_t)s.n_seq * HG * (d / 32 + m / 32) * 64 * 8 * 2;
+  uint16_t* wq = (uint16_t*)ws;
+  float* wqn = (float*)((char*)ws + (q_bytes + 255) / 256 * 256);
+  int rc = launch_gen_prep(mats, d, m, s, HG, wq, wqn, stream);
+  if (rc) return rc;
   GenScoreArgs a;
   a.rec = (const uint32_t*)key_records;
   a.scores = scores;
-  a.wq = p.wq;
-  a.wqn = p.wqn;
+  a.wq = wq;
+  a.wqn = wqn;
   a.n_tokens = s.n_tokens;
   a.capacity = s.capacity;
   a.n_seq = s.n_seq;

@@ -98,6 +98,10 @@ int launch_general_keys(const GenMats& g, const CodebookDev& cb, int bits, int d
 int launch_general_values(const GenMats& g, const CodebookDev& cb, int bits, int d, const AppendShape& s,
                           void* value_blocks, void* stream);
 size_t general_scores_workspace(int d, int m, int n_seq, int G);
+// Query operands for HG groups of 16 heads: wq [n_seq][HG][d/32 + m/32][64][8] fp16, wqn [n_seq][16 HG]
+// (with HG = 1 the layout the single-kernel score and attend kernels read).
+int launch_gen_prep(const Matrices& mats, int d, int m, const AttnShape& s, int HG, uint16_t* wq, float* wqn,
+                    void* stream);
 struct GenAttnPlan {
   int blocks_per_wave, ranges;  // split of each slot's token axis for the value accumulation
   size_t off_scores;            // materialised scores [n_seq][G][n_tokens] fp32
