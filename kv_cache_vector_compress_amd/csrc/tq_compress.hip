@@ -47,9 +47,23 @@ constexpr size_t key_lds_bytes() {
   return (size_t)(2 * kRImg + 2 * M * kLdsStride) * 2;
 }
 
+// Copy n_halves fp16 values (a multiple of 8) from global memory into LDS,
+// 8 independent 16-byte loads in flight per thread.
 __device__ __forceinline__ void copy_u4(uint16_t* dst, const uint16_t* src, int n_halves) {
   const int n = n_halves / 8;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) ((u4*)dst)[i] = ((const u4*)src)[i];
+  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * blockDim.x) {
+    u4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * blockDim.x;
+      if (i < n) v[j] = ((const u4*)src)[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * blockDim.x;
+      if (i < n) ((u4*)dst)[i] = v[j];
+    }
+  }
 }
 
 // Load the 32 input coordinates a lane owns (8 per K block: 32 kb + 8 q ..)
