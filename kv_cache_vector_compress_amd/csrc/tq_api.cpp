@@ -132,9 +132,13 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   // order" per 128-coordinate chunk: column 128 u + 32 kb + 8 q + e holds
   // rotated coordinate 128 u + 16 (2 kb + e/4) + 4 q + e%4, the order in which
   // a key lane holds its residual after the rotation.
+  // The d = 128 key kernel built on 32 x 32 matrix-core tiles holds its
+  // residual in another order and takes a second copy of S: column
+  // 16 kk + 8 g + e holds coordinate 16 kk + 8 (e/4) + 4 g + e%4 (bits 2 and
+  // 3 of the coordinate swapped).
   const int ld = d + 8;
   const size_t r_img = (size_t)d * ld, s_img = (size_t)m * ld;
-  std::vector<uint16_t> rh(r_img, 0), rl(r_img, 0), sh(s_img, 0), sl(s_img, 0);
+  std::vector<uint16_t> rh(r_img, 0), rl(r_img, 0), sh(s_img, 0), sl(s_img, 0), sh32(s_img, 0), sl32(s_img, 0);
   std::vector<float> r32((size_t)d * d), s32((size_t)m * d);
   auto split = [](double x, uint16_t& hi, uint16_t& lo) {
     const double xs = x * (double)kRotScale;
@@ -153,6 +157,10 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
       split(S[(size_t)i * d + coord], sh[(size_t)i * ld + col], sl[(size_t)i * ld + col]);
     }
     for (int k = 0; k < d; ++k) s32[(size_t)i * d + k] = (float)S[(size_t)i * d + k];
+    for (int col = 0; col < d; ++col) {
+      const int coord = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+      split(S[(size_t)i * d + coord], sh32[(size_t)i * ld + col], sl32[(size_t)i * ld + col]);
+    }
   }
 
   std::call_once(g_init_flag, [] { g_init_rc = compress_device_init() | attention_device_init(); });
@@ -165,7 +173,8 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
     return fail(TQ_EDEVICE, "tq_create: hipGetDevice failed");
   }
   const size_t b_rimg = r_img * 2, b_simg = s_img * 2;
-  const size_t off_rl = b_rimg, off_sh = 2 * b_rimg, off_sl = off_sh + b_simg, off_r32 = off_sl + b_simg;
+  const size_t off_rl = b_rimg, off_sh = 2 * b_rimg, off_sl = off_sh + b_simg, off_sh32 = off_sl + b_simg;
+  const size_t off_sl32 = off_sh32 + b_simg, off_r32 = off_sl32 + b_simg;
   const size_t off_s32 = off_r32 + r32.size() * 4, end_imgs = off_s32 + s32.size() * 4;
   // general-path scratch (row norms, key residual hi/lo, residual square sums)
   const bool gen = !fast_keys(*cfg) || !fast_values(*cfg);
@@ -183,6 +192,8 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
             hipMemcpy(base + off_rl, rl.data(), b_rimg, hipMemcpyHostToDevice) == hipSuccess &&
             hipMemcpy(base + off_sh, sh.data(), b_simg, hipMemcpyHostToDevice) == hipSuccess &&
             hipMemcpy(base + off_sl, sl.data(), b_simg, hipMemcpyHostToDevice) == hipSuccess &&
+            hipMemcpy(base + off_sh32, sh32.data(), b_simg, hipMemcpyHostToDevice) == hipSuccess &&
+            hipMemcpy(base + off_sl32, sl32.data(), b_simg, hipMemcpyHostToDevice) == hipSuccess &&
             hipMemcpy(base + off_r32, r32.data(), r32.size() * 4, hipMemcpyHostToDevice) == hipSuccess &&
             hipMemcpy(base + off_s32, s32.data(), s32.size() * 4, hipMemcpyHostToDevice) == hipSuccess;
   if (!ok) {
@@ -194,6 +205,8 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   c->mats.r_lo = (const uint16_t*)(base + off_rl);
   c->mats.s_hi = (const uint16_t*)(base + off_sh);
   c->mats.s_lo = (const uint16_t*)(base + off_sl);
+  c->mats.s_hi32 = (const uint16_t*)(base + off_sh32);
+  c->mats.s_lo32 = (const uint16_t*)(base + off_sl32);
   c->mats.r32 = (const float*)(base + off_r32);
   c->mats.s32 = (const float*)(base + off_s32);
   c->gen.mats = c->mats;

@@ -113,11 +113,75 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Stage 16 U tokens of key records (one contiguous run of the cache) in this
+// wave's LDS slice: the wave loads them with 16-byte loads, lane l taking
+// bytes 16 l + 1024 j, so every load is fully coalesced; lanes then pick
+// their words from LDS.  (A lane needs three or four scattered words of one
+// record; loading those straight from memory reaches only about 60% of the
+// read bandwidth a coalesced stream gets.)  In LDS a record takes STR >= RW
+// words with STR/2 odd: the 16 records a read instruction touches then sit
+// in distinct banks (word offsets 2 (STR/2) r mod 32 are distinct even
+// numbers for r < 16).
+template <int RW, int U>
+struct KeyStage {
+  static constexpr int TW = 16 * RW;                      // words per 16-token tile
+  static constexpr int NL = (U * TW + 255) / 256;         // 16-byte loads per lane
+  static constexpr int STR = ((RW + 2) / 2) % 2 ? RW + 2 : RW + 4;
+  static constexpr int ROWS = (NL * 256 + RW - 1) / RW;   // records a stage covers
+  static constexpr int SLICE = ROWS * STR;                // LDS words per wave
+  u4 v[NL];
+};
+
+template <int RW, int U>
+__device__ __forceinline__ void stage_load(KeyStage<RW, U>& s, __amdgpu_buffer_rsrc_t r, int tile, int lane) {
+  const uint32_t o = (uint32_t)tile * (uint32_t)(KeyStage<RW, U>::TW * 4) + 16u * (uint32_t)lane;
+#pragma unroll
+  for (int j = 0; j < KeyStage<RW, U>::NL; ++j)
+    s.v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, o + 1024u * j, 0, 0);
+}
+
+// Write the staged registers to the wave's LDS slice, one 8-byte store per
+// word pair (RW is even, so a pair never straddles two records).  The fences
+// keep the compiler from moving this wave's LDS reads of the previous
+// contents past the writes, or its reads of the new contents before them (a
+// wave's LDS operations complete in order, so lanes need no wait).
+template <int RW, int U>
+__device__ __forceinline__ void stage_store(uint32_t* slice, const KeyStage<RW, U>& s, int lane) {
+  using S = KeyStage<RW, U>;
+  static_assert(RW % 2 == 0, "records are whole word pairs");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+  for (int j = 0; j < S::NL; ++j)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int g = 256 * j + 4 * lane + 2 * p;  // word index within the stage
+      const int row = g / RW;
+      *(uint2*)(slice + row * S::STR + (g - row * RW)) = make_uint2(s.v[j][2 * p], s.v[j][2 * p + 1]);
+    }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The words of the staged record of token row t this lane needs.
+template <int B, int M, int STR>
+__device__ __forceinline__ void stage_key(KeyTile<B, M>& k, const uint32_t* slice, int t, int q) {
+  constexpr int RW = B * kD / 32 + M / 32 + 2;
+  const uint32_t* rp = slice + t * STR;
+#pragma unroll
+  for (int w = 0; w < B; ++w) k.cw[w] = rp[q * B + w];
+#pragma unroll
+  for (int c = 0; c < M / 64; ++c) k.sw[c] = rp[4 * B + 2 * c + (q >> 1)];
+  const uint2 ng = *(const uint2*)(rp + RW - 2);
+  k.n = __uint_as_float(ng.x);
+  k.g = __uint_as_float(ng.y);
+}
+
 template <int B, int M>
 __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
   constexpr int KBT = 4 + M / 32;
   constexpr int RW = rec_words<B, M>();
-  constexpr int U = 4;          // 16-token tiles per iteration (next U tiles in flight)
+  constexpr int U = 4;          // 16-token tiles per iteration (the next U tiles in flight)
+  using Stage = KeyStage<RW, U>;
+  __shared__ __align__(16) uint32_t kst[4][Stage::SLICE];  // per wave: the iteration's records
   __shared__ float nsh[4][16 * U];  // per wave: ||k|| of the iteration's tokens
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
@@ -143,25 +207,23 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
   const __amdgpu_buffer_rsrc_t ors =
       slot_rsrc(a.scores + (size_t)slot * a.G * (size_t)n_tok, (uint32_t)a.G * (uint32_t)n_tok * 4u);
   const uint32_t orow = (uint32_t)r16 * (uint32_t)n_tok;
-
+  // records of tokens past n_tokens (up to the slot's capacity, zeros past
+  // it) are staged too; their rows are never stored
   const __amdgpu_buffer_rsrc_t krs = slot_rsrc(base, (uint32_t)a.capacity * (uint32_t)(RW * 4));
-  auto load = [&](KeyTile<B, M>& k, int tile) {
-    const int t = min(tile * 16 + r16, n_tok - 1);  // rows past the end: any valid row
-    load_key<B, M>(k, krs, (uint32_t)t * (uint32_t)(RW * 4), q);
-  };
+  uint32_t* slice = kst[wave];
 
-  // One iteration: scores of U tiles from `cur` while the next U tiles load
-  // into `nxt`.  Iterations alternate the two buffers (no register copies).
-  auto iteration = [&](KeyTile<B, M> (&cur)[U], KeyTile<B, M> (&nxt)[U], int tile) {
-    if (tile + U < t_end) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) load(nxt[u], tile + U + u);
-    }
+  // One iteration: scores of U tiles staged from `cur` while the next U
+  // tiles load into `nxt`.  Iterations alternate the two buffers.
+  auto iteration = [&](Stage& cur, Stage& nxt, int tile) {
+    if (tile + U < t_end) stage_load<RW, U>(nxt, krs, tile + U, lane);
+    stage_store<RW, U>(slice, cur, lane);
     f4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      acc[u] = key_tile_scores<B, M>(cur[u], qb, tlo, thi, a.kappa, sh0);
-      if (q == 0) nsh[wave][16 * u + r16] = cur[u].n;
+      KeyTile<B, M> k;
+      stage_key<B, M, Stage::STR>(k, slice, 16 * u + r16, q);
+      acc[u] = key_tile_scores<B, M>(k, qb, tlo, thi, a.kappa, sh0);
+      if (q == 0) nsh[wave][16 * u + r16] = k.n;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -181,12 +243,11 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
     }
   };
 
-  KeyTile<B, M> ta[U], tb[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) load(ta[u], t_begin + u);
+  Stage sa, sb;
+  if (t_begin < t_end) stage_load<RW, U>(sa, krs, t_begin, lane);
   for (int tile = t_begin; tile < t_end; tile += 2 * U) {
-    iteration(ta, tb, tile);
-    if (tile + U < t_end) iteration(tb, ta, tile + U);
+    iteration(sa, sb, tile);
+    if (tile + U < t_end) iteration(sb, sa, tile + U);
   }
 }
 

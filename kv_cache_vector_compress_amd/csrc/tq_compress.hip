@@ -268,6 +268,150 @@ __global__ __launch_bounds__(512, 1) void compress_keys_kernel(const KeyArgs a) 
   }
 }
 
+// Keys on 32 x 32 x 16 matrix-core tiles (fp16 keys, m = 64).  A wave takes
+// 32 tokens per iteration.  Lane l owns token l % 32 and, of every 32-
+// coordinate output tile t, the 16 coordinates 32 t + 8 j + 4 g + i
+// (g = l / 32, acc[4 j + i]); over the four tiles those are exactly the
+// record's code groups g and g + 2, so the record is written lane-locally in
+// the same layout as above.  The residual of tile t feeds projection K steps
+// 2t and 2t + 1 straight from the accumulator (S's columns are permuted to
+// match, bits 2 and 3 of the coordinate swapped).  Rotation t + 1 is issued
+// before the bucketing of tile t so the two can overlap on a SIMD.
+template <int B>
+__global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a) {
+  constexpr int H = 1 << (B - 1);
+  extern __shared__ __align__(16) uint16_t lds[];
+  __shared__ float ctab[16];  // 2^12 c_i
+  uint16_t* Rh = lds;
+  uint16_t* Rl = Rh + kRImg;
+  uint16_t* Sh = Rl + kRImg;
+  uint16_t* Sl = Sh + 64 * kLdsStride;
+  copy_u4(Rh, a.r_hi, kRImg);
+  copy_u4(Rl, a.r_lo, kRImg);
+  copy_u4(Sh, a.s_hi, 64 * kLdsStride);
+  copy_u4(Sl, a.s_lo, 64 * kLdsStride);
+  if (threadIdx.x < 16) ctab[threadIdx.x] = a.cb.cent[threadIdx.x] * kResScale;
+  __syncthreads();
+
+  float bpos[8];
+  load_pos_beta<B>(bpos, a.cb);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n32 = lane & 31, g = lane >> 5;
+  const int64_t tps = (a.n_new + 31) / 32;
+  const int64_t ntiles = tps * a.n_seq;
+  const int waves = blockDim.x >> 6;
+  const int arow = n32 * kLdsStride + 8 * g;  // this lane's A-operand offset in a 32-row band
+
+  for (int64_t tile = (int64_t)blockIdx.x * waves + wave; tile < ntiles; tile += (int64_t)gridDim.x * waves) {
+    const int slot = (int)(tile / tps);
+    const int64_t t0 = (tile - (int64_t)slot * tps) * 32;
+    const int64_t tok = t0 + n32;
+    // rows past n_new are clamped to the last row (computed, never stored)
+    const int64_t row = (int64_t)slot * a.n_new + (tok < a.n_new ? tok : a.n_new - 1);
+    const _Float16* src = (const _Float16*)a.x + row * kD + 8 * g;
+    h8 xk[8];  // B operands: coordinates 16 kk + 8 g .. + 7
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) xk[kk] = *(const h8*)(src + 16 * kk);
+    float ss[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const h2 v = {xk[kk][e], xk[kk][e + 1]};
+        ss[kk & 1] = __builtin_amdgcn_fdot2(v, v, ss[kk & 1], false);
+      }
+    float sq = ss[0] + ss[1];
+    sq += shfl_xor(sq, 32);
+    const float nrm = sqrtf(sq);
+    const float sigma = kRotScale * nrm;
+    const float s16 = nrm > 0.f ? kResScale / sigma : 0.f;
+    float bs[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) bs[t] = t < H - 1 ? bpos[t] * sigma : 0.f;
+
+    auto rotate = [&](int t) {
+      f16v y;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) y[e] = 0.f;
+      const int o = 32 * t * kLdsStride + arow;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const h8 ah = *(const h8*)(Rh + o + 16 * kk);
+        const h8 al = *(const h8*)(Rl + o + 16 * kk);
+        y = mfma32(ah, xk[kk], y);
+        y = mfma32(al, xk[kk], y);
+      }
+      return y;
+    };
+
+    f16v zacc[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) zacc[p][e] = 0.f;
+    uint32_t cw[2][B];
+#pragma unroll
+    for (int w = 0; w < B; ++w) cw[0][w] = cw[1][w] = 0u;
+    float g2 = 0.f;
+
+    f16v ycur = rotate(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      f16v ynext;
+      if (t < 3) ynext = rotate(t + 1);
+      // cells, scaled residual 2^12 (y - c[idx]) as the B operands of
+      // projection K steps 2t (acc 0..7) and 2t + 1 (acc 8..15)
+      u4 rhi[2], rlo[2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float rs[4];
+        const uint32_t x4 = quantize4<B>(quarter(ycur, j), bs, s16, ctab, rs, g2);
+        const HiLo t01 = split2m(rs[0], rs[1], a.m1), t23 = split2m(rs[2], rs[3], a.m1);
+        rhi[j >> 1][2 * (j & 1)] = t01.hi;
+        rlo[j >> 1][2 * (j & 1)] = t01.lo;
+        rhi[j >> 1][2 * (j & 1) + 1] = t23.hi;
+        rlo[j >> 1][2 * (j & 1) + 1] = t23.lo;
+        put_sel4_rt<B>(cw[j & 1], 2 * t + (j >> 1), x4);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const h8 rh = as_h8(rhi[h]), rl = as_h8(rlo[h]);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int o = 32 * p * kLdsStride + arow + 16 * (2 * t + h);
+          const h8 sh = *(const h8*)(Sh + o);
+          const h8 sl = *(const h8*)(Sl + o);
+          zacc[p] = mfma32(sh, rh, zacc[p]);
+          zacc[p] = mfma32(sl, rh, zacc[p]);
+          zacc[p] = mfma32(sh, rl, zacc[p]);
+        }
+      }
+      if (t < 3) ycur = ynext;
+    }
+
+    g2 += shfl_xor(g2, 32);
+    const float gamma = sqrtf(g2) * (1.f / kResScale);
+    // projection 32 p + 8 j + 4 g + i = 16 (2 p + j/2) + 4 (2 (j%2) + g) + i:
+    // sign group g (j even) and g + 2 (j odd), bit 4 (2 p + j/2) + i
+    const uint32_t bits_a = sign_bits16(quarter(zacc[0], 0), quarter(zacc[0], 2), quarter(zacc[1], 0),
+                                        quarter(zacc[1], 2));
+    const uint32_t bits_b = sign_bits16(quarter(zacc[0], 1), quarter(zacc[0], 3), quarter(zacc[1], 1),
+                                        quarter(zacc[1], 3));
+    if (tok < a.n_new) {
+      uint32_t* rp = a.rec + ((int64_t)slot * a.capacity + a.pos + tok) * a.rec_words;
+#pragma unroll
+      for (int w = 0; w < B; ++w) {
+        rp[g * B + w] = cw[0][w];
+        rp[(g + 2) * B + w] = cw[1][w];
+      }
+      ((uint16_t*)(rp + 4 * B))[g] = (uint16_t)bits_a;
+      ((uint16_t*)(rp + 4 * B + 1))[g] = (uint16_t)bits_b;
+      rp[a.rec_words - 2 + g] = __float_as_uint(g == 0 ? nrm : gamma);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // values
 // ---------------------------------------------------------------------------
@@ -469,6 +613,13 @@ static int set_key_attr() {
              ? 0 : -1;
 }
 
+template <int B>
+static int set_key32_attr() {
+  return hipFuncSetAttribute((const void*)compress_keys32_kernel<B>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)key_lds_bytes<64>()) == hipSuccess
+             ? 0 : -1;
+}
+
 template <int B, bool F32>
 static int set_val_attr() {
   return hipFuncSetAttribute((const void*)compress_values_kernel<B, F32>,
@@ -486,6 +637,7 @@ int compress_device_init() {
         set_key_attr<B, 128, false>() | set_key_attr<B, 128, true>();
   TQ_KEY_ATTR(1) TQ_KEY_ATTR(2) TQ_KEY_ATTR(3) TQ_KEY_ATTR(4)
 #undef TQ_KEY_ATTR
+  rc |= set_key32_attr<1>() | set_key32_attr<2>() | set_key32_attr<3>() | set_key32_attr<4>();
   rc |= set_val_attr<1, false>() | set_val_attr<1, true>() | set_val_attr<2, false>() | set_val_attr<2, true>();
   rc |= set_val_attr<3, false>() | set_val_attr<3, true>() | set_val_attr<4, false>() | set_val_attr<4, true>();
   return rc;
@@ -499,6 +651,16 @@ static void key_launch(const KeyArgs& a, int64_t ntiles, hipStream_t st) {
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL((compress_keys_kernel<B, M, F32>), dim3((unsigned)grid), dim3(64 * waves),
                      key_lds_bytes<M>(), st, a);
+}
+
+template <int B>
+static void key32_launch(const KeyArgs& a, int64_t ntiles, hipStream_t st) {
+  const int waves = 8;
+  int64_t grid = (ntiles + waves - 1) / waves;
+  const int64_t cap = (int64_t)(g_num_cus > 0 ? g_num_cus : 256);
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL((compress_keys32_kernel<B>), dim3((unsigned)grid), dim3(64 * waves), key_lds_bytes<64>(), st,
+                     a);
 }
 
 int launch_compress_keys(const Matrices& mats, const CodebookDev& cb, int bits, int m, const AppendShape& s,
@@ -521,6 +683,17 @@ int launch_compress_keys(const Matrices& mats, const CodebookDev& cb, int bits, 
   const int64_t per = (f32 || m > 64) ? 16 : 32;
   const int64_t ntiles = ((s.n_new + per - 1) / per) * s.n_seq;
   hipStream_t st = (hipStream_t)stream;
+  if (!f32 && m == 64 && bits >= 1 && bits <= 4) {  // fp16 keys, m = 64: the 32 x 32 tile kernel
+    a.s_hi = mats.s_hi32;
+    a.s_lo = mats.s_lo32;
+    switch (bits) {
+      case 1: key32_launch<1>(a, ntiles, st); break;
+      case 2: key32_launch<2>(a, ntiles, st); break;
+      case 3: key32_launch<3>(a, ntiles, st); break;
+      default: key32_launch<4>(a, ntiles, st); break;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+  }
 #define TQ_KEY_CASE(B, M)                                  \
   if (bits == B && m == M) {                               \
     if (f32) key_launch<B, M, true>(a, ntiles, st);        \

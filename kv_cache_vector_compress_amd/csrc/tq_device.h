@@ -24,6 +24,18 @@ __device__ __forceinline__ f4 mfma(const h8& a, const h8& b, const f4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_32x32x16_f16 (wave64):
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. +7
+//   B (16 x 32): lane l holds column l%32, k = 8*(l/32) .. +7
+//   D (32 x 32): lane l holds column l%32, rows 8 j + 4*(l/32) + i at acc[4 j + i]
+typedef float f16v __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f16v mfma32(const h8& a, const h8& b, const f16v& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 quarter(const f16v& v, int j) {
+  return f4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+}
+
 __device__ __forceinline__ h8 as_h8(const u4& v) { return __builtin_bit_cast(h8, v); }
 __device__ __forceinline__ u4 as_u4(const h8& v) { return __builtin_bit_cast(u4, v); }
 

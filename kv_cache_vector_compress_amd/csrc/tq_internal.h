@@ -34,6 +34,8 @@ struct Matrices {
   const uint16_t* r_lo;
   const uint16_t* s_hi;  // [m][kLdsStride] fp16 bits, S * 2^8 high part, columns in slot order
   const uint16_t* s_lo;
+  const uint16_t* s_hi32;  // the same for d = 128 with columns in 32-lane slot order
+  const uint16_t* s_lo32;
   const float* r32;      // [d][d] fp32 R
   const float* s32;      // [m][d] fp32 S (natural column order)
 };
