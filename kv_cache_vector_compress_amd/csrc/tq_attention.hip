@@ -461,65 +461,76 @@ struct CombineArgs {
   int n_seq, G, waves_per_slot;
 };
 
-__global__ __launch_bounds__(128) void combine_kernel(const CombineArgs a) {
+// One workgroup of 4 x 128 threads per (slot, query head): thread (g, j)
+// takes coordinate j of every fourth partial, then a quarter of R's rows.
+__global__ __launch_bounds__(512) void combine_kernel(const CombineArgs a) {
   __shared__ float w[kMaxPartials];  // per-partial weights exp2(m_c - M)
-  __shared__ float red[128];
+  __shared__ float red[2][8];
+  __shared__ float part[4][kD];
   __shared__ __align__(16) float y[kD];
-  const int sh = blockIdx.x, slot = sh / a.G, h = sh % a.G, j = threadIdx.x;
+  const int sh = blockIdx.x, slot = sh / a.G, h = sh % a.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = tid & (kD - 1), g = tid >> 7;
   const int W = a.waves_per_slot;
   const float* pr = a.part + ((int64_t)slot * W * a.G + h) * kPartFloats;
   const int64_t stride = (int64_t)a.G * kPartFloats;
-  // maximum of the partial maxima
+  // M = max of the partial maxima (wave reductions, one exchange)
   float M = -INFINITY;
-  for (int c = j; c < W; c += blockDim.x) M = fmaxf(M, pr[c * stride]);
-  red[j] = M;
+  for (int c = tid; c < W; c += blockDim.x) M = fmaxf(M, pr[c * stride]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
+  if (lane == 0) red[0][wave] = M;
   __syncthreads();
-  for (int o = 64; o > 0; o >>= 1) {
-    if (j < o) red[j] = fmaxf(red[j], red[j + o]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
+  M = red[0][0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) M = fmaxf(M, red[0][i]);
   // weights and the weighted sum of the partial sums
   float L = 0.f;
-  for (int c = j; c < W; c += blockDim.x) {
+  for (int c = tid; c < W; c += blockDim.x) {
     const float mc = pr[c * stride];
     const float wc = mc == -INFINITY ? 0.f : exp2f(mc - M);
     w[c] = wc;
     L = fmaf(wc, pr[c * stride + 1], L);
   }
-  red[j] = L;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += shfl_xor(L, o);
+  if (lane == 0) red[1][wave] = L;
   __syncthreads();
-  for (int o = 64; o > 0; o >>= 1) {
-    if (j < o) red[j] += red[j + o];
-    __syncthreads();
+  L = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) L += red[1][i];
+  // thread (g, j): partials c = g, g + 4, ..., 8 loads in flight
+  float acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  int c = g;
+  for (; c + 28 < W; c += 32) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = fmaf(w[c + 4 * u], pr[(c + 4 * u) * stride + 4 + j], acc[u]);
   }
-  L = red[0];
-  // 16 partial loads in flight per thread
-  float acc[16];
+  for (; c < W; c += 4) acc[0] = fmaf(w[c], pr[c * stride + 4 + j], acc[0]);
 #pragma unroll
-  for (int u = 0; u < 16; ++u) acc[u] = 0.f;
-  int c = 0;
-  for (; c + 16 <= W; c += 16) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) acc[u] = fmaf(w[c + u], pr[(c + u) * stride + 4 + j], acc[u]);
-  }
-  for (; c < W; ++c) acc[0] = fmaf(w[c], pr[c * stride + 4 + j], acc[0]);
-#pragma unroll
-  for (int u = 1; u < 16; ++u) acc[0] += acc[u];
-  y[j] = acc[0] / L;
+  for (int u = 1; u < 8; ++u) acc[0] += acc[u];
+  part[g][j] = acc[0];
   __syncthreads();
-  // out = R^T y (column j of R, coalesced across threads), 16 loads in flight
-  float o[16];
+  if (g == 0) y[j] = ((part[0][j] + part[1][j]) + (part[2][j] + part[3][j])) / L;
+  __syncthreads();
+  // out = R^T y: thread (g, j) sums rows i = 32 g .. 32 g + 31 of column j
+  float o[8];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) o[u] = 0.f;
-  for (int i = 0; i < kD; i += 16) {
+  for (int u = 0; u < 8; ++u) o[u] = 0.f;
+  const float* rc = a.r32 + (size_t)(32 * g) * kD + j;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) o[u] = fmaf(a.r32[(i + u) * kD + j], y[i + u], o[u]);
+  for (int i = 0; i < 32; i += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = fmaf(rc[(i + u) * kD], y[32 * g + i + u], o[u]);
   }
 #pragma unroll
-  for (int u = 1; u < 16; ++u) o[0] += o[u];
-  a.out[((int64_t)slot * a.G + h) * kD + j] = o[0];
+  for (int u = 1; u < 8; ++u) o[0] += o[u];
+  __syncthreads();
+  part[g][j] = o[0];
+  __syncthreads();
+  if (g == 0) a.out[((int64_t)slot * a.G + h) * kD + j] = (part[0][j] + part[1][j]) + (part[2][j] + part[3][j]);
 }
 
 // ---------------------------------------------------------------------------
@@ -662,7 +673,7 @@ int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const
   c.n_seq = s.n_seq;
   c.G = s.G;
   c.waves_per_slot = p.waves_per_slot;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(s.n_seq * s.G)), dim3(kD), 0, st, c);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(s.n_seq * s.G)), dim3(4 * kD), 0, st, c);
   return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
 }
 

@@ -509,30 +509,39 @@ __global__ __launch_bounds__(256) void gen_prep_queries(const GenPrepArgs a) {
   if (lane == 0) red[wave] = s;
   __syncthreads();
   const float qn = sqrtf((red[0] + red[1]) + (red[2] + red[3]));
-  // q~ = R q and p = S q~: one output row per thread, its row of R (S) read
-  // as float4 runs so that many loads are in flight at once
-  for (int j = tid; j < a.d; j += blockDim.x) {
-    const f4* rr = (const f4*)(a.r32 + (size_t)j * a.d);
-    float t0 = 0.f, t1 = 0.f;
+  // q~ = R q and p = S q~.  A head lane past G has q = 0 and takes no
+  // products.  Each output row is split over 4 neighbouring threads (a
+  // quarter of its columns each, all of their loads in flight at once), and
+  // the quarters are summed with two lane exchanges.
+  if (live) {
+    auto rows = [&](const float* mat, int n_rows, const float* x, float* y) {
+      const int c = tid & 3, d4 = a.d / 4;
+      for (int j0 = 0; j0 < n_rows; j0 += blockDim.x / 4) {
+        const int j = j0 + (tid >> 2);
+        float t = 0.f;
+        if (j < n_rows) {
+          const f4* rr = (const f4*)(mat + (size_t)j * a.d + c * d4);
+          const float* xx = x + c * d4;
+          float t1 = 0.f;
 #pragma unroll 8
-    for (int k4 = 0; k4 < a.d / 4; k4 += 2) {
-      const f4 x = rr[k4], y = rr[k4 + 1];
-      t0 = fmaf(x[0], qs[4 * k4], fmaf(x[1], qs[4 * k4 + 1], fmaf(x[2], qs[4 * k4 + 2], fmaf(x[3], qs[4 * k4 + 3], t0))));
-      t1 = fmaf(y[0], qs[4 * k4 + 4], fmaf(y[1], qs[4 * k4 + 5], fmaf(y[2], qs[4 * k4 + 6], fmaf(y[3], qs[4 * k4 + 7], t1))));
-    }
-    qt[j] = t0 + t1;
-  }
-  __syncthreads();
-  for (int i = tid; i < a.m; i += blockDim.x) {
-    const f4* sr = (const f4*)(a.s32 + (size_t)i * a.d);
-    float t0 = 0.f, t1 = 0.f;
-#pragma unroll 8
-    for (int k4 = 0; k4 < a.d / 4; k4 += 2) {
-      const f4 x = sr[k4], y = sr[k4 + 1];
-      t0 = fmaf(x[0], qt[4 * k4], fmaf(x[1], qt[4 * k4 + 1], fmaf(x[2], qt[4 * k4 + 2], fmaf(x[3], qt[4 * k4 + 3], t0))));
-      t1 = fmaf(y[0], qt[4 * k4 + 4], fmaf(y[1], qt[4 * k4 + 5], fmaf(y[2], qt[4 * k4 + 6], fmaf(y[3], qt[4 * k4 + 7], t1))));
-    }
-    pp[i] = t0 + t1;
+          for (int k4 = 0; k4 < d4 / 4; k4 += 2) {
+            const f4 u = rr[k4], v = rr[k4 + 1];
+            t = fmaf(u[0], xx[4 * k4], fmaf(u[1], xx[4 * k4 + 1], fmaf(u[2], xx[4 * k4 + 2], fmaf(u[3], xx[4 * k4 + 3], t))));
+            t1 = fmaf(v[0], xx[4 * k4 + 4], fmaf(v[1], xx[4 * k4 + 5], fmaf(v[2], xx[4 * k4 + 6], fmaf(v[3], xx[4 * k4 + 7], t1))));
+          }
+          t += t1;
+        }
+        t += shfl_xor(t, 1);
+        t += shfl_xor(t, 2);
+        if (j < n_rows && c == 0) y[j] = t;
+      }
+    };
+    rows(a.r32, a.d, qs, qt);
+    __syncthreads();
+    rows(a.s32, a.m, qt, pp);
+  } else {
+    for (int k = tid; k < a.d; k += blockDim.x) qt[k] = 0.f;
+    for (int i = tid; i < a.m; i += blockDim.x) pp[i] = 0.f;
   }
   __syncthreads();
   const float inv = live && qn > 0.f ? 1.f / qn : 0.f;
