@@ -573,6 +573,106 @@ __global__ __launch_bounds__(256) void gen_prep_queries(const GenPrepArgs a) {
   if (tid == 0) a.wqn[(int64_t)slot * H16 + h] = live ? qn : 0.f;
 }
 
+// The same operands for d = 128 and m = 64, one workgroup of 512 threads
+// per (slot, group of 16 head lanes): thread t holds a quarter of R's row
+// t/4 and an eighth of S's row t/8 in registers, loaded before the queries
+// arrive, and applies them to every live head of the group (R and S are read
+// once per group rather than once per head).
+__global__ __launch_bounds__(512) void prep_queries128(const GenPrepArgs a) {
+  constexpr int D = 128, Mp = 64, KBT = D / 32 + Mp / 32;
+  __shared__ __align__(16) float qs[16][D];
+  __shared__ __align__(16) float qt[16][D];
+  __shared__ float pp[16][Mp];
+  __shared__ float qn[16];
+  const int slot = blockIdx.x / a.HG, hg = blockIdx.x % a.HG;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = max(0, min(16, a.G - 16 * hg));  // live head lanes of this group
+  f4 rv[8], sv[4];
+  {
+    const f4* rr = (const f4*)(a.r32 + (size_t)(tid >> 2) * D + 32 * (tid & 3));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rv[u] = rr[u];
+    const f4* sr = (const f4*)(a.s32 + (size_t)(tid >> 3) * D + 16 * (tid & 7));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sv[u] = sr[u];
+  }
+  for (int i = tid; i < 16 * D; i += blockDim.x) {
+    const int hh = i / D, k = i % D;
+    float v = 0.f;
+    if (hh < nl) {
+      const int64_t off = ((int64_t)slot * a.G + 16 * hg + hh) * D + k;
+      v = a.dtype == TQ_F32 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
+    }
+    qs[hh][k] = v;
+  }
+  __syncthreads();
+  for (int hh = wave; hh < 16; hh += 8) {
+    float s = qs[hh][lane] * qs[hh][lane] + qs[hh][lane + 64] * qs[hh][lane + 64];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += shfl_xor(s, o);
+    if (lane == 0) qn[hh] = sqrtf(s);
+  }
+  // q~ = R q: row tid/4, columns 32 (tid%4) ..; the four parts summed by lane exchanges
+  for (int hh = 0; hh < nl; ++hh) {
+    const f4* x = (const f4*)(&qs[hh][32 * (tid & 3)]);
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      const f4 x0 = x[u], x1 = x[u + 1];
+      t0 = fmaf(rv[u][0], x0[0], fmaf(rv[u][1], x0[1], fmaf(rv[u][2], x0[2], fmaf(rv[u][3], x0[3], t0))));
+      t1 = fmaf(rv[u + 1][0], x1[0], fmaf(rv[u + 1][1], x1[1], fmaf(rv[u + 1][2], x1[2], fmaf(rv[u + 1][3], x1[3], t1))));
+    }
+    float t = t0 + t1;
+    t += shfl_xor(t, 1);
+    t += shfl_xor(t, 2);
+    if ((tid & 3) == 0) qt[hh][tid >> 2] = t;
+  }
+  __syncthreads();
+  // p = S q~: row tid/8, columns 16 (tid%8) ..
+  for (int hh = 0; hh < nl; ++hh) {
+    const f4* x = (const f4*)(&qt[hh][16 * (tid & 7)]);
+    float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; u += 2) {
+      const f4 x0 = x[u], x1 = x[u + 1];
+      z0 = fmaf(sv[u][0], x0[0], fmaf(sv[u][1], x0[1], fmaf(sv[u][2], x0[2], fmaf(sv[u][3], x0[3], z0))));
+      z1 = fmaf(sv[u + 1][0], x1[0], fmaf(sv[u + 1][1], x1[1], fmaf(sv[u + 1][2], x1[2], fmaf(sv[u + 1][3], x1[3], z1))));
+    }
+    float z = z0 + z1;
+    z += shfl_xor(z, 1);
+    z += shfl_xor(z, 2);
+    z += shfl_xor(z, 4);
+    if ((tid & 7) == 0) pp[hh][tid >> 3] = z;
+  }
+  __syncthreads();
+  // operands, as gen_prep_queries lays them out (zeros for head lanes past G)
+  for (int idx = tid; idx < 16 * KBT * 4; idx += blockDim.x) {
+    const int h16 = idx / (KBT * 4), kb = (idx / 4) % KBT, qq = idx % 4;
+    const bool live = h16 < nl;
+    const float inv = live && qn[h16] > 0.f ? 1.f / qn[h16] : 0.f;
+    h8 v;
+    if (kb < D / 32) {
+      const int base = 32 * kb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)(live ? qt[h16][base + 16 * (e / 4) + 4 * qq + e % 4] * inv : 0.f);
+    } else {
+      const int kbp = kb - D / 32;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int p = 8 * (qq % 2) + 4 * (kbp % 2) + e;
+          const int qsg = 2 * (qq / 2) + half;
+          const int t = 4 * (kbp / 2) + p / 4;
+          v[2 * e + half] = (_Float16)(live ? pp[h16][16 * t + 4 * qsg + p % 4] * inv : 0.f);
+        }
+    }
+    const int l = 16 * qq + h16;
+    *(h8*)(a.wq + ((((int64_t)slot * a.HG + hg) * KBT + kb) * 64 + l) * 8) = v;
+  }
+  if (tid < 16) a.wqn[((int64_t)slot * a.HG + hg) * 16 + tid] = tid < nl ? qn[tid] : 0.f;
+}
+
 // ---------------------------------------------------------------------------
 // scores: one wave per 16-token tile; every chunk of a key record is decoded
 // once and multiplied by the query operands of all HG head groups.
@@ -983,6 +1083,12 @@ int launch_gen_prep(const Matrices& mats, int d, int m, const AttnShape& s, int 
   p.s32 = mats.s32;
   p.wq = wq;
   p.wqn = wqn;
+  // grouped form when there are enough groups to fill the chip; with a few
+  // slots (a decode step) one workgroup per head lane has the shorter path
+  if (d == 128 && m == 64 && (int64_t)s.n_seq * HG >= 32) {
+    hipLaunchKernelGGL(prep_queries128, dim3((unsigned)(s.n_seq * HG)), dim3(512), 0, (hipStream_t)stream, p);
+    return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+  }
   const size_t lds = sizeof(float) * (2 * d + m);
   hipLaunchKernelGGL(gen_prep_queries, dim3((unsigned)(s.n_seq * 16 * HG)), dim3(256), lds, (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
