@@ -221,6 +221,25 @@ int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dt
               int64_t n_tokens, float scale, float* out, void* workspace, size_t workspace_bytes,
               void* stream);
 
+/* ---- reconstruction (not on the attention path) --------------------------- */
+
+/* Stage-1 reconstruction of cached values, x^ = ||v|| R^T c[idx]
+ * (TurboQuantKVCache.get_values and TurboQuantMSE.dequantize,
+ * nav.superapi.store 核心 API; the value compressor keeps only this MSE
+ * reconstruction, 生产级压缩器).  Tokens [pos, pos + n_tokens) of every slot.
+ * out: device fp32 [n_seq][n_tokens][d], 16-byte aligned.  Computed in fp32
+ * from the stored codes and norms.  Errors: TQ_EINVAL, TQ_ECAPACITY
+ * (pos < 0 or pos + n_tokens > capacity), TQ_ENOCODEBOOK, TQ_EDEVICE.
+ * n_tokens == 0 is a no-op. */
+int tq_get_values(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_tokens, float* out,
+                  void* stream);
+
+/* The same reconstruction of cached keys from their stage-1 codes and norms,
+ * ||k|| R^T c[idx] (the MSE part; the QJL sign bits estimate inner products
+ * and do not reconstruct the residual).  Same arguments and errors. */
+int tq_get_keys(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_tokens, float* out,
+                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

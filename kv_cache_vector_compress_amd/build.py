@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
-SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_compress.hip", "tq_attention.hip", "tq_general.hip"]
+SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_compress.hip", "tq_attention.hip", "tq_general.hip",
+           "tq_dequant.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -163,7 +163,7 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
     }
   }
 
-  std::call_once(g_init_flag, [] { g_init_rc = compress_device_init() | attention_device_init(); });
+  std::call_once(g_init_flag, [] { g_init_rc = compress_device_init() | attention_device_init() | dequant_device_init(); });
   if (g_init_rc != 0) return fail(TQ_EDEVICE, "tq_create: HIP device initialisation failed");
 
   tq_ctx* c = new tq_ctx();
@@ -408,6 +408,44 @@ int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dt
                                workspace, stream);
   }
   return rc ? fail(rc, "tq_attend: launch failed (%d)", rc) : TQ_OK;
+}
+
+static int get_common(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_tokens, const float* out,
+                      int bits, const char* fn) {
+  int rc = check_cache(ctx, cache, fn);
+  if (rc) return rc;
+  if (n_tokens < 0) return fail(TQ_EINVAL, "%s: n_tokens %lld < 0", fn, (long long)n_tokens);
+  if (pos < 0 || pos > cache->capacity || n_tokens > cache->capacity - pos)
+    return fail(TQ_ECAPACITY, "%s: tokens [%lld, %lld) exceed capacity %lld", fn, (long long)pos,
+                (long long)(pos + n_tokens), (long long)cache->capacity);
+  if (n_tokens > 0 && !out) return fail(TQ_EINVAL, "%s: out is NULL", fn);
+  if (n_tokens > 0 && !aligned16(out)) return fail(TQ_EINVAL, "%s: out must be 16-byte aligned", fn);
+  if (!ctx->loaded[bits]) return fail(TQ_ENOCODEBOOK, "%s: no %d-bit codebook loaded", fn, bits);
+  return TQ_OK;
+}
+
+static int get_vectors(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_tokens, float* out,
+                       void* stream, bool keys, const char* fn) {
+  clear_error();
+  const int bits = ctx ? (keys ? ctx->cfg.key_bits : ctx->cfg.value_bits) : 1;
+  int rc = get_common(ctx, cache, pos, n_tokens, out, bits, fn);
+  if (rc) return rc;
+  if (n_tokens == 0) return TQ_OK;
+  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "%s: hipSetDevice failed", fn);
+  rc = launch_dequant(ctx->mats, ctx->cb[bits], bits, ctx->cfg.head_dim, ctx->cfg.proj_dim, keys,
+                      cache->key_records, cache->value_blocks, cache->capacity, cache->n_seq, pos, n_tokens, out,
+                      stream);
+  return rc ? fail(rc, "%s: launch failed (%d)", fn, rc) : TQ_OK;
+}
+
+int tq_get_values(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_tokens, float* out,
+                  void* stream) {
+  return get_vectors(ctx, cache, pos, n_tokens, out, stream, false, "tq_get_values");
+}
+
+int tq_get_keys(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_tokens, float* out,
+                void* stream) {
+  return get_vectors(ctx, cache, pos, n_tokens, out, stream, true, "tq_get_keys");
 }
 
 }  // extern "C"

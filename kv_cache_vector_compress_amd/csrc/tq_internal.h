@@ -51,6 +51,10 @@ struct AppendShape {
 
 int launch_compress_keys(const Matrices& mats, const CodebookDev& cb, int bits, int m,
                          const AppendShape& s, void* key_records, void* stream);
+int launch_dequant(const Matrices& mats, const CodebookDev& cb, int bits, int d, int m, bool keys,
+                   const void* key_records, const void* value_blocks, int64_t capacity, int n_seq, int64_t pos,
+                   int64_t n_tokens, float* out, void* stream);
+int dequant_device_init();
 int launch_compress_values(const Matrices& mats, const CodebookDev& cb, int bits,
                            const AppendShape& s, void* value_blocks, void* stream);
 

@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         "tq_append_value": (ctypes.c_int, [P, VIEW, P, I32, I64, I64, P]),
         "tq_attention_scores": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, P, P, SZ, P]),
         "tq_attend": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, ctypes.c_float, P, P, SZ, P]),
+        "tq_get_values": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
+        "tq_get_keys": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -260,6 +262,24 @@ class KVCache:
         _check(lib().tq_attend(self.ctx.handle, ctypes.byref(self.view), _dev(q, "q"), _dtype_code(q), G,
                                n_tokens, float(scale), _dev(out, "out"), ctypes.c_void_p(ws.data_ptr()),
                                ws.numel(), _stream_ptr(stream)))
+        return out
+
+    # reconstruction ------------------------------------------------------------
+    def get_values(self, pos: int, n_tokens: int, out=None, stream=None):
+        """Dequantised values ||v|| R^T c[idx] of tokens [pos, pos + n_tokens): fp32 (n_seq, n_tokens, d)."""
+        return self._get(lib().tq_get_values, pos, n_tokens, out, stream)
+
+    def get_keys(self, pos: int, n_tokens: int, out=None, stream=None):
+        """Stage-1 (MSE) reconstruction of the keys, ||k|| R^T c[idx]: fp32 (n_seq, n_tokens, d)."""
+        return self._get(lib().tq_get_keys, pos, n_tokens, out, stream)
+
+    def _get(self, fn, pos, n_tokens, out, stream):
+        torch = _torch()
+        if out is None:
+            out = torch.empty((self.n_seq, n_tokens, self.ctx.cfg.head_dim), dtype=torch.float32,
+                              device=self.key_records.device)
+        _check(fn(self.ctx.handle, ctypes.byref(self.view), pos, n_tokens,
+                  _dev(out, "out") if n_tokens > 0 else None, _stream_ptr(stream)))
         return out
 
     # raw views for inspection ------------------------------------------------

@@ -12,7 +12,12 @@ The acceptance rules (stated once here, used by every parity test):
   * ||k||, ||v||, gamma: 1e-6 relative;
   * scores: |est_gpu - est_oracle| <= 2e-3 ||q|| ||k||;
   * attention output: ||out_gpu - out_oracle|| / ||out_oracle|| <= 5e-3 per
-    (slot, query head).
+    (slot, query head);
+  * reconstruction ||x|| R^T c[idx] (tq_get_keys / tq_get_values): every
+    element within 1e-5 ||x|| of the oracle's.  The kernel sums d fp32
+    products of R and the fp32 centroid times the norm: each carries a
+    rounding of 2^-24, so the error is near sqrt(d) 2^-24 ||x|| <= 2e-6 ||x||
+    at d = 1024 (the centroids in fp32 add 2^-24 relative).
 """
 from __future__ import annotations
 
@@ -25,6 +30,7 @@ FLIP_FRAC = 1e-4
 NORM_RTOL = 1e-6
 SCORE_TOL = 2e-3
 ATTEND_TOL = 5e-3
+DEQ_TOL = 1e-5
 
 
 def near_boundary(y: np.ndarray, beta: np.ndarray) -> np.ndarray:
@@ -96,3 +102,20 @@ def unpack_gpu_keys(cache, d, m, bits, n_tok):
 
 def unpack_gpu_values(cache, d, bits, n_tok):
     return O.unpack_values(cache.value_words(), d, bits, n_tokens=n_tok)
+
+
+def check_dequant(gpu_out, ref_out, norms, tol=DEQ_TOL, skip_tokens=None):
+    """Max over elements of |x^_gpu - x^_oracle| / ||x|| (rows of zero norm
+    must be exactly 0); asserts it is <= tol.  skip_tokens: (n_seq, T) mask
+    of tokens left out (index flips when comparing against the oracle's
+    own codes)."""
+    err = np.abs(gpu_out.astype(np.float64) - ref_out)
+    n = norms.astype(np.float64)[..., None]
+    zero = (n == 0)[..., 0]
+    assert not err[zero].any(), "a zero-norm row did not reconstruct to 0"
+    rel = np.where(n > 0, err / np.where(n > 0, n, 1.0), 0.0).max(axis=-1)
+    if skip_tokens is not None:
+        rel = np.where(skip_tokens, 0.0, rel)
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= tol, f"reconstruction error {worst:.3g} ||x|| > {tol}"
+    return worst

@@ -337,3 +337,54 @@ def test_error_paths_leave_buffers_untouched():
     assert bool((cache.key_records == canary).all())
     ctx.close()
     ctx2.close()
+
+
+@pytest.mark.parametrize("d,m,kb,vb,T,chunks,rng", [
+    (128, 64, 3, 3, 300, [37, 263], (0, 300)),
+    (128, 64, 3, 3, 300, [300], (37, 200)),
+    (128, 64, 1, 2, 200, [129, 71], (5, 190)),
+    (128, 128, 4, 4, 160, [160], (0, 160)),
+    (256, 128, 2, 3, 200, [200], (11, 170)),
+    (1024, 512, 4, 4, 40, [40], (0, 40)),
+])
+def test_reconstruction_matches_oracle(d, m, kb, vb, T, chunks, rng):
+    """tq_get_keys / tq_get_values (TurboQuantMSE.dequantize,
+    TurboQuantKVCache.get_values): ||x|| R^T c[idx] for a token range,
+    against the oracle's dequantize_values on the GPU's own codes and, for
+    tokens without an index flip, on the oracle's codes."""
+    n_seq = 2
+    K = np.stack([synth.kv_slot(70, s, s, T, d) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(71, s, s, T, d) for s in range(n_seq)])
+    K[1, 3] = 0  # a zero row reconstructs to 0
+    _say("reconstruction", (d, m, kb, vb, T, rng))
+    ctx, R, S = make_ctx(d, m, kb, vb)
+    cache = tq.KVCache(ctx, n_seq, -(-T // 128) * 128)
+    pos = 0
+    for n in chunks:
+        cache.append_key(torch.from_numpy(np.ascontiguousarray(K[:, pos:pos + n])).cuda(), pos)
+        cache.append_value(torch.from_numpy(np.ascontiguousarray(V[:, pos:pos + n])).cuda(), pos)
+        pos += n
+    p0, nt = rng
+    gk_out = cache.get_keys(p0, nt).cpu().numpy()
+    gv_out = cache.get_values(p0, nt).cpu().numpy()
+    torch.cuda.synchronize()
+    kbeta, kc = O.lloyd_max_codebook(d, kb)
+    vbeta, vc = O.lloyd_max_codebook(d, vb)
+    sl = lambda dct: {k: v[:, p0:p0 + nt] for k, v in dct.items()}
+    gk = sl(P.unpack_gpu_keys(cache, d, m, kb, T))
+    gv = sl(P.unpack_gpu_values(cache, d, vb, T))
+    st = {"keys_gpu_codes": P.check_dequant(gk_out, O.dequantize_values(R, kc, gk), gk["norm"]),
+          "values_gpu_codes": P.check_dequant(gv_out, O.dequantize_values(R, vc, gv), gv["norm"])}
+    ref_k = sl(O.compress_keys(K, R, S, kbeta, kc))
+    ref_v = sl(O.compress_values(V, R, vbeta, vc))
+    st["keys_end_to_end"] = P.check_dequant(gk_out, O.dequantize_values(R, kc, ref_k), ref_k["norm"],
+                                            skip_tokens=(gk["idx"] != ref_k["idx"]).any(-1))
+    st["values_end_to_end"] = P.check_dequant(gv_out, O.dequantize_values(R, vc, ref_v), ref_v["norm"],
+                                              skip_tokens=(gv["idx"] != ref_v["idx"]).any(-1))
+    # an empty range is a no-op; a range past the capacity is rejected
+    cache.get_values(0, 0)
+    with pytest.raises(tq.TQError) as e:
+        cache.get_keys(cache.capacity - 3, 4)
+    assert e.value.code == -2
+    _say(st)
+    ctx.close()
