@@ -221,6 +221,27 @@ int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dt
               int64_t n_tokens, float scale, float* out, void* workspace, size_t workspace_bytes,
               void* stream);
 
+/* ---- vector search ----------------------------------------------------------- */
+
+/* Device workspace bytes tq_topk_scores needs (query operands and per-wave
+ * candidate lists).  0 on invalid arguments (cfg NULL/invalid, n_seq < 1,
+ * G not in 1..512, n_tokens < 1, k not in 1..16). */
+size_t tq_topk_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, int64_t n_tokens, int32_t k);
+
+/* The k best tokens of each query by the asymmetric score estimate, without
+ * writing the n_seq x G x n_tokens scores (inner-product search over a
+ * compressed database: ai-manual.ru article, Где TurboQuant выстреливает;
+ * jansverre.net post, Hvem er dette nyttig for?).  The estimate is the one
+ * tq_attention_scores returns.  top_scores: device fp32 [n_seq][G][k],
+ * top_index: device int32 [n_seq][G][k] (token positions in the slot),
+ * ordered by score descending, equal scores by position ascending; when
+ * n_tokens < k the rest is (-inf, -1).  q as for tq_attention_scores,
+ * 1 <= G <= 512, 1 <= k <= 16.  workspace >= tq_topk_workspace_bytes.
+ * Errors: TQ_EINVAL, TQ_ENOCODEBOOK, TQ_EWORKSPACE, TQ_EDEVICE. */
+int tq_topk_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
+                   int64_t n_tokens, int32_t k, float* top_scores, int32_t* top_index, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* ---- reconstruction (not on the attention path) --------------------------- */
 
 /* Stage-1 reconstruction of cached values, x^ = ||v|| R^T c[idx]

@@ -163,7 +163,8 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
     }
   }
 
-  std::call_once(g_init_flag, [] { g_init_rc = compress_device_init() | attention_device_init() | dequant_device_init(); });
+  std::call_once(g_init_flag, [] { g_init_rc = compress_device_init() | attention_device_init() | dequant_device_init() |
+                                     topk_device_init(); });
   if (g_init_rc != 0) return fail(TQ_EDEVICE, "tq_create: HIP device initialisation failed");
 
   tq_ctx* c = new tq_ctx();
@@ -435,6 +436,39 @@ static int get_vectors(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int
   rc = launch_dequant(ctx->mats, ctx->cb[bits], bits, ctx->cfg.head_dim, ctx->cfg.proj_dim, keys,
                       cache->key_records, cache->value_blocks, cache->capacity, cache->n_seq, pos, n_tokens, out,
                       stream);
+  return rc ? fail(rc, "%s: launch failed (%d)", fn, rc) : TQ_OK;
+}
+
+size_t tq_topk_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, int64_t n_tokens, int32_t k) {
+  if (!cfg || check_config(cfg) != TQ_OK || n_seq < 1 || G < 1 || G > kMaxGeneralHeads || n_tokens < 1 || k < 1 ||
+      k > kTopkMax)
+    return 0;
+  return topk_plan(cfg->head_dim, cfg->proj_dim, n_seq, G, n_tokens, k).total;
+}
+
+int tq_topk_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
+                   int64_t n_tokens, int32_t k, float* top_scores, int32_t* top_index, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* fn = "tq_topk_scores";
+  int rc = check_cache(ctx, cache, fn);
+  if (rc) return rc;
+  if (dtype != TQ_F16 && dtype != TQ_F32) return fail(TQ_EINVAL, "%s: dtype %d", fn, dtype);
+  if (G < 1 || G > kMaxGeneralHeads) return fail(TQ_EINVAL, "%s: G %d not in 1..%d", fn, G, kMaxGeneralHeads);
+  if (k < 1 || k > kTopkMax) return fail(TQ_EINVAL, "%s: k %d not in 1..%d", fn, k, kTopkMax);
+  if (n_tokens < 1 || n_tokens > cache->capacity)
+    return fail(TQ_EINVAL, "%s: n_tokens %lld not in [1, capacity]", fn, (long long)n_tokens);
+  if (!q || !top_scores || !top_index || !workspace) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  if (!aligned16(q) || !aligned16(top_scores) || !aligned16(top_index) || !aligned16(workspace))
+    return fail(TQ_EINVAL, "%s: q, outputs and workspace must be 16-byte aligned", fn);
+  if (!ctx->loaded[ctx->cfg.key_bits])
+    return fail(TQ_ENOCODEBOOK, "%s: no %d-bit key codebook loaded", fn, ctx->cfg.key_bits);
+  const size_t need = topk_plan(ctx->cfg.head_dim, ctx->cfg.proj_dim, cache->n_seq, G, n_tokens, k).total;
+  if (workspace_bytes < need) return fail(TQ_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "%s: hipSetDevice failed", fn);
+  AttnShape s{q, dtype, G, n_tokens, cache->capacity, cache->n_seq};
+  rc = launch_topk(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.head_dim, ctx->cfg.proj_dim,
+                   s, k, cache->key_records, top_scores, top_index, workspace, stream);
   return rc ? fail(rc, "%s: launch failed (%d)", fn, rc) : TQ_OK;
 }
 

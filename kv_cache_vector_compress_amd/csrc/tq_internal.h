@@ -121,4 +121,16 @@ int launch_general_attend(const Matrices& mats, const CodebookDev& cbk, int kbit
 int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, int m,
                           const AttnShape& s, const void* key_records, float* scores, void* ws, void* stream);
 
+// Fused inner-product top-k over the packed keys (tq_topk.hip).
+constexpr int kTopkMax = 16;  // largest k of tq_topk_scores
+struct TopkPlan {
+  int HG, n_qblk, n_ranges, n_lists;
+  int64_t tiles_per_range;
+  size_t q_bytes, qn_bytes, cand_bytes, total;
+};
+TopkPlan topk_plan(int d, int m, int n_seq, int G, int64_t n_tokens, int k);
+int topk_device_init();
+int launch_topk(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, int m, const AttnShape& s, int k,
+                const void* key_records, float* top_s, int32_t* top_i, void* ws, void* stream);
+
 }  // namespace tq

@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         "tq_append_value": (ctypes.c_int, [P, VIEW, P, I32, I64, I64, P]),
         "tq_attention_scores": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, P, P, SZ, P]),
         "tq_attend": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, ctypes.c_float, P, P, SZ, P]),
+        "tq_topk_workspace_bytes": (SZ, [CFG, I32, I32, I64, I32]),
+        "tq_topk_scores": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, I32, P, P, P, SZ, P]),
         "tq_get_values": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
         "tq_get_keys": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
     }
@@ -263,6 +265,22 @@ class KVCache:
                                n_tokens, float(scale), _dev(out, "out"), ctypes.c_void_p(ws.data_ptr()),
                                ws.numel(), _stream_ptr(stream)))
         return out
+
+    def topk(self, q, n_tokens: int, k: int = 10, stream=None):
+        """The k best tokens per query by the score estimate (no score matrix):
+        (scores fp32 (n_seq, G, k), indices int32 (n_seq, G, k))."""
+        torch = _torch()
+        G = q.shape[1]
+        need = lib().tq_topk_workspace_bytes(ctypes.byref(self.ctx.cfg), self.n_seq, G, n_tokens, k)
+        if need == 0:
+            raise TQError(-1, "tq_topk_workspace_bytes: invalid arguments")
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        top_s = torch.empty((self.n_seq, G, k), dtype=torch.float32, device=q.device)
+        top_i = torch.empty((self.n_seq, G, k), dtype=torch.int32, device=q.device)
+        _check(lib().tq_topk_scores(self.ctx.handle, ctypes.byref(self.view), _dev(q, "q"), _dtype_code(q), G,
+                                    n_tokens, k, _dev(top_s, "top_scores"), _dev(top_i, "top_index"),
+                                    ctypes.c_void_p(ws.data_ptr()), need, _stream_ptr(stream)))
+        return top_s, top_i
 
     # reconstruction ------------------------------------------------------------
     def get_values(self, pos: int, n_tokens: int, out=None, stream=None):

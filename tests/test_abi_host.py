@@ -126,8 +126,19 @@ def test_hot_path_entry_points_reject_null_context():
                                    ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 20, None) == -1
     assert lib.tq_attend(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 4, 1, 0.0,
                          ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 20, None) == -1
+    assert lib.tq_topk_scores(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 4, 1, 10, ctypes.c_void_p(16),
+                              ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 20, None) == -1
     assert lib.tq_get_values(None, ctypes.byref(view), 0, 1, ctypes.c_void_p(16), None) == -1
     assert lib.tq_get_keys(None, ctypes.byref(view), 0, 1, ctypes.c_void_p(16), None) == -1
     assert lib.tq_codebook_load(None, 3, None, None) == -1
     assert lib.tq_destroy(None) == 0
 
+
+
+def test_topk_workspace_rejects_bad_arguments():
+    cfg = tq.Config(128, 64, 3, 3)
+    ws = lambda *a: tq.lib().tq_topk_workspace_bytes(ctypes.byref(cfg), *a)
+    assert ws(1, 512, 2_000_000, 10) > 0
+    assert ws(1, 4, 100, 16) > 0
+    for bad in [(0, 4, 100, 10), (1, 0, 100, 10), (1, 513, 100, 10), (1, 4, 0, 10), (1, 4, 100, 0), (1, 4, 100, 17)]:
+        assert ws(*bad) == 0, bad

@@ -388,3 +388,54 @@ def test_reconstruction_matches_oracle(d, m, kb, vb, T, chunks, rng):
     assert e.value.code == -2
     _say(st)
     ctx.close()
+
+
+def _topk_reference(scores, k):
+    """Indices of the k best scores per row by (score desc, index asc)."""
+    n = scores.shape[-1]
+    order = np.lexsort((np.broadcast_to(np.arange(n), scores.shape), -scores), axis=-1)
+    return order[..., :k]
+
+
+@pytest.mark.parametrize("d,m,b,n_seq,N,G,k", [
+    (128, 64, 3, 2, 3000, 40, 10),
+    (128, 64, 2, 1, 700, 16, 16),
+    (256, 128, 3, 2, 1000, 20, 1),
+    (1024, 512, 4, 1, 2500, 64, 10),
+    (128, 64, 3, 1, 5, 4, 10),
+])
+def test_topk_matches_scores(d, m, b, n_seq, N, G, k):
+    """tq_topk_scores: the k best tokens of each query (vector search over the
+    packed keys) equal the top-k of tq_attention_scores' own output (same
+    estimate, same order: score desc, position asc), and form a valid top-k
+    of the oracle's estimates within the score tolerance."""
+    _say("topk", (d, m, b, n_seq, N, G, k))
+    X = np.stack([synth.vector_database(N, d, seed=80 + s) for s in range(n_seq)])
+    Q = np.stack([synth.unit_gaussian(G, d, seed=90 + s) for s in range(n_seq)])
+    ctx, R, S = make_ctx(d, m, b, b)
+    cache = tq.KVCache(ctx, n_seq, -(-N // 128) * 128)
+    cache.append_key(torch.from_numpy(X).cuda(), 0)
+    qt = torch.from_numpy(Q).cuda()
+    ts, ti = cache.topk(qt, N, k)
+    sc = cache.attention_scores(qt, N)
+    ts, ti, sc = ts.cpu().numpy(), ti.cpu().numpy(), sc.cpu().numpy()
+    kk = min(k, N)
+    ref_i = _topk_reference(sc, kk)
+    assert np.array_equal(ti[..., :kk], ref_i), "top-k indices differ from the materialised scores' top-k"
+    assert np.array_equal(ts[..., :kk], np.take_along_axis(sc, ref_i, -1)), "top-k scores differ"
+    if kk < k:
+        assert np.all(ti[..., kk:] == -1) and np.all(np.isneginf(ts[..., kk:]))
+    # validity against the oracle's estimates on the GPU's codes
+    beta, c = O.lloyd_max_codebook(d, b)
+    gk = P.unpack_gpu_keys(cache, d, m, b, N)
+    ref = O.key_scores(Q.astype(np.float64), R, S, c, gk)
+    qn = np.linalg.norm(Q.astype(np.float64), axis=-1)[..., None]
+    kn = np.linalg.norm(X.astype(np.float64), axis=-1)[:, None, :]
+    tol = P.SCORE_TOL * qn * kn
+    picked = np.zeros(ref.shape, dtype=bool)
+    np.put_along_axis(picked, ti[..., :kk].astype(np.int64), True, axis=-1)
+    lo = np.min(np.where(picked, ref + tol, np.inf), axis=-1)
+    hi = np.max(np.where(picked, -np.inf, ref - tol), axis=-1)
+    assert np.all(hi <= lo), "a token left out beats a returned one by more than the score tolerance"
+    _say({"worst_margin": float(np.max(hi - lo)) if kk < N else None})
+    ctx.close()
