@@ -164,7 +164,7 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   }
 
   std::call_once(g_init_flag, [] { g_init_rc = compress_device_init() | attention_device_init() | dequant_device_init() |
-                                     topk_device_init(); });
+                                     topk_device_init() | small_device_init(); });
   if (g_init_rc != 0) return fail(TQ_EDEVICE, "tq_create: HIP device initialisation failed");
 
   tq_ctx* c = new tq_ctx();
@@ -310,7 +310,13 @@ int tq_append_key(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_
   if (n_new == 0) return TQ_OK;
   AppendShape s{k, dtype, n_new, pos, cache->capacity, cache->n_seq};
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_append_key: hipSetDevice failed");
-  if (fast_keys(ctx->cfg))
+  // a decode step on the general path: one launch instead of the tiled
+  // norm / rotation / projection kernels (with head_dim 128 the single
+  // matrix-core kernel is as quick for a few tokens)
+  if (n_new <= kSmallAppend && !fast_keys(ctx->cfg))
+    rc = launch_small_keys(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.head_dim,
+                           ctx->cfg.proj_dim, s, cache->key_records, stream);
+  else if (fast_keys(ctx->cfg))
     rc = launch_compress_keys(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.proj_dim, s,
                               cache->key_records, stream);
   else
@@ -327,7 +333,10 @@ int tq_append_value(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int3
   if (n_new == 0) return TQ_OK;
   AppendShape s{v, dtype, n_new, pos, cache->capacity, cache->n_seq};
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_append_value: hipSetDevice failed");
-  if (fast_values(ctx->cfg))
+  if (n_new <= kSmallAppend)  // a decode step: no tile set-up
+    rc = launch_small_values(ctx->mats, ctx->cb[ctx->cfg.value_bits], ctx->cfg.value_bits, ctx->cfg.head_dim, s,
+                             cache->value_blocks, stream);
+  else if (fast_values(ctx->cfg))
     rc = launch_compress_values(ctx->mats, ctx->cb[ctx->cfg.value_bits], ctx->cfg.value_bits, s,
                                 cache->value_blocks, stream);
   else

@@ -121,6 +121,15 @@ int launch_general_attend(const Matrices& mats, const CodebookDev& cbk, int kbit
 int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, int m,
                           const AttnShape& s, const void* key_records, float* scores, void* ws, void* stream);
 
+// Appends of at most kSmallAppend tokens per slot (tq_small.hip): fp32
+// vector arithmetic with R and S from L2, for any shape.
+constexpr int kSmallAppend = 16;
+int small_device_init();
+int launch_small_keys(const Matrices& mats, const CodebookDev& cb, int bits, int d, int m, const AppendShape& s,
+                      void* key_records, void* stream);
+int launch_small_values(const Matrices& mats, const CodebookDev& cb, int bits, int d, const AppendShape& s,
+                        void* value_blocks, void* stream);
+
 // Fused inner-product top-k over the packed keys (tq_topk.hip).
 constexpr int kTopkMax = 16;  // largest k of tq_topk_scores
 struct TopkPlan {

@@ -439,3 +439,25 @@ def test_topk_matches_scores(d, m, b, n_seq, N, G, k):
     assert np.all(hi <= lo), "a token left out beats a returned one by more than the score tolerance"
     _say({"worst_margin": float(np.max(hi - lo)) if kk < N else None})
     ctx.close()
+
+
+@pytest.mark.parametrize("d,m,kb,vb,dtype", [
+    (128, 64, 3, 3, np.float16),
+    (128, 128, 4, 2, np.float32),
+    (256, 128, 2, 3, np.float16),
+    (1024, 512, 1, 4, np.float32),
+])
+def test_small_appends_decode_like(d, m, kb, vb, dtype):
+    """Appends of 1..16 tokens (the decode-step path: fp32 vector arithmetic,
+    no matrix-core tiles) between bulk appends, crossing 128-token block
+    boundaries, with zero key/value rows inside the small chunks; every code,
+    sign, norm, score and the attention output against the oracle."""
+    T, n_seq, G = 300, 2, 4
+    K = np.stack([synth.kv_slot(100, s, s, T, d, dtype=dtype) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(101, s, s, T, d, dtype=dtype) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(102, s, s, G, d, dtype=dtype) for s in range(n_seq)])
+    K[0, 131] = 0  # inside the 16-token chunk at 131
+    V[1, 128] = 0  # the one-token chunk at 128
+    chunks = [120, 8, 1, 1, 1, 16, 3, 5, 1, 144]
+    _say("small appends", (d, m, kb, vb, np.dtype(dtype).name), chunks)
+    _say(run_case(K, V, Q, kb=kb, vb=vb, m=m, chunks=chunks))
