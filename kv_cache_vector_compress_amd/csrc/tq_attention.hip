@@ -17,6 +17,8 @@
 // query head (online softmax), and accumulates sum_t p_t ||v_t|| c[idx_t] in
 // the rotated domain with the matrix cores.  A second kernel merges the
 // per-wave partials (log-sum-exp) and applies R^T once per query head.
+#include <type_traits>
+
 #include "tq_device.h"
 
 namespace tq {
@@ -343,9 +345,11 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
     load_values(vcur, b_begin);
     load_keys(kcur, b_begin * kBlockTokens);
   }
-  for (int blk = b_begin; blk < b_end; ++blk) {
+  // One 128-token block.  MASK (the block holds the end of the cache) is a
+  // compile-time flag so that full blocks carry no per-token masking code.
+  auto run_block = [&](int blk, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int tok0 = blk * kBlockTokens;
-    const bool full = tok0 + kBlockTokens <= n_tok;  // wave-uniform
     const bool more = blk + 1 < b_end;
     BlockValues<BV> vnext;
     if (more) load_values(vnext, blk + 1);  // in flight during this block
@@ -353,13 +357,11 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
     // exponent of the norms seen so far, so P stays in fp16 range whatever
     // the norms' scale; the accumulator is rescaled when ve grows.
     float x0 = vcur.vn.x, x1 = vcur.vn.y;
-    if (!full) {
+    if constexpr (MASK) {
       x0 = tok0 + 2 * lane < n_tok ? x0 : 0.f;
       x1 = tok0 + 2 * lane + 1 < n_tok ? x1 : 0.f;
     }
-    float bmax = fmaxf(x0, x1);
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) bmax = fmaxf(bmax, shfl_xor(bmax, sh));
+    const float bmax = wave_max(fmaxf(x0, x1));
     int e_blk = 0;
     frexpf(bmax, &e_blk);
     if (e_blk > ve) {
@@ -395,17 +397,16 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float l = sc[u][i] * nk[u][i] * qsc;
-          if (!full) l = tok0 + 16 * (2 * step + u) + 4 * q + i < n_tok ? l : -INFINITY;
+          if constexpr (MASK) l = tok0 + 16 * (2 * step + u) + 4 * q + i < n_tok ? l : -INFINITY;
           lg[u][i] = l;
           cmax = fmaxf(cmax, l);
         }
-      cmax = fmaxf(cmax, shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, shfl_xor(cmax, 32));
+      cmax = max_xor16_32(cmax);
       // Online softmax with lazy rescaling: the accumulator is rescaled only
       // when some head's running maximum grows (rare after the first blocks).
       if (__any(cmax > m_run)) {
         const float m_new = fmaxf(m_run, cmax);
-        const float alpha = exp2f(m_run - m_new);  // 0 on the first step
+        const float alpha = exp2_hw(m_run - m_new);  // 0 on the first step
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[nt] *= alpha;
         l_run *= alpha;
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
-          const float p0 = exp2f(lg[u][2 * i2] - m_run), p1 = exp2f(lg[u][2 * i2 + 1] - m_run);
+          const float p0 = exp2_hw(lg[u][2 * i2] - m_run), p1 = exp2_hw(lg[u][2 * i2 + 1] - m_run);
           psum += p0 + p1;
           pw[2 * u + i2] = pack_h2(p0 * vn[u][2 * i2], p1 * vn[u][2 * i2 + 1]);
         }
@@ -435,6 +436,12 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
       kcur = knext;
     }
     vcur = vnext;
+  };
+  for (int blk = b_begin; blk < b_end; ++blk) {
+    if ((blk + 1) * kBlockTokens <= n_tok)  // wave-uniform
+      run_block(blk, std::false_type{});
+    else
+      run_block(blk, std::true_type{});
   }
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);

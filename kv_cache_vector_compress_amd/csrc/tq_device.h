@@ -245,6 +245,34 @@ __device__ __forceinline__ HiLo split2(float x0, float x1) {
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// 2^x on the hardware exponential unit (one v_exp_f32, no range fix-ups):
+// results below the normal fp32 range come out as 0, which softmax weights
+// and rescale factors tolerate.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-lane maxima without LDS.  dpp_f<CTRL> reads another lane of the same
+// 16-lane row (quad_perm 0xB1 / 0x4E = lane ^ 1 / ^ 2, 0x124 / 0x128 = row
+// rotate by 4 / 8).  v_permlane16_swap and v_permlane32_swap exchange whole
+// rows: with both operands v, one result holds v of lane l ^ 16 (or l ^ 32)
+// where the other holds v of lane l, so their maximum reduces across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x128>(v));
+  return max_xor16_32(v);
+}
+
 // Runtime-slot form of put_sel4 (the switch folds away when s is a constant).
 template <int B>
 __device__ __forceinline__ void put_sel4_rt(uint32_t (&w)[B], int s, uint32_t x) {

@@ -855,7 +855,7 @@ __global__ __launch_bounds__(256) void gen_attend_kernel(const GenAttendArgs a) 
       cmax = fmaxf(cmax, shfl_xor(cmax, 32));
       if (__any(cmax > m_run)) {
         const float m_new = fmaxf(m_run, cmax);
-        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+        const float alpha = m_new == -INFINITY ? 1.f : exp2_hw(m_run - m_new);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[nt] *= alpha;
         l_run *= alpha;
@@ -868,8 +868,8 @@ __global__ __launch_bounds__(256) void gen_attend_kernel(const GenAttendArgs a) 
         const f4 vn = *(const f4*)&vsh[wave][16 * (2 * step + uu) + 4 * q];
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
-          const float p0 = m_run == -INFINITY ? 0.f : exp2f(lg[uu][2 * i2] - m_run);
-          const float p1 = m_run == -INFINITY ? 0.f : exp2f(lg[uu][2 * i2 + 1] - m_run);
+          const float p0 = m_run == -INFINITY ? 0.f : exp2_hw(lg[uu][2 * i2] - m_run);
+          const float p1 = m_run == -INFINITY ? 0.f : exp2_hw(lg[uu][2 * i2 + 1] - m_run);
           psum += p0 + p1;
           pw[2 * uu + i2] = pack_h2f(p0 * vn[2 * i2], p1 * vn[2 * i2 + 1]);
         }
