@@ -64,16 +64,26 @@ __device__ __forceinline__ void load_key(KeyTile<B, M>& k, __amdgpu_buffer_rsrc_
 }
 
 // acc[i] = (unscaled, unnormalised) score of token row 4q+i of the tile for
-// query head (lane % 16).  est = acc * ||k|| * ||q||.
-template <int B, int M>
+// query head (lane % 16).  est = acc * ||k|| * ||q||.  With PT (3-bit keys)
+// the centroids come from the LDS pair tables and qb[0..3] must be in pair
+// order (to_pair_order).
+template <int B, int M, bool PT = false>
 __device__ __forceinline__ f4 key_tile_scores(const KeyTile<B, M>& k, const h8 (&qb)[4 + M / 32],
                                               const uint32_t (&tlo)[4], const uint32_t (&thi)[4], float kappa,
-                                              int sh0) {
+                                              int sh0, const PairTables* pt = nullptr) {
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-  acc = mfma(decode_pair<B, 0>(k.cw, tlo, thi), qb[0], acc);
-  acc = mfma(decode_pair<B, 2>(k.cw, tlo, thi), qb[1], acc);
-  acc = mfma(decode_pair<B, 4>(k.cw, tlo, thi), qb[2], acc);
-  acc = mfma(decode_pair<B, 6>(k.cw, tlo, thi), qb[3], acc);
+  if constexpr (PT) {
+    static_assert(B == 3, "pair tables hold 3-bit codes");
+    acc = mfma(decode_pair_lds<0>(k.cw, *pt), qb[0], acc);
+    acc = mfma(decode_pair_lds<1>(k.cw, *pt), qb[1], acc);
+    acc = mfma(decode_pair_lds<2>(k.cw, *pt), qb[2], acc);
+    acc = mfma(decode_pair_lds<3>(k.cw, *pt), qb[3], acc);
+  } else {
+    acc = mfma(decode_pair<B, 0>(k.cw, tlo, thi), qb[0], acc);
+    acc = mfma(decode_pair<B, 2>(k.cw, tlo, thi), qb[1], acc);
+    acc = mfma(decode_pair<B, 4>(k.cw, tlo, thi), qb[2], acc);
+    acc = mfma(decode_pair<B, 6>(k.cw, tlo, thi), qb[3], acc);
+  }
   const _Float16 gk = (_Float16)(k.g * kappa);
   const uint32_t gk2 = (uint32_t)__builtin_bit_cast(uint16_t, gk) * 0x00010001u;
 #pragma unroll
@@ -185,6 +195,12 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
   using Stage = KeyStage<RW, U>;
   __shared__ __align__(16) uint32_t kst[4][Stage::SLICE];  // per wave: the iteration's records
   __shared__ float nsh[4][16 * U];  // per wave: ||k|| of the iteration's tokens
+  // (byte-permute decoding: the LDS pair tables of the attend kernel add a
+  // second dependent LDS round trip after the staged record here and
+  // measured slower)
+  uint32_t tlo[4], thi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
@@ -195,9 +211,6 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
 #pragma unroll
   for (int kb = 0; kb < KBT; ++kb) qb[kb] = *(const h8*)(a.wq + (((int64_t)slot * KBT + kb) * 64 + lane) * 8);
   const float qn = a.wqn[slot * 16 + r16];
-  uint32_t tlo[4], thi[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; }
   const int sh0 = 15 - 8 * (q & 1);
   const int n_tok = (int)a.n_tokens;
   const int ntile = (n_tok + 15) >> 4;
@@ -289,6 +302,19 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   constexpr int BW = 4 * BV * kD + kBlockTokens;
   __shared__ float nsh[4][32];               // per wave: ||k|| of the step's 32 tokens
   __shared__ __align__(16) float vsh[4][kBlockTokens];  // per wave: the block's ||v||
+  // 3-bit keys / values decode through LDS pair tables
+  constexpr bool KPT = BK == 3, VPT = BV == 3;
+  __shared__ PairTables ktab, vtab;
+  uint32_t tlo[4], thi[4], vtlo[4], vthi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; vtlo[i] = a.vtlo[i]; vthi[i] = a.vthi[i];
+  }
+  if constexpr (KPT || VPT) {
+    if constexpr (KPT) fill_pair_tables(ktab, tlo, thi, threadIdx.x);
+    if constexpr (VPT) fill_pair_tables(vtab, vtlo, vthi, (int)threadIdx.x - 128);
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
@@ -299,12 +325,11 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   h8 qb[KBT];
 #pragma unroll
   for (int kb = 0; kb < KBT; ++kb) qb[kb] = *(const h8*)(a.wq + (((int64_t)slot * KBT + kb) * 64 + lane) * 8);
-  const float qsc = a.wqn[slot * 16 + r16] * a.scale2;
-  uint32_t tlo[4], thi[4], vtlo[4], vthi[4];
+  if constexpr (KPT) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; vtlo[i] = a.vtlo[i]; vthi[i] = a.vthi[i];
+    for (int kb = 0; kb < 4; ++kb) qb[kb] = to_pair_order(qb[kb]);
   }
+  const float qsc = a.wqn[slot * 16 + r16] * a.scale2;
   const int sh0 = 15 - 8 * (q & 1);
   const int n_tok = (int)a.n_tokens;
   const int nblk = (n_tok + kBlockTokens - 1) / kBlockTokens;
@@ -381,7 +406,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
       f4 sc[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        sc[u] = key_tile_scores<BK, M>(kcur.t[u], qb, tlo, thi, a.kappa, sh0);
+        sc[u] = key_tile_scores<BK, M, KPT>(kcur.t[u], qb, tlo, thi, a.kappa, sh0, &ktab);
         if (q == 0) nsh[wave][16 * u + r16] = kcur.t[u].n;
       }
       f4 nk[2], vn[2];
@@ -413,24 +438,37 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
         m_run = m_new;
       }
       float psum = 0.f;
-      u4 pw;
+      float pv[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const float p0 = exp2_hw(lg[u][2 * i2] - m_run), p1 = exp2_hw(lg[u][2 * i2 + 1] - m_run);
-          psum += p0 + p1;
-          pw[2 * u + i2] = pack_h2(p0 * vn[u][2 * i2], p1 * vn[u][2 * i2 + 1]);
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2_hw(lg[u][i] - m_run);
+          psum += p;
+          pv[u][i] = p * vn[u][i];
         }
       l_run += psum;
+      // P operand: slot order (tokens of tile 0, then tile 1) for byte-permute
+      // decoding, pair order (tile 0 / tile 1 of each row i) for the pair tables
+      u4 pw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pw[j] = VPT ? pack_h2(pv[0][j], pv[1][j]) : pack_h2(pv[j >> 1][2 * (j & 1)], pv[j >> 1][2 * (j & 1) + 1]);
       const h8 P = as_h8(pw);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         h8 A;
-        if (step == 0) A = decode_pair<BV, 0>(vcur.vw[nt], vtlo, vthi);
-        if (step == 1) A = decode_pair<BV, 2>(vcur.vw[nt], vtlo, vthi);
-        if (step == 2) A = decode_pair<BV, 4>(vcur.vw[nt], vtlo, vthi);
-        if (step == 3) A = decode_pair<BV, 6>(vcur.vw[nt], vtlo, vthi);
+        if constexpr (VPT) {
+          if (step == 0) A = decode_pair_lds<0>(vcur.vw[nt], vtab);
+          if (step == 1) A = decode_pair_lds<1>(vcur.vw[nt], vtab);
+          if (step == 2) A = decode_pair_lds<2>(vcur.vw[nt], vtab);
+          if (step == 3) A = decode_pair_lds<3>(vcur.vw[nt], vtab);
+        } else {
+          if (step == 0) A = decode_pair<BV, 0>(vcur.vw[nt], vtlo, vthi);
+          if (step == 1) A = decode_pair<BV, 2>(vcur.vw[nt], vtlo, vthi);
+          if (step == 2) A = decode_pair<BV, 4>(vcur.vw[nt], vtlo, vthi);
+          if (step == 3) A = decode_pair<BV, 6>(vcur.vw[nt], vtlo, vthi);
+        }
         acc[nt] = mfma(A, P, acc[nt]);
       }
       kcur = knext;

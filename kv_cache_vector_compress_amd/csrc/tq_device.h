@@ -179,6 +179,69 @@ __device__ __forceinline__ h8 decode_pair(const uint32_t (&w)[B], const uint32_t
   return as_h8(u4{r0, r1, r2, r3});
 }
 
+// ---- 3-bit code groups decoded through LDS pair tables ----------------------
+// A byte lane of a 3-bit group holds the codes of slots 2p and 2p + 1 in bits
+// 0-5 of word p (p < 3); slots 6 and 7 keep bits 0-1 in bits 6-7 of words 0
+// and 1 and bit 2 in bits 6 and 7 of word 2.  A 64-entry table of fp16 pairs
+// turns one 6-bit index into both centroids with one 4-byte LDS read, so a
+// pair of codes costs 1.5 ALU operations for p < 3 instead of 3 with byte
+// permutes.  The 64 entries of a table sit in distinct LDS banks, so lanes
+// only ever share a bank when they read the same entry (a broadcast).
+//   t01[e] = (c[e & 7], c[e >> 3])
+//   t67[e] = (c[(e & 3) | (e >> 2 & 4)], c[(e >> 2 & 3) | (e >> 3 & 4)]),
+//            e = w0 bits 6-7 | w1 bits 6-7 << 2 | w2 bits 6-7 << 4
+struct PairTables {
+  uint32_t t01[64];
+  uint32_t t67[64];
+};
+
+// Threads tid = 0..127 each write one entry (the caller synchronises).
+__device__ __forceinline__ void fill_pair_tables(PairTables& t, const uint32_t (&tlo)[4], const uint32_t (&thi)[4],
+                                                 int tid) {
+  auto c16 = [&](uint32_t v) -> uint32_t {  // fp16 bits of centroid v < 8
+    const uint32_t lo = (tlo[v >> 2] >> (8 * (v & 3))) & 0xFFu, hi = (thi[v >> 2] >> (8 * (v & 3))) & 0xFFu;
+    return lo | hi << 8;
+  };
+  const uint32_t e = (uint32_t)tid & 63;
+  if (tid >= 0 && tid < 64) t.t01[e] = c16(e & 7) | c16(e >> 3) << 16;
+  else if (tid >= 64 && tid < 128) t.t67[e] = c16((e & 3) | (e >> 2 & 4)) | c16((e >> 2 & 3) | (e >> 3 & 4)) << 16;
+}
+
+// Word whose byte i is the byte address 4 e of pair P's table entry for byte
+// lane i.
+template <int P>
+__device__ __forceinline__ uint32_t pair_addr4(const uint32_t (&w)[3]) {
+  if constexpr (P < 3) {
+    return (w[P] << 2) & 0xFCFCFCFCu;
+  } else {
+    return ((w[0] >> 4) & 0x0C0C0C0Cu) | ((w[1] >> 2) & 0x30303030u) | (w[2] & 0xC0C0C0C0u);
+  }
+}
+
+// The 8 centroids of slots 2P, 2P + 1 as one fp16 operand in pair order:
+// element 2 i = slot 2P, byte lane i; element 2 i + 1 = slot 2P + 1, lane i.
+template <int P>
+__device__ __forceinline__ h8 decode_pair_lds(const uint32_t (&w)[3], const PairTables& t) {
+  const uint32_t a = pair_addr4<P>(w);
+  const char* base = (const char*)(P < 3 ? t.t01 : t.t67);
+  // byte i of a, zero-extended, by one byte permute each (shift-and-mask
+  // forms get re-derived from w by the compiler at two operations apiece)
+  u4 r;
+  r[0] = *(const uint32_t*)(base + perm(0u, a, 0x0C0C0C00u));
+  r[1] = *(const uint32_t*)(base + perm(0u, a, 0x0C0C0C01u));
+  r[2] = *(const uint32_t*)(base + perm(0u, a, 0x0C0C0C02u));
+  r[3] = *(const uint32_t*)(base + perm(0u, a, 0x0C0C0C03u));
+  return as_h8(r);
+}
+
+// Reorder an operand built in slot order (elements 0-3 = slot 2P lanes 0-3,
+// 4-7 = slot 2P + 1) into the pair order of decode_pair_lds.
+__device__ __forceinline__ h8 to_pair_order(const h8& x) {
+  const u4 v = as_u4(x);
+  return as_h8(u4{perm(v[2], v[0], 0x05040100u), perm(v[2], v[0], 0x07060302u), perm(v[3], v[1], 0x05040100u),
+                  perm(v[3], v[1], 0x07060302u)});
+}
+
 // Lloyd-Max cell of y: idx = #{i : beta_i < y} by binary search over the
 // sorted boundaries (beta in registers / kernel arguments).
 template <int B>
