@@ -295,8 +295,23 @@ struct BlockValues {  // one 128-token value block as this lane needs it
   float2 vn;          // norms of block tokens 2 lane, 2 lane + 1
 };
 
-template <int BK, int BV, int M>
+// Scores of a 16-token tile come out as lane (q, r16) = column (query head)
+// r16, token rows 4q + i.  With G <= 4 (GC = 4) only columns 0..3 are real,
+// so before the softmax each lane (q, 4a + h) takes row 4q + a of column h
+// (three DPP row shifts): every lane then carries one real score per tile
+// and the softmax runs on a quarter of the values.  Three more row shifts
+// bring the weights back to the column lanes for the P operand.
+__device__ __forceinline__ float compact4(const f4& v) {
+  float x = v[0];
+  x = dpp_into<0x114, 0x2>(x, v[1]);
+  x = dpp_into<0x118, 0x4>(x, v[2]);
+  x = dpp_into<0x11C, 0x8>(x, v[3]);
+  return x;
+}
+
+template <int BK, int BV, int M, int GC>
 __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
+  static_assert(GC == 1 || GC == 4, "head compaction by 1 or 4");
   constexpr int KBT = 4 + M / 32;
   constexpr int RW = rec_words<BK, M>();
   constexpr int BW = 4 * BV * kD + kBlockTokens;
@@ -329,7 +344,8 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) qb[kb] = to_pair_order(qb[kb]);
   }
-  const float qsc = a.wqn[slot * 16 + r16] * a.scale2;
+  const int a4 = r16 >> 2;  // with GC = 4: this lane's row within a token quad
+  const float qsc = a.wqn[slot * 16 + (GC == 4 ? (r16 & 3) : r16)] * a.scale2;
   const int sh0 = 15 - 8 * (q & 1);
   const int n_tok = (int)a.n_tokens;
   const int nblk = (n_tok + kBlockTokens - 1) / kBlockTokens;
@@ -409,23 +425,41 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
         sc[u] = key_tile_scores<BK, M, KPT>(kcur.t[u], qb, tlo, thi, a.kappa, sh0, &ktab);
         if (q == 0) nsh[wave][16 * u + r16] = kcur.t[u].n;
       }
-      f4 nk[2], vn[2];
+      // NV score values per tile in this lane: rows 4q + i (GC = 1) or row
+      // 4q + a4 (GC = 4)
+      constexpr int NV = 4 / GC;
+      float nk[2][NV], vn[2][NV], lg[2][NV];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        nk[u] = *(const f4*)&nsh[wave][16 * u + 4 * q];
-        vn[u] = *(const f4*)&vsh[wave][16 * (2 * step + u) + 4 * q];
+        if constexpr (GC == 1) {
+          const f4 n4 = *(const f4*)&nsh[wave][16 * u + 4 * q];
+          const f4 v4 = *(const f4*)&vsh[wave][16 * (2 * step + u) + 4 * q];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            nk[u][i] = n4[i];
+            vn[u][i] = v4[i];
+            lg[u][i] = sc[u][i];
+          }
+        } else {
+          nk[u][0] = nsh[wave][16 * u + 4 * q + a4];
+          vn[u][0] = vsh[wave][16 * (2 * step + u) + 4 * q + a4];
+          lg[u][0] = compact4(sc[u]);
+        }
       }
-      float lg[2][4];
       float cmax = -INFINITY;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float l = sc[u][i] * nk[u][i] * qsc;
-          if constexpr (MASK) l = tok0 + 16 * (2 * step + u) + 4 * q + i < n_tok ? l : -INFINITY;
+        for (int i = 0; i < NV; ++i) {
+          float l = lg[u][i] * nk[u][i] * qsc;
+          if constexpr (MASK) l = tok0 + 16 * (2 * step + u) + 4 * q + (GC == 4 ? a4 : i) < n_tok ? l : -INFINITY;
           lg[u][i] = l;
           cmax = fmaxf(cmax, l);
         }
+      if constexpr (GC == 4) {  // the four row lanes 4a + h of a head
+        cmax = fmaxf(cmax, dpp_f<0x124>(cmax));
+        cmax = fmaxf(cmax, dpp_f<0x128>(cmax));
+      }
       cmax = max_xor16_32(cmax);
       // Online softmax with lazy rescaling: the accumulator is rescaled only
       // when some head's running maximum grows (rare after the first blocks).
@@ -438,22 +472,44 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
         m_run = m_new;
       }
       float psum = 0.f;
-      float pv[2][4];
+      float pv[2][NV];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NV; ++i) {
           const float p = exp2_hw(lg[u][i] - m_run);
           psum += p;
           pv[u][i] = p * vn[u][i];
         }
       l_run += psum;
       // P operand: slot order (tokens of tile 0, then tile 1) for byte-permute
-      // decoding, pair order (tile 0 / tile 1 of each row i) for the pair tables
+      // decoding, pair order (tile 0 / tile 1 of each row i) for the pair
+      // tables.  With GC = 4 row i of head h sits in lane 4i + h (read back by
+      // row shifts; lanes of columns >= 4 take values of no head, and their
+      // accumulator columns are never stored).
       u4 pw;
+      if constexpr (GC == 1) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pw[j] = VPT ? pack_h2(pv[0][j], pv[1][j]) : pack_h2(pv[j >> 1][2 * (j & 1)], pv[j >> 1][2 * (j & 1) + 1]);
+        for (int j = 0; j < 4; ++j)
+          pw[j] = VPT ? pack_h2(pv[0][j], pv[1][j]) : pack_h2(pv[j >> 1][2 * (j & 1)], pv[j >> 1][2 * (j & 1) + 1]);
+      } else if constexpr (VPT) {
+        const uint32_t x = pack_h2(pv[0][0], pv[1][0]);
+        pw[0] = x;
+        pw[1] = dpp_into<0x104, 0xF>(0u, x);
+        pw[2] = dpp_into<0x108, 0xF>(0u, x);
+        pw[3] = dpp_into<0x10C, 0xF>(0u, x);
+      } else {
+        float pr[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          pr[u][0] = pv[u][0];
+          pr[u][1] = dpp_into<0x104, 0xF>(0.f, pv[u][0]);
+          pr[u][2] = dpp_into<0x108, 0xF>(0.f, pv[u][0]);
+          pr[u][3] = dpp_into<0x10C, 0xF>(0.f, pv[u][0]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pw[j] = pack_h2(pr[j >> 1][2 * (j & 1)], pr[j >> 1][2 * (j & 1) + 1]);
+      }
       const h8 P = as_h8(pw);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
@@ -480,6 +536,10 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
       run_block(blk, std::false_type{});
     else
       run_block(blk, std::true_type{});
+  }
+  if constexpr (GC == 4) {  // the four row lanes of a head
+    l_run += dpp_f<0x124>(l_run);
+    l_run += dpp_f<0x128>(l_run);
   }
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
@@ -701,7 +761,8 @@ int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const
   bool launched = false;
 #define TQ_AT(BK, BV, M)                                                                   \
   if (!launched && kbits == BK && vbits == BV && m == M) {                                 \
-    hipLaunchKernelGGL((attend_kernel<BK, BV, M>), grid, block, 0, st, a);                 \
+    if (s.G <= 4) hipLaunchKernelGGL((attend_kernel<BK, BV, M, 4>), grid, block, 0, st, a); \
+    else hipLaunchKernelGGL((attend_kernel<BK, BV, M, 1>), grid, block, 0, st, a);          \
     launched = true;                                                                       \
   }
 #define TQ_AT_V(BK, M) TQ_AT(BK, 1, M) TQ_AT(BK, 2, M) TQ_AT(BK, 3, M) TQ_AT(BK, 4, M)

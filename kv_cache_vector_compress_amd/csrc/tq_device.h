@@ -322,6 +322,19 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+// DPP move of src into the lanes of old selected by BANK (bit b = lanes
+// 4b .. 4b + 3 of every 16-lane row); lanes left out, or whose source lies
+// outside the row, keep old.  CTRL: row_shl:n = 0x100 + n (read lane + n),
+// row_shr:n = 0x110 + n (read lane - n).
+template <int CTRL, int BANK>
+__device__ __forceinline__ uint32_t dpp_into(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, 0xF, BANK, false);
+}
+template <int CTRL, int BANK>
+__device__ __forceinline__ float dpp_into(float old, float src) {
+  return __uint_as_float(dpp_into<CTRL, BANK>(__float_as_uint(old), __float_as_uint(src)));
+}
+
 __device__ __forceinline__ float max_xor16_32(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
