@@ -448,6 +448,34 @@ def main():
             "unit": "GB/s", "frac": stage_info[dom]["frac_hbm_peak"], "traffic": counter_traffic(dom),
             "alg_bytes": int(alg[dom])}
 
+    # Practical HBM ceiling beside the theoretical peak: a plain read stream
+    # over the 2 GiB key input, and the same with writes interleaved 4:1 (the
+    # read/write mix of the score kernel and of compress).  Each stage is also
+    # reported against the stream with its own mix.
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    dst = torch.empty(Kd.numel() * Kd.element_size() // 16, dtype=torch.float32, device=dev)
+    stream_ms = {}
+    for name, d_ in (("read", None), ("read4_write1", dst)):
+        for _ in range(2):
+            tq.hbm_stream(Kd, d_, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            tq.hbm_stream(Kd, d_, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        stream_ms[name] = e0.elapsed_time(e1) / 10
+    del dst
+    nbytes = Kd.numel() * Kd.element_size()
+    hbm_stream = {"read_GBps": round(nbytes / (stream_ms["read"] * 1e-3) / 1e9, 1),
+                  "read4_write1_GBps": round(nbytes * 1.25 / (stream_ms["read4_write1"] * 1e-3) / 1e9, 1),
+                  "bytes_read": nbytes}
+    mix = {"compress_keys": "read4_write1_GBps", "compress_values": "read4_write1_GBps",
+           "scores": "read4_write1_GBps", "attend": "read_GBps"}
+    for s_ in stages:
+        stage_info[s_]["frac_of_stream"] = round(stage_info[s_]["GBps"] / hbm_stream[mix[s_]], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -462,6 +490,7 @@ def main():
                    "key_bits": w["key_bits"], "value_bits": w["value_bits"], "query_heads_per_kv": G,
                    "input_dtype": "f16"},
         "roofline": roof,
+        "hbm_stream": hbm_stream,
         "stages": stage_info,
         "cpu_baseline": cpu,
         "wall_s_timed": round(t_wall, 3),

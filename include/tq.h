@@ -261,6 +261,22 @@ int tq_get_values(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t 
 int tq_get_keys(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_tokens, float* out,
                 void* stream);
 
+/* ---- measurement ------------------------------------------------------------ */
+
+/* The HBM ceiling for the bandwidth-bound kernels above: stream read_bytes
+ * from src and, if write_bytes > 0, write write_bytes of a constant fp32
+ * pattern (1.0f) to dst, interleaved with the reads in their ratio; every
+ * wave reads and writes contiguous spans, as the score and attend kernels
+ * do.  The words read are XOR-folded into *sink (the caller initialises it;
+ * the value only proves the reads happened).  Not part of the method: it
+ * measures what a plain stream reaches on the device (the reported
+ * baseline beside the theoretical peak).  src, dst: device, 16-byte aligned;
+ * read_bytes a positive multiple of 4096; write_bytes 0, read_bytes,
+ * read_bytes / 2 or read_bytes / 4; sink: device uint32.  Errors: TQ_EINVAL,
+ * TQ_EDEVICE. */
+int tq_hbm_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

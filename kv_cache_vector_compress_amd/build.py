@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_compress.hip", "tq_attention.hip", "tq_general.hip",
-           "tq_dequant.hip", "tq_topk.hip", "tq_small.hip"]
+           "tq_dequant.hip", "tq_topk.hip", "tq_small.hip", "tq_stream.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

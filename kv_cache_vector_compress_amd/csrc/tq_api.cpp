@@ -491,4 +491,25 @@ int tq_get_keys(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_
   return get_vectors(ctx, cache, pos, n_tokens, out, stream, true, "tq_get_keys");
 }
 
+int tq_hbm_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
+                  void* stream) {
+  clear_error();
+  if (!src || ((uintptr_t)src & 15u)) return fail(TQ_EINVAL, "tq_hbm_stream: src must be a 16-byte aligned device pointer");
+  if (read_bytes == 0 || read_bytes % 4096 != 0)
+    return fail(TQ_EINVAL, "tq_hbm_stream: read_bytes must be a positive multiple of 4096");
+  if (write_bytes != 0) {
+    if (!dst || ((uintptr_t)dst & 15u))
+      return fail(TQ_EINVAL, "tq_hbm_stream: dst must be a 16-byte aligned device pointer");
+    if (!(write_bytes == read_bytes || 2 * write_bytes == read_bytes || 4 * write_bytes == read_bytes))
+      return fail(TQ_EINVAL, "tq_hbm_stream: write_bytes must be 0 or read_bytes / 1, / 2 or / 4");
+  }
+  if (!sink || ((uintptr_t)sink & 3u)) return fail(TQ_EINVAL, "tq_hbm_stream: sink must be a 4-byte aligned device pointer");
+  static std::once_flag once;
+  static int init_rc = 0;
+  std::call_once(once, [] { init_rc = stream_device_init(); });
+  if (init_rc != 0) return fail(TQ_EDEVICE, "tq_hbm_stream: HIP device query failed");
+  const int rc = launch_stream(src, read_bytes, dst, write_bytes, sink, stream);
+  return rc == 0 ? TQ_OK : fail(rc, "tq_hbm_stream: kernel launch failed");
+}
+
 }  // extern "C"

@@ -130,6 +130,11 @@ int launch_small_keys(const Matrices& mats, const CodebookDev& cb, int bits, int
 int launch_small_values(const Matrices& mats, const CodebookDev& cb, int bits, int d, const AppendShape& s,
                         void* value_blocks, void* stream);
 
+// HBM stream for measuring the memory ceiling (tq_stream.hip).
+int stream_device_init();
+int launch_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
+                  void* stream);
+
 // Fused inner-product top-k over the packed keys (tq_topk.hip).
 constexpr int kTopkMax = 16;  // largest k of tq_topk_scores
 struct TopkPlan {

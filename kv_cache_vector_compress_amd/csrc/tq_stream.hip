@@ -1,0 +1,71 @@
+// HBM stream kernel for gfx950: the memory ceiling the bandwidth-bound
+// kernels of the attention path are measured against.  Not part of the
+// method; it moves bytes the way those kernels do and nothing else.
+//
+// Each wave owns a contiguous span of the source and reads it in groups of
+// four 1 KB blocks (one 16-byte load per lane per block, four loads in
+// flight), folding the words into one XOR so the loads cannot be dropped.
+// With writes, after each group it stores 4 / rpw blocks of the matching
+// contiguous span of the destination (rpw = read bytes per written byte: 1,
+// 2 or 4), interleaving reads and writes in the ratio of the score kernel
+// (64 B of key record read per 16 B of scores written at G = 4).
+#include "tq_device.h"
+
+namespace tq {
+
+constexpr int kStreamWavesPerCu = 16;
+
+struct StreamArgs {
+  const u4* src;
+  u4* dst;
+  int64_t groups;  // 4 KB read groups
+  int rpw;         // read bytes per written byte; 0: no writes
+  uint32_t* sink;
+};
+
+__global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t g0 = gw * a.groups / waves, g1 = (gw + 1) * a.groups / waves;
+  const u4 fill = {0x3F800000u, 0x3F800000u, 0x3F800000u, 0x3F800000u};
+  uint32_t acc = 0u;
+  for (int64_t g = g0; g < g1; ++g) {
+    const u4* s = a.src + g * 256 + lane;  // 256 u4 = 4 KB
+    const u4 v0 = s[0], v1 = s[64], v2 = s[128], v3 = s[192];
+    acc ^= (v0[0] ^ v0[1] ^ v0[2] ^ v0[3]) ^ (v1[0] ^ v1[1] ^ v1[2] ^ v1[3]) ^
+           (v2[0] ^ v2[1] ^ v2[2] ^ v2[3]) ^ (v3[0] ^ v3[1] ^ v3[2] ^ v3[3]);
+    if (a.rpw > 0) {
+      const int nb = 4 / a.rpw;  // 1 KB blocks written per group
+      u4* d = a.dst + (g * nb) * 64 + lane;
+      for (int j = 0; j < nb; ++j) d[64 * j] = fill;
+    }
+  }
+  // fold the wave's words into the sink (a device word the caller reads)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+  if (lane == 0) atomicXor(a.sink, acc);
+}
+
+static int g_stream_cus = 0;
+
+int stream_device_init() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  return hipDeviceGetAttribute(&g_stream_cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? 0 : -1;
+}
+
+int launch_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
+                  void* stream) {
+  StreamArgs a;
+  a.src = (const u4*)src;
+  a.dst = (u4*)dst;
+  a.groups = (int64_t)(read_bytes / 4096);
+  a.rpw = write_bytes == 0 ? 0 : (int)(read_bytes / write_bytes);
+  a.sink = sink;
+  const int64_t waves = (int64_t)(g_stream_cus > 0 ? g_stream_cus : 256) * kStreamWavesPerCu;
+  hipLaunchKernelGGL(stream_kernel, dim3((unsigned)(waves / 4)), dim3(256), 0, (hipStream_t)stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+}
+
+}  // namespace tq

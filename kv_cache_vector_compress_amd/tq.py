@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         "tq_topk_scores": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, I32, P, P, P, SZ, P]),
         "tq_get_values": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
         "tq_get_keys": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
+        "tq_hbm_stream": (ctypes.c_int, [P, SZ, P, SZ, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -309,3 +310,20 @@ class KVCache:
     def value_words(self):
         w = self.value_blocks.cpu().numpy().view(np.uint32)
         return w.reshape(self.n_seq, self.capacity // BLOCK_TOKENS, -1)
+
+
+# ---- measurement -------------------------------------------------------------
+
+def hbm_stream(src, dst=None, sink=None, stream=None) -> None:
+    """Stream all of `src` (a contiguous device tensor) and, if `dst` is given,
+    write all of `dst` interleaved with the reads (tq_hbm_stream).  `sink` is
+    a one-element int32 device tensor that receives the XOR of the words read
+    (XOR-ed into its current value)."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=src.device)
+    nr = src.numel() * src.element_size()
+    nw = 0 if dst is None else dst.numel() * dst.element_size()
+    _check(lib().tq_hbm_stream(_dev(src, "src"), nr, _dev(dst, "dst") if dst is not None else None, nw,
+                               _dev(sink, "sink"), _stream_ptr(stream)))
+    return sink

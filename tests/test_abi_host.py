@@ -142,3 +142,21 @@ def test_topk_workspace_rejects_bad_arguments():
     assert ws(1, 4, 100, 16) > 0
     for bad in [(0, 4, 100, 10), (1, 0, 100, 10), (1, 513, 100, 10), (1, 4, 0, 10), (1, 4, 100, 0), (1, 4, 100, 17)]:
         assert ws(*bad) == 0, bad
+
+
+def test_hbm_stream_rejects_bad_arguments_before_any_device_call():
+    """tq_hbm_stream checks pointers, alignment and sizes on the host (fake
+    addresses: an accepted call would fault, so only rejected ones are made)."""
+    lib = tq.lib()
+    A = ctypes.c_void_p(1 << 40)       # aligned, never dereferenced
+    U = ctypes.c_void_p((1 << 40) + 4)  # misaligned
+    assert lib.tq_hbm_stream(None, 4096, None, 0, A, None) == -1
+    assert lib.tq_hbm_stream(U, 4096, None, 0, A, None) == -1
+    assert lib.tq_hbm_stream(A, 0, None, 0, A, None) == -1
+    assert lib.tq_hbm_stream(A, 4096 + 16, None, 0, A, None) == -1
+    assert lib.tq_hbm_stream(A, 8192, None, 2048, A, None) == -1      # writes without dst
+    assert lib.tq_hbm_stream(A, 8192, A, 3000, A, None) == -1         # ratio not 1, 2 or 4
+    assert lib.tq_hbm_stream(A, 8192, A, 8192 // 8, A, None) == -1    # ratio 8
+    assert lib.tq_hbm_stream(A, 8192, A, 2048, None, None) == -1      # no sink
+    assert lib.tq_hbm_stream(A, 8192, A, 2048, ctypes.c_void_p((1 << 40) + 2), None) == -1
+    assert "tq_hbm_stream" in tq.last_error()
