@@ -22,6 +22,8 @@
 // Values are rotated with tokens on M: a lane owns one coordinate of 32
 // tokens of a 128-token block, which is the order the attention kernel
 // contracts them in.
+#include <type_traits>
+
 #include "tq_device.h"
 
 namespace tq {
@@ -460,12 +462,15 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
 #pragma unroll
       for (int w = 0; w < B; ++w) cw[nt][w] = 0u;
 
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
+    // One half block (64 tokens, slots 4 half .. 4 half + 3).  The half is a
+    // compile-time constant so that the code slots are too: with a run-time
+    // slot the packing goes through a branchy switch and register copies.
+    auto run_half = [&](auto half_tag) {
+      constexpr int half = decltype(half_tag)::value;
       // a half with no token of [pos, pos + n_new) keeps all its codes (a
       // short append, e.g. one decode token, touches one half)
       const int64_t h0 = tok0 + 64 * half;
-      if (h0 + 64 <= a.pos || h0 >= a.pos + a.n_new) continue;
+      if (h0 + 64 <= a.pos || h0 >= a.pos + a.n_new) return;
       h8 xa[4][4];
       h8 xl[F32 ? 4 : 1][4];
       float tok_sc[4];  // per token: sigma = 2^8 sc ||v|| (4-bit codes: 1 / sigma)
@@ -510,11 +515,14 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
       constexpr bool kScaled = B <= 3;
       float inv_d[4][4];
       float bsd[4][4][kScaled ? 8 : 1];
+      uint32_t zmask[4];  // per row tile: bytes 0xFF for tokens of zero norm
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt) {
+        zmask[mt] = 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = __shfl(tok_sc[mt], 4 * q + i, 64);
+          zmask[mt] |= v == 0.f ? 0xFFu << (8 * i) : 0u;
           if constexpr (kScaled) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) bsd[mt][i][t] = t < (1 << (B - 1)) - 1 ? bp[t] * v : 0.f;
@@ -522,6 +530,7 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
             inv_d[mt][i] = v;
           }
         }
+      }
 
 #pragma unroll
       for (int ntp = 0; ntp < 4; ++ntp) {
@@ -563,13 +572,15 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
                   if (t == 0) v[i] *= inv_d[mt][i];
                 }
               }
-            const uint32_t x4 = cells4<B>(v, bsx);
+            const uint32_t x4 = cells4_signs<B>(v, bsx, zmask[mt]);
             put_sel4_rt<B>(cw[2 * ntp + u], 4 * half + mt, x4);  // slot of these 16 tokens
           }
         // keep the scheduler from hoisting the next coordinate tiles' R loads
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    };
+    run_half(std::integral_constant<int, 0>{});
+    run_half(std::integral_constant<int, 1>{});
 
     const bool full = tok0 >= a.pos && tok0 + kBlockTokens <= a.pos + a.n_new;
     if (full) {

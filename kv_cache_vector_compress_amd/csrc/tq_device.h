@@ -436,6 +436,33 @@ __device__ __forceinline__ uint32_t cells4(const f4& a, const float (&bs)[4][8])
   return perm(ia[1], ia[0], 0x0C0C0400u) | perm(ia[3], ia[2], 0x04000C0Cu);
 }
 
+// cells4 with the reflection done once for all four coordinates: the select
+// chains give the magnitude cells H + k, v_perm's sign-replicating
+// selectors give a byte mask of the coordinates whose sign bit is set, one
+// bitop3 reflects those cells to H - 1 - k, and zmask (bytes 0xFF for the
+// tokens of zero norm, whose coordinates are all +0 and belong to cell
+// H - 1) overrides those tokens.  A coordinate that comes out exactly +0 in
+// a token of nonzero norm gets cell H rather than H - 1; it lies on the
+// middle boundary, where either cell is within the code tolerance.
+template <int B>
+__device__ __forceinline__ uint32_t cells4_signs(const f4& a, const float (&bs)[4][8], uint32_t zmask) {
+  constexpr uint32_t H = 1u << (B - 1);
+  uint32_t ad[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float m = fabsf(a[i]);
+    uint32_t c = H;
+#pragma unroll
+    for (uint32_t t = 0; t + 1 < H; ++t) c = m > bs[i][t] ? H + 1u + t : c;
+    ad[i] = c;
+  }
+  const uint32_t mag = perm(ad[1], ad[0], 0x0C0C0400u) | perm(ad[3], ad[2], 0x04000C0Cu);
+  const uint32_t neg = perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x0C0C0B09u) |
+                       perm(__float_as_uint(a[3]), __float_as_uint(a[2]), 0x0B090C0Cu);
+  const uint32_t code = mag ^ (neg & ((2u * H - 1u) * 0x01010101u));
+  return (code & ~zmask) | ((H - 1u) * 0x01010101u & zmask);
+}
+
 // Split x0, x1 into fp16 high parts (round toward zero) and fp16 low parts
 // (the remainders, rounded): x = hi + lo to ~2^-22 relative.  m1 must be the
 // fp16 value -1 passed in at run time: with a constant the compiler turns

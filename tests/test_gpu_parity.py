@@ -133,18 +133,22 @@ def test_partial_token_window_and_scale():
     _say(run_case(K, V, Q, n_tokens=509, scale=0.3))
 
 
-def test_zero_and_single_token():
-    """Zero key/value rows are encoded as direction 0 and score 0; a cache of
-    one token attends to exactly that token's dequantised value."""
+@pytest.mark.parametrize("kb,vb,dtype", [(3, 3, np.float16), (4, 4, np.float16), (2, 1, np.float32),
+                                         (1, 2, np.float32)])
+def test_zero_and_single_token(kb, vb, dtype):
+    """Zero key/value rows are encoded as direction 0 (every cell L/2 - 1)
+    and score 0, in bulk appends of each code width and input type; a cache
+    of one token attends to exactly that token's dequantised value."""
     d, T, n_seq, G = 128, 40, 1, 4
-    K = synth.kv_slot(40, 0, 0, T, d)[None].copy()
-    V = synth.kv_slot(41, 0, 0, T, d)[None].copy()
+    K = synth.kv_slot(40, 0, 0, T, d, dtype=dtype)[None].copy()
+    V = synth.kv_slot(41, 0, 0, T, d, dtype=dtype)[None].copy()
     K[0, 5] = 0
     V[0, 7] = 0
-    Q = synth.kv_slot(42, 0, 0, G, d)[None]
-    _say("zeros")
-    _say(run_case(K, V, Q))
-    _say(run_case(K[:, :1], V[:, :1], Q))
+    V[0, 33] = 0
+    Q = synth.kv_slot(42, 0, 0, G, d, dtype=dtype)[None]
+    _say("zeros", kb, vb, np.dtype(dtype).name)
+    _say(run_case(K, V, Q, kb=kb, vb=vb))
+    _say(run_case(K[:, :1], V[:, :1], Q, kb=kb, vb=vb))
 
 
 def test_fp32_inputs_kv_like():
