@@ -368,7 +368,7 @@ __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float rs[4];
-        const uint32_t x4 = quantize4<B>(quarter(ycur, j), bs, s16, ctab, rs, g2);
+        const uint32_t x4 = quantize4_signs<B>(quarter(ycur, j), bs, -s16, ctab, rs, g2);  // rs = -residual
         const HiLo t01 = split2m(rs[0], rs[1], a.m1), t23 = split2m(rs[2], rs[3], a.m1);
         rhi[j >> 1][2 * (j & 1)] = t01.hi;
         rlo[j >> 1][2 * (j & 1)] = t01.lo;
@@ -396,10 +396,21 @@ __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a
     const float gamma = sqrtf(g2) * (1.f / kResScale);
     // projection 32 p + 8 j + 4 g + i = 16 (2 p + j/2) + 4 (2 (j%2) + g) + i:
     // sign group g (j even) and g + 2 (j odd), bit 4 (2 p + j/2) + i
-    const uint32_t bits_a = sign_bits16(quarter(zacc[0], 0), quarter(zacc[0], 2), quarter(zacc[1], 0),
-                                        quarter(zacc[1], 2));
-    const uint32_t bits_b = sign_bits16(quarter(zacc[0], 1), quarter(zacc[0], 3), quarter(zacc[1], 1),
-                                        quarter(zacc[1], 3));
+    // (zacc holds S applied to the negated residual)
+    uint32_t bits_a = sign_bits16_neg(quarter(zacc[0], 0), quarter(zacc[0], 2), quarter(zacc[1], 0),
+                                      quarter(zacc[1], 2));
+    uint32_t bits_b = sign_bits16_neg(quarter(zacc[0], 1), quarter(zacc[0], 3), quarter(zacc[1], 1),
+                                      quarter(zacc[1], 3));
+    if (nrm == 0.f) {
+      // A zero key has every rotated coordinate +0, which quantize4_signs
+      // puts in cell H with residual -c+_0.  Its cell is H - 1 (0 is the
+      // middle boundary and ties go to the lower cell), whose residual is
+      // +c+_0: the opposite residual, so every projection flips sign.
+      fill_code_words<B>(cw[0], (uint32_t)H - 1u);
+      fill_code_words<B>(cw[1], (uint32_t)H - 1u);
+      bits_a = ~bits_a & 0xFFFFu;
+      bits_b = ~bits_b & 0xFFFFu;
+    }
     if (tok < a.n_new) {
       uint32_t* rp = a.rec + ((int64_t)slot * a.capacity + a.pos + tok) * a.rec_words;
 #pragma unroll

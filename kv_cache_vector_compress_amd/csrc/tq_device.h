@@ -416,6 +416,56 @@ __device__ __forceinline__ uint32_t quantize4(const f4& a, const float (&bs)[8],
   return (perm(ia[1], ia[0], 0x0C0C0400u) | perm(ia[3], ia[2], 0x04000C0Cu)) >> 2;
 }
 
+// quantize4 with the sign handled once for four coordinates, returning the
+// NEGATED scaled residual rn = -2^12 (y - c[idx]) (one bit insert and one
+// FMA per coordinate; the caller projects rn and reads the sign bits with
+// the opposite polarity, sign_bits16_neg).  The select chain gives the byte
+// address 4 (H + k) of the positive centroid c[H + k] = c+_k, and
+// copysign(c+_k, a) is the signed centroid of a's cell.  The cells H + k are
+// reflected to H - 1 - k where a's sign bit is set by one bitop3 on the
+// four code bytes, with the sign mask from v_perm's sign-replicating
+// selectors.  ns16 = -2^12 / sigma.  A coordinate that is exactly +0 lands
+// in cell H (residual -c+_0) instead of H - 1: it lies on the middle
+// boundary, where either cell is within the code tolerance, and a token of
+// zero norm (all coordinates +0) is set right by its caller.
+template <int B>
+__device__ __forceinline__ uint32_t quantize4_signs(const f4& a, const float (&bs)[8], float ns16, const float* ctab,
+                                                    float (&rn)[4], float& g2) {
+  constexpr uint32_t H = 1u << (B - 1);
+  uint32_t ad[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float m = fabsf(a[i]);
+    uint32_t c = 4u * H;
+#pragma unroll
+    for (uint32_t t = 0; t + 1 < H; ++t) c = m > bs[t] ? 4u * (H + 1u + t) : c;
+    ad[i] = c;
+    const float cp = *(const float*)((const char*)ctab + c);
+    rn[i] = fmaf(a[i], ns16, __builtin_copysignf(cp, a[i]));
+    g2 = fmaf(rn[i], rn[i], g2);
+  }
+  const uint32_t mag = (perm(ad[1], ad[0], 0x0C0C0400u) | perm(ad[3], ad[2], 0x04000C0Cu)) >> 2;
+  const uint32_t neg = perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x0C0C0B09u) |
+                       perm(__float_as_uint(a[3]), __float_as_uint(a[2]), 0x0B090C0Cu);
+  return mag ^ (neg & ((2u * H - 1u) * 0x01010101u));
+}
+
+// Code words of a b-bit group whose 32 codes all equal v (v < 2^b).
+template <int B>
+__device__ __forceinline__ void fill_code_words(uint32_t (&w)[B], uint32_t v) {
+  const uint32_t x = v * 0x01010101u;
+#pragma unroll
+  for (int k = 0; k < B; ++k) w[k] = 0u;
+  put_sel4<B, 0>(w, x);
+  put_sel4<B, 1>(w, x);
+  put_sel4<B, 2>(w, x);
+  put_sel4<B, 3>(w, x);
+  put_sel4<B, 4>(w, x);
+  put_sel4<B, 5>(w, x);
+  put_sel4<B, 6>(w, x);
+  put_sel4<B, 7>(w, x);
+}
+
 // Cells of 4 coordinates without the residual (the value path): a_i are
 // scaled rotated coordinates sigma_i y_i and bs[i][t] = beta_{H+t} sigma_i
 // the matching scaled positive boundaries (one token per i).  Same select
@@ -484,6 +534,22 @@ __device__ __forceinline__ uint32_t sign_bits16(const f4& z0, const f4& z1, cons
     const uint32_t m = perm(__float_as_uint(z[1]), __float_as_uint(z[0]), 0x0C0C0B09u) |
                        perm(__float_as_uint(z[3]), __float_as_uint(z[2]), 0x0B090C0Cu);
     return ~m & bits;
+  };
+  const uint32_t lo =
+      __builtin_amdgcn_sad_u8(keep(z1, 0x80402010u), 0u, __builtin_amdgcn_sad_u8(keep(z0, 0x08040201u), 0u, 0u));
+  const uint32_t hi =
+      __builtin_amdgcn_sad_u8(keep(z3, 0x80402010u), 0u, __builtin_amdgcn_sad_u8(keep(z2, 0x08040201u), 0u, 0u));
+  return lo | (hi << 8);
+}
+
+// sign_bits16 for the projections zn = -z of a negated residual: bit 4 p + i
+// is set where zn[p][i] has its sign bit set, i.e. z > 0 (the same as
+// [z >= 0] except at z = 0 exactly, which lies on the sign tolerance).
+__device__ __forceinline__ uint32_t sign_bits16_neg(const f4& z0, const f4& z1, const f4& z2, const f4& z3) {
+  auto keep = [](const f4& z, uint32_t bits) {
+    const uint32_t m = perm(__float_as_uint(z[1]), __float_as_uint(z[0]), 0x0C0C0B09u) |
+                       perm(__float_as_uint(z[3]), __float_as_uint(z[2]), 0x0B090C0Cu);
+    return m & bits;
   };
   const uint32_t lo =
       __builtin_amdgcn_sad_u8(keep(z1, 0x80402010u), 0u, __builtin_amdgcn_sad_u8(keep(z0, 0x08040201u), 0u, 0u));
