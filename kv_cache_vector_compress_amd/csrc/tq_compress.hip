@@ -127,7 +127,8 @@ __global__ __launch_bounds__(512, 1) void compress_keys_kernel(const KeyArgs a) 
 
   float bpos[8];
   load_pos_beta<B>(bpos, a.cb);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave-uniform (a scalar register): tile, slot and offset arithmetic stays on the scalar unit
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t tps = (a.n_new + 16 * NT - 1) / (16 * NT);
   const int64_t ntiles = tps * a.n_seq;
@@ -297,7 +298,8 @@ __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a
 
   float bpos[8];
   load_pos_beta<B>(bpos, a.cb);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave-uniform (a scalar register): tile, slot and offset arithmetic stays on the scalar unit
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n32 = lane & 31, g = lane >> 5;
   const int64_t tps = (a.n_new + 31) / 32;
   const int64_t ntiles = tps * a.n_seq;
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a
     f16v ycur = rotate(0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0x0008);  // (matrix-core instructions may cross)
       f16v ynext;
       if (t < 3) ynext = rotate(t + 1);
       // cells, scaled residual 2^12 (y - c[idx]) as the B operands of
@@ -454,7 +456,8 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
 
   float bp[8];
   load_pos_beta<B>(bp, a.cb);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave-uniform (a scalar register): tile, slot and offset arithmetic stays on the scalar unit
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
   const int waves = blockDim.x >> 6;
   const int64_t nitems = a.nblk * a.n_seq;
