@@ -364,6 +364,10 @@ __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a
       __builtin_amdgcn_sched_barrier(0x0008);  // (matrix-core instructions may cross)
       f16v ynext;
       if (t < 3) ynext = rotate(t + 1);
+      // Raised wave priority while this wave buckets and projects tile t:
+      // the other wave of the SIMD then issues its rotation MFMAs in the
+      // gaps rather than competing for VALU issue (measured ~2% faster).
+      __builtin_amdgcn_s_setprio(1);
       // cells, scaled residual 2^12 (y - c[idx]) as the B operands of
       // projection K steps 2t (acc 0..7) and 2t + 1 (acc 8..15)
       u4 rhi[2], rlo[2];
@@ -391,6 +395,7 @@ __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a
           zacc[p] = mfma32(sh, rl, zacc[p]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (t < 3) ycur = ynext;
     }
 
@@ -569,6 +574,9 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
               if constexpr (F32) acc[mt][u] = mfma(xl[mt][kb], bh[u], acc[mt][u]);
             }
         }
+        // raised wave priority while bucketing (the other wave's MFMAs fill
+        // the gaps; measured ~2% faster)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -589,6 +597,7 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
             const uint32_t x4 = cells4_signs<B>(v, bsx, zmask[mt]);
             put_sel4_rt<B>(cw[2 * ntp + u], 4 * half + mt, x4);  // slot of these 16 tokens
           }
+        __builtin_amdgcn_s_setprio(0);
         // keep the scheduler from hoisting the next coordinate tiles' R loads
         __builtin_amdgcn_sched_barrier(0);
       }
