@@ -213,12 +213,38 @@ def bench_qwen_decode(args):
         one_layer()
         torch.cuda.synchronize()
     lat_graph = _timed(torch, graph.replay, reps)
+    # the same step through tq_decode_step: the appends and the query
+    # preparation in one launch, then the attention's two
+    def one_layer_fused():
+        layer.decode_step(k1, v1, q1, T - 1, out=o1)
+    for _ in range(max(args.warmup, 1)):
+        one_layer_fused()
+    torch.cuda.synchronize()
+    lat_fused = _timed(torch, one_layer_fused, reps)
+    fused_o = o1.clone()
+    graph_f = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        one_layer_fused()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph_f, stream=side):
+            one_layer_fused()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        o1.zero_()
+        graph_f.replay()
+        torch.cuda.synchronize()
+        graph_ok &= bool(torch.equal(o1, fused_o))
+    lat_fused_graph = _timed(torch, graph_f.replay, reps)
+    fused_vs_calls = float((fused_o - ref_o).norm() / ref_o.norm())
     b_sc = n_seq * T * (tq.key_record_bytes(ctx.cfg) + 4 * G)
     b_at = n_seq * T * (tq.key_record_bytes(ctx.cfg) + tq.value_block_bytes(ctx.cfg) / 128)
     gb = lambda b, ms: round(b / (ms * 1e-3) / 1e9, 1)
     line = {"metric": "per-layer decode latency (append 1 token K+V, attend 8192) and 36-layer score/attend HBM GB/s",
             "value": round(lat * 1e3, 2), "unit": "us/layer", "higher_is_better": False, "n_gpus": 1,
             "graph_replay_us_per_layer": round(lat_graph * 1e3, 2), "graph_replays_match_eager": graph_ok,
+            "decode_step_us_per_layer": round(lat_fused * 1e3, 2),
+            "decode_step_graph_us_per_layer": round(lat_fused_graph * 1e3, 2),
+            "decode_step_vs_three_calls_rel": fused_vs_calls,
             "data": "synthetic", "dtype": "f16",
             "config": {"workload": w.name, "n_seq": n_seq, "tokens_per_slot": T, "head_dim": d, "proj_dim": m,
                        "key_bits": 3, "value_bits": 3, "query_heads_per_kv": G},

@@ -221,6 +221,25 @@ int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dt
               int64_t n_tokens, float scale, float* out, void* workspace, size_t workspace_bytes,
               void* stream);
 
+/* One decode step: append n_new tokens' keys and values at token slots
+ * [pos, pos + n_new) of every slot, then attend with q over the whole cache
+ * [0, pos + n_new) -- the same results as tq_append_key, tq_append_value and
+ * tq_attend called in that order (the streaming use of the cache,
+ * nav.superapi.store 常见使用模式: append_key / append_value per token, then
+ * attention over the compressed cache).  k, v: device [n_seq][n_new][d]; q:
+ * device [n_seq][G][d]; all three of type dtype.  scale, out, workspace as
+ * for tq_attend with n_tokens = pos + n_new (workspace >=
+ * tq_workspace_bytes(cfg, n_seq, G, pos + n_new)).  On the single-kernel
+ * shapes (head_dim 128, proj_dim 64 or 128, G <= 16) with n_new <= 16 the
+ * appends and the query preparation run as one launch, followed by the
+ * attention's own two; otherwise the three calls run in order.  Every
+ * argument is checked before anything is launched.  Errors: TQ_EINVAL
+ * (including n_new < 1), TQ_ECAPACITY, TQ_ENOCODEBOOK, TQ_EWORKSPACE,
+ * TQ_EDEVICE. */
+int tq_decode_step(tq_ctx* ctx, const tq_cache_view* cache, const void* k, const void* v, int32_t dtype,
+                   int64_t pos, int64_t n_new, const void* q, int32_t G, float scale, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* ---- vector search ----------------------------------------------------------- */
 
 /* Device workspace bytes tq_topk_scores needs (query operands and per-wave

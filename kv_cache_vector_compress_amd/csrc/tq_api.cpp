@@ -420,6 +420,46 @@ int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dt
   return rc ? fail(rc, "tq_attend: launch failed (%d)", rc) : TQ_OK;
 }
 
+int tq_decode_step(tq_ctx* ctx, const tq_cache_view* cache, const void* k, const void* v, int32_t dtype,
+                   int64_t pos, int64_t n_new, const void* q, int32_t G, float scale, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* fn = "tq_decode_step";
+  if (n_new < 1) return fail(TQ_EINVAL, "%s: n_new %lld < 1", fn, (long long)n_new);
+  // every argument of the three operations is checked before anything runs
+  int rc = append_common(ctx, cache, k, dtype, pos, n_new, ctx ? ctx->cfg.key_bits : 1, fn);
+  if (rc) return rc;
+  rc = append_common(ctx, cache, v, dtype, pos, n_new, ctx->cfg.value_bits, fn);
+  if (rc) return rc;
+  AttnPlan plan;
+  rc = attn_common(ctx, cache, q, dtype, G, pos + n_new, out, workspace, workspace_bytes, true, fn, &plan);
+  if (rc) return rc;
+  if (!std::isfinite(scale)) return fail(TQ_EINVAL, "%s: scale is not finite", fn);
+  if (!(fast_attn(ctx->cfg, G) && n_new <= kSmallAppend)) {
+    // other shapes or longer appends: the three calls, in order
+    rc = tq_append_key(ctx, cache, k, dtype, pos, n_new, stream);
+    if (!rc) rc = tq_append_value(ctx, cache, v, dtype, pos, n_new, stream);
+    if (!rc) rc = tq_attend(ctx, cache, q, dtype, G, pos + n_new, scale, out, workspace, workspace_bytes, stream);
+    return rc;
+  }
+  if (scale <= 0.f) scale = 1.f / std::sqrt((float)ctx->cfg.head_dim);
+  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "%s: hipSetDevice failed", fn);
+  const AppendShape ks{k, dtype, n_new, pos, cache->capacity, cache->n_seq};
+  const AppendShape vs{v, dtype, n_new, pos, cache->capacity, cache->n_seq};
+  const AttnShape s{q, dtype, G, pos + n_new, cache->capacity, cache->n_seq};
+  uint16_t* wq = nullptr;
+  float* wqn = nullptr;
+  attend_query_buffers(workspace, plan, &wq, &wqn);
+  rc = launch_decode_prep(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cb[ctx->cfg.value_bits],
+                          ctx->cfg.value_bits, ctx->cfg.head_dim, ctx->cfg.proj_dim, ks, vs, s, cache->key_records,
+                          cache->value_blocks, wq, wqn, stream);
+  if (!rc)
+    rc = launch_attend(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cb[ctx->cfg.value_bits],
+                       ctx->cfg.value_bits, ctx->cfg.proj_dim, s, cache->key_records, cache->value_blocks, scale, out,
+                       workspace, plan, stream);
+  return rc ? fail(rc, "%s: launch failed (%d)", fn, rc) : TQ_OK;
+}
+
 static int get_common(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_tokens, const float* out,
                       int bits, const char* fn) {
   int rc = check_cache(ctx, cache, fn);

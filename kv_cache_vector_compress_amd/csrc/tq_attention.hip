@@ -687,6 +687,12 @@ static WsPtrs ws_ptrs(void* ws, const AttnPlan& p) {
   return w;
 }
 
+void attend_query_buffers(void* ws, const AttnPlan& p, uint16_t** wq, float** wqn) {
+  const WsPtrs w = ws_ptrs(ws, p);
+  *wq = w.wq;
+  *wqn = w.wqn;
+}
+
 int launch_prep_queries(const Matrices& mats, int m, const AttnShape& s, void* ws, const AttnPlan& p,
                         void* stream) {
   // one workgroup per (slot, head), wave-parallel dot products (tq_general.hip);

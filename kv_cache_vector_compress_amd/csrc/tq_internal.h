@@ -130,6 +130,14 @@ int launch_small_keys(const Matrices& mats, const CodebookDev& cb, int bits, int
 int launch_small_values(const Matrices& mats, const CodebookDev& cb, int bits, int d, const AppendShape& s,
                         void* value_blocks, void* stream);
 
+// A decode step's appends and query preparation in one launch (tq_small.hip);
+// wq / wqn: the query operand buffers of the attend workspace.
+int launch_decode_prep(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
+                       int d, int m, const AppendShape& ks, const AppendShape& vs, const AttnShape& qs,
+                       void* key_records, void* value_blocks, uint16_t* wq, float* wqn, void* stream);
+// Where the single-kernel attend keeps its query operands in the workspace.
+void attend_query_buffers(void* ws, const AttnPlan& p, uint16_t** wq, float** wqn);
+
 // HBM stream for measuring the memory ceiling (tq_stream.hip).
 int stream_device_init();
 int launch_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,

@@ -1,0 +1,115 @@
+// Query preparation shared by the attention paths and the fused decode step
+// (device code, included by the .hip sources that launch it).
+//
+// q~ = R q and p = S q~ for one query head (the query side of the asymmetric
+// estimate: nav.superapi.store "turboquant-pytorch", 常见使用模式), then the
+// fp16 MFMA B operands divided by ||q||, in the lane layout the score and
+// attend kernels read.
+#pragma once
+
+#include "tq_device.h"
+
+namespace tq {
+
+struct GenPrepArgs {
+  const void* q;
+  int dtype, G, HG, n_seq, d, m, n_oct;
+  const float* r32;
+  const float* s32;
+  uint16_t* wq;   // [n_seq][HG][KBT][64][8] fp16, KBT = d/32 + m/32
+  float* wqn;     // [n_seq][16 HG]
+};
+
+// The work of one workgroup (256 threads) for block index bid: slot
+// bid / (16 HG), head lane bid % (16 HG).  Dynamic LDS: (2 d + m) floats.
+__device__ __forceinline__ void gen_prep_block(const GenPrepArgs& a, int bid) {
+  extern __shared__ float gsm[];
+  float* qs = gsm;          // [d]
+  float* qt = qs + a.d;     // [d]
+  float* pp = qt + a.d;     // [m]
+  __shared__ float red[4];
+  const int H16 = 16 * a.HG;
+  const int slot = bid / H16, h = bid % H16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool live = h < a.G;
+  float s = 0.f;
+  for (int k = tid; k < a.d; k += blockDim.x) {
+    float v = 0.f;
+    if (live) {
+      const int64_t off = ((int64_t)slot * a.G + h) * a.d + k;
+      v = a.dtype == TQ_F32 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
+    }
+    qs[k] = v;
+    s = fmaf(v, v, s);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += shfl_xor(s, o);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  const float qn = sqrtf((red[0] + red[1]) + (red[2] + red[3]));
+  // q~ = R q and p = S q~.  A head lane past G has q = 0 and takes no
+  // products.  Each output row is split over 4 neighbouring threads (a
+  // quarter of its columns each, all of their loads in flight at once), and
+  // the quarters are summed with two lane exchanges.
+  if (live) {
+    auto rows = [&](const float* mat, int n_rows, const float* x, float* y) {
+      const int c = tid & 3, d4 = a.d / 4;
+      for (int j0 = 0; j0 < n_rows; j0 += blockDim.x / 4) {
+        const int j = j0 + (tid >> 2);
+        float t = 0.f;
+        if (j < n_rows) {
+          const f4* rr = (const f4*)(mat + (size_t)j * a.d + c * d4);
+          const float* xx = x + c * d4;
+          float t1 = 0.f;
+#pragma unroll 8
+          for (int k4 = 0; k4 < d4 / 4; k4 += 2) {
+            const f4 u = rr[k4], v = rr[k4 + 1];
+            t = fmaf(u[0], xx[4 * k4], fmaf(u[1], xx[4 * k4 + 1], fmaf(u[2], xx[4 * k4 + 2], fmaf(u[3], xx[4 * k4 + 3], t))));
+            t1 = fmaf(v[0], xx[4 * k4 + 4], fmaf(v[1], xx[4 * k4 + 5], fmaf(v[2], xx[4 * k4 + 6], fmaf(v[3], xx[4 * k4 + 7], t1))));
+          }
+          t += t1;
+        }
+        t += shfl_xor(t, 1);
+        t += shfl_xor(t, 2);
+        if (j < n_rows && c == 0) y[j] = t;
+      }
+    };
+    rows(a.r32, a.d, qs, qt);
+    __syncthreads();
+    rows(a.s32, a.m, qt, pp);
+  } else {
+    for (int k = tid; k < a.d; k += blockDim.x) qt[k] = 0.f;
+    for (int i = tid; i < a.m; i += blockDim.x) pp[i] = 0.f;
+  }
+  __syncthreads();
+  const float inv = live && qn > 0.f ? 1.f / qn : 0.f;
+  const int KBT = a.d / 32 + a.m / 32;
+  const int hg = h / 16, h16 = h % 16;
+  for (int idx = tid; idx < KBT * 4; idx += blockDim.x) {
+    const int kb = idx / 4, qq = idx % 4;
+    h8 v;
+    if (kb < a.d / 32) {
+      // centroid part of chunk kb/4: k slot e <-> coordinate 128 (kb/4) + 16 (2 (kb%4) + e/4) + 4 qq + e%4
+      const int base = 128 * (kb / 4) + 32 * (kb % 4);
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)(qt[base + 16 * (e / 4) + 4 * qq + e % 4] * inv);
+    } else {
+      // sign part: k slot 2e+half <-> bit p + 16 half of sign word 2 (kbp/2) + qq/2,
+      // p = 8 (qq%2) + 4 (kbp%2) + e, which holds projection coordinate 16 t + 4 qs + p%4
+      // with qs = 2 (qq/2) + half, t = 4 (kbp/2) + p/4
+      const int kbp = kb - a.d / 32;
+      for (int e = 0; e < 4; ++e)
+        for (int half = 0; half < 2; ++half) {
+          const int p = 8 * (qq % 2) + 4 * (kbp % 2) + e;
+          const int qsg = 2 * (qq / 2) + half;
+          const int t = 4 * (kbp / 2) + p / 4;
+          v[2 * e + half] = (_Float16)(pp[16 * t + 4 * qsg + p % 4] * inv);
+        }
+    }
+    const int l = 16 * qq + h16;
+    *(h8*)(a.wq + ((((int64_t)slot * a.HG + hg) * KBT + kb) * 64 + l) * 8) = v;
+  }
+  if (tid == 0) a.wqn[(int64_t)slot * H16 + h] = live ? qn : 0.f;
+}
+
+
+}  // namespace tq

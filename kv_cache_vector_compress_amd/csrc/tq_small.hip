@@ -15,7 +15,10 @@
 //                        the block's new tokens are coded one after the
 //                        other and each code word is read, merged and
 //                        written by one thread (words are shared by tokens).
+#include <algorithm>
+
 #include "tq_device.h"
+#include "tq_prep.h"
 
 namespace tq {
 
@@ -137,7 +140,8 @@ __device__ __forceinline__ uint32_t code_bits(int b, int w, int s, int i, uint32
 
 __device__ __forceinline__ uint32_t code_mask(int b, int w, int s, int i) { return code_bits(b, w, s, i, 0xFu >> (4 - b)); }
 
-__global__ __launch_bounds__(kSmallThreads) void small_keys_kernel(const SmallArgs a) {
+// One workgroup's work of small_keys_kernel for block index bid.
+__device__ __forceinline__ void small_keys_block(const SmallArgs& a, int64_t bid) {
   extern __shared__ float ssm[];
   float* xs = ssm;             // [d] input
   float* ys = xs + a.d;        // [d] R x
@@ -146,8 +150,8 @@ __global__ __launch_bounds__(kSmallThreads) void small_keys_kernel(const SmallAr
   int* is = (int*)(zs + a.m);  // [d] cells
   __shared__ float red[kSmallThreads / 64];
   __shared__ float ctab[16];
-  const int slot = (int)(blockIdx.x / a.n_new);
-  const int64_t t = blockIdx.x - (int64_t)slot * a.n_new;
+  const int slot = (int)(bid / a.n_new);
+  const int64_t t = bid - (int64_t)slot * a.n_new;
   float beta[15];
 #pragma unroll
   for (int i = 0; i < 15; ++i) beta[i] = a.beta[i];
@@ -208,7 +212,12 @@ __global__ __launch_bounds__(kSmallThreads) void small_keys_kernel(const SmallAr
   }
 }
 
-__global__ __launch_bounds__(kSmallThreads) void small_values_kernel(const SmallArgs a) {
+__global__ __launch_bounds__(kSmallThreads) void small_keys_kernel(const SmallArgs a) {
+  small_keys_block(a, blockIdx.x);
+}
+
+// One workgroup's work of small_values_kernel for block index bid.
+__device__ __forceinline__ void small_values_block(const SmallArgs& a, int64_t bid) {
   extern __shared__ float ssm[];
   float* xs = ssm;             // [d]
   float* ys = xs + a.d;        // [d]
@@ -218,8 +227,8 @@ __global__ __launch_bounds__(kSmallThreads) void small_values_kernel(const Small
   __shared__ int tau_of[16];
   const int64_t blk0 = a.pos / kBlockTokens;
   const int64_t nblk = (a.pos + a.n_new - 1) / kBlockTokens - blk0 + 1;
-  const int slot = (int)(blockIdx.x / nblk);
-  const int64_t blk = blk0 + (blockIdx.x - (int64_t)slot * nblk);
+  const int slot = (int)(bid / nblk);
+  const int64_t blk = blk0 + (bid - (int64_t)slot * nblk);
   const int64_t t_lo = max(a.pos, blk * kBlockTokens), t_hi = min(a.pos + a.n_new, (blk + 1) * kBlockTokens);
   const int nt = (int)(t_hi - t_lo);  // <= n_new <= 16
   float beta[15];
@@ -262,6 +271,27 @@ __global__ __launch_bounds__(kSmallThreads) void small_values_kernel(const Small
   if (threadIdx.x < nt) vnorm[tau_of[threadIdx.x]] = nrm[threadIdx.x];
 }
 
+__global__ __launch_bounds__(kSmallThreads) void small_values_kernel(const SmallArgs a) {
+  small_values_block(a, blockIdx.x);
+}
+
+// A decode step's independent work in one launch: the key appends (blocks
+// [0, nk)), the value appends ([nk, nk + nv)) and the query preparation of
+// the attention that follows ([nk + nv, ...)).  The role is uniform over a
+// workgroup, so each branch keeps its own barriers.
+struct DecodeArgs {
+  SmallArgs k, v;
+  GenPrepArgs p;
+  int nk, nv;
+};
+
+__global__ __launch_bounds__(kSmallThreads) void decode_prep_kernel(const DecodeArgs a) {
+  const int b = (int)blockIdx.x;
+  if (b < a.nk) small_keys_block(a.k, b);
+  else if (b < a.nk + a.nv) small_values_block(a.v, b - a.nk);
+  else gen_prep_block(a.p, b - a.nk - a.nv);
+}
+
 static SmallArgs small_args(const Matrices& mats, const CodebookDev& cb, int bits, int d, int m, const AppendShape& s,
                             void* out) {
   SmallArgs a;
@@ -289,9 +319,12 @@ static SmallArgs small_args(const Matrices& mats, const CodebookDev& cb, int bit
 int small_device_init() {
   // up to head_dim 1024: values keep 16 x d cells plus 2 d floats in LDS
   const int lds = (int)(sizeof(float) * (2 * 1024 + 16 * 1024));
-  return hipFuncSetAttribute((const void*)small_values_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds) ==
-                 hipSuccess
-             ? 0 : -1;
+  const bool ok =
+      hipFuncSetAttribute((const void*)small_values_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds) ==
+          hipSuccess &&
+      hipFuncSetAttribute((const void*)decode_prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds) ==
+          hipSuccess;
+  return ok ? 0 : -1;
 }
 
 int launch_small_keys(const Matrices& mats, const CodebookDev& cb, int bits, int d, int m, const AppendShape& s,
@@ -299,6 +332,34 @@ int launch_small_keys(const Matrices& mats, const CodebookDev& cb, int bits, int
   const SmallArgs a = small_args(mats, cb, bits, d, m, s, key_records);
   const size_t lds = sizeof(float) * (size_t)(4 * d + m);
   hipLaunchKernelGGL(small_keys_kernel, dim3((unsigned)(s.n_seq * s.n_new)), dim3(kSmallThreads), lds,
+                     (hipStream_t)stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+}
+
+int launch_decode_prep(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
+                       int d, int m, const AppendShape& ks, const AppendShape& vs, const AttnShape& qs,
+                       void* key_records, void* value_blocks, uint16_t* wq, float* wqn, void* stream) {
+  DecodeArgs a;
+  a.k = small_args(mats, cbk, kbits, d, m, ks, key_records);
+  a.v = small_args(mats, cbv, vbits, d, m, vs, value_blocks);
+  const int64_t nblk = (vs.pos + vs.n_new - 1) / kBlockTokens - vs.pos / kBlockTokens + 1;
+  a.nk = (int)(ks.n_seq * ks.n_new);
+  a.nv = (int)(vs.n_seq * nblk);
+  a.p.q = qs.q;
+  a.p.dtype = qs.dtype;
+  a.p.G = qs.G;
+  a.p.HG = 1;
+  a.p.n_seq = qs.n_seq;
+  a.p.d = d;
+  a.p.m = m;
+  a.p.n_oct = d / 128;
+  a.p.r32 = mats.r32;
+  a.p.s32 = mats.s32;
+  a.p.wq = wq;
+  a.p.wqn = wqn;
+  const int np = qs.n_seq * 16;
+  const size_t lds = sizeof(float) * (size_t)std::max(std::max(4 * d + m, 2 * d + kSmallAppend * d), 2 * d + m);
+  hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)(a.nk + a.nv + np)), dim3(kSmallThreads), lds,
                      (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
 }

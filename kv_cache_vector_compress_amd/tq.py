@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
         "tq_get_values": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
         "tq_get_keys": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
         "tq_hbm_stream": (ctypes.c_int, [P, SZ, P, SZ, P, P]),
+        "tq_decode_step": (ctypes.c_int, [P, VIEW, P, P, I32, I64, I64, P, I32, ctypes.c_float, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -265,6 +266,21 @@ class KVCache:
         _check(lib().tq_attend(self.ctx.handle, ctypes.byref(self.view), _dev(q, "q"), _dtype_code(q), G,
                                n_tokens, float(scale), _dev(out, "out"), ctypes.c_void_p(ws.data_ptr()),
                                ws.numel(), _stream_ptr(stream)))
+        return out
+
+    def decode_step(self, k, v, q, pos: int, scale: float = 0.0, out=None, stream=None):
+        """Append k, v (n_seq, n_new, d) at token pos and attend with q over the
+        first pos + n_new tokens (tq_decode_step); fp32 (n_seq, G, d)."""
+        torch = _torch()
+        if k.dtype != v.dtype or k.dtype != q.dtype:
+            raise TypeError("k, v and q must share one dtype")
+        n_new, G = k.shape[1], q.shape[1]
+        if out is None:
+            out = torch.empty((self.n_seq, G, self.ctx.cfg.head_dim), dtype=torch.float32, device=q.device)
+        ws = self.workspace(G, pos + n_new)
+        _check(lib().tq_decode_step(self.ctx.handle, ctypes.byref(self.view), _dev(k, "k"), _dev(v, "v"),
+                                    _dtype_code(k), pos, n_new, _dev(q, "q"), G, float(scale), _dev(out, "out"),
+                                    ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
         return out
 
     def topk(self, q, n_tokens: int, k: int = 10, stream=None):

@@ -130,6 +130,9 @@ def test_hot_path_entry_points_reject_null_context():
                               ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 20, None) == -1
     assert lib.tq_get_values(None, ctypes.byref(view), 0, 1, ctypes.c_void_p(16), None) == -1
     assert lib.tq_get_keys(None, ctypes.byref(view), 0, 1, ctypes.c_void_p(16), None) == -1
+    assert lib.tq_decode_step(None, ctypes.byref(view), ctypes.c_void_p(16), ctypes.c_void_p(16), 1, 0, 1,
+                              ctypes.c_void_p(16), 4, 0.0, ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 20,
+                              None) == -1
     assert lib.tq_codebook_load(None, 3, None, None) == -1
     assert lib.tq_destroy(None) == 0
 
