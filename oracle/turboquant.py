@@ -34,7 +34,9 @@ Readings taken where the pages are silent:
   * norms ||k|| and gamma = ||r|| are kept in fp32;
   * scores are unscaled <q, k> estimates; attention applies scale (1/sqrt(d)
     by default) before the softmax;
-  * a zero vector has x = 0 (it is still encoded, and contributes nothing).
+  * a zero vector has x = 0 (it is still encoded, and contributes nothing);
+  * keys at 0 bits (the (b-1) + QJL bit budget at b = 1) use the single cell
+    0: no code words, r = y, and the score is the plain QJL estimate.
 
 Parity pins for every function are in tests/test_oracle_pins.py.
 """
@@ -132,8 +134,14 @@ def lloyd_max_codebook(dim: int, bits: int) -> tuple[np.ndarray, np.ndarray]:
     The rotated coordinates of a unit vector are modelled as N(0, 1/d)
     ([atskills] Why Random Rotation?; [superapi] 算法细节 / 随机旋转), so the
     codebook is the standard-normal one scaled by 1/sqrt(d)."""
-    if not (1 <= bits <= 8):
-        raise ValueError("bits must be in 1..8")
+    if not (0 <= bits <= 8):
+        raise ValueError("bits must be in 0..8")
+    if bits == 0:
+        # One cell covering the whole line: no boundary, and the Lloyd-Max
+        # centroid of that cell is the mean of N(0, 1/d), 0.  Keys at 0 bits
+        # are then pure QJL signs of the rotated direction ([atskills] Stage 2
+        # applied to r = y).
+        return np.zeros(0), np.zeros(1)
     beta, c = _lloyd_max_standard(bits)
     s = 1.0 / math.sqrt(dim)
     return np.asarray(beta) * s, np.asarray(c) * s
@@ -385,9 +393,11 @@ def pack_keys(idx, signs, norm, gamma, bits: int) -> np.ndarray:
     m = signs.shape[-1]
     n_oct = d // 128
     rec = np.zeros(lead + (key_record_words(d, m, bits),), dtype=np.uint32)
+    if bits == 0 and np.any(idx != 0):
+        raise ValueError("0-bit keys have the single cell 0")
     # coordinate 16 t + 4 q + i  ->  (q, g = t // 8, s = t % 8, i)
     cq = idx.reshape(lead + (n_oct, 8, 4, 4))          # (..., g, s, q, i)
-    for q in range(4):
+    for q in range(4 if bits else 0):
         for g in range(n_oct):
             words = np.zeros(lead + (bits,), dtype=np.uint32)
             _put_codes(words, cq[..., g, :, q, :], bits)
@@ -410,7 +420,7 @@ def unpack_keys(rec, d: int, m: int, bits: int) -> dict:
     lead = rec.shape[:-1]
     n_oct = d // 128
     idx = np.zeros(lead + (n_oct, 8, 4, 4), dtype=np.int64)
-    for q in range(4):
+    for q in range(4 if bits else 0):   # 0-bit records carry no codes
         for g in range(n_oct):
             base = (q * n_oct + g) * bits
             idx[..., g, :, q, :] = _get_codes(rec[..., base:base + bits], bits)

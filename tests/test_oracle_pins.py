@@ -60,11 +60,12 @@ def _gauss_distortion(beta, c):
     return float(np.sum(M2 - 2 * c * M1 + c * c * P))
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("dim", [64, 128, 1024])
 def test_codebook_is_closed_form_fixed_point(bits, dim):
     """P1: the codebook is a fixed point of the Lloyd-Max map written with the
-    closed-form conditional mean of a truncated normal (no integration)."""
+    closed-form conditional mean of a truncated normal (no integration).  At
+    0 bits the one cell is the whole line and its mean is 0."""
     beta, c = O.lloyd_max_codebook(dim, bits)
     s = 1.0 / math.sqrt(dim)
     cs, bs = c / s, beta / s
@@ -92,14 +93,16 @@ def test_one_bit_closed_form():
 def test_distortion_decreases_and_within_shannon_factor():
     """P3: distortion strictly decreases with bits, sits above Shannon's
     bound 4^-b and within the pages' ~2.7x of it (jansverre.net, Hva er
-    TurboQuant, kort fortalt?)."""
+    TurboQuant, kort fortalt?).  At 0 bits it is the variance, 1, exactly."""
     with open(os.path.join(GOLDEN, "pages_figures.txt")) as f:
         ratio_max = [float(l.split()[1]) for l in f if l.startswith("shannon_ratio_max")][0]
     Ds = []
-    for b in (1, 2, 3, 4):
+    for b in (0, 1, 2, 3, 4):
         beta, c = O.lloyd_max_codebook(1, b)
         D = _gauss_distortion(beta, c)
         Ds.append(D)
+        if b == 0:
+            assert abs(D - 1.0) < 1e-15
         assert 4.0 ** -b <= D <= ratio_max * 4.0 ** -b + 1e-3 * 4.0 ** -b
     assert all(x > y for x, y in zip(Ds, Ds[1:]))
 
@@ -168,10 +171,10 @@ def test_zero_vector_encoding():
     d, m = 128, 64
     R = synth.haar_rotation(d, 42)
     S = synth.gaussian_projection(m, d, 43)
-    for bits in (1, 2, 3, 4):
+    for bits in (0, 1, 2, 3, 4):
         beta, c = O.lloyd_max_codebook(d, bits)
         keys = O.compress_keys(np.zeros((1, 1, d)), R, S, beta, c)
-        assert np.all(keys["idx"] == (1 << bits) // 2 - 1)
+        assert np.all(keys["idx"] == max((1 << bits) // 2 - 1, 0))
         assert keys["norm"][0, 0] == 0
         q = synth.unit_gaussian(1, d, 1)[None]
         assert O.key_scores(q, R, S, c, keys)[0, 0, 0] == 0.0
@@ -179,12 +182,15 @@ def test_zero_vector_encoding():
 
 # ----------------------------------------------------------------- QJL -------
 
-def test_qjl_estimator_unbiased_and_variance():
+@pytest.mark.parametrize("bits", [0, 3])
+def test_qjl_estimator_unbiased_and_variance(bits):
     """P6: over 1e5 independent draws of S the score error has mean 0 within
     3 standard errors, and its variance matches the QJL closed form
     ((pi/2) gamma^2 ||q~||^2 - <q~, r>^2) / m within 3%.  The query is picked
-    with <q~, r> = 0.5 ||q~|| gamma so that a wrong constant or sign shows."""
-    d, m, bits, N = 128, 64, 3, 100_000
+    with <q~, r> = 0.5 ||q~|| gamma so that a wrong constant or sign shows.
+    At 0 bits r is the rotated direction itself (gamma = 1): the plain QJL
+    estimator of <q, k>."""
+    d, m, N = 128, 64, 100_000
     R = synth.haar_rotation(d, 42)
     beta, c = O.lloyd_max_codebook(d, bits)
     k = synth.unit_gaussian(1, d, 21, dtype=np.float64)[0] * 1.7
@@ -192,6 +198,8 @@ def test_qjl_estimator_unbiased_and_variance():
     y = vals["y"][0, 0]
     r = y - c[vals["idx"][0, 0]]
     gamma = np.linalg.norm(r)
+    if bits == 0:
+        assert abs(gamma - 1.0) < 1e-14
     # q~ = 0.5 r/|r| + sqrt(0.75) u with u a unit vector orthogonal to r
     u = np.random.default_rng(5).standard_normal(d)
     u -= u @ r / (r @ r) * r
@@ -327,7 +335,7 @@ def _loops_reference(K, V, Q, R, S, beta, c, scale):
     return keys, vals, est, out
 
 
-@pytest.mark.parametrize("bits", [1, 2])
+@pytest.mark.parametrize("bits", [0, 1, 2])
 def test_tiny_brute_force_loops(bits):
     """P10: d=8, m=4, T=16: explicit Python loops equal the vectorised oracle
     exactly for codes and signs and to 1e-12 for scores and attention."""
@@ -380,10 +388,11 @@ def _loops_reference_from(keys, vals, Q, R, S, c, scale, d, m):
 
 # ----------------------------------------------------------------- packing ---
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("d,m", [(128, 64), (256, 128)])
 def test_pack_round_trip(bits, d, m):
-    """P11: unpack(pack(x)) == x for keys and values, ragged token counts."""
+    """P11: unpack(pack(x)) == x for keys and values, ragged token counts
+    (0-bit keys: signs and norms only; values always carry codes)."""
     rng = np.random.default_rng(bits * 7 + d)
     T = 300
     idx = rng.integers(0, 1 << bits, size=(2, T, d))
@@ -397,6 +406,11 @@ def test_pack_round_trip(bits, d, m):
     np.testing.assert_array_equal(u["signs"], signs)
     np.testing.assert_array_equal(u["norm"], norm)
     np.testing.assert_array_equal(u["gamma"], gamma)
+    if bits == 0:
+        assert rec.shape[-1] == m // 32 + 2
+        with pytest.raises(ValueError):
+            O.pack_keys(idx + 1, signs, norm, gamma, 0)
+        return
     blk = O.pack_values(idx, norm, bits)
     assert blk.shape == (2, 3, O.value_block_words(d, bits))
     uv = O.unpack_values(blk, d, bits, n_tokens=T)
@@ -433,6 +447,11 @@ def test_pack_hand_written_bit_positions():
     assert nz(key_rec(0, 0, proj=4)) == {sw0: 0x10000}   # q1 -> upper half
     assert nz(key_rec(0, 0, proj=8)) == {sw0 + 1: 0x1}   # q2 -> next word
     assert nz(key_rec(0, 0, proj=17)) == {sw0: 0x20}     # t1 i1 -> bit 4+1
+    # 0-bit keys: the record starts at the sign words
+    z = O.pack_keys(np.zeros((1, d), np.int64), np.eye(m, dtype=np.uint8)[[41]], np.float32([2.0]),
+                    np.float32([1.0]), 0)[0]
+    assert z.shape == (m // 32 + 2,)
+    assert nz(z) == {1: 0x200, 2: 0x40000000, 3: 0x3F800000}   # proj 41 = t2 q2 i1: word 1 bit 8+1
     # values: one 128-token block
     def val_blk(tok, coord, code):
         idx = np.zeros((1, 128, d), dtype=np.int64)
