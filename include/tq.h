@@ -66,7 +66,7 @@ typedef enum {
   TQ_ENOCODEBOOK = -3,  /* no codebook loaded for the bits this call needs */
   TQ_ENOMEM = -4,       /* device allocation failed (tq_create only) */
   TQ_EDEVICE = -5,      /* a HIP call or kernel launch failed */
-  TQ_EUNSUPPORTED = -6, /* valid but not built (reserved; every valid shape is built) */
+  TQ_EUNSUPPORTED = -6, /* valid but not built (top-k over 0-bit keys) */
   TQ_EWORKSPACE = -7    /* workspace smaller than tq_workspace_bytes */
 } tq_status;
 
@@ -76,8 +76,12 @@ typedef struct tq_ctx tq_ctx;
 
 /* Static shape of a compressed cache.  head_dim d: multiple of 128 up to
  * 1024.  proj_dim m: multiple of 64 up to 512 (default d/2,
- * nav.superapi.store 算法细节 / proj_dim 选择).  key_bits, value_bits in
- * 1..4 (the pages use 2-4; 1 is the 1-bit limit). */
+ * nav.superapi.store 算法细节 / proj_dim 选择).  value_bits in 1..4 and
+ * key_bits in 0..4 (the pages use 2-4; 1 is the 1-bit limit).  key_bits 0
+ * is the bit budget of (b - 1)-bit codes plus QJL signs at b = 1: one cell
+ * whose centroid is 0, so a key keeps only its m sign bits of S R k/||k||
+ * and its norms, and its score is the plain QJL estimate (atskills.one,
+ * Stage 2 applied to the whole rotated direction). */
 typedef struct {
   int32_t head_dim;
   int32_t proj_dim;
@@ -109,7 +113,8 @@ typedef struct {
  *    the code of rotated coordinate 128 g + 16 s + 4 q + i.
  *    Then m/32 sign words: projection coordinate 16 t + 4 q + i is bit
  *    16 (q%2) + 4 (t%4) + i of word 2 (t/4) + q/2 (1 = projection >= 0).
- *    Then fp32 ||k||, then fp32 gamma.  Size 4 (b d/32 + m/32 + 2) bytes.
+ *    Then fp32 ||k||, then fp32 gamma.  Size 4 (b d/32 + m/32 + 2) bytes
+ *    (b = 0: no code groups, the sign words start the record).
  *  Value block (128 tokens): for w = 0..b-1, q = 0..3, coordinate c =
  *    0..d-1, word (w * 4 + q) * d + c; the b words (w = 0..b-1) of (q, c)
  *    form a code group whose slot s, byte lane i is the code of coordinate c
@@ -131,7 +136,8 @@ typedef struct {
  * (nav.superapi.store 核心 API build_lloyd_max_codebook(dim, bits) ->
  * (boundaries, centroids); 限制与注意事项: computed once per (dim, bits)).
  * Writes 2^bits ascending centroids and 2^bits - 1 ascending boundaries
- * (host arrays owned by the caller).  bits in 1..4, head_dim >= 1.
+ * (host arrays owned by the caller).  bits in 0..4, head_dim >= 1; at 0 bits
+ * the one centroid is 0 and boundaries may be NULL.
  * Returns TQ_EINVAL on bad arguments. */
 int tq_lloyd_max_codebook(int32_t head_dim, int32_t bits, double* centroids, double* boundaries);
 
@@ -175,6 +181,8 @@ int tq_destroy(tq_ctx* ctx);
  * key_bits and value_bits before any append or attention call.  Host-only:
  * the codebook travels to the kernels as launch arguments. */
 int tq_codebook_load(tq_ctx* ctx, int32_t bits, const double* centroids, const double* boundaries);
+/* (bits 0..4; at 0 bits the single centroid must be 0 and boundaries may be
+ * NULL.) */
 
 /* ---- hot path ---------------------------------------------------------------- */
 
@@ -256,7 +264,8 @@ size_t tq_topk_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, i
  * ordered by score descending, equal scores by position ascending; when
  * n_tokens < k the rest is (-inf, -1).  q as for tq_attention_scores,
  * 1 <= G <= 512, 1 <= k <= 16.  workspace >= tq_topk_workspace_bytes.
- * Errors: TQ_EINVAL, TQ_ENOCODEBOOK, TQ_EWORKSPACE, TQ_EDEVICE. */
+ * Errors: TQ_EINVAL, TQ_ENOCODEBOOK, TQ_EWORKSPACE, TQ_EDEVICE,
+ * TQ_EUNSUPPORTED (key_bits 0). */
 int tq_topk_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
                    int64_t n_tokens, int32_t k, float* top_scores, int32_t* top_index, void* workspace,
                    size_t workspace_bytes, void* stream);
@@ -276,7 +285,8 @@ int tq_get_values(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t 
 
 /* The same reconstruction of cached keys from their stage-1 codes and norms,
  * ||k|| R^T c[idx] (the MSE part; the QJL sign bits estimate inner products
- * and do not reconstruct the residual).  Same arguments and errors. */
+ * and do not reconstruct the residual; with key_bits 0 it is all zeros).
+ * Same arguments and errors. */
 int tq_get_keys(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_tokens, float* out,
                 void* stream);
 

@@ -50,14 +50,17 @@ static int check_config(const tq_config* c) {
     return fail(TQ_EINVAL, "head_dim %d: need a multiple of 128 in [128, 1024]", c->head_dim);
   if (c->proj_dim < 64 || c->proj_dim > 512 || c->proj_dim % 64)
     return fail(TQ_EINVAL, "proj_dim %d: need a multiple of 64 in [64, 512]", c->proj_dim);
-  if (c->key_bits < 1 || c->key_bits > 4 || c->value_bits < 1 || c->value_bits > 4)
-    return fail(TQ_EINVAL, "key_bits %d / value_bits %d: need 1..4", c->key_bits, c->value_bits);
+  if (c->key_bits < 0 || c->key_bits > 4 || c->value_bits < 1 || c->value_bits > 4)
+    return fail(TQ_EINVAL, "key_bits %d / value_bits %d: need 0..4 / 1..4", c->key_bits, c->value_bits);
   return TQ_OK;
 }
 
 // Shapes with the single-kernel compress / attention path; every other valid
-// shape runs on the general path (tq_general.hip).
-static bool fast_keys(const tq_config& c) { return c.head_dim == kD && (c.proj_dim == 64 || c.proj_dim == 128); }
+// shape runs on the general path (tq_general.hip).  Keys of 0 bits (signs
+// and norms only) always take the general path.
+static bool fast_keys(const tq_config& c) {
+  return c.head_dim == kD && (c.proj_dim == 64 || c.proj_dim == 128) && c.key_bits > 0;
+}
 static bool fast_values(const tq_config& c) { return c.head_dim == kD; }
 static bool fast_attn(const tq_config& c, int G) { return fast_keys(c) && G <= 16; }
 constexpr int64_t kScratchRows = 32768;  // general-path rows per launch
@@ -234,8 +237,8 @@ int tq_destroy(tq_ctx* ctx) {
 int tq_codebook_load(tq_ctx* ctx, int32_t bits, const double* centroids, const double* boundaries) {
   clear_error();
   if (!ctx) return fail(TQ_EINVAL, "tq_codebook_load: ctx is NULL");
-  if (bits < 1 || bits > 4) return fail(TQ_EINVAL, "tq_codebook_load: bits %d not in 1..4", bits);
-  if (!centroids || !boundaries) return fail(TQ_EINVAL, "tq_codebook_load: NULL table");
+  if (bits < 0 || bits > 4) return fail(TQ_EINVAL, "tq_codebook_load: bits %d not in 0..4", bits);
+  if (!centroids || (bits > 0 && !boundaries)) return fail(TQ_EINVAL, "tq_codebook_load: NULL table");
   const int L = 1 << bits;
   for (int i = 0; i < L; ++i) {
     if (!std::isfinite(centroids[i])) return fail(TQ_EINVAL, "tq_codebook_load: non-finite centroid %d", i);
@@ -312,8 +315,9 @@ int tq_append_key(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_append_key: hipSetDevice failed");
   // a decode step on the general path: one launch instead of the tiled
   // norm / rotation / projection kernels (with head_dim 128 the single
-  // matrix-core kernel is as quick for a few tokens)
-  if (n_new <= kSmallAppend && !fast_keys(ctx->cfg))
+  // matrix-core kernel is as quick for a few tokens).  0-bit keys (no codes)
+  // always take this kernel.
+  if ((n_new <= kSmallAppend && !fast_keys(ctx->cfg)) || ctx->cfg.key_bits == 0)
     rc = launch_small_keys(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.head_dim,
                            ctx->cfg.proj_dim, s, cache->key_records, stream);
   else if (fast_keys(ctx->cfg))
@@ -512,6 +516,7 @@ int tq_topk_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32
     return fail(TQ_EINVAL, "%s: q, outputs and workspace must be 16-byte aligned", fn);
   if (!ctx->loaded[ctx->cfg.key_bits])
     return fail(TQ_ENOCODEBOOK, "%s: no %d-bit key codebook loaded", fn, ctx->cfg.key_bits);
+  if (ctx->cfg.key_bits == 0) return fail(TQ_EUNSUPPORTED, "%s: 0-bit keys are not supported", fn);
   const size_t need = topk_plan(ctx->cfg.head_dim, ctx->cfg.proj_dim, cache->n_seq, G, n_tokens, k).total;
   if (workspace_bytes < need) return fail(TQ_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "%s: hipSetDevice failed", fn);

@@ -109,8 +109,12 @@ bool lloyd_max_standard(int bits, double* c, double* beta) {
 }  // namespace tq
 
 extern "C" int tq_lloyd_max_codebook(int32_t head_dim, int32_t bits, double* centroids, double* boundaries) {
-  if (head_dim < 1 || bits < 1 || bits > 4 || !centroids || !boundaries)
-    return tq::fail(TQ_EINVAL, "tq_lloyd_max_codebook: need head_dim >= 1, bits in 1..4, non-null outputs");
+  if (head_dim < 1 || bits < 0 || bits > 4 || !centroids || (bits > 0 && !boundaries))
+    return tq::fail(TQ_EINVAL, "tq_lloyd_max_codebook: need head_dim >= 1, bits in 0..4, non-null outputs");
+  if (bits == 0) {  // one cell, the whole line: its centroid is the mean, 0
+    centroids[0] = 0.0;
+    return TQ_OK;
+  }
   double c[16], b[16];
   if (!tq::lloyd_max_standard(bits, c, b)) return tq::fail(TQ_EINVAL, "tq_lloyd_max_codebook: no convergence");
   const double s = 1.0 / std::sqrt((double)head_dim);

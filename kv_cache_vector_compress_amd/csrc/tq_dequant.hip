@@ -34,6 +34,7 @@ __device__ __forceinline__ int group_code(const uint32_t* w, int stride, int b, 
   const int sh = 8 * i;
   auto byte = [&](int k) { return (w[k * stride] >> sh) & 0xFFu; };
   switch (b) {
+    case 0: return 0;  // one cell
     case 1: return (byte(0) >> s) & 1;
     case 2: return (byte(s >> 2) >> (2 * (s & 3))) & 3;
     case 4: return (byte(s >> 1) >> (4 * (s & 1))) & 15;

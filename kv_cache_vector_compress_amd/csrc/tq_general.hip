@@ -615,19 +615,22 @@ __global__ __launch_bounds__(256) void gen_scores(const GenScoreArgs a) {
   f4 acc[HG];
 #pragma unroll
   for (int g = 0; g < HG; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < a.n_oct; ++c) {
-    uint32_t cw[B];
+  // 0-bit keys have the single centroid 0: no MSE term
+  if constexpr (B > 0) {
+    for (int c = 0; c < a.n_oct; ++c) {
+      uint32_t cw[B];
 #pragma unroll
-    for (int w = 0; w < B; ++w) cw[w] = rp[(q * a.n_oct + c) * B + w];
-    const h8 A0 = decode_pair<B, 0>(cw, tlo, thi), A1 = decode_pair<B, 2>(cw, tlo, thi);
-    const h8 A2 = decode_pair<B, 4>(cw, tlo, thi), A3 = decode_pair<B, 6>(cw, tlo, thi);
+      for (int w = 0; w < B; ++w) cw[w] = rp[(q * a.n_oct + c) * B + w];
+      const h8 A0 = decode_pair<B, 0>(cw, tlo, thi), A1 = decode_pair<B, 2>(cw, tlo, thi);
+      const h8 A2 = decode_pair<B, 4>(cw, tlo, thi), A3 = decode_pair<B, 6>(cw, tlo, thi);
 #pragma unroll
-    for (int g = 0; g < HG; ++g) {
-      const uint16_t* wg = wq + ((int64_t)g * KBT + 4 * c) * 64 * 8;
-      acc[g] = mfma(A0, *(const h8*)(wg), acc[g]);
-      acc[g] = mfma(A1, *(const h8*)(wg + 64 * 8), acc[g]);
-      acc[g] = mfma(A2, *(const h8*)(wg + 2 * 64 * 8), acc[g]);
-      acc[g] = mfma(A3, *(const h8*)(wg + 3 * 64 * 8), acc[g]);
+      for (int g = 0; g < HG; ++g) {
+        const uint16_t* wg = wq + ((int64_t)g * KBT + 4 * c) * 64 * 8;
+        acc[g] = mfma(A0, *(const h8*)(wg), acc[g]);
+        acc[g] = mfma(A1, *(const h8*)(wg + 64 * 8), acc[g]);
+        acc[g] = mfma(A2, *(const h8*)(wg + 2 * 64 * 8), acc[g]);
+        acc[g] = mfma(A3, *(const h8*)(wg + 3 * 64 * 8), acc[g]);
+      }
     }
   }
   const float gamma = __uint_as_float(rp[a.rec_words - 1]);
@@ -1032,7 +1035,7 @@ int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbit
 #define TQ_GS(B, H) \
   if (kbits == B && HG == H) hipLaunchKernelGGL((gen_scores<B, H>), grid, block, 0, st, a);
 #define TQ_GSB(B) TQ_GS(B, 1) TQ_GS(B, 2) TQ_GS(B, 4) TQ_GS(B, 8) TQ_GS(B, 16) TQ_GS(B, 32)
-  TQ_GSB(1) TQ_GSB(2) TQ_GSB(3) TQ_GSB(4)
+  TQ_GSB(0) TQ_GSB(1) TQ_GSB(2) TQ_GSB(3) TQ_GSB(4)
 #undef TQ_GSB
 #undef TQ_GS
   return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;

@@ -31,6 +31,7 @@ struct SmallArgs {
   const float* r32;     // R [d][d]
   const float* s32;     // S [m][d]
   int64_t n_new, pos, capacity;
+  int64_t bid0;         // first (slot, token) index of this launch
   int n_seq, d, m, bits, rec_words, block_words;
   float beta[16];       // boundaries (+inf past the last)
   float cent[16];
@@ -124,6 +125,7 @@ __device__ __forceinline__ int cell(float u, const float (&beta)[15]) {
 __device__ __forceinline__ uint32_t code_bits(int b, int w, int s, int i, uint32_t v) {
   uint32_t f = 0;
   switch (b) {
+    case 0: break;  // no code words
     case 1: f = w == 0 ? v << s : 0u; break;
     case 2: f = w == (s >> 2) ? v << (2 * (s & 3)) : 0u; break;
     case 4: f = w == (s >> 1) ? v << (4 * (s & 1)) : 0u; break;
@@ -213,7 +215,7 @@ __device__ __forceinline__ void small_keys_block(const SmallArgs& a, int64_t bid
 }
 
 __global__ __launch_bounds__(kSmallThreads) void small_keys_kernel(const SmallArgs a) {
-  small_keys_block(a, blockIdx.x);
+  small_keys_block(a, a.bid0 + blockIdx.x);
 }
 
 // One workgroup's work of small_values_kernel for block index bid.
@@ -302,6 +304,7 @@ static SmallArgs small_args(const Matrices& mats, const CodebookDev& cb, int bit
   a.s32 = mats.s32;
   a.n_new = s.n_new;
   a.pos = s.pos;
+  a.bid0 = 0;
   a.capacity = s.capacity;
   a.n_seq = s.n_seq;
   a.d = d;
@@ -329,11 +332,17 @@ int small_device_init() {
 
 int launch_small_keys(const Matrices& mats, const CodebookDev& cb, int bits, int d, int m, const AppendShape& s,
                       void* key_records, void* stream) {
-  const SmallArgs a = small_args(mats, cb, bits, d, m, s, key_records);
+  SmallArgs a = small_args(mats, cb, bits, d, m, s, key_records);
   const size_t lds = sizeof(float) * (size_t)(4 * d + m);
-  hipLaunchKernelGGL(small_keys_kernel, dim3((unsigned)(s.n_seq * s.n_new)), dim3(kSmallThreads), lds,
-                     (hipStream_t)stream, a);
-  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+  // one workgroup per (slot, token); launches of at most 2^23 workgroups
+  // keep the grid's thread count within 32 bits
+  const int64_t total = (int64_t)s.n_seq * s.n_new, chunk = (int64_t)1 << 23;
+  for (a.bid0 = 0; a.bid0 < total; a.bid0 += chunk) {
+    const int64_t nb = std::min(chunk, total - a.bid0);
+    hipLaunchKernelGGL(small_keys_kernel, dim3((unsigned)nb), dim3(kSmallThreads), lds, (hipStream_t)stream, a);
+    if (hipGetLastError() != hipSuccess) return TQ_EDEVICE;
+  }
+  return 0;
 }
 
 int launch_decode_prep(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,

@@ -47,14 +47,23 @@ def test_codebook_builder_rejects_bad_arguments():
     P = c.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
     Q = b.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
     lib = tq.lib()
-    assert lib.tq_lloyd_max_codebook(128, 0, P, Q) == -1
+    assert lib.tq_lloyd_max_codebook(128, -1, P, Q) == -1
     assert lib.tq_lloyd_max_codebook(128, 5, P, Q) == -1
     assert lib.tq_lloyd_max_codebook(0, 3, P, Q) == -1
     assert lib.tq_lloyd_max_codebook(128, 3, None, Q) == -1
     assert "bits" in tq.last_error()
 
 
-@pytest.mark.parametrize("kb,vb,m", [(3, 3, 64), (2, 4, 128), (1, 1, 64), (4, 2, 512)])
+def test_zero_bit_codebook():
+    """0 bits: the one centroid 0 and no boundary, as the oracle has it."""
+    c, b = tq.lloyd_max_codebook(128, 0)
+    ob, oc = O.lloyd_max_codebook(128, 0)
+    assert c.tolist() == oc.tolist() == [0.0] and b.size == ob.size == 0
+    cc = np.zeros(1)
+    assert tq.lib().tq_lloyd_max_codebook(128, 0, cc.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), None) == 0
+
+
+@pytest.mark.parametrize("kb,vb,m", [(3, 3, 64), (2, 4, 128), (1, 1, 64), (4, 2, 512), (0, 3, 64), (0, 1, 512)])
 def test_sizes_follow_record_layout(kb, vb, m):
     cfg = tq.Config(128, m, kb, vb)
     assert tq.key_record_bytes(cfg) == 4 * (kb * 128 // 32 + m // 32 + 2) == 4 * O.key_record_words(128, m, kb)
@@ -91,7 +100,8 @@ def test_3bit_record_is_64_bytes_and_block_is_52_bytes_per_token():
 
 
 @pytest.mark.parametrize("cfg,code", [
-    ((100, 64, 3, 3), -1), ((128, 48, 3, 3), -1), ((128, 64, 0, 3), -1), ((128, 64, 3, 5), -1),
+    ((100, 64, 3, 3), -1), ((128, 48, 3, 3), -1), ((128, 64, -1, 3), -1), ((128, 64, 3, 5), -1),
+    ((128, 64, 3, 0), -1), ((128, 64, 5, 3), -1),
     ((2048, 64, 3, 3), -1), ((1152, 64, 3, 3), -1), ((192, 64, 3, 3), -1), ((128, 576, 3, 3), -1),
     ((128, 96, 3, 3), -1)])
 def test_create_rejects_configs_before_any_device_call(cfg, code):

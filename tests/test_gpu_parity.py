@@ -472,6 +472,7 @@ def test_small_appends_decode_like(d, m, kb, vb, dtype):
     (128, 128, 4, 2, np.float32, 8),
     (128, 64, 2, 1, np.float16, 16),
     (256, 128, 3, 3, np.float16, 4),   # not a single-kernel shape: the three calls in order
+    (128, 64, 0, 3, np.float16, 8),    # 0-bit keys: the three calls in order
 ])
 def test_decode_steps_match_oracle(d, m, kb, vb, dtype, G):
     """tq_decode_step after a prefill: each step appends 1..16 tokens (crossing
@@ -525,4 +526,42 @@ def test_decode_steps_match_oracle(d, m, kb, vb, dtype, G):
     _say("per step (n_tokens, attend vs oracle on GPU codes, end to end)", errs)
     if st["idx_flips"] + st["sign_flips"] + st["v_idx_flips"] == 0:
         assert max(e[2] for e in errs) <= P.ATTEND_TOL
+    ctx.close()
+
+
+# ---------------------------------------------------------------------------
+# 0-bit keys: the (b - 1)-bit + QJL budget at b = 1, signs and norms only
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,m,vb,dtype,G", [
+    (128, 64, 3, np.float16, 8),
+    (128, 128, 2, np.float32, 4),
+    (256, 128, 4, np.float16, 20),   # scores only (G > 16)
+    (1024, 512, 4, np.float32, 16),
+])
+def test_zero_bit_keys(d, m, vb, dtype, G):
+    """key_bits = 0: records of m sign bits of S R k/||k|| and the two norms
+    (gamma = 1), appended in unaligned chunks (one-token and bulk appends)
+    with a zero key inside; signs, norms, scores (the plain QJL estimate) and
+    attention against the oracle.  The key reconstruction is all zeros and
+    top-k reports TQ_EUNSUPPORTED."""
+    n_seq, T = 2, 700
+    K = np.stack([synth.kv_slot(130 + d, s, s, T, d, dtype=dtype) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(131 + d, s, s, T, d, dtype=dtype) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(132 + d, s, s, G, d, dtype=dtype) for s in range(n_seq)])
+    K[1, 130] = 0  # the one-token chunk at 130
+    K[0, 400] = 0
+    _say("zero-bit keys", (d, m, vb, np.dtype(dtype).name, G))
+    assert tq.key_record_bytes(tq.Config(d, m, 0, vb)) == 4 * (m // 32 + 2)
+    _say(run_case(K, V, Q, kb=0, vb=vb, m=m, chunks=[130, 1, 300, 269], check_attend=G <= 16))
+    ctx, R, S = make_ctx(d, m, 0, vb)
+    cache = tq.KVCache(ctx, n_seq, 768)
+    cache.append_key(torch.from_numpy(np.ascontiguousarray(K[:, :50])).cuda(), 0)
+    rec = P.unpack_gpu_keys(cache, d, m, 0, 50)
+    assert np.all(np.abs(rec["gamma"][K[:, :50].any(-1)] - 1.0) < 1e-6)
+    assert not cache.get_keys(0, 50).cpu().numpy().any()
+    qt = torch.from_numpy(np.ascontiguousarray(Q[:, :4])).cuda()
+    with pytest.raises(tq.TQError) as e:
+        cache.topk(qt, 50, 4)
+    assert e.value.code == -6
     ctx.close()
