@@ -59,8 +59,9 @@ __device__ __forceinline__ void tk_insert(float* ls, int32_t* li, int k, float s
 // A lane's words of one 16-token tile: code group (B words) of each of the
 // NOCT coordinate chunks, 8 sign words (m/64 of them used), ||k|| and gamma.
 // Every word is loaded unconditionally (unused sign words read neighbouring
-// record bytes, or zeros past the slot), so the loads of the next tile can be
-// counted exactly and stay in flight while the current tile is processed.
+// record bytes, or zeros past the range's records), so the loads of the next
+// tile can be counted exactly and stay in flight while the current tile is
+// processed.
 template <int B, int NOCT>
 struct TkRec {
   uint32_t cw[NOCT][B];
@@ -112,15 +113,17 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
   float* wls = ls + wave * 32 * a.k;
   int32_t* wli = li + wave * 32 * a.k;
 
-  // this slot's records as a buffer; a lane's words of one tile (its code
-  // group of every chunk, its sign words, the two norms) are loaded one tile
-  // ahead of their use
+  // this range's records as a buffer (the plan keeps a range's records
+  // under 2^31 bytes, so 32-bit offsets reach them at any capacity); a
+  // lane's words of one tile (its code group of every chunk, its sign words,
+  // the two norms) are loaded one tile ahead of their use
+  const int64_t r0 = t_lo * 16, r1 = min(a.capacity, t_hi * 16);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(a.rec + (int64_t)slot * a.capacity * a.rec_words), (short)0,
-      (int)((uint32_t)a.capacity * (uint32_t)a.rec_words * 4u), 0x00020000);
+      const_cast<uint32_t*>(a.rec + ((int64_t)slot * a.capacity + r0) * a.rec_words), (short)0,
+      (int)((uint32_t)(r1 - r0) * (uint32_t)a.rec_words * 4u), 0x00020000);
   auto load_tile = [&](TkRec<B, NOCT>& r, int64_t tile) {
     const int row = min((int)(tile * 16) + r16, n_tok - 1);
-    const uint32_t ro = (uint32_t)row * (uint32_t)a.rec_words * 4u;
+    const uint32_t ro = (uint32_t)(row - (int)r0) * (uint32_t)a.rec_words * 4u;
 #pragma unroll
     for (int c = 0; c < NOCT; ++c) {
       const uint32_t oc = ro + 4u * (uint32_t)((q * NOCT + c) * B);
@@ -336,6 +339,11 @@ TopkPlan topk_plan(int d, int m, int n_seq, int G, int64_t n_tokens, int k) {
   int64_t R = (1024 + (int64_t)n_seq * p.n_qblk - 1) / ((int64_t)n_seq * p.n_qblk);
   R = std::min<int64_t>(R, (ntile + kTkWaves - 1) / kTkWaves);
   R = std::max<int64_t>(1, std::min<int64_t>(R, 256));
+  // a range's records (4-bit codes at most) stay under 2^31 bytes: the
+  // kernel addresses them with 32-bit offsets
+  const int64_t rec_max = 4 * (4 * (int64_t)d / 32 + m / 32 + 2);
+  const int64_t max_tiles = ((int64_t)1 << 31) / (16 * rec_max) - 1;
+  R = std::max<int64_t>(R, (ntile + max_tiles - 1) / max_tiles);
   p.tiles_per_range = (ntile + R - 1) / R;
   p.n_ranges = (int)((ntile + p.tiles_per_range - 1) / p.tiles_per_range);
   p.n_lists = p.n_ranges * kTkWaves;

@@ -565,3 +565,42 @@ def test_zero_bit_keys(d, m, vb, dtype, G):
         cache.topk(qt, 50, 4)
     assert e.value.code == -6
     ctx.close()
+
+
+def test_topk_at_maximum_capacity():
+    """Top-k over a slot of the maximum capacity (2^24 tokens) of 584-byte
+    records (d = 1024, m = 512, 4-bit): 9.8 GB of records, so the tokens at
+    the end of the slot sit past 2^32 bytes from its start.  3000 keys are
+    appended at the end (the rest are zero records, which score 0); the top-k
+    over all 2^24 tokens equals the top-k of tq_attention_scores' estimates
+    of the appended tokens, and is a valid top-k of the oracle's estimates."""
+    d, m, b, G, k, N = 1024, 512, 4, 64, 10, 3000
+    cap = 1 << 24
+    pos = cap - N - 5
+    _say("topk at maximum capacity", (d, m, b, cap, pos, G, k))
+    X = synth.vector_database(N, d, seed=140)[None]
+    Q = synth.unit_gaussian(G, d, seed=141)[None]
+    ctx, R, S = make_ctx(d, m, b, b)
+    cache = tq.KVCache(ctx, 1, cap)
+    cache.append_key(torch.from_numpy(X).cuda(), pos)
+    qt = torch.from_numpy(Q).cuda()
+    ts, ti = cache.topk(qt, cap, k)
+    sc = cache.attention_scores(qt, cap)[..., pos:pos + N].cpu().numpy()
+    ts, ti = ts.cpu().numpy(), ti.cpu().numpy()
+    assert np.all((sc > 0).sum(-1) >= k)  # the zero records (score 0) cannot enter
+    ref_i = _topk_reference(sc, k)
+    assert np.array_equal(ti, ref_i + pos), "top-k indices differ from the materialised scores' top-k"
+    assert np.array_equal(ts, np.take_along_axis(sc, ref_i, -1)), "top-k scores differ"
+    rw = tq.key_record_bytes(ctx.cfg) // 4
+    recs = cache.key_records.view(1, cap, rw)[:, pos:pos + N].cpu().numpy().view(np.uint32)
+    beta, c = O.lloyd_max_codebook(d, b)
+    gk = O.unpack_keys(recs, d, m, b)
+    ref = O.key_scores(Q.astype(np.float64), R, S, c, gk)
+    tol = P.SCORE_TOL * np.linalg.norm(Q, axis=-1)[..., None] * np.linalg.norm(X, axis=-1)[:, None, :]
+    picked = np.zeros(ref.shape, dtype=bool)
+    np.put_along_axis(picked, (ti - pos).astype(np.int64), True, axis=-1)
+    lo = np.min(np.where(picked, ref + tol, np.inf), axis=-1)
+    hi = np.max(np.where(picked, -np.inf, ref - tol), axis=-1)
+    assert np.all(hi <= lo), "a token left out beats a returned one by more than the score tolerance"
+    del cache
+    ctx.close()
