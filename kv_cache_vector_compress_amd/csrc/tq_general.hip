@@ -25,6 +25,8 @@
 //   gen_values        y for one 128-token block x 128 coordinates; codes
 //   gen_prep_queries  q~ = R q and p = S q~ per query head, as MFMA operands
 //   gen_scores        scores of 16 tokens for every query head
+#include <algorithm>
+
 #include "tq_device.h"
 #include "tq_prep.h"
 
@@ -592,6 +594,7 @@ struct GenScoreArgs {
   int64_t n_tokens, capacity;
   int n_seq, G, HG, d, m, n_oct, rec_words;
   int64_t tiles_per_slot;
+  int64_t gw0;  // first (slot, tile) wave of this launch
   float kappa;
   uint32_t tlo[4], thi[4];
 };
@@ -600,7 +603,7 @@ template <int B, int HG>
 __global__ __launch_bounds__(256) void gen_scores(const GenScoreArgs a) {
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, q = lane >> 4;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t gw = a.gw0 + (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (gw >= a.tiles_per_slot * a.n_seq) return;
   const int slot = (int)(gw / a.tiles_per_slot);
   const int64_t tile = gw - (int64_t)slot * a.tiles_per_slot;
@@ -1030,15 +1033,21 @@ int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbit
   a.tiles_per_slot = (s.n_tokens + 15) / 16;
   a.kappa = (float)(1.2533141373155002512 / m);  // sqrt(pi/2) / m
   for (int i = 0; i < 4; ++i) { a.tlo[i] = cbk.tlo[i]; a.thi[i] = cbk.thi[i]; }
-  const int64_t waves = a.tiles_per_slot * s.n_seq;
-  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  // one wave per (slot, 16-token tile), in launches of at most 2^22
+  // workgroups so that a grid's thread count stays within 32 bits
+  const int64_t waves = a.tiles_per_slot * s.n_seq, chunk = (int64_t)4 << 22;
+  for (a.gw0 = 0; a.gw0 < waves; a.gw0 += chunk) {
+    const int64_t nw = std::min(chunk, waves - a.gw0);
+    const dim3 grid((unsigned)((nw + 3) / 4)), block(256);
 #define TQ_GS(B, H) \
   if (kbits == B && HG == H) hipLaunchKernelGGL((gen_scores<B, H>), grid, block, 0, st, a);
 #define TQ_GSB(B) TQ_GS(B, 1) TQ_GS(B, 2) TQ_GS(B, 4) TQ_GS(B, 8) TQ_GS(B, 16) TQ_GS(B, 32)
-  TQ_GSB(0) TQ_GSB(1) TQ_GSB(2) TQ_GSB(3) TQ_GSB(4)
+    TQ_GSB(0) TQ_GSB(1) TQ_GSB(2) TQ_GSB(3) TQ_GSB(4)
 #undef TQ_GSB
 #undef TQ_GS
-  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+    if (hipGetLastError() != hipSuccess) return TQ_EDEVICE;
+  }
+  return 0;
 }
 
 

@@ -604,3 +604,33 @@ def test_topk_at_maximum_capacity():
     assert np.all(hi <= lo), "a token left out beats a returned one by more than the score tolerance"
     del cache
     ctx.close()
+
+
+def test_general_scores_beyond_one_launch():
+    """The general score kernel runs one wave per (slot, 16-token tile) and is
+    launched in pieces of 2^24 waves: 17 slots of 2^24 tokens (0-bit keys,
+    4.6 GB of records) need two.  Keys appended at the end of every slot
+    (the last slot's in the second piece) score as the oracle says on the
+    GPU's records; the zero records score 0."""
+    d, m, kb, vb, G, N = 128, 64, 0, 1, 4, 500
+    n_seq, cap = 17, 1 << 24
+    pos = cap - N
+    _say("general scores in pieces", (n_seq, cap, kb, G))
+    K = np.stack([synth.kv_slot(150, s, s, N, d) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(151, s, s, G, d) for s in range(n_seq)])
+    ctx, R, S = make_ctx(d, m, kb, vb)
+    cache = tq.KVCache(ctx, n_seq, cap)
+    cache.append_key(torch.from_numpy(K).cuda(), pos)
+    sc_all = cache.attention_scores(torch.from_numpy(Q).cuda(), cap)
+    sc = sc_all[..., pos:].cpu().numpy()
+    assert float(sc_all[..., :pos].abs().max()) == 0.0
+    del sc_all
+    rw = tq.key_record_bytes(ctx.cfg) // 4
+    recs = cache.key_records.view(n_seq, cap, rw)[:, pos:].cpu().numpy().view(np.uint32)
+    _, c = O.lloyd_max_codebook(d, kb)
+    ref = O.key_scores(Q.astype(np.float64), R, S, c, O.unpack_keys(recs, d, m, kb))
+    qn = np.linalg.norm(Q.astype(np.float64), axis=-1)
+    kn = np.linalg.norm(K.astype(np.float64), axis=-1)
+    _say({"score_vs_gpu_codes": P.check_scores(sc, ref, qn, kn)})
+    del cache
+    ctx.close()
