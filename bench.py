@@ -260,8 +260,10 @@ def bench_qwen_decode(args):
 
 def bench_bit_sweep(args):
     """Bit-width sweep on the Qwen decode shape (72 slots x 8192 tokens): for
-    2-, 3- and 4-bit keys (m=64) and values, bulk compression rate, score
-    GB/s, and fidelity of the attention weights against exact fp16 attention
+    2-, 3- and 4-bit keys (m=64) and values, and for the bit budget variant
+    with (b - 1)-bit key codes at b = 1..4 (0-bit keys are QJL signs only),
+    bulk compression rate, score GB/s, and fidelity of the attention weights
+    against exact fp16 attention
     (cosine of the softmax rows and top-1 match, evaluated with torch on the
     GPU), with the plain queries and with queries rescaled to a logit
     standard deviation of 2 (a diagnostic: plain queries give nearly uniform
@@ -280,8 +282,11 @@ def bench_bit_sweep(args):
     rescale = 2.0 / float((exact * scale).std())
     reps = max(args.steps, 10)
     res = {}
-    for b in (2, 3, 4):
-        ctx = tq.Context(d, m, b, b, R, S)
+    # b-bit keys (b-bit codes plus m QJL signs) at 2-4 bits, then the bit
+    # budget variant: (b - 1)-bit codes plus the signs at b = 1..4 (key_bits
+    # 0 at b = 1 is pure QJL), values at b bits
+    for b, kb in ((2, 2), (3, 3), (4, 4), (1, 0), (2, 1), (3, 2), (4, 3)):
+        ctx = tq.Context(d, m, kb, b, R, S)
         cache = tq.KVCache(ctx, n_seq, T)
         sc = torch.empty((n_seq, G, T), dtype=torch.float32, device=dev)
         cache.workspace(G, T)
@@ -301,7 +306,9 @@ def bench_bit_sweep(args):
             fid[tag] = {"cosine_mean": round(float(cos.mean()), 5), "cosine_min": round(float(cos.min()), 5),
                         "top1": round(float(top1), 4)}
         b_sc = n_seq * T * (tq.key_record_bytes(ctx.cfg) + 4 * G)
-        res[f"{b}bit"] = {"compress_keys_per_s": round(n_seq * T / (ck * 1e-3), 1),
+        res[f"{b}bit" if kb == b else f"budget_{b}bit_keys{kb}"] = {
+                          "key_record_bytes": tq.key_record_bytes(ctx.cfg),
+                          "compress_keys_per_s": round(n_seq * T / (ck * 1e-3), 1),
                           "compress_values_per_s": round(n_seq * T / (cv * 1e-3), 1),
                           "scores_ms": round(ts, 4), "scores_GBps": round(b_sc / (ts * 1e-3) / 1e9, 1),
                           "fidelity": fid}

@@ -313,16 +313,19 @@ int tq_append_key(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_
   if (n_new == 0) return TQ_OK;
   AppendShape s{k, dtype, n_new, pos, cache->capacity, cache->n_seq};
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_append_key: hipSetDevice failed");
-  // a decode step on the general path: one launch instead of the tiled
-  // norm / rotation / projection kernels (with head_dim 128 the single
-  // matrix-core kernel is as quick for a few tokens).  0-bit keys (no codes)
-  // always take this kernel.
-  if ((n_new <= kSmallAppend && !fast_keys(ctx->cfg)) || ctx->cfg.key_bits == 0)
-    rc = launch_small_keys(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.head_dim,
-                           ctx->cfg.proj_dim, s, cache->key_records, stream);
-  else if (fast_keys(ctx->cfg))
-    rc = launch_compress_keys(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.proj_dim, s,
-                              cache->key_records, stream);
+  // A decode step on the general path takes one launch of the small kernel
+  // instead of the tiled norm / rotation / projection kernels (with head_dim
+  // 128 the single matrix-core kernel is as quick for a few tokens).  0-bit
+  // keys (no codes) take the 32 x 32-tile kernel for bulk fp16 appends at
+  // head_dim 128 and proj_dim 64, and the small kernel otherwise.
+  const tq_config& c = ctx->cfg;
+  const bool zero_tiles = c.key_bits == 0 && c.head_dim == kD && c.proj_dim == 64 && dtype == TQ_F16;
+  if (fast_keys(c) || (zero_tiles && n_new > kSmallAppend))
+    rc = launch_compress_keys(ctx->mats, ctx->cb[c.key_bits], c.key_bits, c.proj_dim, s, cache->key_records,
+                              stream);
+  else if (n_new <= kSmallAppend || c.key_bits == 0)
+    rc = launch_small_keys(ctx->mats, ctx->cb[c.key_bits], c.key_bits, c.head_dim, c.proj_dim, s,
+                           cache->key_records, stream);
   else
     rc = launch_general_keys(ctx->gen, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.head_dim,
                              ctx->cfg.proj_dim, s, cache->key_records, stream);

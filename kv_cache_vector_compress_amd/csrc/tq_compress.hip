@@ -279,10 +279,13 @@ __global__ __launch_bounds__(512, 1) void compress_keys_kernel(const KeyArgs a) 
 // the same layout as above.  The residual of tile t feeds projection K steps
 // 2t and 2t + 1 straight from the accumulator (S's columns are permuted to
 // match, bits 2 and 3 of the coordinate swapped).  Rotation t + 1 is issued
-// before the bucketing of tile t so the two can overlap on a SIMD.
+// before the bucketing of tile t so the two can overlap on a SIMD.  With
+// B = 0 (one cell at 0: signs and norms only) the residual is the rotated
+// coordinate itself and no code words are written.
 template <int B>
 __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a) {
-  constexpr int H = 1 << (B - 1);
+  constexpr int H = B > 0 ? 1 << (B - 1) : 1;
+  constexpr int BW = B > 0 ? B : 1;  // code words per group (none at 0 bits)
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ float ctab[16];  // 2^12 c_i
   uint16_t* Rh = lds;
@@ -296,8 +299,8 @@ __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a
   if (threadIdx.x < 16) ctab[threadIdx.x] = a.cb.cent[threadIdx.x] * kResScale;
   __syncthreads();
 
-  float bpos[8];
-  load_pos_beta<B>(bpos, a.cb);
+  float bpos[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if constexpr (B > 0) load_pos_beta<B>(bpos, a.cb);
   // wave-uniform (a scalar register): tile, slot and offset arithmetic stays on the scalar unit
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n32 = lane & 31, g = lane >> 5;
@@ -353,9 +356,9 @@ __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int e = 0; e < 16; ++e) zacc[p][e] = 0.f;
-    uint32_t cw[2][B];
+    uint32_t cw[2][BW];
 #pragma unroll
-    for (int w = 0; w < B; ++w) cw[0][w] = cw[1][w] = 0u;
+    for (int w = 0; w < BW; ++w) cw[0][w] = cw[1][w] = 0u;
     float g2 = 0.f;
 
     f16v ycur = rotate(0);
@@ -373,14 +376,24 @@ __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a
       u4 rhi[2], rlo[2];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float rs[4];
-        const uint32_t x4 = quantize4_signs<B>(quarter(ycur, j), bs, -s16, ctab, rs, g2);  // rs = -residual
+        float rs[4];  // -residual
+        uint32_t x4 = 0u;
+        if constexpr (B > 0) {
+          x4 = quantize4_signs<B>(quarter(ycur, j), bs, -s16, ctab, rs, g2);
+        } else {
+          const f4 y4 = quarter(ycur, j);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            rs[i] = -s16 * y4[i];
+            g2 = fmaf(rs[i], rs[i], g2);
+          }
+        }
         const HiLo t01 = split2m(rs[0], rs[1], a.m1), t23 = split2m(rs[2], rs[3], a.m1);
         rhi[j >> 1][2 * (j & 1)] = t01.hi;
         rlo[j >> 1][2 * (j & 1)] = t01.lo;
         rhi[j >> 1][2 * (j & 1) + 1] = t23.hi;
         rlo[j >> 1][2 * (j & 1) + 1] = t23.lo;
-        put_sel4_rt<B>(cw[j & 1], 2 * t + (j >> 1), x4);
+        if constexpr (B > 0) put_sel4_rt<B>(cw[j & 1], 2 * t + (j >> 1), x4);
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -409,14 +422,19 @@ __global__ __launch_bounds__(512, 1) void compress_keys32_kernel(const KeyArgs a
     uint32_t bits_b = sign_bits16_neg(quarter(zacc[0], 1), quarter(zacc[0], 3), quarter(zacc[1], 1),
                                       quarter(zacc[1], 3));
     if (nrm == 0.f) {
-      // A zero key has every rotated coordinate +0, which quantize4_signs
-      // puts in cell H with residual -c+_0.  Its cell is H - 1 (0 is the
-      // middle boundary and ties go to the lower cell), whose residual is
-      // +c+_0: the opposite residual, so every projection flips sign.
-      fill_code_words<B>(cw[0], (uint32_t)H - 1u);
-      fill_code_words<B>(cw[1], (uint32_t)H - 1u);
-      bits_a = ~bits_a & 0xFFFFu;
-      bits_b = ~bits_b & 0xFFFFu;
+      if constexpr (B > 0) {
+        // A zero key has every rotated coordinate +0, which quantize4_signs
+        // puts in cell H with residual -c+_0.  Its cell is H - 1 (0 is the
+        // middle boundary and ties go to the lower cell), whose residual is
+        // +c+_0: the opposite residual, so every projection flips sign.
+        fill_code_words<B>(cw[0], (uint32_t)H - 1u);
+        fill_code_words<B>(cw[1], (uint32_t)H - 1u);
+        bits_a = ~bits_a & 0xFFFFu;
+        bits_b = ~bits_b & 0xFFFFu;
+      } else {
+        // residual 0: every projection is 0, whose bit is 1
+        bits_a = bits_b = 0xFFFFu;
+      }
     }
     if (tok < a.n_new) {
       uint32_t* rp = a.rec + ((int64_t)slot * a.capacity + a.pos + tok) * a.rec_words;
@@ -671,7 +689,8 @@ int compress_device_init() {
         set_key_attr<B, 128, false>() | set_key_attr<B, 128, true>();
   TQ_KEY_ATTR(1) TQ_KEY_ATTR(2) TQ_KEY_ATTR(3) TQ_KEY_ATTR(4)
 #undef TQ_KEY_ATTR
-  rc |= set_key32_attr<1>() | set_key32_attr<2>() | set_key32_attr<3>() | set_key32_attr<4>();
+  rc |= set_key32_attr<0>() | set_key32_attr<1>() | set_key32_attr<2>() | set_key32_attr<3>() |
+        set_key32_attr<4>();
   rc |= set_val_attr<1, false>() | set_val_attr<1, true>() | set_val_attr<2, false>() | set_val_attr<2, true>();
   rc |= set_val_attr<3, false>() | set_val_attr<3, true>() | set_val_attr<4, false>() | set_val_attr<4, true>();
   return rc;
@@ -717,10 +736,11 @@ int launch_compress_keys(const Matrices& mats, const CodebookDev& cb, int bits, 
   const int64_t per = (f32 || m > 64) ? 16 : 32;
   const int64_t ntiles = ((s.n_new + per - 1) / per) * s.n_seq;
   hipStream_t st = (hipStream_t)stream;
-  if (!f32 && m == 64 && bits >= 1 && bits <= 4) {  // fp16 keys, m = 64: the 32 x 32 tile kernel
+  if (!f32 && m == 64 && bits >= 0 && bits <= 4) {  // fp16 keys, m = 64: the 32 x 32 tile kernel
     a.s_hi = mats.s_hi32;
     a.s_lo = mats.s_lo32;
     switch (bits) {
+      case 0: key32_launch<0>(a, ntiles, st); break;
       case 1: key32_launch<1>(a, ntiles, st); break;
       case 2: key32_launch<2>(a, ntiles, st); break;
       case 3: key32_launch<3>(a, ntiles, st); break;
