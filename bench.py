@@ -336,16 +336,7 @@ def bench_vector_search(args):
     dev = torch.device("cuda:0")
     R, S = synth.haar_rotation(d), synth.gaussian_projection(m, d)
     ctx = tq.Context(d, m, b, b, R, S)
-    g = torch.Generator(device=dev).manual_seed(4)
-    cent = torch.randn((64, d), device=dev, generator=g)
-    cent /= cent.norm(dim=1, keepdim=True)
-    X = torch.randn((1, N, d), device=dev, generator=g)
-    odd = torch.arange(N, device=dev) % 2 == 1
-    cl = torch.randint(0, 64, (N,), device=dev, generator=g)
-    X[0, odd] = cent[cl[odd]] + 0.3 * X[0, odd] / d ** 0.5
-    X /= X.norm(dim=-1, keepdim=True)
-    Q = torch.randn((1, G, d), device=dev, generator=g)
-    Q /= Q.norm(dim=-1, keepdim=True)
+    X, Q = synth.vector_search_device(torch, N, d, G, dev)
     cache = tq.KVCache(ctx, 1, -(-N // 128) * 128)
     sc = torch.empty((1, G, N), dtype=torch.float32, device=dev)
     cache.workspace(G, N)

@@ -164,3 +164,23 @@ def vector_database(n: int, d: int, seed: int, n_clusters: int = 64, spread: flo
         if lo < hi:
             out[lo - start:hi - start] = x[lo - b0:hi - b0]
     return out
+
+
+def vector_search_device(torch, n: int, d: int, n_queries: int, dev, seed: int = 4, n_clusters: int = 64,
+                         spread: float = 0.3):
+    """The vector-search workload generated on the device with a seeded torch
+    generator (the host generator above would take minutes at 2M rows):
+    database (1, n, d) fp32, unit-norm rows, odd rows from the mixture
+    normalise(mu_c + spread g / sqrt(d)), even rows isotropic Gaussian; and
+    (1, n_queries, d) unit-norm Gaussian queries."""
+    g = torch.Generator(device=dev).manual_seed(seed)
+    cent = torch.randn((n_clusters, d), device=dev, generator=g)
+    cent /= cent.norm(dim=1, keepdim=True)
+    X = torch.randn((1, n, d), device=dev, generator=g)
+    odd = torch.arange(n, device=dev) % 2 == 1
+    cl = torch.randint(0, n_clusters, (n,), device=dev, generator=g)
+    X[0, odd] = cent[cl[odd]] + spread * X[0, odd] / d ** 0.5
+    X /= X.norm(dim=-1, keepdim=True)
+    Q = torch.randn((1, n_queries, d), device=dev, generator=g)
+    Q /= Q.norm(dim=-1, keepdim=True)
+    return X, Q

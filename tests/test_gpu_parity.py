@@ -634,3 +634,45 @@ def test_general_scores_beyond_one_launch():
     _say({"score_vs_gpu_codes": P.check_scores(sc, ref, qn, kn)})
     del cache
     ctx.close()
+
+
+def test_vector_search_full_size_sampled():
+    """The vector-search workload at full size, in the launch configuration
+    bench.py times: 2,000,000 unit-norm fp32 vectors (d = 1024) compressed in
+    one tq_append_key call (4-bit keys, proj_dim 512), scored against 512
+    queries (tq_attention_scores) and searched for the top 10 (tq_topk_scores).
+    The oracle recomputes the records and scores of sampled rows; the top-10
+    of every query equals the 10 best of the materialised scores."""
+    d, m, b, N, G, k = 1024, 512, 4, 2_000_000, 512, 10
+    _say("vector search full size", (N, d, m, b, G))
+    dev = torch.device("cuda:0")
+    X, Q = synth.vector_search_device(torch, N, d, G, dev)
+    ctx, R, S = make_ctx(d, m, b, b)
+    cache = tq.KVCache(ctx, 1, -(-N // 128) * 128)
+    cache.append_key(X, 0)
+    sc = cache.attention_scores(Q, N)
+    ts, ti = cache.topk(Q, N, k)
+    # top-k against the materialised scores, on the device: the same values
+    # in descending order, at the returned positions, no position twice
+    ref_s = torch.topk(sc, k, dim=-1).values
+    assert torch.equal(ts, ref_s), "top-k scores differ from the 10 best materialised scores"
+    assert torch.equal(torch.gather(sc, -1, ti.long()), ts), "top-k positions do not hold their scores"
+    assert bool((ti.sort(dim=-1).values.diff(dim=-1) > 0).all()), "a position returned twice"
+    # sampled rows against the oracle: records, then scores
+    rng = np.random.default_rng(7)
+    toks = np.unique(np.concatenate([rng.choice(N, 1500, replace=False), np.arange(N - 16, N)]))
+    tt = torch.from_numpy(toks).to(dev)
+    xs = X[0, tt].cpu().numpy()[None]
+    rw = tq.key_record_bytes(ctx.cfg) // 4
+    recs = cache.key_records.view(1, cache.capacity, rw)[0, tt].cpu().numpy().view(np.uint32)[None]
+    beta, c = O.lloyd_max_codebook(d, b)
+    ref = O.compress_keys(xs, R, S, beta, c)
+    st = P.check_keys(O.unpack_keys(recs, d, m, b), ref, beta, S, c)
+    flips = st.pop("flip_tokens")
+    q = Q.cpu().numpy()
+    st["score"] = P.check_scores(sc[:, :, tt].cpu().numpy(), O.key_scores(q, R, S, c, ref),
+                                 np.linalg.norm(q.astype(np.float64), axis=-1),
+                                 np.linalg.norm(xs.astype(np.float64), axis=-1), skip_tokens=flips)
+    _say("vector search full size", st)
+    del cache, sc, X
+    ctx.close()
