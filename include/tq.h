@@ -66,7 +66,7 @@ typedef enum {
   TQ_ENOCODEBOOK = -3,  /* no codebook loaded for the bits this call needs */
   TQ_ENOMEM = -4,       /* device allocation failed (tq_create only) */
   TQ_EDEVICE = -5,      /* a HIP call or kernel launch failed */
-  TQ_EUNSUPPORTED = -6, /* valid but not built (top-k over 0-bit keys) */
+  TQ_EUNSUPPORTED = -6, /* valid but not built (reserved; every valid shape is built) */
   TQ_EWORKSPACE = -7    /* workspace smaller than tq_workspace_bytes */
 } tq_status;
 
@@ -264,8 +264,7 @@ size_t tq_topk_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, i
  * ordered by score descending, equal scores by position ascending; when
  * n_tokens < k the rest is (-inf, -1).  q as for tq_attention_scores,
  * 1 <= G <= 512, 1 <= k <= 16.  workspace >= tq_topk_workspace_bytes.
- * Errors: TQ_EINVAL, TQ_ENOCODEBOOK, TQ_EWORKSPACE, TQ_EDEVICE,
- * TQ_EUNSUPPORTED (key_bits 0). */
+ * Errors: TQ_EINVAL, TQ_ENOCODEBOOK, TQ_EWORKSPACE, TQ_EDEVICE. */
 int tq_topk_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
                    int64_t n_tokens, int32_t k, float* top_scores, int32_t* top_index, void* workspace,
                    size_t workspace_bytes, void* stream);

@@ -519,7 +519,6 @@ int tq_topk_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32
     return fail(TQ_EINVAL, "%s: q, outputs and workspace must be 16-byte aligned", fn);
   if (!ctx->loaded[ctx->cfg.key_bits])
     return fail(TQ_ENOCODEBOOK, "%s: no %d-bit key codebook loaded", fn, ctx->cfg.key_bits);
-  if (ctx->cfg.key_bits == 0) return fail(TQ_EUNSUPPORTED, "%s: 0-bit keys are not supported", fn);
   const size_t need = topk_plan(ctx->cfg.head_dim, ctx->cfg.proj_dim, cache->n_seq, G, n_tokens, k).total;
   if (workspace_bytes < need) return fail(TQ_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "%s: hipSetDevice failed", fn);

@@ -64,7 +64,7 @@ __device__ __forceinline__ void tk_insert(float* ls, int32_t* li, int k, float s
 // processed.
 template <int B, int NOCT>
 struct TkRec {
-  uint32_t cw[NOCT][B];
+  uint32_t cw[NOCT][B > 0 ? B : 1];  // (0-bit keys: no code words, unused)
   uint32_t sw[8];
   float n, g;
 };
@@ -125,9 +125,11 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
     const int row = min((int)(tile * 16) + r16, n_tok - 1);
     const uint32_t ro = (uint32_t)(row - (int)r0) * (uint32_t)a.rec_words * 4u;
 #pragma unroll
-    for (int c = 0; c < NOCT; ++c) {
+    for (int c = 0; c < (B > 0 ? NOCT : 0); ++c) {
       const uint32_t oc = ro + 4u * (uint32_t)((q * NOCT + c) * B);
-      if constexpr (B == 1) {
+      if constexpr (B == 0) {
+        (void)oc;
+      } else if constexpr (B == 1) {
         r.cw[c][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, oc, 0, 0);
       } else if constexpr (B == 2) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, oc, 0, 0);
@@ -156,24 +158,26 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
     const uint16_t* ql = qop + lane * 8;
     // (with a single group the second products use LDS never written and
     // are not read)
+    if constexpr (B > 0) {  // (0-bit keys: the centroid 0 adds nothing)
 #pragma unroll
-    for (int c = 0; c < NOCT; ++c) {
-      h8 qa[2][4];
+      for (int c = 0; c < NOCT; ++c) {
+        h8 qa[2][4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        qa[0][kk] = *(const h8*)(ql + (4 * c + kk) * 512);
-        qa[1][kk] = *(const h8*)(ql + (KBT + 4 * c + kk) * 512);
+        for (int kk = 0; kk < 4; ++kk) {
+          qa[0][kk] = *(const h8*)(ql + (4 * c + kk) * 512);
+          qa[1][kk] = *(const h8*)(ql + (KBT + 4 * c + kk) * 512);
+        }
+        const h8 A0 = decode_pair<B, 0>(r.cw[c], tlo, thi), A1 = decode_pair<B, 2>(r.cw[c], tlo, thi);
+        const h8 A2 = decode_pair<B, 4>(r.cw[c], tlo, thi), A3 = decode_pair<B, 6>(r.cw[c], tlo, thi);
+        acc[0] = mfma(A0, qa[0][0], acc[0]);
+        acc[1] = mfma(A0, qa[1][0], acc[1]);
+        acc[0] = mfma(A1, qa[0][1], acc[0]);
+        acc[1] = mfma(A1, qa[1][1], acc[1]);
+        acc[0] = mfma(A2, qa[0][2], acc[0]);
+        acc[1] = mfma(A2, qa[1][2], acc[1]);
+        acc[0] = mfma(A3, qa[0][3], acc[0]);
+        acc[1] = mfma(A3, qa[1][3], acc[1]);
       }
-      const h8 A0 = decode_pair<B, 0>(r.cw[c], tlo, thi), A1 = decode_pair<B, 2>(r.cw[c], tlo, thi);
-      const h8 A2 = decode_pair<B, 4>(r.cw[c], tlo, thi), A3 = decode_pair<B, 6>(r.cw[c], tlo, thi);
-      acc[0] = mfma(A0, qa[0][0], acc[0]);
-      acc[1] = mfma(A0, qa[1][0], acc[1]);
-      acc[0] = mfma(A1, qa[0][1], acc[0]);
-      acc[1] = mfma(A1, qa[1][1], acc[1]);
-      acc[0] = mfma(A2, qa[0][2], acc[0]);
-      acc[1] = mfma(A2, qa[1][2], acc[1]);
-      acc[0] = mfma(A3, qa[0][3], acc[0]);
-      acc[1] = mfma(A3, qa[1][3], acc[1]);
     }
     const _Float16 gk = (_Float16)(r.g * a.kappa);
     const uint32_t gk2 = (uint32_t)__builtin_bit_cast(uint16_t, gk) * 0x00010001u;
@@ -414,6 +418,10 @@ int launch_topk(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, 
     launched = true; \
   }
 #define TQ_TK_B(B) TQ_TK(B, 1) TQ_TK(B, 2) TQ_TK(B, 3) TQ_TK(B, 4) TQ_TK(B, 5) TQ_TK(B, 6) TQ_TK(B, 7) TQ_TK(B, 8)
+  if (kbits == 0) {  // 0-bit keys: no code chunks, one instance for every head_dim
+    hipLaunchKernelGGL((topk_scores_kernel<0, 1>), grid, block, lds, st, a);
+    launched = true;
+  }
   TQ_TK_B(1) TQ_TK_B(2) TQ_TK_B(3) TQ_TK_B(4)
 #undef TQ_TK_B
 #undef TQ_TK

@@ -407,6 +407,8 @@ def _topk_reference(scores, k):
     (256, 128, 3, 2, 1000, 20, 1),
     (1024, 512, 4, 1, 2500, 64, 10),
     (128, 64, 3, 1, 5, 4, 10),
+    (128, 64, 0, 2, 3000, 40, 10),     # 0-bit keys: QJL signs only
+    (1024, 512, 0, 1, 2500, 64, 10),
 ])
 def test_topk_matches_scores(d, m, b, n_seq, N, G, k):
     """tq_topk_scores: the k best tokens of each query (vector search over the
@@ -416,7 +418,7 @@ def test_topk_matches_scores(d, m, b, n_seq, N, G, k):
     _say("topk", (d, m, b, n_seq, N, G, k))
     X = np.stack([synth.vector_database(N, d, seed=80 + s) for s in range(n_seq)])
     Q = np.stack([synth.unit_gaussian(G, d, seed=90 + s) for s in range(n_seq)])
-    ctx, R, S = make_ctx(d, m, b, b)
+    ctx, R, S = make_ctx(d, m, b, max(b, 1))
     cache = tq.KVCache(ctx, n_seq, -(-N // 128) * 128)
     cache.append_key(torch.from_numpy(X).cuda(), 0)
     qt = torch.from_numpy(Q).cuda()
@@ -543,8 +545,8 @@ def test_zero_bit_keys(d, m, vb, dtype, G):
     """key_bits = 0: records of m sign bits of S R k/||k|| and the two norms
     (gamma = 1), appended in unaligned chunks (one-token and bulk appends)
     with a zero key inside; signs, norms, scores (the plain QJL estimate) and
-    attention against the oracle.  The key reconstruction is all zeros and
-    top-k reports TQ_EUNSUPPORTED."""
+    attention against the oracle.  The key reconstruction is all zeros, and
+    top-k returns the best of the materialised scores."""
     n_seq, T = 2, 700
     K = np.stack([synth.kv_slot(130 + d, s, s, T, d, dtype=dtype) for s in range(n_seq)])
     V = np.stack([synth.kv_slot(131 + d, s, s, T, d, dtype=dtype) for s in range(n_seq)])
@@ -561,9 +563,10 @@ def test_zero_bit_keys(d, m, vb, dtype, G):
     assert np.all(np.abs(rec["gamma"][K[:, :50].any(-1)] - 1.0) < 1e-6)
     assert not cache.get_keys(0, 50).cpu().numpy().any()
     qt = torch.from_numpy(np.ascontiguousarray(Q[:, :4])).cuda()
-    with pytest.raises(tq.TQError) as e:
-        cache.topk(qt, 50, 4)
-    assert e.value.code == -6
+    ts, ti = cache.topk(qt, 50, 4)
+    sc = cache.attention_scores(qt, 50)
+    assert torch.equal(ts, torch.topk(sc, 4, dim=-1).values)
+    assert torch.equal(torch.gather(sc, -1, ti.long()), ts)
     ctx.close()
 
 
