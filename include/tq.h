@@ -300,10 +300,11 @@ int tq_get_keys(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_
  * measures what a plain stream reaches on the device (the reported
  * baseline beside the theoretical peak).  src, dst: device, 16-byte aligned;
  * read_bytes a positive multiple of 4096; write_bytes 0, read_bytes,
- * read_bytes / 2 or read_bytes / 4; sink: device uint32.  Errors: TQ_EINVAL,
- * TQ_EDEVICE. */
+ * read_bytes / 2 or read_bytes / 4; sink: device uint32; waves_per_cu: the
+ * grid's waves per compute unit, a multiple of 4 up to 64 (0: 16), since the
+ * best count depends on the read/write mix.  Errors: TQ_EINVAL, TQ_EDEVICE. */
 int tq_hbm_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
-                  void* stream);
+                  int32_t waves_per_cu, void* stream);
 
 #ifdef __cplusplus
 }

@@ -539,7 +539,7 @@ int tq_get_keys(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_
 }
 
 int tq_hbm_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
-                  void* stream) {
+                  int32_t waves_per_cu, void* stream) {
   clear_error();
   if (!src || ((uintptr_t)src & 15u)) return fail(TQ_EINVAL, "tq_hbm_stream: src must be a 16-byte aligned device pointer");
   if (read_bytes == 0 || read_bytes % 4096 != 0)
@@ -551,11 +551,14 @@ int tq_hbm_stream(const void* src, size_t read_bytes, void* dst, size_t write_by
       return fail(TQ_EINVAL, "tq_hbm_stream: write_bytes must be 0 or read_bytes / 1, / 2 or / 4");
   }
   if (!sink || ((uintptr_t)sink & 3u)) return fail(TQ_EINVAL, "tq_hbm_stream: sink must be a 4-byte aligned device pointer");
+  if (waves_per_cu < 0 || waves_per_cu > 64 || waves_per_cu % 4)
+    return fail(TQ_EINVAL, "tq_hbm_stream: waves_per_cu %d: need 0 or a multiple of 4 up to 64", waves_per_cu);
+  if (waves_per_cu == 0) waves_per_cu = 16;
   static std::once_flag once;
   static int init_rc = 0;
   std::call_once(once, [] { init_rc = stream_device_init(); });
   if (init_rc != 0) return fail(TQ_EDEVICE, "tq_hbm_stream: HIP device query failed");
-  const int rc = launch_stream(src, read_bytes, dst, write_bytes, sink, stream);
+  const int rc = launch_stream(src, read_bytes, dst, write_bytes, sink, waves_per_cu, stream);
   return rc == 0 ? TQ_OK : fail(rc, "tq_hbm_stream: kernel launch failed");
 }
 

@@ -17,6 +17,7 @@
 // query head (online softmax), and accumulates sum_t p_t ||v_t|| c[idx_t] in
 // the rotated domain with the matrix cores.  A second kernel merges the
 // per-wave partials (log-sum-exp) and applies R^T once per query head.
+#include <algorithm>
 #include <type_traits>
 
 #include "tq_device.h"
@@ -25,7 +26,18 @@ namespace tq {
 
 constexpr int kPartFloats = 4 + kD;  // m, l, pad, pad, acc[d]
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int64_t kTargetWaves = 256 * 16;
+// Waves over the whole grid, fixed so that the workspace size does not
+// depend on the device.  The attend kernel holds ~230 VGPRs, so a SIMD runs
+// two of its waves: 2048 waves are one resident round of a 256-CU MI355X,
+// and each wave's fixed costs (tables, query operands, partials) are paid
+// once.  The score kernel runs short waves of 8 tiles (16 tokens each)
+// while there are at least 4096 of them, up to 65536 waves: on the
+// long-context cache (524288 tiles) 4096 waves took 0.159 ms, 16384 0.141,
+// 65536 0.132 and 131072 0.139; with fewer tiles, one-tile waves pay their
+// fixed costs for too little work (the 36 layers of a decode step, 36864
+// tiles: 0.029 ms at 9 tiles a wave, 0.047 ms at 1).
+constexpr int64_t kAttendWaves = 256 * 8;
+constexpr int64_t kScoreWavesMin = 256 * 16, kScoreWavesMax = 256 * 256, kScoreTilesPerWave = 8;
 constexpr int kMaxPartials = 1024;
 
 // ---------------------------------------------------------------------------
@@ -655,9 +667,7 @@ AttnPlan plan_attention(int m, int n_seq, int G, int64_t n_tokens) {
   AttnPlan p;
   const int KBT = 4 + m / 32;
   const int64_t nblk = (n_tokens + kBlockTokens - 1) / kBlockTokens;
-  // about 16 waves per compute unit of a 256-CU MI355X over the whole grid;
-  // fixed so that the workspace size does not depend on the device
-  const int64_t target_waves = kTargetWaves;
+  const int64_t target_waves = kAttendWaves;
   int64_t bpw = (nblk * n_seq + target_waves - 1) / target_waves;
   if (bpw < 1) bpw = 1;
   // the combine kernel merges at most kMaxPartials partials per query head
@@ -718,10 +728,9 @@ int launch_scores(const CodebookDev& cbk, int kbits, int m, const AttnShape& s, 
   a.n_seq = s.n_seq;
   a.G = s.G;
   a.rec_words = kbits * kD / 32 + m / 32 + 2;
-  const int64_t ntile = (s.n_tokens + 15) / 16;
-  const int64_t target_waves = kTargetWaves;
-  int64_t tpw = (ntile * s.n_seq + target_waves - 1) / target_waves;
-  if (tpw < 1) tpw = 1;
+  const int64_t ntile = (s.n_tokens + 15) / 16, total = ntile * s.n_seq;
+  const int64_t tpw = std::max((total + kScoreWavesMax - 1) / kScoreWavesMax,
+                               std::min(kScoreTilesPerWave, (total + kScoreWavesMin - 1) / kScoreWavesMin));
   a.tiles_per_wave = (int)tpw;
   a.waves_per_slot = (int)((ntile + tpw - 1) / tpw);
   a.kappa = (float)(1.2533141373155002512 / m);  // sqrt(pi/2) / m

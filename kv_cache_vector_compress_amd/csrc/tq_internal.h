@@ -141,7 +141,7 @@ void attend_query_buffers(void* ws, const AttnPlan& p, uint16_t** wq, float** wq
 // HBM stream for measuring the memory ceiling (tq_stream.hip).
 int stream_device_init();
 int launch_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
-                  void* stream);
+                  int waves_per_cu, void* stream);
 
 // Fused inner-product top-k over the packed keys (tq_topk.hip).
 constexpr int kTopkMax = 16;  // largest k of tq_topk_scores

@@ -13,8 +13,6 @@
 
 namespace tq {
 
-constexpr int kStreamWavesPerCu = 16;
-
 struct StreamArgs {
   const u4* src;
   u4* dst;
@@ -56,14 +54,14 @@ int stream_device_init() {
 }
 
 int launch_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
-                  void* stream) {
+                  int waves_per_cu, void* stream) {
   StreamArgs a;
   a.src = (const u4*)src;
   a.dst = (u4*)dst;
   a.groups = (int64_t)(read_bytes / 4096);
   a.rpw = write_bytes == 0 ? 0 : (int)(read_bytes / write_bytes);
   a.sink = sink;
-  const int64_t waves = (int64_t)(g_stream_cus > 0 ? g_stream_cus : 256) * kStreamWavesPerCu;
+  const int64_t waves = (int64_t)(g_stream_cus > 0 ? g_stream_cus : 256) * waves_per_cu;
   hipLaunchKernelGGL(stream_kernel, dim3((unsigned)(waves / 4)), dim3(256), 0, (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
 }

@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
         "tq_topk_scores": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, I32, P, P, P, SZ, P]),
         "tq_get_values": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
         "tq_get_keys": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
-        "tq_hbm_stream": (ctypes.c_int, [P, SZ, P, SZ, P, P]),
+        "tq_hbm_stream": (ctypes.c_int, [P, SZ, P, SZ, P, I32, P]),
         "tq_decode_step": (ctypes.c_int, [P, VIEW, P, P, I32, I64, I64, P, I32, ctypes.c_float, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -330,16 +330,17 @@ class KVCache:
 
 # ---- measurement -------------------------------------------------------------
 
-def hbm_stream(src, dst=None, sink=None, stream=None) -> None:
+def hbm_stream(src, dst=None, sink=None, waves_per_cu: int = 0, stream=None) -> None:
     """Stream all of `src` (a contiguous device tensor) and, if `dst` is given,
-    write all of `dst` interleaved with the reads (tq_hbm_stream).  `sink` is
-    a one-element int32 device tensor that receives the XOR of the words read
-    (XOR-ed into its current value)."""
+    write all of `dst` interleaved with the reads (tq_hbm_stream), on a grid
+    of `waves_per_cu` waves per compute unit (0: the library's default).
+    `sink` is a one-element int32 device tensor that receives the XOR of the
+    words read (XOR-ed into its current value)."""
     torch = _torch()
     if sink is None:
         sink = torch.zeros(1, dtype=torch.int32, device=src.device)
     nr = src.numel() * src.element_size()
     nw = 0 if dst is None else dst.numel() * dst.element_size()
     _check(lib().tq_hbm_stream(_dev(src, "src"), nr, _dev(dst, "dst") if dst is not None else None, nw,
-                               _dev(sink, "sink"), _stream_ptr(stream)))
+                               _dev(sink, "sink"), waves_per_cu, _stream_ptr(stream)))
     return sink

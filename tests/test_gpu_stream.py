@@ -11,16 +11,16 @@ from kv_cache_vector_compress_amd import tq
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("read_bytes,ratio", [(4096, 0), (1 << 20, 0), (3 << 20, 4), (1 << 22, 2), (1 << 21, 1),
-                                              (64 << 20, 4)])
-def test_stream_reads_everything_and_writes_everything(read_bytes, ratio):
+@pytest.mark.parametrize("read_bytes,ratio,wpc", [(4096, 0, 0), (1 << 20, 0, 16), (3 << 20, 4, 0), (1 << 22, 2, 64),
+                                                  (1 << 21, 1, 4), (64 << 20, 4, 32), (64 << 20, 0, 64)])
+def test_stream_reads_everything_and_writes_everything(read_bytes, ratio, wpc):
     rng = np.random.default_rng(read_bytes + ratio)
     words = rng.integers(0, 2**32, size=read_bytes // 4, dtype=np.uint64).astype(np.uint32)
     src = torch.from_numpy(words.view(np.int32)).cuda()
     dst = torch.zeros(read_bytes // 4 // ratio, dtype=torch.float32, device="cuda") if ratio else None
     sink = torch.full((1,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
-    print("[stream]", read_bytes, ratio, flush=True)
-    tq.hbm_stream(src, dst, sink)
+    print("[stream]", read_bytes, ratio, wpc, flush=True)
+    tq.hbm_stream(src, dst, sink, waves_per_cu=wpc)
     torch.cuda.synchronize()
     expect = np.bitwise_xor.reduce(words) ^ np.uint32(0x5A5A5A5A)
     assert np.uint32(sink.cpu().numpy().view(np.uint32)[0]) == expect
