@@ -190,6 +190,8 @@ int tq_codebook_load(tq_ctx* ctx, int32_t bits, const double* centroids, const d
  * [pos, pos + n_new) of every slot (append_key of TurboQuantKVCache,
  * nav.superapi.store 核心 API; stage 1 + stage 2, atskills.one Stage 2).
  * k: device, [n_seq][n_new][d] contiguous, dtype TQ_F16 or TQ_F32, finite.
+ * fp32 rows may have any magnitude whose norm fits fp32, subnormal
+ * coordinates included: norms are taken over rows shifted by a power of two.
  * A zero vector is encoded with direction 0 and scores 0.
  * Errors: TQ_EINVAL, TQ_ECAPACITY (pos < 0 or pos + n_new > capacity),
  * TQ_ENOCODEBOOK, TQ_EDEVICE.  n_new == 0 is a no-op. */

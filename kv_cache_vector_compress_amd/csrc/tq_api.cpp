@@ -184,7 +184,7 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   const bool gen = !fast_keys(*cfg) || !fast_values(*cfg);
   const int64_t srows = gen ? kScratchRows : 0;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t off_nrm = up(end_imgs), off_rh = off_nrm + up((size_t)srows * 4);
+  const size_t off_nrm = up(end_imgs), off_rh = off_nrm + up((size_t)srows * 8);  // (norm, exponent) pairs
   const size_t off_rlo = off_rh + up((size_t)srows * d * 2), off_g2 = off_rlo + up((size_t)srows * d * 2);
   const size_t total = off_g2 + up((size_t)srows * (d / 128) * 4);
   if (hipMalloc(&c->dev_mem, total) != hipSuccess) {

@@ -69,33 +69,47 @@ __device__ __forceinline__ void copy_u4(uint16_t* dst, const uint16_t* src, int 
 }
 
 // Load the 32 input coordinates a lane owns (8 per K block: 32 kb + 8 q ..)
-// of one fp32 token, plus the token's partial sum of squares (over this
-// lane's coordinates).  The caller needs the norm before it can split the
-// row into fp16 hi/lo operands (split_row32), so the row comes back raw.
-__device__ __forceinline__ float load_row32(const void* x, int64_t row, int q, f4 (&v)[8]) {
+// of one fp32 token and return the norm of the token shifted by 2^-ex, 2^ex
+// the binary exponent of its largest magnitude (the four lanes q of the token
+// reduce together): full precision for any finite row, ||x|| = ldexp(., ex).
+// The caller needs the norm before it can split the row into fp16 hi/lo
+// operands (split_row32), so the row comes back raw.
+__device__ __forceinline__ float load_row32_norm(const void* x, int64_t row, int q, f4 (&v)[8], int& ex) {
   const float* src = (const float*)x + row * kD + 8 * q;
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+  float mx = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     v[2 * kb] = *(const f4*)(src + 32 * kb);
     v[2 * kb + 1] = *(const f4*)(src + 32 * kb + 4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ss[kb] = fmaf(v[2 * kb][e], v[2 * kb][e], ss[kb]);
-      ss[kb] = fmaf(v[2 * kb + 1][e], v[2 * kb + 1][e], ss[kb]);
-    }
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(v[2 * kb][e]), fabsf(v[2 * kb + 1][e])));
   }
-  return (ss[0] + ss[1]) + (ss[2] + ss[3]);
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
+  ex = pow2_exponent(mx);
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float u0 = ldexpf(v[2 * kb][e], -ex), u1 = ldexpf(v[2 * kb + 1][e], -ex);
+      ss[kb] = fmaf(u1, u1, fmaf(u0, u0, ss[kb]));
+    }
+  float t = (ss[0] + ss[1]) + (ss[2] + ss[3]);
+  t += shfl_xor(t, 16);
+  t += shfl_xor(t, 32);
+  return sqrtf(t);
 }
 
-__device__ __forceinline__ void split_row32(const f4 (&v)[8], float sc, h8 (&xh)[4], h8 (&xl)[4]) {
+// The row shifted by 2^sh (input_shift of its norm) as fp16 hi/lo operands.
+__device__ __forceinline__ void split_row32(const f4 (&v)[8], int sh, h8 (&xh)[4], h8 (&xl)[4]) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     u4 hi, lo;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const f4& src = v[2 * kb + p / 2];
-      const HiLo t = split2(src[2 * (p % 2)] * sc, src[2 * (p % 2) + 1] * sc);
+      const HiLo t = split2(ldexpf(src[2 * (p % 2)], sh), ldexpf(src[2 * (p % 2) + 1], sh));
       hi[p] = t.hi;
       lo[p] = t.lo;
     }
@@ -140,8 +154,8 @@ __global__ __launch_bounds__(512, 1) void compress_keys_kernel(const KeyArgs a) 
 
     // Inputs.  Rows past n_new are clamped to the last row: their results
     // are never stored, they only need to be finite.  Per token: the norm,
-    // the boundaries scaled to the accumulator (sigma = 2^8 sc ||k||, sc the
-    // fp32 pre-scale) and s16 = 2^12 / sigma.
+    // the boundaries scaled to the accumulator (sigma = 2^8 2^sh ||k||, 2^sh
+    // the fp32 pre-shift, 1 for fp16) and s16 = 2^12 / sigma.
     h8 xh[NT][4];
     h8 xl[F32 ? NT : 1][4];
     float nrm[NT], s16[NT], bs[NT][8];
@@ -152,15 +166,12 @@ __global__ __launch_bounds__(512, 1) void compress_keys_kernel(const KeyArgs a) 
       float n, sigma;
       if constexpr (F32) {
         f4 v[8];
-        float ss = load_row32(a.x, row, q, v);
-        ss += shfl_xor(ss, 16);
-        ss += shfl_xor(ss, 32);
-        n = sqrtf(ss);
-        int E = 0;
-        frexpf(n, &E);
-        const float sc = n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;  // |k sc| < 2^13
-        split_row32(v, sc, xh[j], xl[j]);
-        sigma = kRotScale * sc * n;
+        int ex = 0;
+        const float ns = load_row32_norm(a.x, row, q, v, ex);  // ||k 2^-ex||
+        const int s0 = input_shift(ns);                        // |k 2^(s0 - ex)| < 2^13
+        split_row32(v, s0 - ex, xh[j], xl[j]);
+        sigma = kRotScale * ldexpf(ns, s0);
+        n = ldexpf(ns, ex);
       } else {
         const _Float16* src = (const _Float16*)a.x + row * kD + 8 * q;
 #pragma unroll
@@ -510,7 +521,7 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
       if (h0 + 64 <= a.pos || h0 >= a.pos + a.n_new) return;
       h8 xa[4][4];
       h8 xl[F32 ? 4 : 1][4];
-      float tok_sc[4];  // per token: sigma = 2^8 sc ||v|| (4-bit codes: 1 / sigma)
+      float tok_sc[4];  // per token: sigma = 2^8 2^sh ||v|| (4-bit codes: 1 / sigma)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         // block token tau -> input row; rows outside [pos, pos + n_new) are
@@ -519,24 +530,21 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
         int64_t row = tok0 + tau - a.pos;
         const bool valid = row >= 0 && row < a.n_new;
         row = (int64_t)slot * a.n_new + (row < 0 ? 0 : (row >= a.n_new ? a.n_new - 1 : row));
-        float ss;
         if constexpr (F32) {
           f4 v[8];
-          ss = load_row32(a.x, row, q, v);
-          ss += shfl_xor(ss, 16);
-          ss += shfl_xor(ss, 32);
-          const float n = sqrtf(ss);
-          int E = 0;
-          frexpf(n, &E);
-          const float sc = n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;
-          split_row32(v, sc, xa[mt], xl[mt]);
-          tok_sc[mt] = B <= 3 ? kRotScale * sc * n : (n > 0.f ? 1.f / (kRotScale * sc * n) : 0.f);
+          int ex = 0;
+          const float n0 = load_row32_norm(a.x, row, q, v, ex);  // ||v 2^-ex||
+          const int s0 = input_shift(n0);
+          split_row32(v, s0 - ex, xa[mt], xl[mt]);
+          const float ns = ldexpf(n0, s0);  // the shifted row's norm, in [2^12, 2^13)
+          const float n = ldexpf(n0, ex);
+          tok_sc[mt] = B <= 3 ? kRotScale * ns : (n0 > 0.f ? 1.f / (kRotScale * ns) : 0.f);
           if (q == 0 && valid) vnorm[tau] = n;
         } else {
           const _Float16* src = (const _Float16*)a.x + row * kD + 8 * q;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) xa[mt][kb] = *(const h8*)(src + 32 * kb);
-          ss = sq_norm16(xa[mt]);
+          float ss = sq_norm16(xa[mt]);
           ss += shfl_xor(ss, 16);
           ss += shfl_xor(ss, 32);
           const float n = sqrtf(ss);
@@ -546,7 +554,7 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void compress_values_kernel(const
       }
       // Per token in the output layout (lane (coordinate, q) holds tokens
       // 4q+i): the boundaries scaled to the accumulator, bs = beta sigma with
-      // sigma = 2^8 sc ||v||; for 4-bit codes (7 boundaries a token) the
+      // sigma = 2^8 2^sh ||v||; for 4-bit codes (7 boundaries a token) the
       // coordinates are normalised instead, y = a / sigma, against the
       // unscaled boundaries
       constexpr bool kScaled = B <= 3;

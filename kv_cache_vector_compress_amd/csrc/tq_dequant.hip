@@ -8,9 +8,11 @@
 // Not on the attention path (the attend kernel never materialises x^): this
 // serves consumers that want the vectors back.  One workgroup takes 32
 // tokens of one slot.  It decodes their codes into LDS in the rotated domain
-// (c[idx] ||x||, coordinate-major), then thread (coordinate c, token half)
-// forms sum_j R[j][c] y[j][t] in fp32 with R's row j read across threads
-// (coalesced) and y broadcast from LDS.  Any head_dim of the layout.
+// (c[idx], coordinate-major), then thread (coordinate c, token half) forms
+// sum_j R[j][c] y[j][t] in fp32 with R's row j read across threads
+// (coalesced) and y broadcast from LDS, and scales the sum by ||x|| last (no
+// intermediate overflows or denormals at any norm).  Any head_dim of the
+// layout.
 #include "tq_device.h"
 
 namespace tq {
@@ -45,31 +47,38 @@ __device__ __forceinline__ int group_code(const uint32_t* w, int stride, int b, 
 }
 
 __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
-  extern __shared__ __align__(16) float ys[];  // [d][kDqTok]
+  extern __shared__ __align__(16) float ys[];  // [d][kDqTok] centroids of the codes
+  __shared__ float nsh[kDqTok];                // the tokens' norms, applied last
   const int64_t tiles = (a.n_tokens + kDqTok - 1) / kDqTok;
   const int slot = (int)(blockIdx.x / tiles);
   const int64_t tl0 = (int64_t)(blockIdx.x - (int64_t)slot * tiles) * kDqTok;  // first token, relative to pos
   const int nt = (int)min((int64_t)kDqTok, a.n_tokens - tl0);
   const int nblk = (int)(a.capacity / kBlockTokens);
+  auto key_rec = [&](int tl) { return a.key_rec + ((int64_t)slot * a.capacity + a.pos + tl0 + tl) * a.rec_words; };
+  auto val_blk = [&](int tl) {
+    return a.val_blocks + ((int64_t)slot * nblk + (a.pos + tl0 + tl) / kBlockTokens) * a.block_words;
+  };
+  if (threadIdx.x < kDqTok) {
+    const int tl = threadIdx.x;
+    float n = 0.f;
+    if (tl < nt)
+      n = __uint_as_float(a.keys ? key_rec(tl)[a.rec_words - 2]
+                                 : val_blk(tl)[4 * a.bits * a.d + (int)((a.pos + tl0 + tl) % kBlockTokens)]);
+    nsh[tl] = n;
+  }
   for (int e = threadIdx.x; e < a.d * kDqTok; e += blockDim.x) {
     const int tl = e % kDqTok, j = e / kDqTok;
     float v = 0.f;
     if (tl < nt) {
-      const int64_t t = a.pos + tl0 + tl;
       int code;
-      float n;
       if (a.keys) {
-        const uint32_t* rp = a.key_rec + ((int64_t)slot * a.capacity + t) * a.rec_words;
         const int g = j >> 7, jj = j & 127;
-        code = group_code(rp + a.bits * (((jj >> 2) & 3) * (a.d >> 7) + g), 1, a.bits, jj >> 4, jj & 3);
-        n = __uint_as_float(rp[a.rec_words - 2]);
+        code = group_code(key_rec(tl) + a.bits * (((jj >> 2) & 3) * (a.d >> 7) + g), 1, a.bits, jj >> 4, jj & 3);
       } else {
-        const uint32_t* vb = a.val_blocks + ((int64_t)slot * nblk + t / kBlockTokens) * a.block_words;
-        const int tau = (int)(t % kBlockTokens);
-        code = group_code(vb + ((tau >> 2) & 3) * a.d + j, 4 * a.d, a.bits, tau >> 4, tau & 3);
-        n = __uint_as_float(vb[4 * a.bits * a.d + tau]);
+        const int tau = (int)((a.pos + tl0 + tl) % kBlockTokens);
+        code = group_code(val_blk(tl) + ((tau >> 2) & 3) * a.d + j, 4 * a.d, a.bits, tau >> 4, tau & 3);
       }
-      v = a.cent[code] * n;
+      v = a.cent[code];
     }
     ys[j * kDqTok + tl] = v;
   }
@@ -94,7 +103,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int tl = 16 * half + u;
-      if (tl < nt) a.out[((int64_t)slot * a.n_tokens + tl0 + tl) * a.d + c] = acc[u];
+      if (tl < nt) a.out[((int64_t)slot * a.n_tokens + tl0 + tl) * a.d + c] = acc[u] * nsh[tl];
     }
   }
 }

@@ -368,6 +368,26 @@ __device__ __forceinline__ void put_sel4_rt(uint32_t (&w)[B], int s, uint32_t x)
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
+// Norms of finite fp32 rows at any magnitude.  e = pow2_exponent(max |x|)
+// gives max |x| in [2^(e-1), 2^e) (0 for a zero row); the scaled coordinates
+// ldexp(x, -e) are exact and their sum of squares lies in [2^-2, n], so it
+// neither overflows nor underflows, and ||x|| = ldexp(sqrt(sum), e).
+__device__ __forceinline__ int pow2_exponent(float a) {
+  int e = 0;
+  frexpf(a, &e);
+  return a > 0.f ? e : 0;
+}
+
+// The fp32 input pre-scale of the matrix-core kernels: the row is brought to
+// |x| < 2^13 (fp16 hi/lo operands) by ldexp(x, input_shift(||x||)), an exact
+// power-of-two shift that, unlike a multiply by 2^(13 - E), cannot overflow
+// for tiny norms.
+__device__ __forceinline__ int input_shift(float n) {
+  int E = 0;
+  frexpf(n, &E);
+  return n > 0.f ? 13 - E : 0;
+}
+
 // Partial sum of squares of 32 fp16 coordinates (dot2 with fp32 accumulation;
 // the fp16 x fp16 products are exact).
 __device__ __forceinline__ float sq_norm16(const h8 (&x)[4]) {

@@ -46,7 +46,7 @@ struct GenArgs {
   const uint16_t* r_lo;
   const uint16_t* s_hi;
   const uint16_t* s_lo;
-  float* nrm;         // [n_seq * n_sub] norms of this launch's rows
+  float* nrm;         // [n_seq * n_sub] rows' (||x 2^-e||, e): norm of the row shifted by its exponent
   uint16_t* res_hi;   // [n_seq * n_sub][d] residual 2^12 (y - c), slot order, fp16 high part
   uint16_t* res_lo;
   float* g2p;         // [n_seq * n_sub][n_oct] partial sums of the squared residual
@@ -91,18 +91,18 @@ struct Slice {
 // 8 inputs of a row as an MFMA operand: fp16 rows as they are; fp32 rows
 // scaled by sc (|x sc| < 2^13) and split into fp16 hi + lo.
 template <bool F32>
-__device__ __forceinline__ void load_x8(const void* x, int64_t row, int d, int k, float sc, h8& xh, h8& xl) {
+__device__ __forceinline__ void load_x8(const void* x, int64_t row, int d, int k, int sh, h8& xh, h8& xl) {
   if constexpr (F32) {
     const float* p = (const float*)x + row * d + k;
     const f4 v0 = *(const f4*)p, v1 = *(const f4*)(p + 4);
     u4 hi, lo;
-    HiLo t = split2(v0[0] * sc, v0[1] * sc);
+    HiLo t = split2(ldexpf(v0[0], sh), ldexpf(v0[1], sh));
     hi[0] = t.hi; lo[0] = t.lo;
-    t = split2(v0[2] * sc, v0[3] * sc);
+    t = split2(ldexpf(v0[2], sh), ldexpf(v0[3], sh));
     hi[1] = t.hi; lo[1] = t.lo;
-    t = split2(v1[0] * sc, v1[1] * sc);
+    t = split2(ldexpf(v1[0], sh), ldexpf(v1[1], sh));
     hi[2] = t.hi; lo[2] = t.lo;
-    t = split2(v1[2] * sc, v1[3] * sc);
+    t = split2(ldexpf(v1[2], sh), ldexpf(v1[3], sh));
     hi[3] = t.hi; lo[3] = t.lo;
     xh = as_h8(hi);
     xl = as_h8(lo);
@@ -129,12 +129,6 @@ __device__ __forceinline__ void xcd_tile_chunk(int64_t b, int64_t ntiles, int nc
   }
 }
 
-// Power-of-two pre-scale of an fp32 row of norm n: |x sc| < 2^13.
-__device__ __forceinline__ float row_scale(float n) {
-  int E = 0;
-  frexpf(n, &E);
-  return n > 0.f ? ldexpf(1.f, 13 - E) : 1.f;
-}
 
 // ---------------------------------------------------------------------------
 
@@ -144,12 +138,29 @@ __global__ __launch_bounds__(256) void gen_row_norms(const GenArgs a, int dtype)
   if (r >= (int64_t)a.n_seq * a.n_sub) return;
   const int64_t row = gen_in_row(a, r);
   float s = 0.f;
+  int ex = 0;
   if (dtype == TQ_F32) {
+    // (pre-scaled by the largest magnitude: any finite row; d <= 1024, so a
+    // lane holds at most 4 quads)
     const float* p = (const float*)a.x + row * a.d;
-    for (int c = 4 * lane; c < a.d; c += 256) {
-      const f4 v = *(const f4*)(p + c);
-      s = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], s))));
+    f4 v[4];
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 4 * lane + 256 * i;
+      v[i] = c < a.d ? *(const f4*)(p + c) : f4{0.f, 0.f, 0.f, 0.f};
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3]))));
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+    ex = pow2_exponent(mx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float u = ldexpf(v[i][e], -ex);
+        s = fmaf(u, u, s);
+      }
   } else {
     const _Float16* p = (const _Float16*)a.x + row * a.d;
     for (int c = 8 * lane; c < a.d; c += 512) {
@@ -160,7 +171,7 @@ __global__ __launch_bounds__(256) void gen_row_norms(const GenArgs a, int dtype)
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += shfl_xor(s, o);
-  if (lane == 0) a.nrm[r] = sqrtf(s);
+  if (lane == 0) ((float2*)a.nrm)[r] = make_float2(sqrtf(s), (float)ex);
 }
 
 // ---------------------------------------------------------------------------
@@ -183,14 +194,18 @@ __global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
   if (tid < 16) ctab[tid] = a.cb.cent[tid] * kResScale;
 
   int64_t row[2], in_row[2];
-  float n[2], sc[2];
+  float n[2], sigma[2];
+  int sh[2];  // fp32 pre-shift: |x 2^sh| < 2^13; 0 for fp16
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     row[j] = rtile * 128 + wave * 32 + 16 * j + r16;
     const int64_t rr = row[j] < rows ? row[j] : rows - 1;  // rows past the end: any valid row, not stored
     in_row[j] = gen_in_row(a, rr);
-    n[j] = a.nrm[rr];
-    sc[j] = F32 ? row_scale(n[j]) : 1.f;
+    const float2 ne = ((const float2*)a.nrm)[rr];
+    const int ex = (int)ne.y, s0 = input_shift(ne.x);
+    n[j] = ldexpf(ne.x, ex);
+    sh[j] = F32 ? s0 - ex : 0;
+    sigma[j] = kRotScale * (F32 ? ldexpf(ne.x, s0) : n[j]);
   }
   f4 acc[2][8];
 #pragma unroll
@@ -202,7 +217,7 @@ __global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
   sl.fetch(a.r_hi, a.r_lo, a.ld, 128 * u, 0);
   h8 xh[2], xl[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) load_x8<F32>(a.x, in_row[j], a.d, 8 * q, sc[j], xh[j], xl[j]);
+  for (int j = 0; j < 2; ++j) load_x8<F32>(a.x, in_row[j], a.d, 8 * q, sh[j], xh[j], xl[j]);
   sl.store(Rs[0]);
   __syncthreads();
   for (int k0 = 0, buf = 0; k0 < a.d; k0 += 32, buf ^= 1) {
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
     if (more) {
       sl.fetch(a.r_hi, a.r_lo, a.ld, 128 * u, k0 + 32);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) load_x8<F32>(a.x, in_row[j], a.d, k0 + 32 + 8 * q, sc[j], nh[j], nl[j]);
+      for (int j = 0; j < 2; ++j) load_x8<F32>(a.x, in_row[j], a.d, k0 + 32 + 8 * q, sh[j], nh[j], nl[j]);
     }
     const uint16_t* Rh = Rs[buf];
     const uint16_t* Rl = Rs[buf] + 128 * kSliceLS;
@@ -242,11 +257,10 @@ __global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const bool valid = row[j] < rows;
-    const float sigma = kRotScale * sc[j] * n[j];
-    const float s16 = n[j] > 0.f ? kResScale / sigma : 0.f;
+    const float s16 = n[j] > 0.f ? kResScale / sigma[j] : 0.f;
     float bs[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) bs[t] = t < H - 1 ? bpos[t] * sigma : 0.f;
+    for (int t = 0; t < 8; ++t) bs[t] = t < H - 1 ? bpos[t] * sigma[j] : 0.f;
     uint32_t cw[B];
 #pragma unroll
     for (int w = 0; w < B; ++w) cw[w] = 0u;
@@ -372,21 +386,23 @@ __global__ __launch_bounds__(256) void gen_values(const GenArgs a) {
   if (tid < kBlockTokens) {
     const int64_t p = tok0 + tid;
     const bool valid = p >= P0 && p < P1;
-    const float nn = valid ? a.nrm[slot * a.n_sub + (p - P0)] : 0.f;
-    const float sigma = kRotScale * (F32 ? row_scale(nn) : 1.f) * nn;
+    const float2 ne = valid ? ((const float2*)a.nrm)[slot * a.n_sub + (p - P0)] : make_float2(0.f, 0.f);
+    const float nn = ldexpf(ne.x, (int)ne.y);
+    const float sigma = kRotScale * (F32 ? ldexpf(ne.x, input_shift(ne.x)) : nn);
     inv_sh[tid] = sigma > 0.f ? 1.f / sigma : 0.f;
     nrm_sh[tid] = nn;
   }
   // A operand rows: block token 16 mt + r16
   int64_t in_row[8];
-  float sc[8];
+  int sh[8];  // fp32 pre-shift (input_shift); 0 for fp16
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
     int64_t p = tok0 + 16 * mt + r16;
     p = p < P0 ? P0 : (p >= P1 ? P1 - 1 : p);  // clamp to a row of this launch (codes masked later)
     const int64_t r = slot * a.n_sub + (p - P0);
     in_row[mt] = gen_in_row(a, r);
-    sc[mt] = F32 ? row_scale(a.nrm[r]) : 1.f;
+    const float2 ne = ((const float2*)a.nrm)[r];
+    sh[mt] = F32 ? input_shift(ne.x) - (int)ne.y : 0;
   }
   f4 acc[8][2];
 #pragma unroll
@@ -409,7 +425,7 @@ __global__ __launch_bounds__(256) void gen_values(const GenArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       h8 xh, xl;
-      load_x8<F32>(a.x, in_row[mt], a.d, k0 + 8 * q, sc[mt], xh, xl);
+      load_x8<F32>(a.x, in_row[mt], a.d, k0 + 8 * q, sh[mt], xh, xl);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         acc[mt][t] = mfma(xh, bh[t], acc[mt][t]);
@@ -491,7 +507,8 @@ __global__ __launch_bounds__(512) void prep_queries128(const GenPrepArgs a) {
   __shared__ __align__(16) float qs[16][D];
   __shared__ __align__(16) float qt[16][D];
   __shared__ float pp[16][Mp];
-  __shared__ float qn[16];
+  __shared__ float qn[16];  // norms of the shifted queries
+  __shared__ int qe[16];    // their shifts: ||q|| = ldexp(qn, qe)
   const int slot = blockIdx.x / a.HG, hg = blockIdx.x % a.HG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = max(0, min(16, a.G - 16 * hg));  // live head lanes of this group
@@ -514,12 +531,27 @@ __global__ __launch_bounds__(512) void prep_queries128(const GenPrepArgs a) {
     qs[hh][k] = v;
   }
   __syncthreads();
+  // each query shifted by 2^-e, 2^e the binary exponent of its largest
+  // magnitude (exact): norms and products neither overflow nor underflow for
+  // any finite query, and the operands q~/||q|| are unchanged
   for (int hh = wave; hh < 16; hh += 8) {
-    float s = qs[hh][lane] * qs[hh][lane] + qs[hh][lane + 64] * qs[hh][lane + 64];
+    const float x0 = qs[hh][lane], x1 = qs[hh][lane + 64];
+    float mx = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+    const int ex = pow2_exponent(mx);
+    const float u0 = ldexpf(x0, -ex), u1 = ldexpf(x1, -ex);
+    qs[hh][lane] = u0;
+    qs[hh][lane + 64] = u1;
+    float s = u0 * u0 + u1 * u1;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += shfl_xor(s, o);
-    if (lane == 0) qn[hh] = sqrtf(s);
+    if (lane == 0) {
+      qn[hh] = sqrtf(s);
+      qe[hh] = ex;
+    }
   }
+  __syncthreads();
   // q~ = R q: row tid/4, columns 32 (tid%4) ..; the four parts summed by lane exchanges
   for (int hh = 0; hh < nl; ++hh) {
     const f4* x = (const f4*)(&qs[hh][32 * (tid & 3)]);
@@ -578,7 +610,7 @@ __global__ __launch_bounds__(512) void prep_queries128(const GenPrepArgs a) {
     const int l = 16 * qq + h16;
     *(h8*)(a.wq + ((((int64_t)slot * a.HG + hg) * KBT + kb) * 64 + l) * 8) = v;
   }
-  if (tid < 16) a.wqn[((int64_t)slot * a.HG + hg) * 16 + tid] = tid < nl ? qn[tid] : 0.f;
+  if (tid < 16) a.wqn[((int64_t)slot * a.HG + hg) * 16 + tid] = tid < nl ? ldexpf(qn[tid], qe[tid]) : 0.f;
 }
 
 // ---------------------------------------------------------------------------

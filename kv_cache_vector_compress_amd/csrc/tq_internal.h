@@ -93,7 +93,7 @@ constexpr int kMaxGeneralHeads = 512;   // query heads per KV slot for general s
 struct GenMats {
   Matrices mats;         // R / S images (row stride ld halves) and fp32 copies
   int ld;                // d + 8
-  float* nrm;            // scratch: [scratch_rows] row norms
+  float* nrm;            // scratch: [scratch_rows] (shifted norm, exponent) pairs
   uint16_t* res_hi;      // scratch: [scratch_rows][d] key residual, fp16 high part
   uint16_t* res_lo;      //          and low part
   float* g2p;            // scratch: [scratch_rows][d/128] residual square sums

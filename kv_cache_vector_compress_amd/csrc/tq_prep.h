@@ -32,15 +32,35 @@ __device__ __forceinline__ void gen_prep_block(const GenPrepArgs& a, int bid) {
   const int slot = bid / H16, h = bid % H16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool live = h < a.G;
-  float s = 0.f;
-  for (int k = tid; k < a.d; k += blockDim.x) {
-    float v = 0.f;
-    if (live) {
+  // The query is kept in LDS shifted by 2^-e, 2^e the binary exponent of its
+  // largest magnitude (exact), so that its norm and the products below
+  // neither overflow nor underflow for any finite query; qn is the shifted
+  // query's norm, the operands q~/||q|| are unchanged, and ||q|| = ldexp(qn, e).
+  // (256 threads and d <= 1024: at most 4 coordinates a thread.)
+  float v4[4], mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = tid + i * (int)blockDim.x;
+    v4[i] = 0.f;
+    if (live && k < a.d) {
       const int64_t off = ((int64_t)slot * a.G + h) * a.d + k;
-      v = a.dtype == TQ_F32 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
+      v4[i] = a.dtype == TQ_F32 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
     }
-    qs[k] = v;
-    s = fmaf(v, v, s);
+    mx = fmaxf(mx, fabsf(v4[i]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  const int ex = pow2_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = tid + i * (int)blockDim.x;
+    const float u = ldexpf(v4[i], -ex);
+    if (k < a.d) qs[k] = u;
+    s = fmaf(u, u, s);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += shfl_xor(s, o);
@@ -108,7 +128,7 @@ __device__ __forceinline__ void gen_prep_block(const GenPrepArgs& a, int bid) {
     const int l = 16 * qq + h16;
     *(h8*)(a.wq + ((((int64_t)slot * a.HG + hg) * KBT + kb) * 64 + l) * 8) = v;
   }
-  if (tid == 0) a.wqn[(int64_t)slot * H16 + h] = live ? qn : 0.f;
+  if (tid == 0) a.wqn[(int64_t)slot * H16 + h] = live ? ldexpf(qn, ex) : 0.f;
 }
 
 

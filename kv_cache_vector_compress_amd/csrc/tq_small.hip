@@ -99,15 +99,45 @@ __device__ __forceinline__ void matvec_pref(const HalfRows& h, int n_rows, const
   if (j < n_rows && half == 0) out[j] = t;
 }
 
-// Load row `row` of the input into LDS (fp32) and return its norm.
-__device__ __forceinline__ float load_input(const SmallArgs& a, int64_t row, float* xs, float* red) {
-  float ss = 0.f;
-  for (int k = threadIdx.x; k < a.d; k += blockDim.x) {
-    const int64_t o = row * a.d + k;
-    const float v = a.dtype == TQ_F32 ? ((const float*)a.x)[o] : (float)((const _Float16*)a.x)[o];
-    xs[k] = v;
-    ss = fmaf(v, v, ss);
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float m = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+// Load row `row` of the input into LDS as fp32, shifted by 2^-e with 2^e the
+// binary exponent of its largest magnitude (exact), so that sums of squares
+// and products with R and S neither overflow nor underflow for any finite
+// row.  Returns the norm of the stored (shifted) row; the row's own norm is
+// ldexp of it by e (*ex).  d <= 1024: a thread holds at most 4 coordinates.
+__device__ __forceinline__ float load_input(const SmallArgs& a, int64_t row, float* xs, float* red, int* ex) {
+  float v[4], mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = threadIdx.x + i * (int)blockDim.x;
+    v[i] = 0.f;
+    if (k < a.d) {
+      const int64_t o = row * a.d + k;
+      v[i] = a.dtype == TQ_F32 ? ((const float*)a.x)[o] : (float)((const _Float16*)a.x)[o];
+    }
+    mx = fmaxf(mx, fabsf(v[i]));
   }
+  const int e = pow2_exponent(block_max(mx, red));
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = threadIdx.x + i * (int)blockDim.x;
+    const float u = ldexpf(v[i], -e);
+    if (k < a.d) xs[k] = u;
+    ss = fmaf(u, u, ss);
+  }
+  *ex = e;
   return sqrtf(block_sum(ss, red));
 }
 
@@ -160,14 +190,16 @@ __device__ __forceinline__ void small_keys_block(const SmallArgs& a, int64_t bid
   if (threadIdx.x < 16) ctab[threadIdx.x] = a.cent[threadIdx.x];
   // (head_dim 128 with proj_dim 64 or 128 takes the matrix-core kernel, so
   // the matrices here are read row by row from L2)
-  const float n = load_input(a, (int64_t)slot * a.n_new + t, xs, red);
+  int ex = 0;
+  const float ns = load_input(a, (int64_t)slot * a.n_new + t, xs, red, &ex);  // norm of the shifted row
+  const float n = ldexpf(ns, ex);
   __syncthreads();
   matvec(a.r32, a.d, a.d, xs, ys);
   __syncthreads();
-  const float inv = n > 0.f ? 1.f / n : 0.f;
+  const float inv = ns > 0.f ? 1.f / ns : 0.f;
   float g2 = 0.f;
   for (int j = threadIdx.x; j < a.d; j += blockDim.x) {
-    const float u = n > 0.f ? ys[j] * inv : 0.f;
+    const float u = ns > 0.f ? ys[j] * inv : 0.f;
     const int idx = cell(u, beta);
     const float r = u - ctab[idx];
     is[j] = idx;
@@ -241,15 +273,16 @@ __device__ __forceinline__ void small_values_block(const SmallArgs& a, int64_t b
   if (d128) prefetch_rows(a.r32, 128, hr);
   for (int u = 0; u < nt; ++u) {
     const int64_t t = t_lo + u;
-    const float n = load_input(a, (int64_t)slot * a.n_new + (t - a.pos), xs, red);
+    int ex = 0;
+    const float ns = load_input(a, (int64_t)slot * a.n_new + (t - a.pos), xs, red, &ex);  // shifted row's norm
     __syncthreads();
     if (d128) matvec_pref(hr, 128, xs, ys);
     else matvec(a.r32, a.d, a.d, xs, ys);
     __syncthreads();
-    const float inv = n > 0.f ? 1.f / n : 0.f;
-    for (int j = threadIdx.x; j < a.d; j += blockDim.x) cs[u * a.d + j] = cell(n > 0.f ? ys[j] * inv : 0.f, beta);
+    const float inv = ns > 0.f ? 1.f / ns : 0.f;
+    for (int j = threadIdx.x; j < a.d; j += blockDim.x) cs[u * a.d + j] = cell(ns > 0.f ? ys[j] * inv : 0.f, beta);
     if (threadIdx.x == 0) {
-      nrm[u] = n;
+      nrm[u] = ldexpf(ns, ex);
       tau_of[u] = (int)(t - blk * kBlockTokens);
     }
     __syncthreads();

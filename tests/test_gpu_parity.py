@@ -679,3 +679,74 @@ def test_vector_search_full_size_sampled():
     _say("vector search full size", st)
     del cache, sc, X
     ctx.close()
+
+
+def _pow2_rows(X, exps):
+    """Rows of X (n_seq, T, d) scaled by powers of two cycling through exps,
+    as fp32 (exact scalings; 2^-135 gives subnormal coordinates)."""
+    e = np.asarray(exps, dtype=np.float64)[np.arange(X.shape[1]) % len(exps)]
+    return (X.astype(np.float64) * np.exp2(e)[None, :, None]).astype(np.float32)
+
+
+@pytest.mark.parametrize("d,m,chunks", [(128, 64, [256, 3, 41]), (256, 128, [200, 100])])
+def test_extreme_fp32_magnitudes(d, m, chunks):
+    """fp32 inputs across the fp32 range: keys and values with per-token
+    scales 2^-135 (subnormal coordinates) .. 2^100 and queries 2^-10 .. 2^10,
+    appended in bulk and in small chunks (single-kernel, small-append and
+    general paths).  Norms are taken over rows pre-shifted by their largest
+    magnitude, so codes, signs, norms and scores match the oracle at every
+    scale (products |q| ||k|| stay inside the fp32 range).  Attention with
+    values at 2^-120 .. 2^120 and moderate keys matches as well."""
+    n_seq, T, G = 2, 300, 4
+    exps = [-135, -126, -100, -60, -20, 0, 20, 60, 100]
+    K0 = np.stack([synth.kv_slot(170 + d, s, s, T, d, dtype=np.float32) for s in range(n_seq)])
+    V0 = np.stack([synth.kv_slot(171 + d, s, s, T, d, dtype=np.float32) for s in range(n_seq)])
+    Q0 = np.stack([synth.kv_slot(172 + d, s, s, G, d, dtype=np.float32) for s in range(n_seq)])
+    K, V = _pow2_rows(K0, exps), _pow2_rows(V0, exps[::-1])
+    Q = (Q0.astype(np.float64) * np.exp2([-10.0, 0.0, 10.0, 3.0])[None, :, None]).astype(np.float32)
+    _say("extreme magnitudes", (d, m, chunks))
+    _say(run_case(K, V, Q, kb=3, vb=3, m=m, chunks=chunks, check_attend=False))
+    V2 = _pow2_rows(V0, [-120, -60, 0, 60, 120, 7, -7])
+    _say(run_case(K0, V2, Q0, kb=3, vb=3, m=m, chunks=chunks, check_attend=True))
+
+
+def test_extreme_fp32_magnitudes_decode_step():
+    """The fused decode step (small appends and query preparation in one
+    launch) on fp32 rows at 2^-130 .. 2^100 and queries at 2^-100 and 2^-96:
+    codes and norms against the oracle, attention against the oracle on the
+    GPU's codes."""
+    d, m, G, n_seq, prefill = 128, 64, 4, 2, 130
+    steps = [1, 3, 1]
+    T = prefill + sum(steps)
+    K = _pow2_rows(np.stack([synth.kv_slot(180, s, s, T, d, dtype=np.float32) for s in range(n_seq)]),
+                   [-130, 0, 100, -60, 30])
+    V = _pow2_rows(np.stack([synth.kv_slot(181, s, s, T, d, dtype=np.float32) for s in range(n_seq)]),
+                   [100, -130, 0, 50])
+    Q0 = np.stack([synth.kv_slot(182, s, s, G, d, dtype=np.float32) for s in range(n_seq)])
+    _say("extreme magnitudes, decode steps")
+    ctx, R, S = make_ctx(d, m, 3, 3)
+    cache = tq.KVCache(ctx, n_seq, 256)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    cache.append_key(dev(K[:, :prefill]), 0)
+    cache.append_value(dev(V[:, :prefill]), 0)
+    pos, outs, qs = prefill, [], []
+    for i, n in enumerate(steps):
+        # tiny queries against the 2^100 keys keep the logits moderate (no
+        # hard argmax between nearly equal estimates)
+        Q = (Q0.astype(np.float64) * 2.0 ** (-100 if i % 2 == 0 else -96)).astype(np.float32)
+        qs.append(Q)
+        outs.append(cache.decode_step(dev(K[:, pos:pos + n]), dev(V[:, pos:pos + n]), dev(Q), pos).cpu().numpy())
+        pos += n
+    beta, c = O.lloyd_max_codebook(d, 3)
+    gk = P.unpack_gpu_keys(cache, d, m, 3, T)
+    gv = P.unpack_gpu_values(cache, d, 3, T)
+    st = P.check_keys(gk, O.compress_keys(K, R, S, beta, c), beta, S, c)
+    st.pop("flip_tokens")
+    st.update({"v_" + k: v for k, v in P.check_values(gv, O.compress_values(V, R, beta, c), beta).items()})
+    pos, errs = prefill, []
+    for n, Q, out in zip(steps, qs, outs):
+        pos += n
+        ref = O.attend(Q, R, S, c, {k: a[:, :pos] for k, a in gk.items()}, {k: a[:, :pos] for k, a in gv.items()})
+        errs.append(P.check_attend(out, ref))
+    _say(st, errs)
+    ctx.close()
