@@ -378,6 +378,24 @@ __device__ __forceinline__ int pow2_exponent(float a) {
   return a > 0.f ? e : 0;
 }
 
+// One-pass form for block reductions: a partial (e, s) stands for a sum of
+// squares s 2^(2e) with s taken over coordinates shifted by 2^-e, e the
+// exponent of the partial's largest magnitude (kNoExp for a zero partial, so
+// that it never sets the exponent).  Two partials merge exactly at the larger
+// exponent; the merged e is that of the whole row's largest magnitude, and
+// ||x|| = ldexp(sqrt(s), e).
+constexpr int kNoExp = -1000;
+__device__ __forceinline__ void norm2_partial(float mx, int& e) { e = mx > 0.f ? pow2_exponent(mx) : kNoExp; }
+__device__ __forceinline__ void merge_norm2(int& e, float& s, int e2, float s2) {
+  const int E = e > e2 ? e : e2;
+  s = ldexpf(s, 2 * (e - E)) + ldexpf(s2, 2 * (e2 - E));
+  e = E;
+}
+__device__ __forceinline__ void wave_norm2(int& e, float& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) merge_norm2(e, s, __shfl_xor(e, o, 64), __shfl_xor(s, o, 64));
+}
+
 // The fp32 input pre-scale of the matrix-core kernels: the row is brought to
 // |x| < 2^13 (fp16 hi/lo operands) by ldexp(x, input_shift(||x||)), an exact
 // power-of-two shift that, unlike a multiply by 2^(13 - E), cannot overflow

@@ -27,7 +27,7 @@ __device__ __forceinline__ void gen_prep_block(const GenPrepArgs& a, int bid) {
   float* qs = gsm;          // [d]
   float* qt = qs + a.d;     // [d]
   float* pp = qt + a.d;     // [m]
-  __shared__ float red[4];
+  __shared__ float red[8];
   const int H16 = 16 * a.HG;
   const int slot = bid / H16, h = bid % H16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -48,25 +48,33 @@ __device__ __forceinline__ void gen_prep_block(const GenPrepArgs& a, int bid) {
     }
     mx = fmaxf(mx, fabsf(v4[i]));
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  const int ex = pow2_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-  __syncthreads();
+  // one block reduction of (exponent, sum of squares) partials
+  int e;
+  norm2_partial(mx, e);
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int k = tid + i * (int)blockDim.x;
-    const float u = ldexpf(v4[i], -ex);
-    if (k < a.d) qs[k] = u;
+    const float u = ldexpf(v4[i], -e);
     s = fmaf(u, u, s);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += shfl_xor(s, o);
-  if (lane == 0) red[wave] = s;
+  wave_norm2(e, s);
+  if (lane == 0) {
+    red[2 * wave] = s;
+    red[2 * wave + 1] = __int_as_float(e);
+  }
   __syncthreads();
-  const float qn = sqrtf((red[0] + red[1]) + (red[2] + red[3]));
+  float S = red[0];
+  int ex = __float_as_int(red[1]);
+#pragma unroll
+  for (int w = 1; w < 4; ++w) merge_norm2(ex, S, __float_as_int(red[2 * w + 1]), red[2 * w]);
+  if (ex == kNoExp) ex = 0;  // a zero query (or a head lane past G)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = tid + i * (int)blockDim.x;
+    if (k < a.d) qs[k] = ldexpf(v4[i], -ex);
+  }
+  const float qn = sqrtf(S);
+  __syncthreads();  // qs complete
   // q~ = R q and p = S q~.  A head lane past G has q = 0 and takes no
   // products.  Each output row is split over 4 neighbouring threads (a
   // quarter of its columns each, all of their loads in flight at once), and

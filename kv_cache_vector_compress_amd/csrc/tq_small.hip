@@ -99,23 +99,12 @@ __device__ __forceinline__ void matvec_pref(const HalfRows& h, int n_rows, const
   if (j < n_rows && half == 0) out[j] = t;
 }
 
-__device__ __forceinline__ float block_max(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float m = 0.f;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
-  return m;
-}
-
 // Load row `row` of the input into LDS as fp32, shifted by 2^-e with 2^e the
 // binary exponent of its largest magnitude (exact), so that sums of squares
 // and products with R and S neither overflow nor underflow for any finite
 // row.  Returns the norm of the stored (shifted) row; the row's own norm is
-// ldexp of it by e (*ex).  d <= 1024: a thread holds at most 4 coordinates.
+// ldexp of it by e (*ex).  One block reduction of (exponent, sum) partials.
+// d <= 1024: a thread holds at most 4 coordinates.
 __device__ __forceinline__ float load_input(const SmallArgs& a, int64_t row, float* xs, float* red, int* ex) {
   float v[4], mx = 0.f;
 #pragma unroll
@@ -128,17 +117,33 @@ __device__ __forceinline__ float load_input(const SmallArgs& a, int64_t row, flo
     }
     mx = fmaxf(mx, fabsf(v[i]));
   }
-  const int e = pow2_exponent(block_max(mx, red));
-  float ss = 0.f;
+  int e;
+  norm2_partial(mx, e);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float u = ldexpf(v[i], -e);
+    s = fmaf(u, u, s);
+  }
+  wave_norm2(e, s);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();  // (red may still be read by an earlier reduction)
+  if (lane == 0) {
+    red[2 * wave] = s;
+    red[2 * wave + 1] = __int_as_float(e);
+  }
+  __syncthreads();
+  float S = red[0];
+  int E = __float_as_int(red[1]);
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) merge_norm2(E, S, __float_as_int(red[2 * w + 1]), red[2 * w]);
+  if (E == kNoExp) E = 0;  // a zero row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int k = threadIdx.x + i * (int)blockDim.x;
-    const float u = ldexpf(v[i], -e);
-    if (k < a.d) xs[k] = u;
-    ss = fmaf(u, u, ss);
+    if (k < a.d) xs[k] = ldexpf(v[i], -E);
   }
-  *ex = e;
-  return sqrtf(block_sum(ss, red));
+  *ex = E;
+  return sqrtf(S);
 }
 
 // #{i : beta_i < u}; beta holds +inf past the last boundary, so all 15
@@ -180,7 +185,7 @@ __device__ __forceinline__ void small_keys_block(const SmallArgs& a, int64_t bid
   float* rs = ys + a.d;        // [d] residual
   float* zs = rs + a.d;        // [m] S r
   int* is = (int*)(zs + a.m);  // [d] cells
-  __shared__ float red[kSmallThreads / 64];
+  __shared__ float red[2 * (kSmallThreads / 64)];
   __shared__ float ctab[16];
   const int slot = (int)(bid / a.n_new);
   const int64_t t = bid - (int64_t)slot * a.n_new;
@@ -256,7 +261,7 @@ __device__ __forceinline__ void small_values_block(const SmallArgs& a, int64_t b
   float* xs = ssm;             // [d]
   float* ys = xs + a.d;        // [d]
   int* cs = (int*)(ys + a.d);  // [16][d] cells of the block's new tokens (at most 16)
-  __shared__ float red[kSmallThreads / 64];
+  __shared__ float red[2 * (kSmallThreads / 64)];
   __shared__ float nrm[16];
   __shared__ int tau_of[16];
   const int64_t blk0 = a.pos / kBlockTokens;
