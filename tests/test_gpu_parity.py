@@ -750,3 +750,32 @@ def test_extreme_fp32_magnitudes_decode_step():
         errs.append(P.check_attend(out, ref))
     _say(st, errs)
     ctx.close()
+
+
+@pytest.mark.parametrize("d,m,dtype", [(128, 64, np.float16), (256, 128, np.float32)])
+def test_zero_query_heads(d, m, dtype):
+    """A query head of all zeros scores exactly 0 against every key, and its
+    attention is the plain average of the dequantised values (softmax of
+    equal logits), as the oracle has it; the other heads are unaffected."""
+    n_seq, T, G = 2, 200, 4
+    K = np.stack([synth.kv_slot(190 + d, s, s, T, d, dtype=dtype) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(191 + d, s, s, T, d, dtype=dtype) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(192 + d, s, s, G, d, dtype=dtype) for s in range(n_seq)])
+    Q[0, 1] = 0
+    Q[1, 3] = 0
+    _say("zero query heads", (d, m, np.dtype(dtype).name))
+    ctx, R, S = make_ctx(d, m, 3, 3)
+    cache = tq.KVCache(ctx, n_seq, 256)
+    cache.append_key(torch.from_numpy(K).cuda(), 0)
+    cache.append_value(torch.from_numpy(V).cuda(), 0)
+    qt = torch.from_numpy(Q).cuda()
+    sc = cache.attention_scores(qt, T).cpu().numpy()
+    out = cache.attend(qt, T).cpu().numpy()
+    assert not sc[0, 1].any() and not sc[1, 3].any()
+    gk = P.unpack_gpu_keys(cache, d, m, 3, T)
+    gv = P.unpack_gpu_values(cache, d, 3, T)
+    _, c = O.lloyd_max_codebook(d, 3)
+    ref = O.attend(Q, R, S, c, gk, gv)
+    np.testing.assert_allclose(ref[0, 1], O.dequantize_values(R, c, gv)[0].mean(0), rtol=1e-12, atol=1e-12)
+    _say({"attend_rel": P.check_attend(out, ref)})
+    ctx.close()
