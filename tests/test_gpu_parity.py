@@ -779,3 +779,52 @@ def test_zero_query_heads(d, m, dtype):
     np.testing.assert_allclose(ref[0, 1], O.dequantize_values(R, c, gv)[0].mean(0), rtol=1e-12, atol=1e-12)
     _say({"attend_rel": P.check_attend(out, ref)})
     ctx.close()
+
+
+def test_scores_and_attend_at_maximum_capacity():
+    """The single-kernel score and attend kernels over a slot of the maximum
+    capacity (2^24 tokens; ~1 GB of key records and ~0.9 GB of value blocks
+    addressed through per-slot buffer descriptors).  300 tokens are appended
+    at the very end; the zero records before them score exactly 0, and in the
+    softmax they add N_zero exp(0 - M) to the denominator and nothing to the
+    numerator (zero values), so the oracle's attention over all 2^24 tokens is
+    formed from the 300 real tokens in closed form."""
+    d, m, b, G, N = 128, 64, 3, 4, 300
+    cap = 1 << 24
+    pos = cap - N
+    _say("scores and attend at maximum capacity", (cap, pos, G))
+    K = synth.kv_slot(200, 0, 0, N, d)[None]
+    V = synth.kv_slot(201, 0, 0, N, d)[None]
+    Q = synth.kv_slot(202, 0, 0, G, d)[None] * 4
+    ctx, R, S = make_ctx(d, m, b, b)
+    cache = tq.KVCache(ctx, 1, cap)
+    cache.append_key(torch.from_numpy(K).cuda(), pos)
+    cache.append_value(torch.from_numpy(V).cuda(), pos)
+    qt = torch.from_numpy(np.ascontiguousarray(Q)).cuda()
+    sc_all = cache.attention_scores(qt, cap)
+    out = cache.attend(qt, cap).cpu().numpy()
+    assert float(sc_all[..., :pos].abs().max()) == 0.0
+    sc = sc_all[..., pos:].cpu().numpy()
+    del sc_all
+    rw = tq.key_record_bytes(ctx.cfg) // 4
+    recs = cache.key_records.view(1, cap, rw)[:, pos:].cpu().numpy().view(np.uint32)
+    bw = tq.value_block_bytes(ctx.cfg) // 4
+    blocks = cache.value_blocks.view(1, cap // 128, bw)[:, (pos // 128):].cpu().numpy().view(np.uint32)
+    _, c = O.lloyd_max_codebook(d, b)
+    gk = O.unpack_keys(recs, d, m, b)
+    gv_blk = O.unpack_values(blocks, d, b)
+    off = pos - (pos // 128) * 128
+    gv = {k: v[:, off:off + N] for k, v in gv_blk.items()}
+    est = O.key_scores(Q.astype(np.float64), R, S, c, gk)
+    qn = np.linalg.norm(Q.astype(np.float64), axis=-1)
+    kn = np.linalg.norm(K.astype(np.float64), axis=-1)
+    st = {"score": P.check_scores(sc, est, qn, kn)}
+    lg = est / np.sqrt(d)                                          # (1, G, N) logits of the real tokens
+    M = np.maximum(lg.max(-1, keepdims=True), 0.0)                 # the zero records' logit is 0
+    w = np.exp(lg - M)
+    den = w.sum(-1) + (cap - N) * np.exp(-M[..., 0])
+    ref = np.einsum("sgt,std->sgd", w, O.dequantize_values(R, c, gv)) / den[..., None]
+    st["attend_rel"] = P.check_attend(out, ref)
+    _say(st)
+    del cache
+    ctx.close()
