@@ -327,11 +327,22 @@ def test_error_paths_leave_buffers_untouched():
     b_bad = np.array([-0.1, 0.0, 0.1])
     expect(-1, lambda: tq._check(tq.lib().tq_codebook_load(ctx.handle, 2, c_bad.ctypes.data_as(D),
                                                           b_bad.ctypes.data_as(D))))
+    # 0 bits: the single centroid must be 0 (boundaries may be NULL); bits outside 0..4
+    c_one = np.array([0.01])
+    expect(-1, lambda: tq._check(tq.lib().tq_codebook_load(ctx.handle, 0, c_one.ctypes.data_as(D), None)))
+    c_zero = np.array([0.0])
+    tq._check(tq.lib().tq_codebook_load(ctx.handle, 0, c_zero.ctypes.data_as(D), None))
+    expect(-1, lambda: tq._check(tq.lib().tq_codebook_load(ctx.handle, 5, c_bad.ctypes.data_as(D),
+                                                          b_bad.ctypes.data_as(D))))
     # no codebook for the requested bits
     ctx2 = tq.Context(128, 64, 2, 2, R, S, load_codebooks=False)
     cache2 = tq.KVCache(ctx2, 2, 256)
     expect(-3, lambda: cache2.append_key(k, 0))
     expect(-3, lambda: cache2.attend(q, 5))
+    ctx3 = tq.Context(128, 64, 0, 2, R, S, load_codebooks=False)   # 0-bit keys need their codebook too
+    cache3 = tq.KVCache(ctx3, 2, 256)
+    expect(-3, lambda: cache3.append_key(k, 0))
+    expect(-3, lambda: cache3.attention_scores(q, 5))
     torch.cuda.synchronize()
     assert bool((cache.key_records == canary).all()) and bool((cache.value_blocks == canary).all())
     assert bool((cache2.key_records == 0).all())
@@ -341,6 +352,7 @@ def test_error_paths_leave_buffers_untouched():
     assert bool((cache.key_records == canary).all())
     ctx.close()
     ctx2.close()
+    ctx3.close()
 
 
 @pytest.mark.parametrize("d,m,kb,vb,T,chunks,rng", [
