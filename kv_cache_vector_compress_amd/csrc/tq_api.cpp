@@ -57,12 +57,12 @@ static int check_config(const tq_config* c) {
 
 // Shapes with the single-kernel compress / attention path; every other valid
 // shape runs on the general path (tq_general.hip).  Keys of 0 bits (signs
-// and norms only) always take the general path.
-static bool fast_keys(const tq_config& c) {
-  return c.head_dim == kD && (c.proj_dim == 64 || c.proj_dim == 128) && c.key_bits > 0;
-}
+// and norms only) are compressed by the 32 x 32-tile or the small kernel
+// (tq_append_key) and scored and attended on the single-kernel path.
+static bool fast_shape(const tq_config& c) { return c.head_dim == kD && (c.proj_dim == 64 || c.proj_dim == 128); }
+static bool fast_keys(const tq_config& c) { return fast_shape(c) && c.key_bits > 0; }
 static bool fast_values(const tq_config& c) { return c.head_dim == kD; }
-static bool fast_attn(const tq_config& c, int G) { return fast_keys(c) && G <= 16; }
+static bool fast_attn(const tq_config& c, int G) { return fast_shape(c) && G <= 16; }
 constexpr int64_t kScratchRows = 32768;  // general-path rows per launch
 
 static size_t key_rec_bytes(const tq_config& c) { return 4u * (c.key_bits * c.head_dim / 32 + c.proj_dim / 32 + 2); }
@@ -181,7 +181,7 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   const size_t off_sl32 = off_sh32 + b_simg, off_r32 = off_sl32 + b_simg;
   const size_t off_s32 = off_r32 + r32.size() * 4, end_imgs = off_s32 + s32.size() * 4;
   // general-path scratch (row norms, key residual hi/lo, residual square sums)
-  const bool gen = !fast_keys(*cfg) || !fast_values(*cfg);
+  const bool gen = (!fast_keys(*cfg) && cfg->key_bits > 0) || !fast_values(*cfg);
   const int64_t srows = gen ? kScratchRows : 0;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t off_nrm = up(end_imgs), off_rh = off_nrm + up((size_t)srows * 8);  // (norm, exponent) pairs

@@ -46,7 +46,7 @@ constexpr int kMaxPartials = 1024;
 
 template <int B, int M>
 struct KeyTile {
-  uint32_t cw[B];
+  uint32_t cw[B > 0 ? B : 1];  // (0-bit keys: no code words, unused)
   uint32_t sw[M / 64];
   float n, g;
 };
@@ -84,7 +84,9 @@ __device__ __forceinline__ f4 key_tile_scores(const KeyTile<B, M>& k, const h8 (
                                               const uint32_t (&tlo)[4], const uint32_t (&thi)[4], float kappa,
                                               int sh0, const PairTables* pt = nullptr) {
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (PT) {
+  if constexpr (B == 0) {
+    // 0-bit keys: the single centroid 0 adds nothing
+  } else if constexpr (PT) {
     static_assert(B == 3, "pair tables hold 3-bit codes");
     acc = mfma(decode_pair_lds<0>(k.cw, *pt), qb[0], acc);
     acc = mfma(decode_pair_lds<1>(k.cw, *pt), qb[1], acc);
@@ -740,8 +742,8 @@ int launch_scores(const CodebookDev& cbk, int kbits, int m, const AttnShape& s, 
   hipStream_t st = (hipStream_t)stream;
 #define TQ_SC(B, M) \
   if (kbits == B && m == M) { hipLaunchKernelGGL((scores_kernel<B, M>), grid, block, 0, st, a); goto done; }
-  TQ_SC(1, 64) TQ_SC(2, 64) TQ_SC(3, 64) TQ_SC(4, 64)
-  TQ_SC(1, 128) TQ_SC(2, 128) TQ_SC(3, 128) TQ_SC(4, 128)
+  TQ_SC(0, 64) TQ_SC(1, 64) TQ_SC(2, 64) TQ_SC(3, 64) TQ_SC(4, 64)
+  TQ_SC(0, 128) TQ_SC(1, 128) TQ_SC(2, 128) TQ_SC(3, 128) TQ_SC(4, 128)
 #undef TQ_SC
   return TQ_EUNSUPPORTED;
 done:
@@ -781,8 +783,8 @@ int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const
     launched = true;                                                                       \
   }
 #define TQ_AT_V(BK, M) TQ_AT(BK, 1, M) TQ_AT(BK, 2, M) TQ_AT(BK, 3, M) TQ_AT(BK, 4, M)
-  TQ_AT_V(1, 64) TQ_AT_V(2, 64) TQ_AT_V(3, 64) TQ_AT_V(4, 64)
-  TQ_AT_V(1, 128) TQ_AT_V(2, 128) TQ_AT_V(3, 128) TQ_AT_V(4, 128)
+  TQ_AT_V(0, 64) TQ_AT_V(1, 64) TQ_AT_V(2, 64) TQ_AT_V(3, 64) TQ_AT_V(4, 64)
+  TQ_AT_V(0, 128) TQ_AT_V(1, 128) TQ_AT_V(2, 128) TQ_AT_V(3, 128) TQ_AT_V(4, 128)
 #undef TQ_AT_V
 #undef TQ_AT
   if (!launched) return TQ_EUNSUPPORTED;
