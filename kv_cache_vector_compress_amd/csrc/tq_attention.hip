@@ -323,9 +323,15 @@ __device__ __forceinline__ float compact4(const f4& v) {
   return x;
 }
 
+// With 5 <= G <= 8 (GC = 2) lane (q, 8c + h) takes rows 4q + 2c + i (i = 0,
+// 1) of column h: lanes 8..15 fetch rows 2 and 3 from lane h by a row shift.
+__device__ __forceinline__ float compact2(const f4& v, int i) {
+  return dpp_into<0x118, 0xC>(i == 0 ? v[0] : v[1], i == 0 ? v[2] : v[3]);
+}
+
 template <int BK, int BV, int M, int GC>
 __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
-  static_assert(GC == 1 || GC == 4, "head compaction by 1 or 4");
+  static_assert(GC == 1 || GC == 2 || GC == 4, "head compaction by 1, 2 or 4");
   constexpr int KBT = 4 + M / 32;
   constexpr int RW = rec_words<BK, M>();
   constexpr int BW = 4 * BV * kD + kBlockTokens;
@@ -359,7 +365,8 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
     for (int kb = 0; kb < 4; ++kb) qb[kb] = to_pair_order(qb[kb]);
   }
   const int a4 = r16 >> 2;  // with GC = 4: this lane's row within a token quad
-  const float qsc = a.wqn[slot * 16 + (GC == 4 ? (r16 & 3) : r16)] * a.scale2;
+  const int c2 = r16 >> 3;  // with GC = 2: this lane's row pair within a token quad
+  const float qsc = a.wqn[slot * 16 + (r16 & (16 / GC - 1))] * a.scale2;
   const int sh0 = 15 - 8 * (q & 1);
   const int n_tok = (int)a.n_tokens;
   const int nblk = (n_tok + kBlockTokens - 1) / kBlockTokens;
@@ -454,6 +461,13 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
             vn[u][i] = v4[i];
             lg[u][i] = sc[u][i];
           }
+        } else if constexpr (GC == 2) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            nk[u][i] = nsh[wave][16 * u + 4 * q + 2 * c2 + i];
+            vn[u][i] = vsh[wave][16 * (2 * step + u) + 4 * q + 2 * c2 + i];
+            lg[u][i] = compact2(sc[u], i);
+          }
         } else {
           nk[u][0] = nsh[wave][16 * u + 4 * q + a4];
           vn[u][0] = vsh[wave][16 * (2 * step + u) + 4 * q + a4];
@@ -466,12 +480,15 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
           float l = lg[u][i] * nk[u][i] * qsc;
-          if constexpr (MASK) l = tok0 + 16 * (2 * step + u) + 4 * q + (GC == 4 ? a4 : i) < n_tok ? l : -INFINITY;
+          if constexpr (MASK)
+            l = tok0 + 16 * (2 * step + u) + 4 * q + (GC == 4 ? a4 : GC == 2 ? 2 * c2 + i : i) < n_tok ? l : -INFINITY;
           lg[u][i] = l;
           cmax = fmaxf(cmax, l);
         }
       if constexpr (GC == 4) {  // the four row lanes 4a + h of a head
         cmax = fmaxf(cmax, dpp_f<0x124>(cmax));
+        cmax = fmaxf(cmax, dpp_f<0x128>(cmax));
+      } else if constexpr (GC == 2) {  // the two row lanes h, h + 8 of a head
         cmax = fmaxf(cmax, dpp_f<0x128>(cmax));
       }
       cmax = max_xor16_32(cmax);
@@ -506,6 +523,23 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           pw[j] = VPT ? pack_h2(pv[0][j], pv[1][j]) : pack_h2(pv[j >> 1][2 * (j & 1)], pv[j >> 1][2 * (j & 1) + 1]);
+      } else if constexpr (GC == 2 && VPT) {  // rows 2, 3 of head h sit in lane h + 8
+        const uint32_t x0 = pack_h2(pv[0][0], pv[1][0]), x1 = pack_h2(pv[0][1], pv[1][1]);
+        pw[0] = x0;
+        pw[1] = x1;
+        pw[2] = dpp_into<0x108, 0xF>(0u, x0);
+        pw[3] = dpp_into<0x108, 0xF>(0u, x1);
+      } else if constexpr (GC == 2) {
+        float pr[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          pr[u][0] = pv[u][0];
+          pr[u][1] = pv[u][1];
+          pr[u][2] = dpp_into<0x108, 0xF>(0.f, pv[u][0]);
+          pr[u][3] = dpp_into<0x108, 0xF>(0.f, pv[u][1]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pw[j] = pack_h2(pr[j >> 1][2 * (j & 1)], pr[j >> 1][2 * (j & 1) + 1]);
       } else if constexpr (VPT) {
         const uint32_t x = pack_h2(pv[0][0], pv[1][0]);
         pw[0] = x;
@@ -553,6 +587,8 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   }
   if constexpr (GC == 4) {  // the four row lanes of a head
     l_run += dpp_f<0x124>(l_run);
+    l_run += dpp_f<0x128>(l_run);
+  } else if constexpr (GC == 2) {  // the two row lanes of a head
     l_run += dpp_f<0x128>(l_run);
   }
   l_run += shfl_xor(l_run, 16);
@@ -779,6 +815,7 @@ int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const
 #define TQ_AT(BK, BV, M)                                                                   \
   if (!launched && kbits == BK && vbits == BV && m == M) {                                 \
     if (s.G <= 4) hipLaunchKernelGGL((attend_kernel<BK, BV, M, 4>), grid, block, 0, st, a); \
+    else if (s.G <= 8) hipLaunchKernelGGL((attend_kernel<BK, BV, M, 2>), grid, block, 0, st, a); \
     else hipLaunchKernelGGL((attend_kernel<BK, BV, M, 1>), grid, block, 0, st, a);          \
     launched = true;                                                                       \
   }

@@ -100,7 +100,7 @@ def test_bits_and_proj_dim_fp16_ragged(kb, vb, m):
     _say(run_case(K, V, Q, kb=kb, vb=vb, m=m))
 
 
-@pytest.mark.parametrize("G", [1, 2, 4, 16])
+@pytest.mark.parametrize("G", [1, 2, 4, 5, 7, 8, 16])
 def test_query_group_sizes(G):
     d, T, n_seq = 128, 515, 2
     K = np.stack([synth.kv_slot(10, s, s, T, d) for s in range(n_seq)])
