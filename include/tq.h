@@ -28,7 +28,7 @@
  *    library allocates device memory only in tq_create (its own copies of R,
  *    S and the codebooks: d^2 + m d fp32 plus the same again as fp16 halves;
  *    for shapes on the general path, see below, also a scratch buffer of
- *    32768 rows x (4 d + 4 + d/32) bytes, 128 MB at d = 1024) and frees it
+ *    32768 rows x (4 d + 8 + d/32) bytes, 128 MB at d = 1024) and frees it
  *    in tq_destroy.
  *  - Calls that take a stream enqueue work on it and return at once; they
  *    are ordered with other work on that stream.  stream == NULL means the
@@ -44,7 +44,9 @@
  *    multiple of 128 up to 1024, proj_dim a multiple of 64 up to 512) runs
  *    the general path: tiled rotation / projection kernels for the appends,
  *    a chunked score kernel, and an attend that materialises the scores in
- *    the workspace and merges per-range softmax partials.
+ *    the workspace and merges per-range softmax partials.  0-bit keys are
+ *    appended by the single-kernel key path (fp16, proj_dim 64) or by one
+ *    workgroup per token, and scored and attended as above.
  *  - Device pointers must be 16-byte aligned.
  */
 #ifndef TQ_H
