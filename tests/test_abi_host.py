@@ -176,3 +176,16 @@ def test_hbm_stream_rejects_bad_arguments_before_any_device_call():
     assert lib.tq_hbm_stream(A, 8192, A, 2048, A, 68, None) == -1     # above 64
     assert lib.tq_hbm_stream(A, 8192, A, 2048, A, -4, None) == -1
     assert "tq_hbm_stream" in tq.last_error()
+
+
+def test_zero_bit_keys_take_the_single_kernel_workspace():
+    """0-bit keys at head_dim 128 attend on the single-kernel path: the same
+    workspace plan as any other key width (it depends on m, n_seq, G and the
+    token count only); at other head_dims they take the general plan."""
+    for m in (64, 128):
+        for G in (1, 4, 8, 16):
+            a = tq.workspace_bytes(tq.Config(128, m, 0, 3), 4, G, 5000)
+            b = tq.workspace_bytes(tq.Config(128, m, 3, 3), 4, G, 5000)
+            assert a == b > 0
+    assert tq.workspace_bytes(tq.Config(256, 128, 0, 3), 4, 8, 5000) == \
+        tq.workspace_bytes(tq.Config(256, 128, 2, 3), 4, 8, 5000) > 0
