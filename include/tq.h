@@ -59,7 +59,11 @@
 extern "C" {
 #endif
 
-#define TQ_LAYOUT_VERSION 1
+/* Version of the packed record layout described below.  Version 1 was the
+ * planned bit-plane layout (index bit p of 32 consecutive coordinates in one
+ * word); it was never built.  Version 2 is the matrix-core operand layout
+ * below, whose code groups decode straight into MFMA operands. */
+#define TQ_LAYOUT_VERSION 2
 
 typedef enum {
   TQ_OK = 0,
@@ -69,7 +73,7 @@ typedef enum {
   TQ_ENOMEM = -4,       /* device allocation failed (tq_create only) */
   TQ_EDEVICE = -5,      /* a HIP call or kernel launch failed */
   TQ_EUNSUPPORTED = -6, /* valid but not built (reserved; every valid shape is built) */
-  TQ_EWORKSPACE = -7    /* workspace smaller than tq_workspace_bytes */
+  TQ_EWORKSPACE = -7    /* workspace smaller than tq_attend_workspace_bytes / tq_workspace_bytes */
 } tq_status;
 
 typedef enum { TQ_F16 = 1, TQ_F32 = 2 } tq_dtype;
@@ -95,15 +99,15 @@ typedef struct {
  * sequence/layer), each holding up to `capacity` tokens (a multiple of 128,
  * at most 2^24).
  *
- * key_records: device, n_seq * capacity * tq_key_record_bytes() bytes.  Slot
- *   s, token t starts at byte (s * capacity + t) * tq_key_record_bytes().
- * value_blocks: device, n_seq * (capacity/128) * tq_value_block_bytes()
- *   bytes; block (s, t/128) starts at byte
- *   (s * capacity/128 + t/128) * tq_value_block_bytes().
+ * key_records: device, n_seq * capacity * tq_key_record_bytes(ctx) bytes.
+ *   Slot s, token t starts at byte (s * capacity + t) * tq_key_record_bytes(ctx).
+ * value_blocks: device, n_seq * capacity * tq_value_record_bytes(ctx) bytes
+ *   (= n_seq * (capacity/128) * tq_value_block_bytes(cfg)); block (s, t/128)
+ *   starts at byte (s * capacity/128 + t/128) * tq_value_block_bytes(cfg).
  * Zero-fill both buffers before first use if tokens will be read before
  * they are written.
  *
- * Record layout v1 (32-bit little-endian words; b = bits, d = head_dim):
+ * Record layout v2 (32-bit little-endian words; b = bits, d = head_dim):
  *  Code groups.  b consecutive words hold 32 b-bit codes as 8 slots s x 4
  *  byte lanes i; byte lane i of every word belongs to code (s, i):
  *    b=1: bit s;  b=2: word s/4, bits 2(s%4)..;  b=4: word s/2, bits 4(s%2)..;
@@ -143,19 +147,21 @@ typedef struct {
  * Returns TQ_EINVAL on bad arguments. */
 int tq_lloyd_max_codebook(int32_t head_dim, int32_t bits, double* centroids, double* boundaries);
 
-/* Bytes of one key record / one 128-token value block / a whole cache of
- * n_seq slots x capacity tokens, for a configuration.  0 if cfg is NULL or
- * invalid (the same checks as tq_create) or capacity is not a positive
- * multiple of 128. */
-size_t tq_key_record_bytes(const tq_config* cfg);
+/* Sizes for a configuration, usable before any context exists (to size the
+ * caller's buffers): bytes of one key record / one 128-token value block / a
+ * whole cache of n_seq slots x capacity tokens.  0 if cfg is NULL or invalid
+ * (the same checks as tq_create) or capacity is not a positive multiple of
+ * 128. */
+size_t tq_config_key_record_bytes(const tq_config* cfg);
 size_t tq_value_block_bytes(const tq_config* cfg);
 size_t tq_cache_key_bytes(const tq_config* cfg, int32_t n_seq, int64_t capacity);
 size_t tq_cache_value_bytes(const tq_config* cfg, int32_t n_seq, int64_t capacity);
 
-/* Device workspace bytes needed by tq_attention_scores and tq_attend for
- * this shape (query operands, query norms, per-wave attention partials).
- * 0 on invalid arguments (cfg NULL/invalid, n_seq < 1, G not in 1..512,
- * n_tokens < 1). */
+/* Device workspace bytes needed by tq_attention_scores, tq_attend and
+ * tq_decode_step for this shape (query operands, query norms, per-wave
+ * attention partials; on the general path also the materialised scores of
+ * tq_attend).  0 on invalid arguments (cfg NULL/invalid, n_seq < 1, G not in
+ * 1..512, n_tokens < 1). */
 size_t tq_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, int64_t n_tokens);
 
 /* Thread-local message describing the last failure of this thread. */
@@ -174,6 +180,24 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
 /* Free the context's device memory.  NULL is accepted.  Work still queued
  * that uses the context must have finished. */
 int tq_destroy(tq_ctx* ctx);
+
+/* Size queries of a context (the sizes behind TurboQuantKVCache's buffers,
+ * nav.superapi.store 核心 API).  Host-only; 0 if ctx is NULL or an argument
+ * is out of range.
+ *   tq_key_record_bytes:   one token's key record, 4 (b d/32 + m/32 + 2)
+ *                          bytes (b = key_bits).
+ *   tq_value_record_bytes: one token's share of a 128-token value block,
+ *                          4 (b d/32 + 1) bytes (b = value_bits): the block
+ *                          is 128 times this.
+ *   tq_attend_workspace_bytes: the workspace tq_attention_scores, tq_attend
+ *                          and tq_decode_step need for n_seq slots, G query
+ *                          heads per slot and n_tokens attended tokens; the
+ *                          same value as tq_workspace_bytes for the
+ *                          context's configuration (n_seq >= 1, 1 <= G <= 512,
+ *                          n_tokens >= 1). */
+size_t tq_key_record_bytes(const tq_ctx* ctx);
+size_t tq_value_record_bytes(const tq_ctx* ctx);
+size_t tq_attend_workspace_bytes(const tq_ctx* ctx, int32_t n_seq, int32_t G, int64_t n_tokens);
 
 /* Load the codebook for `bits` (host arrays, copied): 2^bits strictly
  * ascending finite centroids and 2^bits - 1 strictly ascending finite
@@ -215,7 +239,12 @@ int tq_append_value(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int3
  * of G contiguous heads), dtype TQ_F16 or TQ_F32.  1 <= G <= 512 (a
  * vector-search batch of queries against one slot is G queries, n_seq = 1).
  * scores: device fp32 [n_seq][G][n_tokens].
- * workspace: device, >= tq_workspace_bytes(ctx, n_seq, G, n_tokens).
+ * workspace: device, >= tq_attend_workspace_bytes(ctx, n_seq, G, n_tokens).
+ * The call takes a workspace because each query is rotated and projected
+ * once per call (q~ = R q, p = S q~, as split-fp16 matrix-core operands) into
+ * device memory that the score kernel then streams the keys against; the
+ * library allocates no device memory after tq_create, so that memory is the
+ * caller's.
  * Errors: TQ_EINVAL (n_tokens <= 0 or > capacity, G out of range, ...),
  * TQ_ENOCODEBOOK, TQ_EWORKSPACE, TQ_EDEVICE. */
 int tq_attention_scores(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype,

@@ -89,7 +89,7 @@ extern "C" {
 
 const char* tq_last_error(void) { return g_err; }
 
-size_t tq_key_record_bytes(const tq_config* cfg) {
+size_t tq_config_key_record_bytes(const tq_config* cfg) {
   if (check_config(cfg) == TQ_EINVAL) return 0;
   return key_rec_bytes(*cfg);
 }
@@ -114,6 +114,14 @@ size_t tq_workspace_bytes(const tq_config* cfg, int32_t n_seq, int32_t G, int64_
   if (fast_attn(*cfg, G)) return plan_attention(cfg->proj_dim, n_seq, G, n_tokens).total;
   if (G <= 16) return general_attend_plan(cfg->head_dim, cfg->proj_dim, n_seq, G, n_tokens).total;
   return general_scores_workspace(cfg->head_dim, cfg->proj_dim, n_seq, G);
+}
+
+size_t tq_key_record_bytes(const tq_ctx* ctx) { return ctx ? key_rec_bytes(ctx->cfg) : 0; }
+
+size_t tq_value_record_bytes(const tq_ctx* ctx) { return ctx ? val_blk_bytes(ctx->cfg) / kBlockTokens : 0; }
+
+size_t tq_attend_workspace_bytes(const tq_ctx* ctx, int32_t n_seq, int32_t G, int64_t n_tokens) {
+  return ctx ? tq_workspace_bytes(&ctx->cfg, n_seq, G, n_tokens) : 0;
 }
 
 int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** out) {

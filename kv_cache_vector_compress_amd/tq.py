@@ -60,7 +60,10 @@ def lib() -> ctypes.CDLL:
     VIEW = ctypes.POINTER(CacheView)
     sig = {
         "tq_lloyd_max_codebook": (ctypes.c_int, [I32, I32, D, D]),
-        "tq_key_record_bytes": (SZ, [CFG]),
+        "tq_config_key_record_bytes": (SZ, [CFG]),
+        "tq_key_record_bytes": (SZ, [P]),
+        "tq_value_record_bytes": (SZ, [P]),
+        "tq_attend_workspace_bytes": (SZ, [P, I32, I32, I64]),
         "tq_value_block_bytes": (SZ, [CFG]),
         "tq_cache_key_bytes": (SZ, [CFG, I32, I64]),
         "tq_cache_value_bytes": (SZ, [CFG, I32, I64]),
@@ -114,7 +117,7 @@ def lloyd_max_codebook(head_dim: int, bits: int) -> tuple[np.ndarray, np.ndarray
 
 
 def key_record_bytes(cfg: Config) -> int:
-    return lib().tq_key_record_bytes(ctypes.byref(cfg))
+    return lib().tq_config_key_record_bytes(ctypes.byref(cfg))
 
 
 def value_block_bytes(cfg: Config) -> int:
@@ -185,6 +188,18 @@ class Context:
     def handle(self):
         return self._h
 
+    def key_record_bytes(self) -> int:
+        """tq_key_record_bytes: bytes of one token's key record."""
+        return lib().tq_key_record_bytes(self._h)
+
+    def value_record_bytes(self) -> int:
+        """tq_value_record_bytes: one token's share of a 128-token value block."""
+        return lib().tq_value_record_bytes(self._h)
+
+    def attend_workspace_bytes(self, n_seq: int, G: int, n_tokens: int) -> int:
+        """tq_attend_workspace_bytes: workspace of the score / attend calls."""
+        return lib().tq_attend_workspace_bytes(self._h, n_seq, G, n_tokens)
+
     def codebook_load(self, bits: int, centroids: Optional[np.ndarray] = None,
                       boundaries: Optional[np.ndarray] = None) -> None:
         """Load a codebook; by default the library's own Lloyd-Max codebook."""
@@ -223,34 +238,61 @@ class KVCache:
         self.key_records = torch.zeros(kb // 4, dtype=torch.int32, device=device)
         self.value_blocks = torch.zeros(vb // 4, dtype=torch.int32, device=device)
         self.view = CacheView(self.key_records.data_ptr(), self.value_blocks.data_ptr(), capacity, n_seq)
-        self._ws = None
+        self._ws = {}  # one workspace per stream: calls on different streams never share one
 
-    def workspace(self, G: int, n_tokens: int):
+    def workspace(self, G: int, n_tokens: int, stream=None):
+        """The attention workspace of the given stream (torch's current
+        stream by default), grown to tq_attend_workspace_bytes."""
         torch = _torch()
-        need = workspace_bytes(self.ctx.cfg, self.n_seq, G, n_tokens)
+        need = self.ctx.attend_workspace_bytes(self.n_seq, G, n_tokens)
         if need == 0:
-            raise TQError(-1, last_error())
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self.key_records.device)
-        return self._ws
+            raise TQError(-1, f"tq_attend_workspace_bytes: invalid arguments (n_seq {self.n_seq}, G {G}, "
+                              f"n_tokens {n_tokens})")
+        key = _stream_ptr(stream).value
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < need:
+            ws = self._ws[key] = torch.empty(need, dtype=torch.uint8, device=self.key_records.device)
+        return ws
+
+    # shape checks: the C ABI receives raw pointers and cannot see tensor
+    # sizes, so every tensor is checked here against the cache's shape
+    def _rows(self, t, name: str) -> int:
+        """t must be (n_seq, n, head_dim) on the cache's device; returns n."""
+        if t.dim() != 3 or t.shape[0] != self.n_seq or t.shape[2] != self.ctx.cfg.head_dim:
+            raise ValueError(f"{name} must have shape (n_seq={self.n_seq}, n, head_dim={self.ctx.cfg.head_dim}), "
+                             f"got {tuple(t.shape)}")
+        if t.device != self.key_records.device:
+            raise ValueError(f"{name} is on {t.device}, the cache on {self.key_records.device}")
+        return int(t.shape[1])
+
+    def _out(self, out, shape, name: str):
+        torch = _torch()
+        if out is None:
+            return torch.empty(shape, dtype=torch.float32, device=self.key_records.device)
+        if out.dtype != torch.float32 or tuple(out.shape) != tuple(shape) or not out.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}, "
+                             f"got {out.dtype} {tuple(out.shape)}")
+        if out.device != self.key_records.device:
+            raise ValueError(f"{name} is on {out.device}, the cache on {self.key_records.device}")
+        return out
 
     # hot path ---------------------------------------------------------------
     def append_key(self, k, pos: int, stream=None) -> None:
         """k: (n_seq, n_new, d) fp16/fp32 device tensor."""
+        n_new = self._rows(k, "k")
         _check(lib().tq_append_key(self.ctx.handle, ctypes.byref(self.view), _dev(k, "k"), _dtype_code(k),
-                                   pos, k.shape[1], _stream_ptr(stream)))
+                                   pos, n_new, _stream_ptr(stream)))
 
     def append_value(self, v, pos: int, stream=None) -> None:
+        n_new = self._rows(v, "v")
         _check(lib().tq_append_value(self.ctx.handle, ctypes.byref(self.view), _dev(v, "v"), _dtype_code(v),
-                                     pos, v.shape[1], _stream_ptr(stream)))
+                                     pos, n_new, _stream_ptr(stream)))
 
     def attention_scores(self, q, n_tokens: int, out=None, stream=None):
         """q: (n_seq, G, d).  Returns fp32 (n_seq, G, n_tokens) unscaled estimates."""
-        torch = _torch()
-        G = q.shape[1]
-        if out is None:
-            out = torch.empty((self.n_seq, G, n_tokens), dtype=torch.float32, device=q.device)
-        ws = self.workspace(G, n_tokens)
+        G = self._rows(q, "q")
+        out = self._out(out, (self.n_seq, G, n_tokens), "scores")
+        ws = self.workspace(G, n_tokens, stream)
         _check(lib().tq_attention_scores(self.ctx.handle, ctypes.byref(self.view), _dev(q, "q"), _dtype_code(q),
                                          G, n_tokens, _dev(out, "scores"), ctypes.c_void_p(ws.data_ptr()),
                                          ws.numel(), _stream_ptr(stream)))
@@ -258,11 +300,9 @@ class KVCache:
 
     def attend(self, q, n_tokens: int, scale: float = 0.0, out=None, stream=None):
         """softmax(scale * est) . V^ over the first n_tokens; fp32 (n_seq, G, d)."""
-        torch = _torch()
-        G = q.shape[1]
-        if out is None:
-            out = torch.empty((self.n_seq, G, self.ctx.cfg.head_dim), dtype=torch.float32, device=q.device)
-        ws = self.workspace(G, n_tokens)
+        G = self._rows(q, "q")
+        out = self._out(out, (self.n_seq, G, self.ctx.cfg.head_dim), "out")
+        ws = self.workspace(G, n_tokens, stream)
         _check(lib().tq_attend(self.ctx.handle, ctypes.byref(self.view), _dev(q, "q"), _dtype_code(q), G,
                                n_tokens, float(scale), _dev(out, "out"), ctypes.c_void_p(ws.data_ptr()),
                                ws.numel(), _stream_ptr(stream)))
@@ -271,13 +311,15 @@ class KVCache:
     def decode_step(self, k, v, q, pos: int, scale: float = 0.0, out=None, stream=None):
         """Append k, v (n_seq, n_new, d) at token pos and attend with q over the
         first pos + n_new tokens (tq_decode_step); fp32 (n_seq, G, d)."""
-        torch = _torch()
         if k.dtype != v.dtype or k.dtype != q.dtype:
             raise TypeError("k, v and q must share one dtype")
-        n_new, G = k.shape[1], q.shape[1]
-        if out is None:
-            out = torch.empty((self.n_seq, G, self.ctx.cfg.head_dim), dtype=torch.float32, device=q.device)
-        ws = self.workspace(G, pos + n_new)
+        n_new = self._rows(k, "k")
+        if tuple(v.shape) != tuple(k.shape):
+            raise ValueError(f"v must have the shape of k {tuple(k.shape)}, got {tuple(v.shape)}")
+        self._rows(v, "v")
+        G = self._rows(q, "q")
+        out = self._out(out, (self.n_seq, G, self.ctx.cfg.head_dim), "out")
+        ws = self.workspace(G, pos + n_new, stream)
         _check(lib().tq_decode_step(self.ctx.handle, ctypes.byref(self.view), _dev(k, "k"), _dev(v, "v"),
                                     _dtype_code(k), pos, n_new, _dev(q, "q"), G, float(scale), _dev(out, "out"),
                                     ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
@@ -287,7 +329,7 @@ class KVCache:
         """The k best tokens per query by the score estimate (no score matrix):
         (scores fp32 (n_seq, G, k), indices int32 (n_seq, G, k))."""
         torch = _torch()
-        G = q.shape[1]
+        G = self._rows(q, "q")
         need = lib().tq_topk_workspace_bytes(ctypes.byref(self.ctx.cfg), self.n_seq, G, n_tokens, k)
         if need == 0:
             raise TQError(-1, "tq_topk_workspace_bytes: invalid arguments")
@@ -309,10 +351,7 @@ class KVCache:
         return self._get(lib().tq_get_keys, pos, n_tokens, out, stream)
 
     def _get(self, fn, pos, n_tokens, out, stream):
-        torch = _torch()
-        if out is None:
-            out = torch.empty((self.n_seq, n_tokens, self.ctx.cfg.head_dim), dtype=torch.float32,
-                              device=self.key_records.device)
+        out = self._out(out, (self.n_seq, n_tokens, self.ctx.cfg.head_dim), "out")
         _check(fn(self.ctx.handle, ctypes.byref(self.view), pos, n_tokens,
                   _dev(out, "out") if n_tokens > 0 else None, _stream_ptr(stream)))
         return out

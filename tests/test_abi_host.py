@@ -157,9 +157,19 @@ def test_topk_workspace_rejects_bad_arguments():
         assert ws(*bad) == 0, bad
 
 
+def _hip_device_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0   # counts devices without initialising one
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_hip_device_visible(), reason="made-up device addresses: run only where no GPU is visible")
 def test_hbm_stream_rejects_bad_arguments_before_any_device_call():
     """tq_hbm_stream checks pointers, alignment and sizes on the host (fake
-    addresses: an accepted call would fault, so only rejected ones are made)."""
+    addresses: an accepted call would fault, so only rejected ones are made,
+    and only on a host without a GPU)."""
     lib = tq.lib()
     A = ctypes.c_void_p(1 << 40)       # aligned, never dereferenced
     U = ctypes.c_void_p((1 << 40) + 4)  # misaligned
@@ -189,3 +199,26 @@ def test_zero_bit_keys_take_the_single_kernel_workspace():
             assert a == b > 0
     assert tq.workspace_bytes(tq.Config(256, 128, 0, 3), 4, 8, 5000) == \
         tq.workspace_bytes(tq.Config(256, 128, 2, 3), 4, 8, 5000) > 0
+
+
+def test_context_size_queries_reject_null_context():
+    """The size queries of a context (tq_key_record_bytes,
+    tq_value_record_bytes, tq_attend_workspace_bytes) return 0 for NULL;
+    their values for a live context are checked on the GPU."""
+    lib = tq.lib()
+    assert lib.tq_key_record_bytes(None) == 0
+    assert lib.tq_value_record_bytes(None) == 0
+    assert lib.tq_attend_workspace_bytes(None, 4, 4, 1000) == 0
+
+
+@pytest.mark.parametrize("d,m,kb,vb", [(128, 64, 3, 3), (128, 128, 0, 2), (1024, 512, 4, 4), (256, 128, 2, 1)])
+def test_value_record_is_the_per_token_share_of_a_block(d, m, kb, vb):
+    """4 (b d/32 + 1) bytes per token: the block of 128 tokens holds b d/32
+    code words and one fp32 norm per token."""
+    cfg = tq.Config(d, m, kb, vb)
+    assert tq.value_block_bytes(cfg) == 128 * 4 * (vb * d // 32 + 1)
+
+
+def test_layout_version_is_2():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    assert re.search(r"#define\s+TQ_LAYOUT_VERSION\s+2\b", src)

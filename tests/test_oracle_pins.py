@@ -502,3 +502,36 @@ def test_attention_fidelity_metric():
     assert top1.all()
     cos2, _ = O.attention_fidelity(Q, K, est + rng.standard_normal(est.shape))
     assert np.all(cos2 < 1.0)
+
+
+def test_attention_fidelity_hand_computed_two_tokens():
+    """O9 on a case worked by hand.  True logits (0, ln 3) give the softmax
+    (1/4, 3/4); estimated logits (ln 3, 0) give (3/4, 1/4).  Their cosine is
+    (3/16 + 3/16) / (1/16 + 9/16) = 3/5 exactly, and the argmaxes differ.
+    (A cosine taken over the logits themselves would give 0.)"""
+    Q = np.array([[[1.0, 0.0]]])                      # (seq 1, head 1, d 2)
+    K = np.array([[[0.0, 0.0], [math.log(3.0), 0.0]]])  # q.k = (0, ln 3)
+    est = np.array([[[math.log(3.0), 0.0]]])
+    cos, top1 = O.attention_fidelity(Q, K, est, scale=1.0)
+    assert cos.shape == (1, 1) and top1.shape == (1, 1)
+    assert abs(float(cos[0, 0]) - 0.6) < 1e-15
+    assert not bool(top1[0, 0])
+    # the default scale is 1/sqrt(d): the same case with q and est scaled by sqrt(2)
+    cos_d, top1_d = O.attention_fidelity(Q * math.sqrt(2.0), K, est * math.sqrt(2.0))
+    assert abs(float(cos_d[0, 0]) - 0.6) < 1e-14 and not bool(top1_d[0, 0])
+
+
+def test_attention_fidelity_hand_computed_per_head_axis():
+    """O9 with two query heads and three tokens, worked by hand, so a softmax
+    over the head axis (or over the wrong one of two axes) fails.
+    Head 0: true logits (0, ln 3, 0) -> (1/5, 3/5, 1/5); its estimate is
+    exact, so cosine 1 and top-1 agree.  Head 1: true logits (0, 0, ln 3) ->
+    (1/5, 1/5, 3/5), estimate (ln 3, 0, 0) -> (3/5, 1/5, 1/5); cosine
+    (3 + 1 + 3) / (9 + 1 + 1) = 7/11, top-1 differs."""
+    L3 = math.log(3.0)
+    Q = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    K = np.array([[[0.0, 0.0], [L3, 0.0], [0.0, L3]]])
+    est = np.array([[[0.0, L3, 0.0], [L3, 0.0, 0.0]]])
+    cos, top1 = O.attention_fidelity(Q, K, est, scale=1.0)
+    np.testing.assert_allclose(cos[0], [1.0, 7.0 / 11.0], rtol=0, atol=1e-15)
+    assert top1[0].tolist() == [True, False]
