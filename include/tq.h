@@ -262,6 +262,21 @@ int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dt
               int64_t n_tokens, float scale, float* out, void* workspace, size_t workspace_bytes,
               void* stream);
 
+/* tq_attend without the workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same results as tq_attend with the
+ * same arguments.  The workspace is a static device array of 32 MiB that
+ * the library holds on each GPU it runs on until the process ends (its
+ * address is looked up when a context is created on that device); shapes
+ * whose tq_attend_workspace_bytes exceeds 32 MiB are rejected with
+ * TQ_EWORKSPACE before anything is launched.  Nothing is allocated.  Every
+ * call on one GPU shares that array, so calls that overlap on one GPU (on
+ * different streams, or from several threads or contexts) race; serialise
+ * them.  Errors as tq_attend, plus TQ_EWORKSPACE for a shape too large and
+ * TQ_EDEVICE if the scratch address is unknown for ctx's device. */
+int tq_attend_noalloc(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
+                      int64_t n_tokens, float scale, float* out, void* stream);
+
 /* One decode step: append n_new tokens' keys and values at token slots
  * [pos, pos + n_new) of every slot, then attend with q over the whole cache
  * [0, pos + n_new) -- the same results as tq_append_key, tq_append_value and

@@ -184,6 +184,11 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
     delete c;
     return fail(TQ_EDEVICE, "tq_create: hipGetDevice failed");
   }
+  // set-up of tq_attend_noalloc's scratch on this device (once per device)
+  if (noalloc_scratch_init(c->device) != 0) {
+    delete c;
+    return fail(TQ_EDEVICE, "tq_create: device address of the no-allocation scratch not found");
+  }
   const size_t b_rimg = r_img * 2, b_simg = s_img * 2;
   const size_t off_rl = b_rimg, off_sh = 2 * b_rimg, off_sl = off_sh + b_simg, off_sh32 = off_sl + b_simg;
   const size_t off_sl32 = off_sh32 + b_simg, off_r32 = off_sl32 + b_simg;
@@ -433,6 +438,20 @@ int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dt
                                workspace, stream);
   }
   return rc ? fail(rc, "tq_attend: launch failed (%d)", rc) : TQ_OK;
+}
+
+int tq_attend_noalloc(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,
+                      int64_t n_tokens, float scale, float* out, void* stream) {
+  clear_error();
+  const char* fn = "tq_attend_noalloc";
+  if (!ctx) return fail(TQ_EINVAL, "%s: ctx is NULL", fn);
+  void* ws = noalloc_scratch_ptr(ctx->device);
+  if (!ws) return fail(TQ_EDEVICE, "%s: no scratch address for device %d", fn, ctx->device);
+  // the checks of tq_attend, against the scratch's fixed size
+  AttnPlan plan;
+  int rc = attn_common(ctx, cache, q, dtype, G, n_tokens, out, ws, kNoAllocScratchBytes, true, fn, &plan);
+  if (rc) return rc;
+  return tq_attend(ctx, cache, q, dtype, G, n_tokens, scale, out, ws, kNoAllocScratchBytes, stream);
 }
 
 int tq_decode_step(tq_ctx* ctx, const tq_cache_view* cache, const void* k, const void* v, int32_t dtype,

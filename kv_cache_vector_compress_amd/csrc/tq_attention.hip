@@ -18,6 +18,7 @@
 // the rotated domain with the matrix cores.  A second kernel merges the
 // per-wave partials (log-sum-exp) and applies R^T once per query head.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "tq_device.h"
@@ -693,6 +694,41 @@ __global__ __launch_bounds__(512) void combine_kernel(const CombineArgs a) {
 // ---------------------------------------------------------------------------
 
 static int g_cus = 256;
+
+// Scratch of tq_attend_noalloc, for callers that cannot allocate device
+// memory: a file-scope device array (each GPU the library runs on holds its
+// own copy until the process ends) standing in for the attend workspace.
+// In host code `scratch` is only a host-side stand-in for the symbol; its
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current and kept per device.  Every call on one GPU
+// shares the array, so calls that overlap on one GPU race.  Nothing in it
+// needs clearing between calls: the query preparation writes the operands
+// and norms, and the attend kernel writes every partial the combine reads.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int noalloc_scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return TQ_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return 0;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != device) return TQ_EDEVICE;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TQ_EDEVICE;
+  g_scratch_ptr[device] = ptr;
+  return 0;
+}
+
+void* noalloc_scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 int attention_device_init() {
   int dev = 0;

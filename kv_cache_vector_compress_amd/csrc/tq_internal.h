@@ -138,6 +138,14 @@ int launch_decode_prep(const Matrices& mats, const CodebookDev& cbk, int kbits, 
 // Where the single-kernel attend keeps its query operands in the workspace.
 void attend_query_buffers(void* ws, const AttnPlan& p, uint16_t** wq, float** wqn);
 
+// Device scratch of tq_attend_noalloc (tq_attention.hip): a static device
+// array of kNoAllocScratchBytes per GPU.  noalloc_scratch_init looks up its
+// address on `device` (which must be current) once; noalloc_scratch_ptr
+// returns it (nullptr before the look-up).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+int noalloc_scratch_init(int device);
+void* noalloc_scratch_ptr(int device);
+
 // HBM stream for measuring the memory ceiling (tq_stream.hip).
 int stream_device_init();
 int launch_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,

@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         "tq_get_values": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
         "tq_get_keys": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
         "tq_hbm_stream": (ctypes.c_int, [P, SZ, P, SZ, P, I32, P]),
+        "tq_attend_noalloc": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, ctypes.c_float, P, P]),
         "tq_decode_step": (ctypes.c_int, [P, VIEW, P, P, I32, I64, I64, P, I32, ctypes.c_float, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -306,6 +307,17 @@ class KVCache:
         _check(lib().tq_attend(self.ctx.handle, ctypes.byref(self.view), _dev(q, "q"), _dtype_code(q), G,
                                n_tokens, float(scale), _dev(out, "out"), ctypes.c_void_p(ws.data_ptr()),
                                ws.numel(), _stream_ptr(stream)))
+        return out
+
+    def attend_noalloc(self, q, n_tokens: int, scale: float = 0.0, out=None, stream=None):
+        """tq_attend_noalloc: attend with the library's static device scratch
+        instead of a workspace (no device allocation by the library; pass
+        `out` to allocate nothing here either).  Calls on one GPU must not
+        overlap."""
+        G = self._rows(q, "q")
+        out = self._out(out, (self.n_seq, G, self.ctx.cfg.head_dim), "out")
+        _check(lib().tq_attend_noalloc(self.ctx.handle, ctypes.byref(self.view), _dev(q, "q"), _dtype_code(q), G,
+                                       n_tokens, float(scale), _dev(out, "out"), _stream_ptr(stream)))
         return out
 
     def decode_step(self, k, v, q, pos: int, scale: float = 0.0, out=None, stream=None):
