@@ -94,15 +94,33 @@ def counter_traffic(kernel: str):
     return int(k["fetch_bytes"] + k["write_bytes"])
 
 
+def host_threads():
+    """Host cores this process may run on, and the BLAS numpy calls (the
+    oracle's matrix products run there; its element-wise steps run on one
+    thread)."""
+    info = {"affinity_cores": len(os.sched_getaffinity(0)), "blas_vendor": None, "blas_threads": None}
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas_vendor"] = "/".join(sorted({str(i.get("internal_api")) for i in blas}))
+            info["blas_threads"] = max(int(i.get("num_threads", 1)) for i in blas)
+    except Exception:
+        pass
+    return info
+
+
+def _cpu_line(value, unit, sample, dt):
+    h = host_threads()
+    return {"value": value, "unit": unit, "cores": int(h["blas_threads"] or 1), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2), "affinity_cores": h["affinity_cores"],
+            "blas": {"vendor": h["blas_vendor"], "threads": h["blas_threads"]}}
+
+
 def cpu_baseline(w, slots=16):
     """The fp64 oracle, untuned, on a bounded sample of the same workload."""
     from oracle import turboquant as O
     from kv_cache_vector_compress_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
     d, m, T, G = w["d"], w["m"], w["n_tok"], w["G"]
     R = synth.haar_rotation(d, synth.SEED_R)
     S = synth.gaussian_projection(m, d, synth.SEED_S)
@@ -115,9 +133,26 @@ def cpu_baseline(w, slots=16):
     O.key_scores(Q, R, S, kc, keys)
     O.attend(Q, R, S, kc, keys, vals, value_centroids=vc)
     dt = time.perf_counter() - t0
-    return {"value": slots * T / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"slots 0-{slots - 1} of {w['n_seq']} ({slots}x{T} tokens, G={G}): compress K and V, "
-                      f"scores and attend, numpy fp64; {dt:.1f} s"}
+    return _cpu_line(slots * T / dt, "keys/s",
+                     f"slots 0-{slots - 1} of {w['n_seq']} ({slots}x{T} tokens, G={G}): compress K and V, "
+                     f"scores and attend, numpy fp64; {dt:.1f} s", dt)
+
+
+def cpu_baseline_qwen(K, V, Q, R, S, bits=3):
+    """The oracle over a whole decode-shaped cache (all slots and tokens):
+    compress K and V, scores and attend of every query head; per-token rate."""
+    from oracle import turboquant as O
+    d = K.shape[-1]
+    beta, c = O.lloyd_max_codebook(d, bits)
+    t0 = time.perf_counter()
+    keys = O.compress_keys(K, R, S, beta, c)
+    vals = O.compress_values(V, R, beta, c)
+    O.key_scores(Q, R, S, c, keys)
+    O.attend(Q, R, S, c, keys, vals, value_centroids=c)
+    dt = time.perf_counter() - t0
+    n = K.shape[0] * K.shape[1]
+    return _cpu_line(n / dt, "tokens/s", f"the whole cache ({K.shape[0]}x{K.shape[1]} tokens, "
+                     f"G={Q.shape[1]}): compress K and V, scores and attend, numpy fp64; {dt:.1f} s", dt)
 
 
 def _timed(torch, fn, reps):
@@ -152,9 +187,9 @@ def bench_qwen_decode(args):
     dev = torch.device("cuda:0")
     R, S = synth.haar_rotation(d), synth.gaussian_projection(m, d)
     ctx = tq.Context(d, m, 3, 3, R, S)
-    K = _kv_device(torch, n_seq, T, d, synth.SEED_K, n_seq, dev)
-    V = _kv_device(torch, n_seq, T, d, synth.SEED_V, n_seq, dev)
-    Q = torch.from_numpy(synth.workload_queries(w)).to(dev)
+    Kh, Vh, Qh = gen_inputs(n_seq, T, d, G, n_seq)
+    Qh = synth.workload_queries(w)
+    K, V, Q = torch.from_numpy(Kh).to(dev), torch.from_numpy(Vh).to(dev), torch.from_numpy(Qh).to(dev)
     copies = 8
     caches = [tq.KVCache(ctx, n_seq, T) for _ in range(copies)]
     for c in caches:
@@ -254,6 +289,9 @@ def bench_qwen_decode(args):
                            "attend_cold": {"ms": round(cold_a, 4), "GBps": gb(b_at, cold_a)},
                            "alg_bytes": {"scores": int(b_sc), "attend": int(b_at)},
                            "cold_copies": copies, "hbm_peak_GBps": HBM_PEAK_GBPS}}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_qwen(Kh, Vh, Qh, R, S)
     print(json.dumps(line))
     ctx.close()
 
@@ -274,9 +312,9 @@ def bench_bit_sweep(args):
     d, m, T, G, n_seq = w.d, w.m, w.n_tok, w.G, w.n_seq
     dev = torch.device("cuda:0")
     R, S = synth.haar_rotation(d), synth.gaussian_projection(m, d)
-    K = _kv_device(torch, n_seq, T, d, synth.SEED_K, n_seq, dev)
-    V = _kv_device(torch, n_seq, T, d, synth.SEED_V, n_seq, dev)
-    Q = torch.from_numpy(synth.workload_queries(w)).to(dev)
+    Kh, Vh, _ = gen_inputs(n_seq, T, d, G, n_seq)
+    Qh = synth.workload_queries(w)
+    K, V, Q = torch.from_numpy(Kh).to(dev), torch.from_numpy(Vh).to(dev), torch.from_numpy(Qh).to(dev)
     exact = torch.matmul(Q.float(), K.float().transpose(1, 2).contiguous())   # (n_seq, G, T)
     scale = 1.0 / d ** 0.5
     rescale = 2.0 / float((exact * scale).std())
@@ -313,6 +351,9 @@ def bench_bit_sweep(args):
                           "scores_ms": round(ts, 4), "scores_GBps": round(b_sc / (ts * 1e-3) / 1e9, 1),
                           "fidelity": fid}
         ctx.close()
+        if not args.no_cpu_baseline and kb == b:
+            print(f"[bench] cpu baseline (oracle) {b} bits", file=sys.stderr, flush=True)
+            res[f"{b}bit"]["cpu_baseline"] = cpu_baseline_qwen(Kh, Vh, Qh, R, S, bits=b)
     line = {"metric": "bit-width sweep: compress keys/s, score GB/s, attention cosine and top-1 vs fp16",
             "value": res["3bit"]["compress_keys_per_s"], "unit": "keys/s (3-bit)", "higher_is_better": True,
             "n_gpus": 1, "data": "synthetic", "dtype": "f16",
@@ -368,6 +409,19 @@ def bench_vector_search(args):
             "scores_alg_TFLOPs": round(N * G * 2 * (d + m) / (ts * 1e-3) / 1e12, 1),
             "topk10_alg_TFLOPs": round(N * G * 2 * (d + m) / (tk * 1e-3) / 1e12, 1),
             "recall_at_10": round(float(np.mean(rec)), 4)}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        from oracle import turboquant as O
+        n_cpu = 131072
+        Xs = X[0, :n_cpu].cpu().numpy()[None]
+        Qs = Q.cpu().numpy()
+        beta, c = O.lloyd_max_codebook(d, b)
+        t0 = time.perf_counter()
+        keys = O.compress_keys(Xs, R, S, beta, c)
+        O.key_scores(Qs, R, S, c, keys)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = _cpu_line(n_cpu / dt, "vectors/s", f"slice: the first {n_cpu} of {N} vectors, all "
+                                         f"{G} queries: compress and scores, numpy fp64; {dt:.1f} s", dt)
     print(json.dumps(line))
     ctx.close()
 
@@ -466,7 +520,19 @@ def main():
     stage_info["compress_keys"]["keys_per_s"] = units / (stage_ms["compress_keys"] * 1e-3)
     stage_info["compress_values"]["values_per_s"] = units / (stage_ms["compress_values"] * 1e-3)
     # matrix-core work of compress (algorithmic: 2(d^2 + m d) flops per key, 2 d^2 per value)
-    stage_info["compress_keys"]["alg_TFLOPs"] = round(units * 2 * (d * d + m * d) / (stage_ms["compress_keys"] * 1e-3) / 1e12, 1)
+    # Matrix-core work of compress against the fp16 MFMA peak: algorithmic
+    # flops (2(d^2 + m d) per key, 2 d^2 per value) and the flops the split-
+    # fp16 arithmetic executes (rotation R_hi k + R_lo k: 2 x 2 d^2; projection
+    # S_hi r_hi + S_lo r_hi + S_hi r_lo: 3 x 2 m d; values 2 x 2 d^2).
+    for s_, alg_f, exe_f in (("compress_keys", 2 * (d * d + m * d), 2 * 2 * d * d + 3 * 2 * m * d),
+                             ("compress_values", 2 * d * d, 2 * 2 * d * d)):
+        sec = stage_ms[s_] * 1e-3
+        stage_info[s_]["mfma"] = {
+            "alg_TFLOPs": round(units * alg_f / sec / 1e12, 1),
+            "executed_TFLOPs": round(units * exe_f / sec / 1e12, 1),
+            "peak_TFLOPs": FP16_MFMA_PEAK_TFLOPS,
+            "alg_frac": round(units * alg_f / sec / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
+            "executed_frac": round(units * exe_f / sec / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4)}
     dom = max(stages, key=lambda s: stage_ms[s])
     roof = {"bound": "hbm", "kernel": dom, "achieved": stage_info[dom]["GBps"], "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": stage_info[dom]["frac_hbm_peak"], "traffic": counter_traffic(dom),

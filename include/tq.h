@@ -285,11 +285,18 @@ int tq_attend_noalloc(tq_ctx* ctx, const tq_cache_view* cache, const void* q, in
  * attention over the compressed cache).  k, v: device [n_seq][n_new][d]; q:
  * device [n_seq][G][d]; all three of type dtype.  scale, out, workspace as
  * for tq_attend with n_tokens = pos + n_new (workspace >=
- * tq_workspace_bytes(cfg, n_seq, G, pos + n_new)).  On the single-kernel
- * shapes (head_dim 128, proj_dim 64 or 128, G <= 16) with n_new <= 16 the
- * appends and the query preparation run as one launch, followed by the
- * attention's own two; otherwise the three calls run in order.  Every
- * argument is checked before anything is launched.  Errors: TQ_EINVAL
+ * tq_attend_workspace_bytes(ctx, n_seq, G, pos + n_new)).  On the
+ * single-kernel shapes (head_dim 128, proj_dim 64 or 128, G <= 16) with
+ * n_new <= 16 (and at most 4096 attention partials per slot, waves per slot
+ * / 4 + 2 times G) the whole step is one kernel launch: appends, query
+ * preparation, attention and the final merge, its workgroups synchronised
+ * through flags and a count in the workspace (each tagged with a value
+ * unique to the launch, so the workspace needs no clearing; a replayed
+ * graph of the call works too).  A wait inside that launch is bounded: in
+ * the pathological case of inputs that never become ready (about a second)
+ * the output is NaN and a status word in the workspace is set.  Otherwise
+ * the three calls run in order.  Calls that overlap on one workspace race.
+ * Every argument is checked before anything is launched.  Errors: TQ_EINVAL
  * (including n_new < 1), TQ_ECAPACITY, TQ_ENOCODEBOOK, TQ_EWORKSPACE,
  * TQ_EDEVICE. */
 int tq_decode_step(tq_ctx* ctx, const tq_cache_view* cache, const void* k, const void* v, int32_t dtype,

@@ -469,7 +469,8 @@ int tq_decode_step(tq_ctx* ctx, const tq_cache_view* cache, const void* k, const
   rc = attn_common(ctx, cache, q, dtype, G, pos + n_new, out, workspace, workspace_bytes, true, fn, &plan);
   if (rc) return rc;
   if (!std::isfinite(scale)) return fail(TQ_EINVAL, "%s: scale is not finite", fn);
-  if (!(fast_attn(ctx->cfg, G) && n_new <= kSmallAppend)) {
+  if (!(fast_attn(ctx->cfg, G) && n_new <= kSmallAppend &&
+        (int64_t)(plan.waves_per_slot / 4 + 2) * G <= kStepMaxPartials)) {
     // other shapes or longer appends: the three calls, in order
     rc = tq_append_key(ctx, cache, k, dtype, pos, n_new, stream);
     if (!rc) rc = tq_append_value(ctx, cache, v, dtype, pos, n_new, stream);
@@ -481,16 +482,9 @@ int tq_decode_step(tq_ctx* ctx, const tq_cache_view* cache, const void* k, const
   const AppendShape ks{k, dtype, n_new, pos, cache->capacity, cache->n_seq};
   const AppendShape vs{v, dtype, n_new, pos, cache->capacity, cache->n_seq};
   const AttnShape s{q, dtype, G, pos + n_new, cache->capacity, cache->n_seq};
-  uint16_t* wq = nullptr;
-  float* wqn = nullptr;
-  attend_query_buffers(workspace, plan, &wq, &wqn);
-  rc = launch_decode_prep(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cb[ctx->cfg.value_bits],
+  rc = launch_decode_step(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cb[ctx->cfg.value_bits],
                           ctx->cfg.value_bits, ctx->cfg.head_dim, ctx->cfg.proj_dim, ks, vs, s, cache->key_records,
-                          cache->value_blocks, wq, wqn, stream);
-  if (!rc)
-    rc = launch_attend(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cb[ctx->cfg.value_bits],
-                       ctx->cfg.value_bits, ctx->cfg.proj_dim, s, cache->key_records, cache->value_blocks, scale, out,
-                       workspace, plan, stream);
+                          cache->value_blocks, scale, out, workspace, plan, stream);
   return rc ? fail(rc, "%s: launch failed (%d)", fn, rc) : TQ_OK;
 }
 

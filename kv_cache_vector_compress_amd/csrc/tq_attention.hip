@@ -18,14 +18,19 @@
 // the rotated domain with the matrix cores.  A second kernel merges the
 // per-wave partials (log-sum-exp) and applies R^T once per query head.
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <mutex>
+#include <random>
 #include <type_traits>
 
 #include "tq_device.h"
+#include "tq_small.h"
 
 namespace tq {
 
-constexpr int kPartFloats = 4 + kD;  // m, l, pad, pad, acc[d]
+constexpr int kPartFloats = 4 + kD;  // m, l, ve, pad, acc[d]
+constexpr int kSyncWords = 40;       // fused decode step, per slot: producer flags (<= 16 + 2 + 16 = 34), done count
 constexpr float kLog2e = 1.4426950408889634f;
 // Waves over the whole grid, fixed so that the workspace size does not
 // depend on the device.  The attend kernel holds ~230 VGPRs, so a SIMD runs
@@ -330,8 +335,21 @@ __device__ __forceinline__ float compact2(const f4& v, int i) {
   return dpp_into<0x118, 0xC>(i == 0 ? v[0] : v[1], i == 0 ? v[2] : v[3]);
 }
 
-template <int BK, int BV, int M, int GC>
-__global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
+// The attend work of wave gw of the grid (waves_per_slot waves per slot).
+// Every wave of the workgroup must call it (the pair tables are filled
+// under a workgroup barrier).  sync() is called once by every wave (it may
+// hold a workgroup barrier) after the wave has issued the loads of its
+// first key and value block, if that block lies wholly before token
+// `fresh_from`, and before anything else the wave reads: the fused decode
+// step waits there for the step's new records and prepared queries, while
+// the loads of older blocks are already in flight.  sync() returns true if
+// the inputs never became ready; the wave then writes NaN partials.
+struct NoSync {
+  __device__ bool operator()() const { return false; }
+};
+
+template <int BK, int BV, int M, int GC, typename Sync>
+__device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t gw, const Sync& sync, int64_t fresh_from) {
   static_assert(GC == 1 || GC == 2 || GC == 4, "head compaction by 1, 2 or 4");
   constexpr int KBT = 4 + M / 32;
   constexpr int RW = rec_words<BK, M>();
@@ -353,21 +371,17 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
-  const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
-  const int slot = (int)(gw / a.waves_per_slot);
-  if (slot >= a.n_seq) return;
-  const int wc = (int)(gw - (int64_t)slot * a.waves_per_slot);
-
-  h8 qb[KBT];
-#pragma unroll
-  for (int kb = 0; kb < KBT; ++kb) qb[kb] = *(const h8*)(a.wq + (((int64_t)slot * KBT + kb) * 64 + lane) * 8);
-  if constexpr (KPT) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) qb[kb] = to_pair_order(qb[kb]);
+  // gw is wave-uniform (a scalar register): the slot's buffer descriptors
+  // then stay scalar too
+  const int gwu = __builtin_amdgcn_readfirstlane((int)gw);
+  const int slot = gwu / a.waves_per_slot;
+  if (slot >= a.n_seq) {
+    (void)sync();
+    return;
   }
+  const int wc = gwu - slot * a.waves_per_slot;
   const int a4 = r16 >> 2;  // with GC = 4: this lane's row within a token quad
   const int c2 = r16 >> 3;  // with GC = 2: this lane's row pair within a token quad
-  const float qsc = a.wqn[slot * 16 + (r16 & (16 / GC - 1))] * a.scale2;
   const int sh0 = 15 - 8 * (q & 1);
   const int n_tok = (int)a.n_tokens;
   const int nblk = (n_tok + kBlockTokens - 1) / kBlockTokens;
@@ -404,10 +418,24 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 
   BlockValues<BV> vcur;
   StepKeys<BK, BV, M> kcur;
-  if (b_begin < b_end) {
+  const bool early = (int64_t)(b_begin + 1) * kBlockTokens <= fresh_from;  // first block holds no new token
+  if (early && b_begin < b_end) {
     load_values(vcur, b_begin);
     load_keys(kcur, b_begin * kBlockTokens);
   }
+  const bool poison = sync();
+  if (!early && b_begin < b_end) {
+    load_values(vcur, b_begin);
+    load_keys(kcur, b_begin * kBlockTokens);
+  }
+  h8 qb[KBT];
+#pragma unroll
+  for (int kb = 0; kb < KBT; ++kb) qb[kb] = *(const h8*)(a.wq + (((int64_t)slot * KBT + kb) * 64 + lane) * 8);
+  if constexpr (KPT) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qb[kb] = to_pair_order(qb[kb]);
+  }
+  const float qsc = a.wqn[slot * 16 + (r16 & (16 / GC - 1))] * a.scale2;
   // One 128-token block.  MASK (the block holds the end of the cache) is a
   // compile-time flag so that full blocks carry no per-token masking code.
   auto run_block = [&](int blk, auto mask_tag) {
@@ -594,16 +622,31 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   }
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
+  // The partial keeps the accumulator in the scale of P (value norms times
+  // 2^-ve) and stores ve beside it: the combine merges partials at their
+  // largest exponent, so no intermediate leaves the fp32 range when the true
+  // output is inside it (value norms up to the fp32 maximum).
   if (r16 < a.G) {
     float* pr = a.part + (((int64_t)slot * a.waves_per_slot + wc) * a.G + r16) * kPartFloats;
-    const float f = ldexpf(1.f, ve);
+    if (poison) {
+      m_run = l_run = __builtin_nanf("");
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[nt] = f4{m_run, m_run, m_run, m_run};
+    }
     if (q == 0) {
       pr[0] = m_run;
       pr[1] = l_run;
+      pr[2] = (float)ve;
     }
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) *(f4*)(pr + 4 + 16 * nt + 4 * q) = acc[nt] * f;
+    for (int nt = 0; nt < 8; ++nt) *(f4*)(pr + 4 + 16 * nt + 4 * q) = acc[nt];
   }
+}
+
+template <int BK, int BV, int M, int GC>
+__global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
+  attend_body<BK, BV, M, GC>(a, (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), NoSync{},
+                             INT64_MAX);
 }
 
 // ---------------------------------------------------------------------------
@@ -617,36 +660,60 @@ struct CombineArgs {
   int n_seq, G, waves_per_slot;
 };
 
-// One workgroup of 4 x 128 threads per (slot, query head): thread (g, j)
-// takes coordinate j of every fourth partial, then a quarter of R's rows.
-__global__ __launch_bounds__(512) void combine_kernel(const CombineArgs a) {
-  __shared__ float w[kMaxPartials];  // per-partial weights exp2(m_c - M)
-  __shared__ float red[2][8];
-  __shared__ float part[4][kD];
+// The combine of one (slot, query head) by a workgroup of NG x 128 threads
+// (NG = 2 or 4): thread (g, j) takes coordinate j of every NG-th partial,
+// then 128 / NG of R's rows.  A partial c holds (m_c, l_c, ve_c, acc_c) with
+// the head's output share acc_c 2^ve_c; the merge scales each by
+// exp2(m_c - M) 2^(ve_c - VE) with M and VE the largest m_c and ve_c of the
+// partials that carry weight, divides by L before the final 2^VE, and rotates
+// back last.  The workgroup's shared arrays are reused by the next call, so
+// calls are separated by the barriers inside.
+template <int NG>
+__device__ __forceinline__ void combine_body(const CombineArgs& a, int slot, int h) {
+  __shared__ float w[kMaxPartials];  // per-partial weights exp2(m_c - M) 2^(ve_c - VE)
+  __shared__ float red[3][8];
+  __shared__ float part[NG][kD];
   __shared__ __align__(16) float y[kD];
-  const int sh = blockIdx.x, slot = sh / a.G, h = sh % a.G;
+  constexpr int nw = 2 * NG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = tid & (kD - 1), g = tid >> 7;
   const int W = a.waves_per_slot;
   const float* pr = a.part + ((int64_t)slot * W * a.G + h) * kPartFloats;
   const int64_t stride = (int64_t)a.G * kPartFloats;
-  // M = max of the partial maxima (wave reductions, one exchange)
-  float M = -INFINITY;
-  for (int c = tid; c < W; c += blockDim.x) M = fmaxf(M, pr[c * stride]);
+  __syncthreads();  // (the previous call's reads of the shared arrays are done)
+  // M = max of the partial maxima; VE = max exponent among partials with weight
+  float M = -INFINITY, VE = -INFINITY;
+  for (int c = tid; c < W; c += blockDim.x) {
+    const float mc = pr[c * stride];
+    M = fmaxf(M, mc);
+    if (mc != -INFINITY) VE = fmaxf(VE, pr[c * stride + 2]);
+  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
-  if (lane == 0) red[0][wave] = M;
+  for (int o = 32; o > 0; o >>= 1) {
+    M = fmaxf(M, shfl_xor(M, o));
+    VE = fmaxf(VE, shfl_xor(VE, o));
+  }
+  if (lane == 0) {
+    red[0][wave] = M;
+    red[2][wave] = VE;
+  }
   __syncthreads();
   M = red[0][0];
+  VE = red[2][0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) M = fmaxf(M, red[0][i]);
-  // weights and the weighted sum of the partial sums
+  for (int i = 1; i < nw; ++i) {
+    M = fmaxf(M, red[0][i]);
+    VE = fmaxf(VE, red[2][i]);
+  }
+  const int ve_max = VE == -INFINITY ? 0 : (int)VE;
+  // weights and the weighted sum of the partial sums (l_c is in softmax
+  // units, so it takes exp2(m_c - M) only)
   float L = 0.f;
   for (int c = tid; c < W; c += blockDim.x) {
     const float mc = pr[c * stride];
-    const float wc = mc == -INFINITY ? 0.f : exp2f(mc - M);
-    w[c] = wc;
-    L = fmaf(wc, pr[c * stride + 1], L);
+    const float e = mc == -INFINITY ? 0.f : exp2f(mc - M);
+    w[c] = ldexpf(e, (int)pr[c * stride + 2] - ve_max);
+    L = fmaf(e, pr[c * stride + 1], L);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) L += shfl_xor(L, o);
@@ -654,39 +721,149 @@ __global__ __launch_bounds__(512) void combine_kernel(const CombineArgs a) {
   __syncthreads();
   L = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) L += red[1][i];
-  // thread (g, j): partials c = g, g + 4, ..., 8 loads in flight
+  for (int i = 0; i < nw; ++i) L += red[1][i];
+  // thread (g, j): partials c = g, g + NG, ..., 8 loads in flight
   float acc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) acc[u] = 0.f;
   int c = g;
-  for (; c + 28 < W; c += 32) {
+  for (; c + 7 * NG < W; c += 8 * NG) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = fmaf(w[c + 4 * u], pr[(c + 4 * u) * stride + 4 + j], acc[u]);
+    for (int u = 0; u < 8; ++u) acc[u] = fmaf(w[c + NG * u], pr[(c + NG * u) * stride + 4 + j], acc[u]);
   }
-  for (; c < W; c += 4) acc[0] = fmaf(w[c], pr[c * stride + 4 + j], acc[0]);
+  for (; c < W; c += NG) acc[0] = fmaf(w[c], pr[c * stride + 4 + j], acc[0]);
 #pragma unroll
   for (int u = 1; u < 8; ++u) acc[0] += acc[u];
   part[g][j] = acc[0];
   __syncthreads();
-  if (g == 0) y[j] = ((part[0][j] + part[1][j]) + (part[2][j] + part[3][j])) / L;
+  if (g == 0) {
+    float t = part[0][j];
+#pragma unroll
+    for (int i = 1; i < NG; ++i) t += part[i][j];
+    y[j] = t / L;
+  }
   __syncthreads();
-  // out = R^T y: thread (g, j) sums rows i = 32 g .. 32 g + 31 of column j
+  // out = 2^VE R^T y: thread (g, j) sums rows g (128/NG) .. of column j
+  constexpr int nr = kD / NG;
   float o[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) o[u] = 0.f;
-  const float* rc = a.r32 + (size_t)(32 * g) * kD + j;
+  const float* rc = a.r32 + (size_t)(nr * g) * kD + j;
 #pragma unroll
-  for (int i = 0; i < 32; i += 8) {
+  for (int i = 0; i < nr; i += 8) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o[u] = fmaf(rc[(i + u) * kD], y[32 * g + i + u], o[u]);
+    for (int u = 0; u < 8; ++u) o[u] = fmaf(rc[(i + u) * kD], y[nr * g + i + u], o[u]);
   }
 #pragma unroll
   for (int u = 1; u < 8; ++u) o[0] += o[u];
   __syncthreads();
   part[g][j] = o[0];
   __syncthreads();
-  if (g == 0) a.out[((int64_t)slot * a.G + h) * kD + j] = (part[0][j] + part[1][j]) + (part[2][j] + part[3][j]);
+  if (g == 0) {
+    float t = part[0][j];
+#pragma unroll
+    for (int i = 1; i < NG; ++i) t += part[i][j];
+    a.out[((int64_t)slot * a.G + h) * kD + j] = ldexpf(t, ve_max);
+  }
+}
+
+// One workgroup of 4 x 128 threads per (slot, query head).
+__global__ __launch_bounds__(512) void combine_kernel(const CombineArgs a) {
+  combine_body<4>(a, (int)(blockIdx.x / a.G), (int)(blockIdx.x % a.G));
+}
+
+// The combine of all G query heads of one slot by a workgroup of 256
+// threads (the fused decode step's last workgroup of the slot), over W
+// partials [c][h][kPartFloats] at pr, with the arithmetic of combine_body.
+// Written for latency (the partials come from other compute units, past
+// this unit's caches), in three rounds of loads issued together:
+//  1. thread t loads its 64 entries of R (rows 16 (t / 32) .. + 15,
+//     columns 4 (t % 32) .. + 3) and the (m, l, ve) of the partials of its
+//     heads;
+//  2. thread (h, j4) loads coordinates 4 j4 .. 4 j4 + 3 of head h of every
+//     partial and forms the merged rotated-domain output y[h] in LDS;
+//  3. R^T y: each thread multiplies its R entries with y of every head, and
+//     the 8 row blocks are summed through LDS (two of them per wave by a
+//     lane exchange first).
+__device__ __forceinline__ void combine_slot(const CombineArgs& a, int slot, const float* pr, int W) {
+  __shared__ float wsh[kStepMaxPartials];  // weights of (c, h); W G <= kStepMaxPartials (checked by the launcher)
+  __shared__ float hL[16];
+  __shared__ int hE[16];
+  __shared__ __align__(16) float y[16][kD];
+  __shared__ __align__(16) float ob[4][16][kD];  // R^T y partial sums of the 4 waves
+  const int G = a.G, tid = threadIdx.x;
+  const int j4 = tid & 31, rb = tid >> 5;  // R: columns 4 j4 .. +3, rows 16 rb .. +15
+  f4 rr[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) rr[u] = *(const f4*)(a.r32 + (size_t)(16 * rb + u) * kD + 4 * j4);
+  __syncthreads();  // (the shared arrays are free)
+  {
+    const int h = tid >> 4, sub = tid & 15;
+    float M = -INFINITY, VE = -INFINITY;
+    if (h < G)
+      for (int c = sub; c < W; c += 16) {
+        const float* p = pr + ((int64_t)c * G + h) * kPartFloats;
+        const float mc = p[0];
+        M = fmaxf(M, mc);
+        if (mc != -INFINITY) VE = fmaxf(VE, p[2]);
+      }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      M = fmaxf(M, shfl_xor(M, o));
+      VE = fmaxf(VE, shfl_xor(VE, o));
+    }
+    const int ve_max = VE == -INFINITY ? 0 : (int)VE;
+    float L = 0.f;
+    if (h < G)
+      for (int c = sub; c < W; c += 16) {  // (the same lines again: now cached here)
+        const float* p = pr + ((int64_t)c * G + h) * kPartFloats;
+        const float mc = p[0];
+        const float e = mc == -INFINITY ? 0.f : exp2f(mc - M);
+        wsh[c * G + h] = ldexpf(e, (int)p[2] - ve_max);
+        L = fmaf(e, p[1], L);
+      }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) L += shfl_xor(L, o);
+    if (sub == 0 && h < G) {
+      hL[h] = L;
+      hE[h] = ve_max;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < 32 * G; e += blockDim.x) {
+    const int h = e >> 5, q4 = e & 31;
+    const float* p = pr + (int64_t)h * kPartFloats + 4 + 4 * q4;
+    const int64_t st = (int64_t)G * kPartFloats;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    int c = 0;
+    for (; c + 15 < W; c += 16) {
+      f4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = *(const f4*)(p + (c + u) * st);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc += wsh[(c + u) * G + h] * v[u];
+    }
+    for (; c < W; ++c) acc += wsh[c * G + h] * *(const f4*)(p + c * st);
+    *(f4*)&y[h][4 * q4] = acc / hL[h];
+  }
+  __syncthreads();
+  {
+    const int wv = tid >> 6;
+    for (int h = 0; h < G; ++h) {
+      f4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 16; ++u) o += rr[u] * y[h][16 * rb + u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += shfl_xor(o[e], 32);  // the wave's two row blocks
+      if ((tid & 32) == 0) *(f4*)&ob[wv][h][4 * j4] = o;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * kD; e += blockDim.x) {
+    const int h = e >> 7, j = e & (kD - 1);
+    a.out[((int64_t)slot * G + h) * kD + j] =
+        ldexpf((ob[0][h][j] + ob[1][h][j]) + (ob[2][h][j] + ob[3][h][j]), hE[h]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -751,7 +928,10 @@ AttnPlan plan_attention(int m, int n_seq, int G, int64_t n_tokens) {
   p.q_bytes = (size_t)n_seq * KBT * 64 * 8 * 2;
   p.qn_bytes = (size_t)n_seq * 16 * 4;
   p.part_bytes = (size_t)n_seq * p.waves_per_slot * G * kPartFloats * 4;
-  p.total = ((p.q_bytes + 255) / 256 + (p.qn_bytes + 255) / 256 + (p.part_bytes + 255) / 256) * 256;
+  p.sync_bytes = (size_t)n_seq * kSyncWords * 8 + 16;  // fused decode step: flags and counts, a status word
+  p.group_bytes = (size_t)n_seq * (p.waves_per_slot / 4 + 2) * G * kPartFloats * 4;  // its workgroup partials
+  p.total = ((p.q_bytes + 255) / 256 + (p.qn_bytes + 255) / 256 + (p.part_bytes + 255) / 256 +
+             (p.sync_bytes + 255) / 256 + (p.group_bytes + 255) / 256) * 256;
   return p;
 }
 
@@ -759,6 +939,8 @@ struct WsPtrs {
   uint16_t* wq;
   float* wqn;
   float* part;
+  unsigned long long* sync;
+  float* group;
 };
 static WsPtrs ws_ptrs(void* ws, const AttnPlan& p) {
   char* b = (char*)ws;
@@ -768,14 +950,13 @@ static WsPtrs ws_ptrs(void* ws, const AttnPlan& p) {
   w.wqn = (float*)b;
   b += (p.qn_bytes + 255) / 256 * 256;
   w.part = (float*)b;
+  b += (p.part_bytes + 255) / 256 * 256;
+  w.sync = (unsigned long long*)b;
+  b += (p.sync_bytes + 255) / 256 * 256;
+  w.group = (float*)b;
   return w;
 }
 
-void attend_query_buffers(void* ws, const AttnPlan& p, uint16_t** wq, float** wqn) {
-  const WsPtrs w = ws_ptrs(ws, p);
-  *wq = w.wq;
-  *wqn = w.wqn;
-}
 
 int launch_prep_queries(const Matrices& mats, int m, const AttnShape& s, void* ws, const AttnPlan& p,
                         void* stream) {
@@ -822,11 +1003,10 @@ done:
   return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
 }
 
-int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
-                  int m, const AttnShape& s, const void* key_records, const void* value_blocks, float scale,
-                  float* out, void* ws, const AttnPlan& p, void* stream) {
+static AttendArgs attend_args(const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits, int m,
+                              const AttnShape& s, const void* key_records, const void* value_blocks, float scale,
+                              const WsPtrs& w, const AttnPlan& p) {
   AttendArgs a;
-  const WsPtrs w = ws_ptrs(ws, p);
   a.rec = (const uint32_t*)key_records;
   a.vblocks = (const uint32_t*)value_blocks;
   a.part = w.part;
@@ -844,6 +1024,26 @@ int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const
   a.scale2 = scale * kLog2e;
   fill_tables(cbk, a.tlo, a.thi);
   fill_tables(cbv, a.vtlo, a.vthi);
+  return a;
+}
+
+static CombineArgs combine_args(const Matrices& mats, const AttnShape& s, float* out, const WsPtrs& w,
+                                const AttnPlan& p) {
+  CombineArgs c;
+  c.part = w.part;
+  c.out = out;
+  c.r32 = mats.r32;
+  c.n_seq = s.n_seq;
+  c.G = s.G;
+  c.waves_per_slot = p.waves_per_slot;
+  return c;
+}
+
+int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
+                  int m, const AttnShape& s, const void* key_records, const void* value_blocks, float scale,
+                  float* out, void* ws, const AttnPlan& p, void* stream) {
+  const WsPtrs w = ws_ptrs(ws, p);
+  const AttendArgs a = attend_args(cbk, kbits, cbv, vbits, m, s, key_records, value_blocks, scale, w, p);
   const int64_t waves = (int64_t)a.waves_per_slot * s.n_seq;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   hipStream_t st = (hipStream_t)stream;
@@ -862,14 +1062,241 @@ int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const
 #undef TQ_AT
   if (!launched) return TQ_EUNSUPPORTED;
   if (hipGetLastError() != hipSuccess) return TQ_EDEVICE;
-  CombineArgs c;
-  c.part = w.part;
-  c.out = out;
-  c.r32 = mats.r32;
-  c.n_seq = s.n_seq;
-  c.G = s.G;
-  c.waves_per_slot = p.waves_per_slot;
+  const CombineArgs c = combine_args(mats, s, out, w, p);
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(s.n_seq * s.G)), dim3(4 * kD), 0, st, c);
+  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+}
+
+// ---------------------------------------------------------------------------
+// the fused decode step: appends, query preparation, attend and combine in
+// one launch
+// ---------------------------------------------------------------------------
+//
+// The grid's first workgroups are the producers of the step's inputs (the
+// key appends, the value appends and the query preparation, one workgroup
+// each, as in the separate small-append and preparation kernels); the rest
+// run the attend waves, which issue the loads of their first block (if it
+// predates the step) before they wait for the producers, then merge their
+// partials and combine (see decode_step_kernel).
+//
+// The flags and counts live in the caller's workspace, which nobody clears:
+// a flag is set to a 40-bit epoch that no earlier launch of the process
+// used, so stale flags of earlier steps, or of other contexts sharing the
+// workspace, are never mistaken for this step's.  (Uninitialised memory
+// holding this launch's tag by chance is the one case not covered: odds of
+// 2^-40 a word.)
+
+constexpr int kWaitSpins = 1 << 20;  // polls of about 1 us (the flags' round trip and s_sleep(2)): about a second
+
+// Wait (bounded) until the n flags at f all hold `tag`.  The spin reads
+// relaxed (device-coherent loads, no cache maintenance per poll); the
+// caller issues one acquire fence after the wait.
+__device__ __forceinline__ bool flags_wait(const unsigned long long* f, int n, unsigned long long tag) {
+  for (int i = 0; i < kWaitSpins; ++i) {
+    bool all = true;
+    for (int k = 0; k < n; ++k)
+      all = (__hip_atomic_load(f + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) && all;
+    if (all) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+
+struct StepArgs {
+  DecodeArgs prep;             // producers: key appends, value appends, query preparation
+  AttendArgs att;
+  CombineArgs comb;
+  unsigned long long* sync;    // [n_seq][kSyncWords]: producer flags, then the done count (word kSyncWords - 1)
+  uint32_t* status;            // 1 after a wait gave up
+  unsigned long long epoch;    // this launch's tag (1 .. 2^40 - 1)
+  float* group;                // [n_seq][group_stride][G][kPartFloats] workgroup partials
+  int group_stride;            // workgroup partials a slot has room for (waves_per_slot / 4 + 2)
+  int64_t fresh_from;          // first new token (its block onwards is read only after the wait)
+  int n_prod;                  // producer workgroups
+  int prod_per_slot;           // producer workgroups of one slot
+  int vblk_per_slot;           // value-append workgroups of one slot
+};
+
+// Synchronisation.  Producer k of slot s, once its stores are out, sets
+// flag k of the slot to this launch's tag with a release store; producer 0
+// also zeroes the slot's done count first.  An attend workgroup waits for
+// all flags of the slots its waves cover (acquire), attends, merges its
+// waves' partials into one, and adds 1 to each slot's done count; the add
+// that completes a slot (acquire-release) makes its workgroup the one that
+// combines the slot, after which it clears the slot's flags so that a
+// replayed launch (a captured HIP graph keeps its arguments, tag included)
+// waits again.  No count is shared by contending producers, and no
+// workgroup waits for one of higher index, which the dispatcher starts
+// later, so every wait ends.
+template <int BK, int BV, int M, int GC>
+__global__ __launch_bounds__(256) void decode_step_kernel(const StepArgs a) {
+  __shared__ int flag[5];  // [0]: inputs missing; [1 + i]: this workgroup completes slot s_lo + i
+  const int b = (int)blockIdx.x;
+  if (b < a.n_prod) {
+    const DecodeArgs& p = a.prep;
+    int slot, k;
+    if (b < p.nk) {
+      small_keys_block(p.k, b);
+      slot = (int)(b / p.k.n_new);
+      k = (int)(b % p.k.n_new);
+    } else if (b < p.nk + p.nv) {
+      small_values_block(p.v, b - p.nk);
+      slot = (b - p.nk) / a.vblk_per_slot;
+      k = (int)p.k.n_new + (b - p.nk) % a.vblk_per_slot;
+    } else {
+      gen_prep_block(p.p, b - p.nk - p.nv);
+      slot = (b - p.nk - p.nv) / 16;
+      k = (int)p.k.n_new + a.vblk_per_slot + (b - p.nk - p.nv) % 16;
+    }
+    // The barrier waits for the workgroup's stores; the release store then
+    // makes them visible device-wide (one L2 write-back for the workgroup).
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long* f = a.sync + (size_t)slot * kSyncWords;
+      if (k == 0) __hip_atomic_store(f + kSyncWords - 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(f + k, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  const int W = a.att.waves_per_slot;
+  const int64_t gw0 = (int64_t)(b - a.n_prod) * 4;
+  const int s_lo = (int)(gw0 / W);
+  const int64_t s_end = (gw0 + 3) / W;
+  const int s_hi = (int)(s_end < a.att.n_seq - 1 ? s_end : a.att.n_seq - 1);
+  auto sync = [&]() {
+    if (threadIdx.x == 0) {
+      bool ok = true;
+      for (int s = s_lo; s <= s_hi; ++s)
+        ok = flags_wait(a.sync + (size_t)s * kSyncWords, a.prod_per_slot, a.epoch) && ok;
+      if (!ok) __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      flag[0] = ok ? 0 : 1;
+      // acquire: this CU's caches drop lines older than the producers' stores
+      // (the other waves read after the barrier below)
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    return flag[0] != 0;
+  };
+  attend_body<BK, BV, M, GC>(a.att, gw0 + (threadIdx.x >> 6), sync, a.fresh_from);
+  __syncthreads();  // the workgroup's wave partials written (read back below from this CU)
+  // Merge the workgroup's waves of each slot into one workgroup partial
+  // (the same log-sum-exp merge as the combine), so the slot's completing
+  // workgroup reads a quarter as many.  Workgroup partial gi of slot s is
+  // written by the workgroup whose first wave is 4 (gi + floor(s W / 4)).
+  const int G = a.att.G;
+  for (int s = s_lo; s <= s_hi; ++s) {
+    const int64_t lo = (int64_t)s * W, hi = (int64_t)(s + 1) * W;
+    const int c0 = (int)((gw0 > lo ? gw0 : lo) - lo), c1 = (int)((gw0 + 4 < hi ? gw0 + 4 : hi) - lo);
+    const int gi = (int)(gw0 / 4 - lo / 4);
+    const float* src = a.att.part + (int64_t)s * W * G * kPartFloats;
+    float* dst = a.group + ((int64_t)s * a.group_stride + gi) * G * kPartFloats;
+    for (int e = threadIdx.x; e < 32 * G; e += blockDim.x) {
+      const int h = e >> 5, j4 = e & 31;
+      float Mx = -INFINITY, VE = -INFINITY;
+      for (int c = c0; c < c1; ++c) {
+        const float* p = src + ((int64_t)c * G + h) * kPartFloats;
+        Mx = fmaxf(Mx, p[0]);
+        if (p[0] != -INFINITY) VE = fmaxf(VE, p[2]);
+      }
+      const int ve = VE == -INFINITY ? -1000 : (int)VE;
+      float L = 0.f;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int c = c0; c < c1; ++c) {
+        const float* p = src + ((int64_t)c * G + h) * kPartFloats;
+        const float e2 = p[0] == -INFINITY ? 0.f : exp2f(p[0] - Mx);
+        L = fmaf(e2, p[1], L);
+        acc += ldexpf(e2, (int)p[2] - ve) * *(const f4*)(p + 4 + 4 * j4);
+      }
+      float* d = dst + (int64_t)h * kPartFloats;
+      *(f4*)(d + 4 + 4 * j4) = acc;
+      if (j4 == 0) {
+        d[0] = Mx;
+        d[1] = L;
+        d[2] = (float)ve;
+      }
+    }
+  }
+  __syncthreads();  // the workgroup partials written (the adds below release them)
+  if (threadIdx.x == 0) {
+    for (int s = s_lo; s <= s_hi; ++s) {
+      const int64_t lo = (int64_t)s * W, hi = (int64_t)(s + 1) * W;
+      const uint32_t n_groups = (uint32_t)((hi - 1) / 4 - lo / 4 + 1);
+      unsigned long long* done = a.sync + (size_t)s * kSyncWords + kSyncWords - 1;
+      const unsigned long long c = __hip_atomic_fetch_add(done, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      flag[1 + s - s_lo] = c + 1 == n_groups ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  for (int s = s_lo; s <= s_hi; ++s) {
+    if (flag[1 + s - s_lo]) {
+      const int64_t lo = (int64_t)s * W, hi = (int64_t)(s + 1) * W;
+      const int n_groups = (int)((hi - 1) / 4 - lo / 4 + 1);
+      combine_slot(a.comb, s, a.group + (int64_t)s * a.group_stride * G * kPartFloats, n_groups);
+      // every producer and attend workgroup of the slot is past its use of
+      // the flags: clear them for a replay
+      if (threadIdx.x < a.prod_per_slot)
+        __hip_atomic_store(a.sync + (size_t)s * kSyncWords + threadIdx.x, 0ull, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+static unsigned long long next_epoch() {
+  // process-wide, distinct for 2^40 launches; the start is drawn at random so
+  // that workspaces left by other processes hold other tags
+  static std::atomic<unsigned long long> counter{0};
+  static std::once_flag once;
+  std::call_once(once, [] {
+    std::random_device rd;
+    const unsigned long long seed = ((unsigned long long)rd() << 32) ^ (unsigned long long)rd() ^
+                                    (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    counter.store(seed);
+  });
+  unsigned long long e;
+  do {
+    e = (counter.fetch_add(1) + 1) & ((1ull << 40) - 1);
+  } while (e == 0);
+  return e;
+}
+
+int launch_decode_step(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
+                       int d, int m, const AppendShape& ks, const AppendShape& vs, const AttnShape& s,
+                       void* key_records, void* value_blocks, float scale, float* out, void* ws, const AttnPlan& p,
+                       void* stream) {
+  if ((int64_t)(p.waves_per_slot / 4 + 2) * s.G > kStepMaxPartials) return TQ_EUNSUPPORTED;
+  const WsPtrs w = ws_ptrs(ws, p);
+  StepArgs a;
+  a.prep = decode_args(mats, cbk, kbits, cbv, vbits, d, m, ks, vs, s, key_records, value_blocks, w.wq, w.wqn);
+  a.att = attend_args(cbk, kbits, cbv, vbits, m, s, key_records, value_blocks, scale, w, p);
+  a.comb = combine_args(mats, s, out, w, p);
+  a.sync = w.sync;
+  a.status = (uint32_t*)(w.sync + (size_t)kSyncWords * s.n_seq);
+  a.fresh_from = ks.pos;
+  a.epoch = next_epoch();
+  a.group = w.group;
+  a.group_stride = p.waves_per_slot / 4 + 2;
+  const int np = a.prep.nk + a.prep.nv + s.n_seq * 16;
+  a.n_prod = np;
+  a.vblk_per_slot = a.prep.nv / s.n_seq;
+  a.prod_per_slot = (int)ks.n_new + a.vblk_per_slot + 16;
+  const int64_t waves = (int64_t)p.waves_per_slot * s.n_seq;
+  const dim3 grid((unsigned)(np + (waves + 3) / 4)), block(256);
+  const size_t lds = decode_lds_bytes(d, m);
+  hipStream_t st = (hipStream_t)stream;
+  bool launched = false;
+#define TQ_DS(BK, BV, M)                                                                              \
+  if (!launched && kbits == BK && vbits == BV && m == M) {                                            \
+    if (s.G <= 4) hipLaunchKernelGGL((decode_step_kernel<BK, BV, M, 4>), grid, block, lds, st, a);      \
+    else if (s.G <= 8) hipLaunchKernelGGL((decode_step_kernel<BK, BV, M, 2>), grid, block, lds, st, a); \
+    else hipLaunchKernelGGL((decode_step_kernel<BK, BV, M, 1>), grid, block, lds, st, a);               \
+    launched = true;                                                                                  \
+  }
+#define TQ_DS_V(BK, M) TQ_DS(BK, 1, M) TQ_DS(BK, 2, M) TQ_DS(BK, 3, M) TQ_DS(BK, 4, M)
+  TQ_DS_V(0, 64) TQ_DS_V(1, 64) TQ_DS_V(2, 64) TQ_DS_V(3, 64) TQ_DS_V(4, 64)
+  TQ_DS_V(0, 128) TQ_DS_V(1, 128) TQ_DS_V(2, 128) TQ_DS_V(3, 128) TQ_DS_V(4, 128)
+#undef TQ_DS_V
+#undef TQ_DS
+  if (!launched) return TQ_EUNSUPPORTED;
   return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
 }
 

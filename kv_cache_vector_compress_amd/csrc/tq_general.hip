@@ -833,15 +833,17 @@ __global__ __launch_bounds__(256) void gen_attend_kernel(const GenAttendArgs a) 
   }
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
+  // (the accumulator stays in the scale of P, 2^-ve, with ve stored beside
+  // it; gen_combine merges the ranges at their largest exponent)
   if (head_ok) {
     float* pr = a.part + ((((int64_t)slot * a.ranges + rg) * a.n_oct + u) * a.G + h) * kGenPart;
-    const float f = ldexpf(1.f, ve);
     if (q == 0) {
       pr[0] = m_run;
       pr[1] = l_run;
+      pr[2] = (float)ve;
     }
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) *(f4*)(pr + 4 + 16 * nt + 4 * q) = acc[nt] * f;
+    for (int nt = 0; nt < 8; ++nt) *(f4*)(pr + 4 + 16 * nt + 4 * q) = acc[nt];
   }
 }
 
@@ -852,30 +854,45 @@ struct GenCombineArgs {
   int n_seq, G, d, n_oct, ranges;
 };
 
-// One workgroup per (slot, query head): out = R^T (sum_r w_r acc_r) / sum_r w_r l_r,
-// w_r = exp2(m_r - max_r m_r).
+// One workgroup per (slot, query head): out = 2^VE R^T (sum_r w_r 2^(ve_r - VE)
+// acc_r) / sum_r w_r l_r, w_r = exp2(m_r - max_r m_r), VE the largest ve_r of
+// the ranges that carry weight (the accumulators are stored at scale 2^-ve_r).
 __global__ __launch_bounds__(256) void gen_combine(const GenCombineArgs a) {
   extern __shared__ float ysh[];  // [d] combined rotated-domain accumulator, then [ranges] weights
   float* wsh = ysh + a.d;
-  __shared__ float red[4];
-  __shared__ float Msh, Lsh;
+  __shared__ float red[4], rede[4];
+  __shared__ float Msh, Lsh, Esh;
   const int sh = blockIdx.x, slot = sh / a.G, h = sh % a.G, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   auto P = [&](int r, int u) { return a.part + ((((int64_t)slot * a.ranges + r) * a.n_oct + u) * a.G + h) * kGenPart; };
-  float mx = -INFINITY;
-  for (int r = tid; r < a.ranges; r += blockDim.x) mx = fmaxf(mx, P(r, 0)[0]);
+  float mx = -INFINITY, ex = -INFINITY;
+  for (int r = tid; r < a.ranges; r += blockDim.x) {
+    const float mr = P(r, 0)[0];
+    mx = fmaxf(mx, mr);
+    if (mr != -INFINITY) ex = fmaxf(ex, P(r, 0)[2]);
+  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
-  if (lane == 0) red[wave] = mx;
+  for (int o = 32; o > 0; o >>= 1) {
+    mx = fmaxf(mx, shfl_xor(mx, o));
+    ex = fmaxf(ex, shfl_xor(ex, o));
+  }
+  if (lane == 0) {
+    red[wave] = mx;
+    rede[wave] = ex;
+  }
   __syncthreads();
-  if (tid == 0) Msh = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (tid == 0) {
+    Msh = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    Esh = fmaxf(fmaxf(rede[0], rede[1]), fmaxf(rede[2], rede[3]));
+  }
   __syncthreads();
   const float M = Msh;
+  const int VE = Esh == -INFINITY ? 0 : (int)Esh;
   float L = 0.f;
   for (int r = tid; r < a.ranges; r += blockDim.x) {
     const float mr = P(r, 0)[0];
     const float w = (mr == -INFINITY || M == -INFINITY) ? 0.f : exp2f(mr - M);
-    wsh[r] = w;
+    wsh[r] = ldexpf(w, (int)P(r, 0)[2] - VE);
     L += w * P(r, 0)[1];
   }
 #pragma unroll
@@ -896,7 +913,7 @@ __global__ __launch_bounds__(256) void gen_combine(const GenCombineArgs a) {
   for (int j = tid; j < a.d; j += blockDim.x) {
     float t = 0.f;
     for (int i = 0; i < a.d; ++i) t = fmaf(a.r32[(size_t)i * a.d + j], ysh[i], t);
-    out[j] = t * inv;
+    out[j] = ldexpf(t * inv, VE);
   }
 }
 

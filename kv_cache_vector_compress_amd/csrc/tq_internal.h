@@ -73,6 +73,8 @@ struct AttnPlan {
   size_t q_bytes;          // prepared query operands
   size_t qn_bytes;         // query norms
   size_t part_bytes;       // attend partials
+  size_t sync_bytes;       // counters and status word of the fused decode step
+  size_t group_bytes;      // the fused decode step's workgroup partials
   size_t total;
 };
 AttnPlan plan_attention(int m, int n_seq, int G, int64_t n_tokens);
@@ -130,13 +132,17 @@ int launch_small_keys(const Matrices& mats, const CodebookDev& cb, int bits, int
 int launch_small_values(const Matrices& mats, const CodebookDev& cb, int bits, int d, const AppendShape& s,
                         void* value_blocks, void* stream);
 
-// A decode step's appends and query preparation in one launch (tq_small.hip);
-// wq / wqn: the query operand buffers of the attend workspace.
-int launch_decode_prep(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
-                       int d, int m, const AppendShape& ks, const AppendShape& vs, const AttnShape& qs,
-                       void* key_records, void* value_blocks, uint16_t* wq, float* wqn, void* stream);
-// Where the single-kernel attend keeps its query operands in the workspace.
-void attend_query_buffers(void* ws, const AttnPlan& p, uint16_t** wq, float** wqn);
+// The whole decode step in one launch (tq_attention.hip) serves shapes whose
+// workgroup partials per slot (waves per slot / 4 + 2, x G) are at most this
+// many (its combine keeps their weights in LDS).
+constexpr int kStepMaxPartials = 4096;
+// The whole decode step in one launch (tq_attention.hip): key and value
+// appends and query preparation (tq_small.h, tq_prep.h), attend and combine,
+// synchronised through flags and a count in the workspace.
+int launch_decode_step(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
+                       int d, int m, const AppendShape& ks, const AppendShape& vs, const AttnShape& s,
+                       void* key_records, void* value_blocks, float scale, float* out, void* ws, const AttnPlan& p,
+                       void* stream);
 
 // Device scratch of tq_attend_noalloc (tq_attention.hip): a static device
 // array of kNoAllocScratchBytes per GPU.  noalloc_scratch_init looks up its

@@ -891,3 +891,64 @@ def test_binding_rejects_mismatched_tensor_shapes():
     with pytest.raises(ValueError):
         cache.decode_step(k, torch.zeros((2, 2, 128), dtype=torch.float16, device=dev), q, 0)
     ctx.close()
+
+
+def test_decode_step_single_launch_slot_spanning_and_graph_replay():
+    """The single-launch decode step with attend workgroups that span slots
+    (6 waves per slot at 700 tokens, so 4-wave workgroups straddle two
+    slots), step by step against the oracle on the GPU's codes; then the
+    same step captured in a HIP graph and replayed several times (the launch
+    keeps its tag on replay, so its flags must be cleared by each replay's
+    last workgroup), every replay equal to the eager output, with eager work
+    and synchronisations between replays."""
+    d, m, G, n_seq, prefill = 128, 64, 8, 5, 690
+    steps = [1, 3, 1, 5]
+    T = prefill + sum(steps)
+    K = np.stack([synth.kv_slot(230, s, s, T, d) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(231, s, s, T, d) for s in range(n_seq)])
+    Qs = [np.stack([synth.kv_slot(232 + i, s, s, G, d) for s in range(n_seq)]) for i in range(len(steps))]
+    _say("decode step, slot-spanning workgroups", (n_seq, T, G))
+    ctx, R, S = make_ctx(d, m, 3, 3)
+    cache = tq.KVCache(ctx, n_seq, 768)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    cache.append_key(dev(K[:, :prefill]), 0)
+    cache.append_value(dev(V[:, :prefill]), 0)
+    pos, outs = prefill, []
+    for n, Q in zip(steps, Qs):
+        outs.append(cache.decode_step(dev(K[:, pos:pos + n]), dev(V[:, pos:pos + n]), dev(Q), pos).cpu().numpy())
+        pos += n
+    kbeta, kc = O.lloyd_max_codebook(d, 3)
+    gk = P.unpack_gpu_keys(cache, d, m, 3, T)
+    gv = P.unpack_gpu_values(cache, d, 3, T)
+    st = P.check_keys(gk, O.compress_keys(K, R, S, kbeta, kc), kbeta, S, kc)
+    st.pop("flip_tokens")
+    pos, errs = prefill, []
+    for n, Q, out in zip(steps, Qs, outs):
+        pos += n
+        ref = O.attend(Q, R, S, kc, {k: a[:, :pos] for k, a in gk.items()}, {k: a[:, :pos] for k, a in gv.items()})
+        errs.append(P.check_attend(out, ref))
+    _say(st, errs)
+    # graph capture and replay of one more step (re-appending the last token)
+    k1, v1, q1 = dev(K[:, T - 1:T]), dev(V[:, T - 1:T]), dev(Qs[-1])
+    o = torch.empty((n_seq, G, d), dtype=torch.float32, device="cuda")
+    cache.decode_step(k1, v1, q1, T - 1, out=o)
+    torch.cuda.synchronize()
+    eager = o.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        cache.decode_step(k1, v1, q1, T - 1, out=o, stream=side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            cache.decode_step(k1, v1, q1, T - 1, out=o, stream=side)
+    torch.cuda.synchronize()
+    for r in range(4):
+        o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager), f"graph replay {r} differs from the eager step"
+        cache.decode_step(k1, v1, q1, T - 1)  # eager work between replays
+        torch.cuda.synchronize()
+    del g
+    ctx.close()
