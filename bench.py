@@ -541,30 +541,37 @@ def main():
     # Practical HBM ceiling beside the theoretical peak: a plain read stream
     # over the 2 GiB key input, and the same with writes interleaved 4:1 (the
     # read/write mix of the score kernel and of compress), each the best over
-    # grids of 8 to 64 waves per compute unit.  Each stage is also reported
-    # against the stream with its own mix.
+    # grids of 8 to 64 waves per compute unit and over 4, 8 or 16 loads in
+    # flight per lane, plain or nontemporal.  Each stage is also reported
+    # against the stream with its own mix.  A torch sum over the same bytes
+    # is an independent check of the read figure.
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     dst = torch.empty(Kd.numel() * Kd.element_size() // 16, dtype=torch.float32, device=dev)
-    stream_ms, stream_wpc = {}, {}
+    stream_ms, stream_cfg = {}, {}
     for name, d_ in (("read", None), ("read4_write1", dst)):
-        for wpc in (8, 16, 32, 64):
-            for _ in range(2):
-                tq.hbm_stream(Kd, d_, sink, wpc)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(10):
-                tq.hbm_stream(Kd, d_, sink, wpc)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 10
-            if name not in stream_ms or ms < stream_ms[name]:
-                stream_ms[name], stream_wpc[name] = ms, wpc
+        for nl, nt in ((4, False), (8, True), (16, True)):
+            for wpc in (8, 16, 32, 64):
+                for _ in range(2):
+                    tq.hbm_stream(Kd, d_, sink, wpc, loads_in_flight=nl, nontemporal=nt)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    tq.hbm_stream(Kd, d_, sink, wpc, loads_in_flight=nl, nontemporal=nt)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 10
+                if name not in stream_ms or ms < stream_ms[name]:
+                    stream_ms[name] = ms
+                    stream_cfg[name] = {"waves_per_cu": wpc, "loads_in_flight": nl, "nontemporal": nt}
     del dst
     nbytes = Kd.numel() * Kd.element_size()
+    flat = Kd.view(-1).view(torch.float32)  # (the words' values do not matter to the timing)
+    torch_ms = min(_timed(torch, lambda: flat.sum(), 5) for _ in range(2))
     hbm_stream = {"read_GBps": round(nbytes / (stream_ms["read"] * 1e-3) / 1e9, 1),
                   "read4_write1_GBps": round(nbytes * 1.25 / (stream_ms["read4_write1"] * 1e-3) / 1e9, 1),
-                  "bytes_read": nbytes, "waves_per_cu": stream_wpc}
+                  "torch_sum_read_GBps": round(nbytes / (torch_ms * 1e-3) / 1e9, 1),
+                  "bytes_read": nbytes, "best": stream_cfg}
     mix = {"compress_keys": "read4_write1_GBps", "compress_values": "read4_write1_GBps",
            "scores": "read4_write1_GBps", "attend": "read_GBps"}
     for s_ in stages:

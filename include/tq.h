@@ -354,12 +354,17 @@ int tq_get_keys(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_
  * the value only proves the reads happened).  Not part of the method: it
  * measures what a plain stream reaches on the device (the reported
  * baseline beside the theoretical peak).  src, dst: device, 16-byte aligned;
- * read_bytes a positive multiple of 4096; write_bytes 0, read_bytes,
- * read_bytes / 2 or read_bytes / 4; sink: device uint32; waves_per_cu: the
- * grid's waves per compute unit, a multiple of 4 up to 64 (0: 16), since the
- * best count depends on the read/write mix.  Errors: TQ_EINVAL, TQ_EDEVICE. */
+ * write_bytes 0, read_bytes, read_bytes / 2 or read_bytes / 4; sink: device
+ * uint32; waves_per_cu: the grid's waves per compute unit, a multiple of 4
+ * up to 64 (0: 16), since the best count depends on the read/write mix.
+ * flags: bit 0 (TQ_STREAM_NONTEMPORAL) makes every load and store
+ * nontemporal; bits 8-15 give the 16-byte loads each lane keeps in flight,
+ * 4, 8 or 16 (0: 4); read_bytes must be a positive multiple of that many
+ * KiB.  Errors: TQ_EINVAL, TQ_EDEVICE. */
+#define TQ_STREAM_NONTEMPORAL 1
+#define TQ_STREAM_LOADS(n) ((n) << 8)
 int tq_hbm_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
-                  int32_t waves_per_cu, void* stream);
+                  int32_t waves_per_cu, int32_t flags, void* stream);
 
 #ifdef __cplusplus
 }

@@ -560,11 +560,16 @@ int tq_get_keys(tq_ctx* ctx, const tq_cache_view* cache, int64_t pos, int64_t n_
 }
 
 int tq_hbm_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
-                  int32_t waves_per_cu, void* stream) {
+                  int32_t waves_per_cu, int32_t flags, void* stream) {
   clear_error();
+  const int nl = (flags >> 8) & 0xFF;
+  const int loads = nl == 0 ? 4 : nl;
+  if ((flags & ~0xFF01) != 0 || !(loads == 4 || loads == 8 || loads == 16))
+    return fail(TQ_EINVAL, "tq_hbm_stream: flags 0x%x: bit 0 and loads in flight 4, 8 or 16 in bits 8-15", flags);
   if (!src || ((uintptr_t)src & 15u)) return fail(TQ_EINVAL, "tq_hbm_stream: src must be a 16-byte aligned device pointer");
-  if (read_bytes == 0 || read_bytes % 4096 != 0)
-    return fail(TQ_EINVAL, "tq_hbm_stream: read_bytes must be a positive multiple of 4096");
+  const size_t group = 1024u * (size_t)loads;
+  if (read_bytes == 0 || read_bytes % group != 0)
+    return fail(TQ_EINVAL, "tq_hbm_stream: read_bytes must be a positive multiple of %zu", group);
   if (write_bytes != 0) {
     if (!dst || ((uintptr_t)dst & 15u))
       return fail(TQ_EINVAL, "tq_hbm_stream: dst must be a 16-byte aligned device pointer");
@@ -579,7 +584,7 @@ int tq_hbm_stream(const void* src, size_t read_bytes, void* dst, size_t write_by
   static int init_rc = 0;
   std::call_once(once, [] { init_rc = stream_device_init(); });
   if (init_rc != 0) return fail(TQ_EDEVICE, "tq_hbm_stream: HIP device query failed");
-  const int rc = launch_stream(src, read_bytes, dst, write_bytes, sink, waves_per_cu, stream);
+  const int rc = launch_stream(src, read_bytes, dst, write_bytes, sink, waves_per_cu, loads, (flags & 1) != 0, stream);
   return rc == 0 ? TQ_OK : fail(rc, "tq_hbm_stream: kernel launch failed");
 }
 

@@ -164,12 +164,18 @@ struct KeyStage {
   u4 v[NL];
 };
 
+// Cache policy of the score kernel's record loads and score stores: each
+// byte is touched once, and nontemporal accesses measured a few percent
+// faster on this stream (the attend kernel, whose lanes read scattered words
+// of lines other lanes also read, keeps the default policy).
+constexpr int kNonTemporal = 2;
+
 template <int RW, int U>
 __device__ __forceinline__ void stage_load(KeyStage<RW, U>& s, __amdgpu_buffer_rsrc_t r, int tile, int lane) {
   const uint32_t o = (uint32_t)tile * (uint32_t)(KeyStage<RW, U>::TW * 4) + 16u * (uint32_t)lane;
 #pragma unroll
   for (int j = 0; j < KeyStage<RW, U>::NL; ++j)
-    s.v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, o + 1024u * j, 0, 0);
+    s.v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, o + 1024u * j, 0, kNonTemporal);
 }
 
 // Write the staged registers to the wave's LDS slice, one 8-byte store per
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
         const f4 v = acc[u] * nk * qn;
         const uint32_t ob = (orow + (uint32_t)t0) * 4u;
         if (t0 + 4 <= n_tok) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), ors, ob, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), ors, ob, 0, kNonTemporal);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)

@@ -80,7 +80,7 @@ def lib() -> ctypes.CDLL:
         "tq_topk_scores": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, I32, P, P, P, SZ, P]),
         "tq_get_values": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
         "tq_get_keys": (ctypes.c_int, [P, VIEW, I64, I64, P, P]),
-        "tq_hbm_stream": (ctypes.c_int, [P, SZ, P, SZ, P, I32, P]),
+        "tq_hbm_stream": (ctypes.c_int, [P, SZ, P, SZ, P, I32, I32, P]),
         "tq_attend_noalloc": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, ctypes.c_float, P, P]),
         "tq_decode_step": (ctypes.c_int, [P, VIEW, P, P, I32, I64, I64, P, I32, ctypes.c_float, P, P, SZ, P]),
     }
@@ -381,17 +381,24 @@ class KVCache:
 
 # ---- measurement -------------------------------------------------------------
 
-def hbm_stream(src, dst=None, sink=None, waves_per_cu: int = 0, stream=None) -> None:
+STREAM_NONTEMPORAL = 1
+
+
+def hbm_stream(src, dst=None, sink=None, waves_per_cu: int = 0, loads_in_flight: int = 4,
+               nontemporal: bool = False, stream=None) -> None:
     """Stream all of `src` (a contiguous device tensor) and, if `dst` is given,
     write all of `dst` interleaved with the reads (tq_hbm_stream), on a grid
-    of `waves_per_cu` waves per compute unit (0: the library's default).
-    `sink` is a one-element int32 device tensor that receives the XOR of the
-    words read (XOR-ed into its current value)."""
+    of `waves_per_cu` waves per compute unit (0: the library's default),
+    each lane keeping `loads_in_flight` 16-byte loads (4, 8 or 16) in flight,
+    with nontemporal loads and stores if asked.  `sink` is a one-element
+    int32 device tensor that receives the XOR of the words read (XOR-ed into
+    its current value)."""
     torch = _torch()
     if sink is None:
         sink = torch.zeros(1, dtype=torch.int32, device=src.device)
     nr = src.numel() * src.element_size()
     nw = 0 if dst is None else dst.numel() * dst.element_size()
+    flags = (loads_in_flight << 8) | (STREAM_NONTEMPORAL if nontemporal else 0)
     _check(lib().tq_hbm_stream(_dev(src, "src"), nr, _dev(dst, "dst") if dst is not None else None, nw,
-                               _dev(sink, "sink"), waves_per_cu, _stream_ptr(stream)))
+                               _dev(sink, "sink"), waves_per_cu, flags, _stream_ptr(stream)))
     return sink

@@ -173,18 +173,21 @@ def test_hbm_stream_rejects_bad_arguments_before_any_device_call():
     lib = tq.lib()
     A = ctypes.c_void_p(1 << 40)       # aligned, never dereferenced
     U = ctypes.c_void_p((1 << 40) + 4)  # misaligned
-    assert lib.tq_hbm_stream(None, 4096, None, 0, A, 0, None) == -1
-    assert lib.tq_hbm_stream(U, 4096, None, 0, A, 0, None) == -1
-    assert lib.tq_hbm_stream(A, 0, None, 0, A, 0, None) == -1
-    assert lib.tq_hbm_stream(A, 4096 + 16, None, 0, A, 0, None) == -1
-    assert lib.tq_hbm_stream(A, 8192, None, 2048, A, 0, None) == -1      # writes without dst
-    assert lib.tq_hbm_stream(A, 8192, A, 3000, A, 0, None) == -1         # ratio not 1, 2 or 4
-    assert lib.tq_hbm_stream(A, 8192, A, 8192 // 8, A, 0, None) == -1    # ratio 8
-    assert lib.tq_hbm_stream(A, 8192, A, 2048, None, 0, None) == -1   # no sink
-    assert lib.tq_hbm_stream(A, 8192, A, 2048, ctypes.c_void_p((1 << 40) + 2), 0, None) == -1
-    assert lib.tq_hbm_stream(A, 8192, A, 2048, A, 6, None) == -1      # waves per CU not a multiple of 4
-    assert lib.tq_hbm_stream(A, 8192, A, 2048, A, 68, None) == -1     # above 64
-    assert lib.tq_hbm_stream(A, 8192, A, 2048, A, -4, None) == -1
+    assert lib.tq_hbm_stream(None, 4096, None, 0, A, 0, 0, None) == -1
+    assert lib.tq_hbm_stream(U, 4096, None, 0, A, 0, 0, None) == -1
+    assert lib.tq_hbm_stream(A, 0, None, 0, A, 0, 0, None) == -1
+    assert lib.tq_hbm_stream(A, 4096 + 16, None, 0, A, 0, 0, None) == -1
+    assert lib.tq_hbm_stream(A, 8192, None, 2048, A, 0, 0, None) == -1      # writes without dst
+    assert lib.tq_hbm_stream(A, 8192, A, 3000, A, 0, 0, None) == -1         # ratio not 1, 2 or 4
+    assert lib.tq_hbm_stream(A, 8192, A, 8192 // 8, A, 0, 0, None) == -1    # ratio 8
+    assert lib.tq_hbm_stream(A, 8192, A, 2048, None, 0, 0, None) == -1   # no sink
+    assert lib.tq_hbm_stream(A, 8192, A, 2048, ctypes.c_void_p((1 << 40) + 2), 0, 0, None) == -1
+    assert lib.tq_hbm_stream(A, 8192, A, 2048, A, 6, 0, None) == -1      # waves per CU not a multiple of 4
+    assert lib.tq_hbm_stream(A, 8192, A, 2048, A, 68, 0, None) == -1     # above 64
+    assert lib.tq_hbm_stream(A, 8192, A, 2048, A, -4, 0, None) == -1
+    assert lib.tq_hbm_stream(A, 8192, A, 2048, A, 0, 3, None) == -1              # unknown flag bit
+    assert lib.tq_hbm_stream(A, 8192, A, 2048, A, 0, 12 << 8, None) == -1        # 12 loads in flight
+    assert lib.tq_hbm_stream(A, 8192, None, 0, A, 0, 16 << 8, None) == -1        # not a multiple of 16 KiB
     assert "tq_hbm_stream" in tq.last_error()
 
 

@@ -952,3 +952,34 @@ def test_decode_step_single_launch_slot_spanning_and_graph_replay():
         torch.cuda.synchronize()
     del g
     ctx.close()
+
+
+@pytest.mark.parametrize("d,m", [(128, 64), (256, 128)])
+def test_attend_values_near_fp32_max_over_many_partials(d, m):
+    """Value norms of 2^120 with uniform attention (zero queries) over 8000
+    tokens: each attend partial's share of the output is near 2^124 and the
+    merge adds tens of them, which overflowed fp32 while partials were stored
+    scaled back to the norms' magnitude.  With the exponent stored beside the
+    accumulator the output (a mean of 2^120-sized vectors) is finite and
+    matches the oracle on the GPU's codes; on both the single-kernel and the
+    general attend."""
+    n_seq, T, G = 1, 8000, 4
+    K = np.stack([synth.kv_slot(240, s, s, T, d, dtype=np.float32) for s in range(n_seq)])
+    V = (np.stack([synth.kv_slot(241, s, s, T, d, dtype=np.float32) for s in range(n_seq)]).astype(np.float64)
+         / np.linalg.norm(np.stack([synth.kv_slot(241, s, s, T, d, dtype=np.float32) for s in range(n_seq)])
+                          .astype(np.float64), axis=-1, keepdims=True) * 2.0 ** 120).astype(np.float32)
+    Q = np.zeros((n_seq, G, d), dtype=np.float32)
+    Q[0, 1] = synth.kv_slot(242, 0, 0, 1, d, dtype=np.float32)[0] * 1e-3  # nearly uniform
+    _say("values near fp32 max", (d, m, T))
+    ctx, R, S = make_ctx(d, m, 3, 3)
+    cache = tq.KVCache(ctx, n_seq, 8064)
+    cache.append_key(torch.from_numpy(K).cuda(), 0)
+    cache.append_value(torch.from_numpy(V).cuda(), 0)
+    out = cache.attend(torch.from_numpy(Q).cuda(), T).cpu().numpy()
+    assert np.isfinite(out).all(), "attention output overflowed"
+    _, c = O.lloyd_max_codebook(d, 3)
+    gk = P.unpack_gpu_keys(cache, d, m, 3, T)
+    gv = P.unpack_gpu_values(cache, d, 3, T)
+    ref = O.attend(Q, R, S, c, gk, gv)
+    _say({"attend_rel": P.check_attend(out, ref), "max_abs": float(np.abs(out).max())})
+    ctx.close()
