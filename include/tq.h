@@ -28,7 +28,7 @@
  *    library allocates device memory only in tq_create (its own copies of R,
  *    S and the codebooks: d^2 + m d fp32 plus the same again as fp16 halves;
  *    for shapes on the general path, see below, also a scratch buffer of
- *    32768 rows x (4 d + 8 + d/32) bytes, 128 MB at d = 1024) and frees it
+ *    32768 rows x (4 d + 8 + 4 ceil(d/128)) bytes, 128 MB at d = 1024) and frees it
  *    in tq_destroy.
  *  - Calls that take a stream enqueue work on it and return at once; they
  *    are ordered with other work on that stream.  stream == NULL means the
@@ -41,7 +41,7 @@
  *    or one context per stream).
  *  - Shapes.  head_dim 128 with proj_dim 64 or 128 runs single-kernel
  *    compress and attention paths; every other valid shape (head_dim a
- *    multiple of 128 up to 1024, proj_dim a multiple of 64 up to 512) runs
+ *    multiple of 64 up to 1024, proj_dim a multiple of 32 up to 512) runs
  *    the general path: tiled rotation / projection kernels for the appends,
  *    a chunked score kernel, and an attend that materialises the scores in
  *    the workspace and merges per-range softmax partials.  0-bit keys are
@@ -80,9 +80,9 @@ typedef enum { TQ_F16 = 1, TQ_F32 = 2 } tq_dtype;
 
 typedef struct tq_ctx tq_ctx;
 
-/* Static shape of a compressed cache.  head_dim d: multiple of 128 up to
- * 1024.  proj_dim m: multiple of 64 up to 512 (default d/2,
- * nav.superapi.store 算法细节 / proj_dim 选择).  value_bits in 1..4 and
+/* Static shape of a compressed cache.  head_dim d: multiple of 64 in
+ * [64, 1024].  proj_dim m: multiple of 32 in [32, 512] (default d/2, so
+ * 64 -> 32 and 128 -> 64: nav.superapi.store 算法细节 / proj_dim 选择).  value_bits in 1..4 and
  * key_bits in 0..4 (the pages use 2-4; 1 is the 1-bit limit).  key_bits 0
  * is the bit budget of (b - 1)-bit codes plus QJL signs at b = 1: one cell
  * whose centroid is 0, so a key keeps only its m sign bits of S R k/||k||
@@ -114,11 +114,16 @@ typedef struct {
  *    b=3: s<6: word s/2, bits 3(s%2)..; s=6: code bits 0-1 at bits 6-7 of
  *         word 0, bit 2 at bit 6 of word 2; s=7: bits 0-1 at bits 6-7 of
  *         word 1, bit 2 at bit 7 of word 2   (bit numbers within the byte).
- *  Key record: 4 d/128 code groups (q, g), q = 0..3, g = 0..d/128 - 1, at
- *    words b (q d/128 + g) .. + b - 1; group (q, g), slot s, byte lane i is
- *    the code of rotated coordinate 128 g + 16 s + 4 q + i.
- *    Then m/32 sign words: projection coordinate 16 t + 4 q + i is bit
- *    16 (q%2) + 4 (t%4) + i of word 2 (t/4) + q/2 (1 = projection >= 0).
+ *  Key record, n = floor(d/128) full chunks: 4 n code groups (q, g),
+ *    q = 0..3, g = 0..n - 1, at words b (q n + g) .. + b - 1; group (q, g),
+ *    slot s, byte lane i is the code of rotated coordinate
+ *    128 g + 16 s + 4 q + i.  If d % 128 == 64, two more groups p = 0, 1
+ *    (the half chunk) at words b (4 n + p) .. + b - 1; slot s, byte lane i
+ *    of group p is coordinate 128 n + 16 (s%4) + 4 (p + 2 (s/4)) + i.
+ *    Then m/32 sign words, n' = floor(m/64): projection coordinate
+ *    16 t + 4 q + i < 64 n' is bit 16 (q%2) + 4 (t%4) + i of word
+ *    2 (t/4) + q/2; if m % 64 == 32, projection 64 n' + j is bit j of word
+ *    2 n' (1 = projection >= 0).
  *    Then fp32 ||k||, then fp32 gamma.  Size 4 (b d/32 + m/32 + 2) bytes
  *    (b = 0: no code groups, the sign words start the record).
  *  Value block (128 tokens): for w = 0..b-1, q = 0..3, coordinate c =

@@ -46,10 +46,10 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // TQ_EINVAL or TQ_EUNSUPPORTED.
 static int check_config(const tq_config* c) {
   if (!c) return fail(TQ_EINVAL, "config is NULL");
-  if (c->head_dim < 128 || c->head_dim > 1024 || c->head_dim % 128)
-    return fail(TQ_EINVAL, "head_dim %d: need a multiple of 128 in [128, 1024]", c->head_dim);
-  if (c->proj_dim < 64 || c->proj_dim > 512 || c->proj_dim % 64)
-    return fail(TQ_EINVAL, "proj_dim %d: need a multiple of 64 in [64, 512]", c->proj_dim);
+  if (c->head_dim < 64 || c->head_dim > 1024 || c->head_dim % 64)
+    return fail(TQ_EINVAL, "head_dim %d: need a multiple of 64 in [64, 1024]", c->head_dim);
+  if (c->proj_dim < 32 || c->proj_dim > 512 || c->proj_dim % 32)
+    return fail(TQ_EINVAL, "proj_dim %d: need a multiple of 32 in [32, 512]", c->proj_dim);
   if (c->key_bits < 0 || c->key_bits > 4 || c->value_bits < 1 || c->value_bits > 4)
     return fail(TQ_EINVAL, "key_bits %d / value_bits %d: need 0..4 / 1..4", c->key_bits, c->value_bits);
   return TQ_OK;
@@ -64,6 +64,11 @@ static bool fast_keys(const tq_config& c) { return fast_shape(c) && c.key_bits >
 static bool fast_values(const tq_config& c) { return c.head_dim == kD; }
 static bool fast_attn(const tq_config& c, int G) { return fast_shape(c) && G <= 16; }
 constexpr int64_t kScratchRows = 32768;  // general-path rows per launch
+
+// 128-coordinate chunks and 64-projection tiles of the general path (the
+// last one possibly half full).
+static int key_chunks(int d) { return (d + 127) / 128; }
+static int sign_blocks(int m) { return (m + 63) / 64; }
 
 static size_t key_rec_bytes(const tq_config& c) { return 4u * (c.key_bits * c.head_dim / 32 + c.proj_dim / 32 + 2); }
 static size_t val_blk_bytes(const tq_config& c) { return 4u * (4 * c.value_bits * c.head_dim + kBlockTokens); }
@@ -147,8 +152,12 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   // residual in another order and takes a second copy of S: column
   // 16 kk + 8 g + e holds coordinate 16 kk + 8 (e/4) + 4 g + e%4 (bits 2 and
   // 3 of the coordinate swapped).
+  // The images have d rounded up to 128 rows (R) and m rounded up to 64 rows
+  // (S), the extra rows zero: the general-path kernels work on whole 128-
+  // coordinate chunks and 64-projection tiles, and a zero row gives a zero
+  // coordinate that is never stored.
   const int ld = d + 8;
-  const size_t r_img = (size_t)d * ld, s_img = (size_t)m * ld;
+  const size_t r_img = (size_t)(128 * key_chunks(d)) * ld, s_img = (size_t)(64 * sign_blocks(m)) * ld;
   std::vector<uint16_t> rh(r_img, 0), rl(r_img, 0), sh(s_img, 0), sl(s_img, 0), sh32(s_img, 0), sl32(s_img, 0);
   std::vector<float> r32((size_t)d * d), s32((size_t)m * d);
   auto split = [](double x, uint16_t& hi, uint16_t& lo) {
@@ -199,7 +208,7 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t off_nrm = up(end_imgs), off_rh = off_nrm + up((size_t)srows * 8);  // (norm, exponent) pairs
   const size_t off_rlo = off_rh + up((size_t)srows * d * 2), off_g2 = off_rlo + up((size_t)srows * d * 2);
-  const size_t total = off_g2 + up((size_t)srows * (d / 128) * 4);
+  const size_t total = off_g2 + up((size_t)srows * key_chunks(d) * 4);
   if (hipMalloc(&c->dev_mem, total) != hipSuccess) {
     delete c;
     return fail(TQ_ENOMEM, "tq_create: hipMalloc of %zu bytes failed", total);

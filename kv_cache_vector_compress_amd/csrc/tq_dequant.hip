@@ -14,6 +14,7 @@
 // intermediate overflows or denormals at any norm).  Any head_dim of the
 // layout.
 #include "tq_device.h"
+#include "tq_layout.h"
 
 namespace tq {
 
@@ -31,7 +32,7 @@ struct DequantArgs {
 };
 
 // Code of slot s, byte lane i of a code group whose b words sit `stride`
-// words apart (record layout v1).
+// words apart (record layout v2).
 __device__ __forceinline__ int group_code(const uint32_t* w, int stride, int b, int s, int i) {
   const int sh = 8 * i;
   auto byte = [&](int k) { return (w[k * stride] >> sh) & 0xFFu; };
@@ -72,8 +73,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
     if (tl < nt) {
       int code;
       if (a.keys) {
-        const int g = j >> 7, jj = j & 127;
-        code = group_code(key_rec(tl) + a.bits * (((jj >> 2) & 3) * (a.d >> 7) + g), 1, a.bits, jj >> 4, jj & 3);
+        int word, sl;
+        key_code_place(j, a.d, a.bits, word, sl);
+        code = group_code(key_rec(tl) + word, 1, a.bits, sl, j & 3);
       } else {
         const int tau = (int)((a.pos + tl0 + tl) % kBlockTokens);
         code = group_code(val_blk(tl) + ((tau >> 2) & 3) * a.d + j, 4 * a.d, a.bits, tau >> 4, tau & 3);

@@ -1,5 +1,5 @@
 // Device-side helpers for the gfx950 kernels: matrix-core operand types, the
-// code-word layout (record layout v1) and codebook lookups.
+// code-word layout (record layout v2) and codebook lookups.
 //
 // Operand layouts of v_mfma_f32_16x16x32_f16 (wave64), used everywhere:
 //   A (16 x 32): lane l holds row l%16, k = 8*(l/16) .. +7   (8 fp16)

@@ -1,6 +1,6 @@
-// General-shape path on gfx950: head_dim d a multiple of 128 up to 1024,
-// proj_dim m a multiple of 64 up to 512 (the d = 128, m <= 128 shapes have
-// their own single-kernel path in tq_compress.hip / tq_attention.hip).
+// General-shape path on gfx950: head_dim d a multiple of 64 up to 1024,
+// proj_dim m a multiple of 32 up to 512 (the d = 128, m in {64, 128} shapes
+// have their own single-kernel path in tq_compress.hip / tq_attention.hip).
 //
 // The computation is the same as on the fast path (nav.superapi.store
 // "turboquant-pytorch", 主要能力 / 算法细节; atskills.one Stage 1 / Stage 2):
@@ -10,8 +10,12 @@
 //   scores: est = ||k|| (<R q, c[idx]> + gamma sqrt(pi/2)/m <S R q, 2s - 1>)
 // with the same split-fp16 arithmetic (R, S scaled by 2^8 and split into fp16
 // hi + lo; fp16 inputs exact, fp32 inputs split after a power-of-two scale)
-// and the same record layout, which is defined for any d multiple of 128 and
-// m multiple of 64.  What changes is the blocking: R (up to 4 MB as hi/lo
+// and the same record layout (a d of 128 n + 64 ends in a half chunk and an
+// m of 64 n' + 32 in a half sign block, tq_layout.h).  The kernels work on
+// whole 128-coordinate chunks and 64-projection tiles: the R and S images
+// carry zero rows up to those sizes, and the coordinates and projections
+// past d and m are computed as zeros and never stored or summed.  What
+// changes is the blocking: R (up to 4 MB as hi/lo
 // fp16) no longer fits in LDS, so the rotation and the projection are tiled
 // GEMMs that stream 32-column slices of R and S through LDS, and the key
 // residual goes through a scratch buffer between the two.
@@ -28,6 +32,7 @@
 #include <algorithm>
 
 #include "tq_device.h"
+#include "tq_layout.h"
 #include "tq_prep.h"
 
 namespace tq {
@@ -265,8 +270,12 @@ __global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
 #pragma unroll
     for (int w = 0; w < B; ++w) cw[w] = 0u;
     float g2 = 0.f;
+    // a half chunk (the last 64 coordinates of d = 128 n + 64) keeps slots
+    // 0..3: its rotated coordinates 16 s + 4 q + i with s >= 4 lie past d
+    const int n_kb2 = min(4, (a.d - 128 * u) / 32);
 #pragma unroll
     for (int kb2 = 0; kb2 < 4; ++kb2) {
+      if (kb2 >= n_kb2) break;
       u4 rhi, rlo;
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
@@ -287,11 +296,23 @@ __global__ __launch_bounds__(256) void gen_keys_rotate(const GenArgs a) {
     }
     g2 += shfl_xor(g2, 16);
     g2 += shfl_xor(g2, 32);
+    const int n_full = key_full_chunks(a.d);
+    const bool half = u >= n_full;  // (uniform over the workgroup)
+    if (half) {
+      // lane groups q and q + 2 share code group q % 2: q + 2 takes slots
+      // 4..7, and the two halves are merged across lanes l and l ^ 32
+      if (q >= 2) lift_half<B>(cw);
+#pragma unroll
+      for (int w = 0; w < B; ++w) cw[w] |= (uint32_t)__shfl_xor((int)cw[w], 32, 64);
+    }
     if (valid) {
       const int64_t slot = row[j] / a.n_sub, t = row[j] - slot * a.n_sub;
       uint32_t* rp = a.out + (slot * a.capacity + a.pos + a.tok_off + t) * a.rec_words;
+      if (!half || q < 2) {
+        const int w0 = key_group_word(q, u, n_full, B);
 #pragma unroll
-      for (int w = 0; w < B; ++w) rp[(q * a.n_oct + u) * B + w] = cw[w];
+        for (int w = 0; w < B; ++w) rp[w0 + w] = cw[w];
+      }
       if (q == 0) a.g2p[row[j] * a.n_oct + u] = g2;
       if (q == 0 && u == 0) rp[a.rec_words - 2] = __float_as_uint(n[j]);
     }
@@ -310,7 +331,7 @@ __global__ __launch_bounds__(256) void gen_keys_project(const GenArgs a, int bit
   const int64_t rows = (int64_t)a.n_seq * a.n_sub;
   int64_t rtile;
   int u;  // 64-projection chunk
-  xcd_tile_chunk(blockIdx.x, (rows + 63) / 64, a.m / 64, rtile, u);
+  xcd_tile_chunk(blockIdx.x, (rows + 63) / 64, sign_blocks(a.m), rtile, u);
   const int64_t row = rtile * 64 + wave * 16 + r16;
   const int64_t rr = row < rows ? row : rows - 1;
   f4 z[4];
@@ -349,11 +370,22 @@ __global__ __launch_bounds__(256) void gen_keys_project(const GenArgs a, int bit
     __syncthreads();
   }
   const uint32_t bits16 = sign_bits16(z[0], z[1], z[2], z[3]);
+  // A half block (the last 32 projections of m = 64 n' + 32) is one word
+  // holding projection 64 u + j at bit j: lane group q holds j = 16 p + 4 q + i
+  // at bit 4 p + i (p = 0, 1), and the four lane groups' parts are merged.
+  const bool half_blk = 64 * u + 64 > a.m;  // (uniform over the workgroup)
+  uint32_t hw = 0u;
+  if (half_blk) {
+    hw = ((bits16 & 0xFu) << (4 * q)) | (((bits16 >> 4) & 0xFu) << (16 + 4 * q));
+    hw |= (uint32_t)__shfl_xor((int)hw, 16, 64);
+    hw |= (uint32_t)__shfl_xor((int)hw, 32, 64);
+  }
   if (row < rows) {
     const int64_t slot = row / a.n_sub, t = row - slot * a.n_sub;
     uint32_t* rp = a.out + (slot * a.capacity + a.pos + a.tok_off + t) * a.rec_words;
     const int sw0 = bits * a.d / 32;
-    ((uint16_t*)(rp + sw0 + 2 * u + (q >> 1)))[q & 1] = (uint16_t)bits16;
+    if (!half_blk) ((uint16_t*)(rp + sw0 + 2 * u + (q >> 1)))[q & 1] = (uint16_t)bits16;
+    else if (q == 0) rp[sw0 + 2 * u] = hw;
     if (u == 0 && q == 1) {
       float g = 0.f;
       for (int c = 0; c < a.n_oct; ++c) g += a.g2p[row * a.n_oct + c];
@@ -476,6 +508,7 @@ __global__ __launch_bounds__(256) void gen_values(const GenArgs a) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int c = 128 * u + 16 * (2 * wave + t) + r16;
+    if (128 * u + 16 * (2 * wave + t) >= a.d) break;  // past a half chunk (wave-uniform)
 #pragma unroll
     for (int w = 0; w < B; ++w) {
       uint32_t* wp = vb + (size_t)(w * 4 + q) * a.d + c;
@@ -652,10 +685,11 @@ __global__ __launch_bounds__(256) void gen_scores(const GenScoreArgs a) {
   for (int g = 0; g < HG; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
   // 0-bit keys have the single centroid 0: no MSE term
   if constexpr (B > 0) {
-    for (int c = 0; c < a.n_oct; ++c) {
+    const int n_full = key_full_chunks(a.d);
+    for (int c = 0; c < n_full; ++c) {
       uint32_t cw[B];
 #pragma unroll
-      for (int w = 0; w < B; ++w) cw[w] = rp[(q * a.n_oct + c) * B + w];
+      for (int w = 0; w < B; ++w) cw[w] = rp[(q * n_full + c) * B + w];
       const h8 A0 = decode_pair<B, 0>(cw, tlo, thi), A1 = decode_pair<B, 2>(cw, tlo, thi);
       const h8 A2 = decode_pair<B, 4>(cw, tlo, thi), A3 = decode_pair<B, 6>(cw, tlo, thi);
 #pragma unroll
@@ -667,6 +701,25 @@ __global__ __launch_bounds__(256) void gen_scores(const GenScoreArgs a) {
         acc[g] = mfma(A3, *(const h8*)(wg + 3 * 64 * 8), acc[g]);
       }
     }
+    if (a.d % 128) {  // the half chunk: this lane group's slots 0..3 (two K blocks)
+      uint32_t cw[B];
+      const int w0 = key_group_word(q, n_full, n_full, B);
+#pragma unroll
+      for (int w = 0; w < B; ++w) cw[w] = rp[w0 + w];
+      uint32_t cl[B];
+#pragma unroll
+      for (int w = 0; w < B; ++w) cl[w] = cw[w];
+      lower_half<B>(cl);
+#pragma unroll
+      for (int w = 0; w < B; ++w) cw[w] = q >= 2 ? cl[w] : cw[w];
+      const h8 A0 = decode_pair<B, 0>(cw, tlo, thi), A1 = decode_pair<B, 2>(cw, tlo, thi);
+#pragma unroll
+      for (int g = 0; g < HG; ++g) {
+        const uint16_t* wg = wq + ((int64_t)g * KBT + 4 * n_full) * 64 * 8;
+        acc[g] = mfma(A0, *(const h8*)(wg), acc[g]);
+        acc[g] = mfma(A1, *(const h8*)(wg + 64 * 8), acc[g]);
+      }
+    }
   }
   const float gamma = __uint_as_float(rp[a.rec_words - 1]);
   const _Float16 gk = (_Float16)(gamma * a.kappa);
@@ -674,11 +727,15 @@ __global__ __launch_bounds__(256) void gen_scores(const GenScoreArgs a) {
   const int sh0 = 15 - 8 * (q & 1);
   const int sw0 = B * a.d / 32;
   for (int kbp = 0; kbp < a.m / 32; ++kbp) {
-    const uint32_t w = ~rp[sw0 + 2 * (kbp / 2) + (q >> 1)];
+    // a half sign block (the last one of m = 64 n' + 32) is one word in
+    // projection order: lane group q takes bits 4 q + e and 16 + 4 q + e
+    const bool hb = 32 * kbp + 64 > a.m && (kbp % 2) == 0;
+    const uint32_t w = ~rp[sw0 + 2 * (kbp / 2) + (hb ? 0 : (q >> 1))];
+    const int sh1 = hb ? 15 - 4 * q : sh0 - 4 * (kbp % 2);
     u4 v;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t sh = w << (sh0 - 4 * (kbp % 2) - e);  // bits p, p+16 -> 15, 31
+      const uint32_t sh = w << (sh1 - e);  // bits p, p+16 -> 15, 31
       v[e] = (sh & 0x80008000u) | (gk2 & 0x7FFF7FFFu);
     }
     const h8 A = as_h8(v);
@@ -762,10 +819,13 @@ __global__ __launch_bounds__(256) void gen_attend_kernel(const GenAttendArgs a) 
     const int tok0 = blk * kBlockTokens;
     const uint32_t* vb = vbase + (int64_t)blk * a.block_words;
     uint32_t vw[8][BV];
+    // (a half chunk has coordinate tiles 0..3 only; the others decode zero
+    // words into products that are never read)
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-      for (int w = 0; w < BV; ++w) vw[nt][w] = vb[(w * 4 + q) * a.d + 128 * u + 16 * nt + r16];
+      for (int w = 0; w < BV; ++w)
+        vw[nt][w] = 128 * u + 16 * nt < a.d ? vb[(w * 4 + q) * a.d + 128 * u + 16 * nt + r16] : 0u;
     const float2 vn2 = *(const float2*)(vb + 4 * BV * a.d + 2 * lane);
     const float x0 = tok0 + 2 * lane < n_tok ? vn2.x : 0.f, x1 = tok0 + 2 * lane + 1 < n_tok ? vn2.y : 0.f;
     float bmax = fmaxf(x0, x1);
@@ -933,7 +993,7 @@ static GenArgs gen_args(const GenMats& g, const CodebookDev& cb, int bits, const
   a.n_seq = s.n_seq;
   a.d = d;
   a.m = m;
-  a.n_oct = d / 128;
+  a.n_oct = key_chunks(d);
   a.ld = g.ld;
   a.rec_words = bits * d / 32 + m / 32 + 2;
   a.block_words = 4 * bits * d + kBlockTokens;
@@ -969,7 +1029,7 @@ int launch_general_keys(const GenMats& g, const CodebookDev& cb, int bits, int d
     const GenArgs a = gen_args(g, cb, bits, s, d, m, off, n_sub, key_records);
     const int64_t rows = n_sub * s.n_seq;
     hipLaunchKernelGGL(gen_row_norms, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, s.dtype);
-    const dim3 g1((unsigned)((rows + 127) / 128 * (d / 128))), g2((unsigned)((rows + 63) / 64 * (m / 64)));
+    const dim3 g1((unsigned)((rows + 127) / 128 * key_chunks(d))), g2((unsigned)((rows + 63) / 64 * sign_blocks(m)));
     const bool f32 = s.dtype == TQ_F32;
 #define TQ_GK(B)                                                                              \
   if (bits == B) {                                                                            \
@@ -1000,7 +1060,7 @@ int launch_general_values(const GenMats& g, const CodebookDev& cb, int bits, int
     const int64_t rows = n_sub * s.n_seq;
     hipLaunchKernelGGL(gen_row_norms, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, s.dtype);
     const int64_t nblk = (p + n_sub - 1) / kBlockTokens - p / kBlockTokens + 1;
-    const dim3 g1((unsigned)(nblk * s.n_seq * (d / 128)));
+    const dim3 g1((unsigned)(nblk * s.n_seq * key_chunks(d)));
     const bool f32 = s.dtype == TQ_F32;
 #define TQ_GV(B)                                                                   \
   if (bits == B) {                                                                 \
@@ -1039,7 +1099,7 @@ int launch_gen_prep(const Matrices& mats, int d, int m, const AttnShape& s, int 
   p.n_seq = s.n_seq;
   p.d = d;
   p.m = m;
-  p.n_oct = d / 128;
+  p.n_oct = key_chunks(d);
   p.r32 = mats.r32;
   p.s32 = mats.s32;
   p.wq = wq;
@@ -1077,7 +1137,7 @@ int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbit
   a.HG = HG;
   a.d = d;
   a.m = m;
-  a.n_oct = d / 128;
+  a.n_oct = key_chunks(d);
   a.rec_words = kbits * d / 32 + m / 32 + 2;
   a.tiles_per_slot = (s.n_tokens + 15) / 16;
   a.kappa = (float)(1.2533141373155002512 / m);  // sqrt(pi/2) / m
@@ -1106,7 +1166,7 @@ GenAttnPlan general_attend_plan(int d, int m, int n_seq, int G, int64_t n_tokens
   const int HG = head_groups_bucket(G);
   const size_t q_bytes = (size_t)n_seq * HG * (d / 32 + m / 32) * 64 * 8 * 2;
   const size_t qn_bytes = (size_t)n_seq * HG * 16 * 4;
-  const int n_oct = d / 128;
+  const int n_oct = key_chunks(d);
   const int64_t nblk = (n_tokens + kBlockTokens - 1) / kBlockTokens;
   int64_t R = (4096 + (int64_t)n_seq * n_oct - 1) / ((int64_t)n_seq * n_oct);  // ~16 waves per CU in all
   if (R > nblk) R = nblk;
@@ -1138,13 +1198,13 @@ int launch_general_attend(const Matrices& mats, const CodebookDev& cbk, int kbit
   a.n_seq = s.n_seq;
   a.G = s.G;
   a.d = d;
-  a.n_oct = d / 128;
+  a.n_oct = key_chunks(d);
   a.block_words = 4 * vbits * d + kBlockTokens;
   a.blocks_per_wave = p.blocks_per_wave;
   a.ranges = p.ranges;
   a.scale2 = scale * 1.4426950408889634f;
   for (int i = 0; i < 4; ++i) { a.vtlo[i] = cbv.tlo[i]; a.vthi[i] = cbv.thi[i]; }
-  const int64_t waves = (int64_t)s.n_seq * p.ranges * (d / 128);
+  const int64_t waves = (int64_t)s.n_seq * p.ranges * key_chunks(d);
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   if (vbits == 1) hipLaunchKernelGGL(gen_attend_kernel<1>, grid, block, 0, st, a);
   if (vbits == 2) hipLaunchKernelGGL(gen_attend_kernel<2>, grid, block, 0, st, a);
@@ -1157,7 +1217,7 @@ int launch_general_attend(const Matrices& mats, const CodebookDev& cbk, int kbit
   c.n_seq = s.n_seq;
   c.G = s.G;
   c.d = d;
-  c.n_oct = d / 128;
+  c.n_oct = key_chunks(d);
   c.ranges = p.ranges;
   hipLaunchKernelGGL(gen_combine, dim3((unsigned)(s.n_seq * s.G)), dim3(256), sizeof(float) * (d + p.ranges), st, c);
   return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;

@@ -89,8 +89,8 @@ int launch_attend(const Matrices& mats, const CodebookDev& cbk, int kbits, const
                   float* out, void* ws, const AttnPlan& p, void* stream);
 int compress_device_init();
 
-// General-shape path (tq_general.hip): head_dim a multiple of 128 up to 1024,
-// proj_dim a multiple of 64 up to 512.
+// General-shape path (tq_general.hip): head_dim a multiple of 64 up to 1024,
+// proj_dim a multiple of 32 up to 512.
 constexpr int kMaxGeneralHeads = 512;   // query heads per KV slot for general scores
 struct GenMats {
   Matrices mats;         // R / S images (row stride ld halves) and fp32 copies

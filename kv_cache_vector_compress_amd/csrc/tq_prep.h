@@ -124,13 +124,17 @@ __device__ __forceinline__ void gen_prep_block(const GenPrepArgs& a, int bid) {
       // sign part: k slot 2e+half <-> bit p + 16 half of sign word 2 (kbp/2) + qq/2,
       // p = 8 (qq%2) + 4 (kbp%2) + e, which holds projection coordinate 16 t + 4 qs + p%4
       // with qs = 2 (qq/2) + half, t = 4 (kbp/2) + p/4
+      // (a half sign block, the last of m = 64 n' + 32, is one word in
+      // projection order: k slot 2e+half <-> projection 64 n' + 16 half + 4 qq + e)
       const int kbp = kb - a.d / 32;
+      const bool hb = 32 * kbp + 64 > a.m && (kbp % 2) == 0;
       for (int e = 0; e < 4; ++e)
         for (int half = 0; half < 2; ++half) {
           const int p = 8 * (qq % 2) + 4 * (kbp % 2) + e;
           const int qsg = 2 * (qq / 2) + half;
           const int t = 4 * (kbp / 2) + p / 4;
-          v[2 * e + half] = (_Float16)(pp[16 * t + 4 * qsg + p % 4] * inv);
+          const int j = hb ? 32 * kbp + 16 * half + 4 * qq + e : 16 * t + 4 * qsg + p % 4;
+          v[2 * e + half] = (_Float16)(pp[j] * inv);
         }
     }
     const int l = 16 * qq + h16;

@@ -161,7 +161,7 @@ __device__ __forceinline__ int cell(float u, const float (&beta)[15]) {
 }
 
 // The part of code `v` (slot s, byte lane i) that word w of a b-bit code
-// group holds, in place (record layout v1).
+// group holds, in place (record layout v2).
 __device__ __forceinline__ uint32_t code_bits(int b, int w, int s, int i, uint32_t v) {
   uint32_t f = 0;
   switch (b) {
@@ -220,18 +220,22 @@ __device__ __forceinline__ void small_keys_block(const SmallArgs& a, int64_t bid
   matvec(a.s32, a.m, a.d, rs, zs);
   __syncthreads();
   uint32_t* rec = a.out + ((int64_t)slot * a.capacity + a.pos + t) * a.rec_words;
-  const int n_oct = a.d / 128, code_words = a.bits * a.d / 32, sign_words = a.m / 32;
+  const int n_full = a.d / 128, code_words = a.bits * a.d / 32, sign_words = a.m / 32;
   // code words: thread (word, slot s) places the 4 codes of slot s, the 8
   // slot threads of a word (consecutive lanes) are OR-ed by lane exchange;
-  // group (q, g) at words b (q n_oct + g) ..; slot s, byte lane i is
-  // coordinate 128 g + 16 s + 4 q + i
+  // full group (q, g) at words b (q n_full + g) ..; slot s, byte lane i is
+  // coordinate 128 g + 16 s + 4 q + i.  A half chunk (d = 128 n + 64) has
+  // groups p = 0, 1 at words b (4 n + p) ..; slot s, byte lane i is
+  // coordinate 128 n + 16 (s % 4) + 4 (p + 2 (s / 4)) + i.
   for (int e0 = 0; e0 < code_words * 8; e0 += blockDim.x) {
     const int e = e0 + threadIdx.x, wi = e >> 3, sl = e & 7;
     uint32_t part = 0u;
     if (wi < code_words) {
-      const int grp = wi / a.bits, w = wi % a.bits, q = grp / n_oct, g = grp % n_oct;
+      const int grp = wi / a.bits, w = wi % a.bits;
+      const int base = grp < 4 * n_full ? 128 * (grp % n_full) + 16 * sl + 4 * (grp / n_full)
+                                        : 128 * n_full + 16 * (sl % 4) + 4 * (grp - 4 * n_full + 2 * (sl / 4));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part |= code_bits(a.bits, w, sl, i, (uint32_t)is[128 * g + 16 * sl + 4 * q + i]);
+      for (int i = 0; i < 4; ++i) part |= code_bits(a.bits, w, sl, i, (uint32_t)is[base + i]);
     }
     part |= __shfl_xor(part, 1, 64);
     part |= __shfl_xor(part, 2, 64);
@@ -239,13 +243,15 @@ __device__ __forceinline__ void small_keys_block(const SmallArgs& a, int64_t bid
     if (wi < code_words && sl == 0) rec[wi] = part;
   }
   // sign words: thread (word, bit) and a ballot per 32 bits.  Projection
-  // 16 tt + 4 q + i is bit 16 (q%2) + 4 (tt%4) + i of word 2 (tt/4) + q/2.
+  // 16 tt + 4 q + i is bit 16 (q%2) + 4 (tt%4) + i of word 2 (tt/4) + q/2;
+  // a half block (m = 64 n' + 32) is word 2 n' with projection 64 n' + j at
+  // bit j.
   for (int e0 = 0; e0 < sign_words * 32; e0 += blockDim.x) {
     const int e = e0 + threadIdx.x, sw = e >> 5, bit = e & 31;
     bool on = false;
     if (sw < sign_words) {
       const int h = bit >> 4, tt = 4 * (sw >> 1) + ((bit >> 2) & 3), q = 2 * (sw & 1) + h, i = bit & 3;
-      on = zs[16 * tt + 4 * q + i] >= 0.f;
+      on = zs[(sw & 1) == 0 && 32 * sw + 64 > a.m ? 32 * sw + bit : 16 * tt + 4 * q + i] >= 0.f;
     }
     const uint64_t mask = __ballot(on);
     if (sw < sign_words && bit == 0) rec[code_words + sw] = (uint32_t)(mask >> (threadIdx.x & 32));
@@ -367,7 +373,7 @@ inline DecodeArgs decode_args(const Matrices& mats, const CodebookDev& cbk, int 
   a.p.n_seq = qs.n_seq;
   a.p.d = d;
   a.p.m = m;
-  a.p.n_oct = d / 128;
+  a.p.n_oct = (d + 127) / 128;
   a.p.r32 = mats.r32;
   a.p.s32 = mats.s32;
   a.p.wq = wq;

@@ -20,6 +20,7 @@
 #include <algorithm>
 
 #include "tq_device.h"
+#include "tq_layout.h"
 
 namespace tq {
 
@@ -57,19 +58,22 @@ __device__ __forceinline__ void tk_insert(float* ls, int32_t* li, int k, float s
 }
 
 // A lane's words of one 16-token tile: code group (B words) of each of the
-// NOCT coordinate chunks, 8 sign words (m/64 of them used), ||k|| and gamma.
+// NOCT full coordinate chunks and, with HALF, of the half chunk (already
+// moved to slots 0..3), 8 sign words (one per 64 projections, a half block
+// counting as one), ||k|| and gamma.
 // Every word is loaded unconditionally (unused sign words read neighbouring
 // record bytes, or zeros past the range's records), so the loads of the next
 // tile can be counted exactly and stay in flight while the current tile is
 // processed.
-template <int B, int NOCT>
+template <int B, int NOCT, bool HALF>
 struct TkRec {
-  uint32_t cw[NOCT][B > 0 ? B : 1];  // (0-bit keys: no code words, unused)
+  static constexpr int NC = NOCT + (HALF ? 1 : 0);
+  uint32_t cw[NC > 0 ? NC : 1][B > 0 ? B : 1];  // (0-bit keys: no code words, unused)
   uint32_t sw[8];
   float n, g;
 };
 
-template <int B, int NOCT>
+template <int B, int NOCT, bool HALF>
 __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
   extern __shared__ __align__(16) uint16_t tsm[];
   const int KBT = a.d / 32 + a.m / 32;
@@ -121,12 +125,12 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(a.rec + ((int64_t)slot * a.capacity + r0) * a.rec_words), (short)0,
       (int)((uint32_t)(r1 - r0) * (uint32_t)a.rec_words * 4u), 0x00020000);
-  auto load_tile = [&](TkRec<B, NOCT>& r, int64_t tile) {
+  auto load_tile = [&](TkRec<B, NOCT, HALF>& r, int64_t tile) {
     const int row = min((int)(tile * 16) + r16, n_tok - 1);
     const uint32_t ro = (uint32_t)(row - (int)r0) * (uint32_t)a.rec_words * 4u;
 #pragma unroll
-    for (int c = 0; c < (B > 0 ? NOCT : 0); ++c) {
-      const uint32_t oc = ro + 4u * (uint32_t)((q * NOCT + c) * B);
+    for (int c = 0; c < (B > 0 ? TkRec<B, NOCT, HALF>::NC : 0); ++c) {
+      const uint32_t oc = ro + 4u * (uint32_t)(B > 0 ? key_group_word(q, c, NOCT, B) : 0);
       if constexpr (B == 0) {
         (void)oc;
       } else if constexpr (B == 1) {
@@ -142,15 +146,25 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
         r.cw[c][0] = v[0]; r.cw[c][1] = v[1]; r.cw[c][2] = v[2]; r.cw[c][3] = v[3];
       }
     }
+    if constexpr (HALF && B > 0) {  // the half chunk's group, at slots 0..3 for every lane group
+      uint32_t cl[B];
+#pragma unroll
+      for (int w = 0; w < B; ++w) cl[w] = r.cw[NOCT][w];
+      lower_half<B>(cl);
+#pragma unroll
+      for (int w = 0; w < B; ++w) r.cw[NOCT][w] = q >= 2 ? cl[w] : r.cw[NOCT][w];
+    }
+    // (a half sign block is a single word shared by the four lane groups)
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      r.sw[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, ro + 4u * (uint32_t)(sw0 + 2 * j + (q >> 1)), 0, 0);
+      r.sw[j] = __builtin_amdgcn_raw_buffer_load_b32(
+          rs, ro + 4u * (uint32_t)(sw0 + 2 * j + (2 * j + 2 <= a.m / 32 ? (q >> 1) : 0)), 0, 0);
     const auto ng2 = __builtin_amdgcn_raw_buffer_load_b64(rs, ro + 4u * (uint32_t)(a.rec_words - 2), 0, 0);
     r.n = __uint_as_float(ng2[0]);
     r.g = __uint_as_float(ng2[1]);
   };
 
-  auto step = [&](const TkRec<B, NOCT>& r, int64_t tile) {
+  auto step = [&](const TkRec<B, NOCT, HALF>& r, int64_t tile) {
     f4 acc[2];
     acc[0] = acc[1] = f4{0.f, 0.f, 0.f, 0.f};
     // per chunk: the 4 query operands of each group are read from LDS first,
@@ -178,28 +192,47 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
         acc[0] = mfma(A3, qa[0][3], acc[0]);
         acc[1] = mfma(A3, qa[1][3], acc[1]);
       }
+      if constexpr (HALF) {  // the half chunk: K blocks 4 NOCT and 4 NOCT + 1
+        h8 qa[2][2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          qa[0][kk] = *(const h8*)(ql + (4 * NOCT + kk) * 512);
+          qa[1][kk] = *(const h8*)(ql + (KBT + 4 * NOCT + kk) * 512);
+        }
+        const h8 A0 = decode_pair<B, 0>(r.cw[NOCT], tlo, thi), A1 = decode_pair<B, 2>(r.cw[NOCT], tlo, thi);
+        acc[0] = mfma(A0, qa[0][0], acc[0]);
+        acc[1] = mfma(A0, qa[1][0], acc[1]);
+        acc[0] = mfma(A1, qa[0][1], acc[0]);
+        acc[1] = mfma(A1, qa[1][1], acc[1]);
+      }
     }
     const _Float16 gk = (_Float16)(r.g * a.kappa);
     const uint32_t gk2 = (uint32_t)__builtin_bit_cast(uint16_t, gk) * 0x00010001u;
     const int n_kbp = a.m / 32;
     const uint16_t* qs = ql + (a.d / 32) * 512;
 #pragma unroll
-    for (int k2 = 0; k2 < 16; k2 += 2) {  // the 2 sign steps of one sign word at a time (m % 64 == 0)
+    for (int k2 = 0; k2 < 16; k2 += 2) {  // the 2 sign steps of one sign word pair at a time
       if (k2 >= n_kbp) break;
+      // a half block (the last of m = 64 n' + 32) has one step, its word in
+      // projection order: lane group q takes bits 4 q + e and 16 + 4 q + e
+      const bool hb = k2 + 1 >= n_kbp;
       h8 qa[2][2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        qa[0][kk] = *(const h8*)(qs + (k2 + kk) * 512);
-        qa[1][kk] = *(const h8*)(qs + (KBT + k2 + kk) * 512);
+        const int kq = hb ? k2 : k2 + kk;
+        qa[0][kk] = *(const h8*)(qs + kq * 512);
+        qa[1][kk] = *(const h8*)(qs + (KBT + kq) * 512);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        if (kk == 1 && hb) break;
         const int kbp = k2 + kk;
         const uint32_t w = ~r.sw[kbp / 2];
+        const int sh1 = hb ? 15 - 4 * q : sh0 - 4 * (kbp % 2);
         u4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t sh = w << (sh0 - 4 * (kbp % 2) - e);  // bits p, p+16 -> 15, 31
+          const uint32_t sh = w << (sh1 - e);  // bits p, p+16 -> 15, 31
           v[e] = (sh & 0x80008000u) | (gk2 & 0x7FFF7FFFu);
         }
         const h8 A = as_h8(v);
@@ -242,7 +275,7 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
     }
   };
 
-  TkRec<B, NOCT> ra, rb;
+  TkRec<B, NOCT, HALF> ra, rb;
   int64_t tile = t_lo + wave;
   if (tile < t_hi) load_tile(ra, tile);
   for (; tile < t_hi; tile += 2 * kTkWaves) {
@@ -366,12 +399,15 @@ static size_t topk_lds(int d, int m, int k) {
 int topk_device_init() {
   int rc = 0;
   const int lds = (int)topk_lds(1024, 512, kTopkMax);
-#define TQ_TK_ATTR(B, N) \
-  rc |= hipFuncSetAttribute((const void*)topk_scores_kernel<B, N>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+#define TQ_TK_ATTR(B, N, H) \
+  rc |= hipFuncSetAttribute((const void*)topk_scores_kernel<B, N, H>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 #define TQ_TK_ATTR_B(B) \
-  TQ_TK_ATTR(B, 1) TQ_TK_ATTR(B, 2) TQ_TK_ATTR(B, 3) TQ_TK_ATTR(B, 4) TQ_TK_ATTR(B, 5) TQ_TK_ATTR(B, 6) \
-  TQ_TK_ATTR(B, 7) TQ_TK_ATTR(B, 8)
+  TQ_TK_ATTR(B, 1, false) TQ_TK_ATTR(B, 2, false) TQ_TK_ATTR(B, 3, false) TQ_TK_ATTR(B, 4, false)            \
+  TQ_TK_ATTR(B, 5, false) TQ_TK_ATTR(B, 6, false) TQ_TK_ATTR(B, 7, false) TQ_TK_ATTR(B, 8, false)            \
+  TQ_TK_ATTR(B, 0, true) TQ_TK_ATTR(B, 1, true) TQ_TK_ATTR(B, 2, true) TQ_TK_ATTR(B, 3, true)                \
+  TQ_TK_ATTR(B, 4, true) TQ_TK_ATTR(B, 5, true) TQ_TK_ATTR(B, 6, true) TQ_TK_ATTR(B, 7, true)
   TQ_TK_ATTR_B(1) TQ_TK_ATTR_B(2) TQ_TK_ATTR_B(3) TQ_TK_ATTR_B(4)
+  TQ_TK_ATTR(0, 1, false)
 #undef TQ_TK_ATTR_B
 #undef TQ_TK_ATTR
   return rc == hipSuccess ? 0 : -1;
@@ -401,7 +437,7 @@ int launch_topk(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, 
   a.HG = p.HG;
   a.d = d;
   a.m = m;
-  a.n_oct = d / 128;
+  a.n_oct = key_chunks(d);
   a.rec_words = kbits * d / 32 + m / 32 + 2;
   a.k = k;
   a.n_qblk = p.n_qblk;
@@ -412,14 +448,20 @@ int launch_topk(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, 
   const dim3 grid((unsigned)((int64_t)s.n_seq * p.n_ranges * p.n_qblk)), block(64 * kTkWaves);
   const size_t lds = topk_lds(d, m, k);
   bool launched = false;
-#define TQ_TK(B, N) \
-  if (!launched && kbits == B && a.n_oct == N) { \
-    hipLaunchKernelGGL((topk_scores_kernel<B, N>), grid, block, lds, st, a); \
+  const int n_full = d / 128;
+  const bool half = d % 128 != 0;
+#define TQ_TK(B, N, H) \
+  if (!launched && kbits == B && n_full == N && half == H) { \
+    hipLaunchKernelGGL((topk_scores_kernel<B, N, H>), grid, block, lds, st, a); \
     launched = true; \
   }
-#define TQ_TK_B(B) TQ_TK(B, 1) TQ_TK(B, 2) TQ_TK(B, 3) TQ_TK(B, 4) TQ_TK(B, 5) TQ_TK(B, 6) TQ_TK(B, 7) TQ_TK(B, 8)
+#define TQ_TK_B(B)                                                                                   \
+  TQ_TK(B, 1, false) TQ_TK(B, 2, false) TQ_TK(B, 3, false) TQ_TK(B, 4, false) TQ_TK(B, 5, false)     \
+  TQ_TK(B, 6, false) TQ_TK(B, 7, false) TQ_TK(B, 8, false) TQ_TK(B, 0, true) TQ_TK(B, 1, true)       \
+  TQ_TK(B, 2, true) TQ_TK(B, 3, true) TQ_TK(B, 4, true) TQ_TK(B, 5, true) TQ_TK(B, 6, true)          \
+  TQ_TK(B, 7, true)
   if (kbits == 0) {  // 0-bit keys: no code chunks, one instance for every head_dim
-    hipLaunchKernelGGL((topk_scores_kernel<0, 1>), grid, block, lds, st, a);
+    hipLaunchKernelGGL((topk_scores_kernel<0, 1, false>), grid, block, lds, st, a);
     launched = true;
   }
   TQ_TK_B(1) TQ_TK_B(2) TQ_TK_B(3) TQ_TK_B(4)

@@ -321,10 +321,17 @@ def attend_online(Q, R, S, centroids, keys: dict, values: dict, scale: float | N
 #          s = 7: bits 0,1 in word 1 bits 6,7 and bit 2 in word 2 bit 7
 #   (bit positions are within byte lane i, i.e. add 8 i).
 #
-# Key record (one per token), words:
-#   [codes: for q in 0..3, for g in 0..d/128-1, b words of (q, g)]
-#   [signs: m/32 words; proj coordinate 16 t + 4 q + i sits in word
-#           2 (t // 4) + q // 2 at bit 16 (q % 2) + 4 (t % 4) + i]
+# Key record (one per token), words, with n = d // 128 full octet columns
+# and n' = m // 64 full sign pairs:
+#   [codes: for q in 0..3, for g in 0..n-1, b words of (q, g)]
+#   [if d % 128 == 64, the half column g = n (tiles t = 8 n .. 8 n + 3):
+#    b words for p = 0, then b words for p = 1; group p holds lane group p
+#    at slots 0..3 and lane group p + 2 at slots 4..7, slot s <-> tile
+#    8 n + s % 4 of lane group p + 2 (s // 4)]
+#   [signs: proj coordinate 16 t + 4 q + i with t < 4 n' sits in word
+#           2 (t // 4) + q // 2 at bit 16 (q % 2) + 4 (t % 4) + i; if
+#           m % 64 == 32, projection 64 n' + j (j < 32) sits in word 2 n'
+#           at bit j]
 #   [fp32 ||k||] [fp32 gamma]
 #
 # Value block (128 tokens of one slot), words:
@@ -387,29 +394,45 @@ def value_block_words(d: int, bits: int) -> int:
 
 
 def pack_keys(idx, signs, norm, gamma, bits: int) -> np.ndarray:
-    """Encode compressed keys (..., T, d) into records (..., T, words) uint32."""
+    """Encode compressed keys (..., T, d) into records (..., T, words) uint32
+    (d a multiple of 64, m a multiple of 32)."""
     idx = np.asarray(idx)
     lead, d = idx.shape[:-1], idx.shape[-1]
     m = signs.shape[-1]
-    n_oct = d // 128
+    if d % 64 or m % 32:
+        raise ValueError("head_dim must be a multiple of 64 and proj_dim of 32")
+    n_full, half = d // 128, d % 128 == 64
     rec = np.zeros(lead + (key_record_words(d, m, bits),), dtype=np.uint32)
     if bits == 0 and np.any(idx != 0):
         raise ValueError("0-bit keys have the single cell 0")
-    # coordinate 16 t + 4 q + i  ->  (q, g = t // 8, s = t % 8, i)
-    cq = idx.reshape(lead + (n_oct, 8, 4, 4))          # (..., g, s, q, i)
-    for q in range(4 if bits else 0):
-        for g in range(n_oct):
-            words = np.zeros(lead + (bits,), dtype=np.uint32)
-            _put_codes(words, cq[..., g, :, q, :], bits)
-            base = (q * n_oct + g) * bits
-            rec[..., base:base + bits] = words
+    if bits:
+        # coordinate 16 t + 4 q + i  ->  (q, g = t // 8, s = t % 8, i)
+        cq = idx[..., :128 * n_full].reshape(lead + (n_full, 8, 4, 4))          # (..., g, s, q, i)
+        for q in range(4):
+            for g in range(n_full):
+                words = np.zeros(lead + (bits,), dtype=np.uint32)
+                _put_codes(words, cq[..., g, :, q, :], bits)
+                base = (q * n_full + g) * bits
+                rec[..., base:base + bits] = words
+        if half:
+            hq = idx[..., 128 * n_full:].reshape(lead + (4, 4, 4))             # (..., t, q, i)
+            for p in range(2):
+                slots = np.concatenate([hq[..., :, p, :], hq[..., :, p + 2, :]], axis=-2)  # (..., 8, 4)
+                words = np.zeros(lead + (bits,), dtype=np.uint32)
+                _put_codes(words, slots, bits)
+                base = (4 * n_full + p) * bits
+                rec[..., base:base + bits] = words
     sw0 = bits * d // 32
-    sg = np.asarray(signs).astype(np.uint32).reshape(lead + (m // 16, 4, 4))   # (..., t, q, i)
-    for t in range(m // 16):
+    nf = m // 64
+    sg = np.asarray(signs).astype(np.uint32)
+    sgf = sg[..., :64 * nf].reshape(lead + (4 * nf, 4, 4))                      # (..., t, q, i)
+    for t in range(4 * nf):
         for q in range(4):
             for i in range(4):
                 w = sw0 + 2 * (t // 4) + q // 2
-                rec[..., w] |= sg[..., t, q, i] << np.uint32(16 * (q % 2) + 4 * (t % 4) + i)
+                rec[..., w] |= sgf[..., t, q, i] << np.uint32(16 * (q % 2) + 4 * (t % 4) + i)
+    for j in range(m - 64 * nf):
+        rec[..., sw0 + 2 * nf] |= sg[..., 64 * nf + j] << np.uint32(j)
     rec[..., -2] = np.asarray(norm, dtype=np.float32).view(np.uint32)
     rec[..., -1] = np.asarray(gamma, dtype=np.float32).view(np.uint32)
     return rec
@@ -418,20 +441,36 @@ def pack_keys(idx, signs, norm, gamma, bits: int) -> np.ndarray:
 def unpack_keys(rec, d: int, m: int, bits: int) -> dict:
     rec = np.asarray(rec, dtype=np.uint32)
     lead = rec.shape[:-1]
-    n_oct = d // 128
-    idx = np.zeros(lead + (n_oct, 8, 4, 4), dtype=np.int64)
-    for q in range(4 if bits else 0):   # 0-bit records carry no codes
-        for g in range(n_oct):
-            base = (q * n_oct + g) * bits
-            idx[..., g, :, q, :] = _get_codes(rec[..., base:base + bits], bits)
+    n_full, half = d // 128, d % 128 == 64
+    idx = np.zeros(lead + (d,), dtype=np.int64)
+    if bits:   # 0-bit records carry no codes
+        full = np.zeros(lead + (n_full, 8, 4, 4), dtype=np.int64)
+        for q in range(4):
+            for g in range(n_full):
+                base = (q * n_full + g) * bits
+                full[..., g, :, q, :] = _get_codes(rec[..., base:base + bits], bits)
+        idx[..., :128 * n_full] = full.reshape(lead + (128 * n_full,))
+        if half:
+            hq = np.zeros(lead + (4, 4, 4), dtype=np.int64)                       # (..., t, q, i)
+            for p in range(2):
+                base = (4 * n_full + p) * bits
+                slots = _get_codes(rec[..., base:base + bits], bits)               # (..., 8, 4)
+                hq[..., :, p, :] = slots[..., :4, :]
+                hq[..., :, p + 2, :] = slots[..., 4:, :]
+            idx[..., 128 * n_full:] = hq.reshape(lead + (64,))
     sw0 = bits * d // 32
-    signs = np.zeros(lead + (m // 16, 4, 4), dtype=np.uint8)
-    for t in range(m // 16):
+    nf = m // 64
+    signs = np.zeros(lead + (m,), dtype=np.uint8)
+    sgf = np.zeros(lead + (4 * nf, 4, 4), dtype=np.uint8)
+    for t in range(4 * nf):
         for q in range(4):
             for i in range(4):
                 w = sw0 + 2 * (t // 4) + q // 2
-                signs[..., t, q, i] = (rec[..., w] >> np.uint32(16 * (q % 2) + 4 * (t % 4) + i)) & 1
-    return dict(idx=idx.reshape(lead + (d,)), signs=signs.reshape(lead + (m,)),
+                sgf[..., t, q, i] = (rec[..., w] >> np.uint32(16 * (q % 2) + 4 * (t % 4) + i)) & 1
+    signs[..., :64 * nf] = sgf.reshape(lead + (64 * nf,))
+    for j in range(m - 64 * nf):
+        signs[..., 64 * nf + j] = (rec[..., sw0 + 2 * nf] >> np.uint32(j)) & 1
+    return dict(idx=idx, signs=signs,
                 norm=rec[..., -2].view(np.float32), gamma=rec[..., -1].view(np.float32))
 
 

@@ -77,9 +77,11 @@ def test_sizes_follow_record_layout(kb, vb, m):
     assert tq.workspace_bytes(cfg, 4, 4, 0) == 0
 
 
-@pytest.mark.parametrize("d,m,kb,vb", [(256, 128, 3, 3), (1024, 512, 4, 4), (128, 256, 2, 2), (512, 64, 1, 4)])
+@pytest.mark.parametrize("d,m,kb,vb", [(256, 128, 3, 3), (1024, 512, 4, 4), (128, 256, 2, 2), (512, 64, 1, 4),
+                                        (64, 32, 3, 3), (192, 96, 2, 4), (128, 32, 4, 1), (960, 480, 1, 2),
+                                        (64, 32, 0, 2)])
 def test_general_shape_sizes_follow_record_layout(d, m, kb, vb):
-    """head_dim a multiple of 128 up to 1024, proj_dim a multiple of 64 up to
+    """head_dim a multiple of 64 up to 1024, proj_dim a multiple of 32 up to
     512: the same record layout, sized from the oracle's word counts."""
     cfg = tq.Config(d, m, kb, vb)
     assert tq.key_record_bytes(cfg) == 4 * O.key_record_words(d, m, kb)
@@ -102,8 +104,8 @@ def test_3bit_record_is_64_bytes_and_block_is_52_bytes_per_token():
 @pytest.mark.parametrize("cfg,code", [
     ((100, 64, 3, 3), -1), ((128, 48, 3, 3), -1), ((128, 64, -1, 3), -1), ((128, 64, 3, 5), -1),
     ((128, 64, 3, 0), -1), ((128, 64, 5, 3), -1),
-    ((2048, 64, 3, 3), -1), ((1152, 64, 3, 3), -1), ((192, 64, 3, 3), -1), ((128, 576, 3, 3), -1),
-    ((128, 96, 3, 3), -1)])
+    ((2048, 64, 3, 3), -1), ((1152, 64, 3, 3), -1), ((96, 64, 3, 3), -1), ((128, 576, 3, 3), -1),
+    ((128, 80, 3, 3), -1), ((32, 32, 3, 3), -1), ((128, 16, 3, 3), -1), ((1088, 64, 3, 3), -1)])
 def test_create_rejects_configs_before_any_device_call(cfg, code):
     R = np.eye(cfg[0])
     S = np.ones((max(cfg[1], 1), cfg[0]))

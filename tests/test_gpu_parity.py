@@ -239,8 +239,10 @@ def test_long_context_full_size_sampled():
 
 
 # ---------------------------------------------------------------------------
-# general shapes: head_dim a multiple of 128 up to 1024, proj_dim a multiple
-# of 64 up to 512 (tiled rotation / projection kernels)
+# general shapes: head_dim a multiple of 64 up to 1024, proj_dim a multiple
+# of 32 up to 512 (tiled rotation / projection kernels; a head_dim of
+# 128 n + 64 ends in a half code chunk, a proj_dim of 64 n + 32 in a half
+# sign block)
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("d,m,kb,vb,dtype,G", [
@@ -249,6 +251,18 @@ def test_long_context_full_size_sampled():
     (512, 192, 1, 2, np.float32, 3),
     (384, 64, 4, 3, np.float16, 40),
     (1024, 512, 4, 4, np.float32, 16),
+    # head_dim 64 with its proj_dim 32 (d / 2), 2- to 4-bit codes, fp16 and fp32
+    (64, 32, 2, 2, np.float16, 4),
+    (64, 32, 2, 3, np.float32, 8),
+    (64, 32, 3, 3, np.float16, 8),
+    (64, 32, 3, 4, np.float32, 4),
+    (64, 32, 4, 4, np.float16, 16),
+    (64, 32, 4, 2, np.float32, 20),    # scores only (G > 16)
+    (64, 64, 1, 1, np.float16, 2),
+    (192, 96, 3, 3, np.float16, 5),    # a full and a half chunk, a full and a half sign block
+    (320, 160, 2, 4, np.float32, 12),
+    (128, 32, 3, 3, np.float16, 8),    # head_dim 128 with a single half sign block
+    (960, 480, 4, 1, np.float32, 3),
 ])
 def test_general_shapes_ragged_chunks(d, m, kb, vb, dtype, G):
     """Codes, signs, norms, gamma of keys and values, scores and (G <= 16)
@@ -376,6 +390,8 @@ def test_error_paths_leave_buffers_untouched():
     (128, 128, 4, 4, 160, [160], (0, 160)),
     (256, 128, 2, 3, 200, [200], (11, 170)),
     (1024, 512, 4, 4, 40, [40], (0, 40)),
+    (64, 32, 3, 2, 200, [129, 71], (3, 190)),
+    (192, 96, 4, 3, 160, [160], (0, 160)),
 ])
 def test_reconstruction_matches_oracle(d, m, kb, vb, T, chunks, rng):
     """tq_get_keys / tq_get_values (TurboQuantMSE.dequantize,
@@ -435,6 +451,10 @@ def _topk_reference(scores, k):
     (128, 64, 3, 1, 5, 4, 10),
     (128, 64, 0, 2, 3000, 40, 10),     # 0-bit keys: QJL signs only
     (1024, 512, 0, 1, 2500, 64, 10),
+    (64, 32, 3, 1, 1500, 20, 10),      # half chunk and half sign block
+    (64, 32, 2, 1, 700, 33, 4),
+    (192, 96, 4, 2, 900, 8, 5),
+    (64, 32, 0, 1, 900, 4, 3),
 ])
 def test_topk_matches_scores(d, m, b, n_seq, N, G, k):
     """tq_topk_scores: the k best tokens of each query (vector search over the
@@ -478,6 +498,8 @@ def test_topk_matches_scores(d, m, b, n_seq, N, G, k):
     (128, 128, 4, 2, np.float32),
     (256, 128, 2, 3, np.float16),
     (1024, 512, 1, 4, np.float32),
+    (64, 32, 3, 3, np.float16),
+    (192, 96, 4, 2, np.float32),
 ])
 def test_small_appends_decode_like(d, m, kb, vb, dtype):
     """Appends of 1..16 tokens (the decode-step path: fp32 vector arithmetic,
@@ -502,6 +524,7 @@ def test_small_appends_decode_like(d, m, kb, vb, dtype):
     (128, 64, 3, 4, np.float16, 11),   # 9 <= G <= 15: the attend instance with unused head columns
     (256, 128, 3, 3, np.float16, 4),   # not a single-kernel shape: the three calls in order
     (128, 64, 0, 3, np.float16, 8),    # 0-bit keys: fused appends and query preparation, like 1-4 bits
+    (64, 32, 3, 3, np.float16, 4),     # head_dim 64 / proj_dim 32: the three calls
 ])
 def test_decode_steps_match_oracle(d, m, kb, vb, dtype, G):
     """tq_decode_step after a prefill: each step appends 1..16 tokens (crossing
@@ -562,6 +585,8 @@ def test_decode_steps_match_oracle(d, m, kb, vb, dtype, G):
     (128, 128, 2, np.float32, 4),
     (256, 128, 4, np.float16, 20),   # scores only (G > 16)
     (1024, 512, 4, np.float32, 16),
+    (64, 32, 2, np.float16, 8),
+    (128, 32, 3, np.float32, 4),
 ])
 def test_zero_bit_keys(d, m, vb, dtype, G):
     """key_bits = 0: records of m sign bits of S R k/||k|| and the two norms
@@ -854,7 +879,8 @@ def test_scores_and_attend_at_maximum_capacity():
     ctx.close()
 
 
-@pytest.mark.parametrize("d,m,kb,vb", [(128, 64, 3, 3), (128, 128, 0, 2), (1024, 512, 4, 4), (256, 128, 2, 1)])
+@pytest.mark.parametrize("d,m,kb,vb", [(128, 64, 3, 3), (128, 128, 0, 2), (1024, 512, 4, 4), (256, 128, 2, 1),
+                                        (64, 32, 3, 2), (192, 96, 0, 4)])
 def test_context_size_queries(d, m, kb, vb):
     """tq_key_record_bytes / tq_value_record_bytes / tq_attend_workspace_bytes
     of a live context agree with the configuration's layout sizes."""

@@ -463,6 +463,50 @@ def test_pack_hand_written_bit_positions():
     assert nz(val_blk(127, 127, 4)) == {2 * 512 + 3 * 128 + 127: 0x80000000}  # s7 q3 i3, bit2 -> word 2 bit 7
 
 
+def test_pack_half_chunk_hand_written_bit_positions():
+    """P11b: head_dim 64 + 128 n and proj_dim 32 + 64 n' (a half code column
+    and a half sign word), single codes placed by hand from the layout
+    description: d = 192, m = 96, 3 bits, then d = 64, m = 32, 2 bits."""
+    def key_rec(d, m, b, coord=None, code=0, proj=None):
+        idx = np.zeros((1, d), dtype=np.int64)
+        if coord is not None:
+            idx[0, coord] = code
+        s = np.zeros((1, m), dtype=np.uint8)
+        if proj is not None:
+            s[0, proj] = 1
+        return O.pack_keys(idx, s, np.zeros(1, np.float32), np.zeros(1, np.float32), b)[0]
+
+    def nz(rec):
+        return {int(i): int(rec[i]) for i in np.nonzero(rec)[0]}
+
+    # d = 192, m = 96, b = 3: full groups words 0..11, half groups p = 0 at
+    # words 12..14 and p = 1 at 15..17, sign words 18, 19 (full) and 20 (half)
+    assert key_rec(192, 96, 3).shape == (3 * 6 + 3 + 2,)
+    assert nz(key_rec(192, 96, 3, 128, 5)) == {12: 0x5}               # t 0, q 0 -> p 0 slot 0
+    assert nz(key_rec(192, 96, 3, 132, 5)) == {15: 0x5}               # q 1 -> p 1 slot 0
+    assert nz(key_rec(192, 96, 3, 136, 5)) == {14: 0x5}               # q 2 -> p 0 slot 4: word 2 bits 0..2
+    assert nz(key_rec(192, 96, 3, 143, 6)) == {17: 0x06000000}        # q 3 i 3 -> p 1 slot 4, byte lane 3
+    assert nz(key_rec(192, 96, 3, 164, 7)) == {16: 0x7}               # t 2 q 1 -> p 1 slot 2: word 1
+    assert nz(key_rec(192, 96, 3, 185, 5)) == {13: 0x4000, 14: 0x8000}  # t 3 q 2 i 1 -> p 0 slot 7
+    assert nz(key_rec(192, 96, 3, 188, 3)) == {16: 0xC0}              # t 3 q 3 -> p 1 slot 7, low bits only
+    assert nz(key_rec(192, 96, 3, 127, 7)) == {10: 0xC0000000, 11: 0x80000000}  # full column unchanged
+    assert nz(key_rec(192, 96, 3, proj=63)) == {19: 0x80000000}       # full block: t 3 q 3 i 3
+    assert nz(key_rec(192, 96, 3, proj=64)) == {20: 0x1}              # half word: natural order
+    assert nz(key_rec(192, 96, 3, proj=95)) == {20: 0x80000000}
+    # d = 64, m = 32, b = 2: half groups at words 0..1 and 2..3, sign word 4
+    assert key_rec(64, 32, 2).shape == (7,)
+    assert nz(key_rec(64, 32, 2, 0, 3)) == {0: 0x3}
+    assert nz(key_rec(64, 32, 2, 8, 3)) == {1: 0x3}                   # q 2 -> slot 4: word 1
+    assert nz(key_rec(64, 32, 2, 22, 1)) == {2: 0x40000}              # t 1 q 1 i 2 -> p 1 slot 1, lane 2
+    assert nz(key_rec(64, 32, 2, 63, 2)) == {3: 0x80000000}           # t 3 q 3 i 3 -> p 1 slot 7
+    assert nz(key_rec(64, 32, 2, proj=0)) == {4: 0x1}
+    assert nz(key_rec(64, 32, 2, proj=31)) == {4: 0x80000000}
+    # 0-bit keys at m = 32: one sign word, then the norms
+    z = O.pack_keys(np.zeros((1, 64), np.int64), np.eye(32, dtype=np.uint8)[[9]], np.float32([2.0]),
+                    np.float32([1.0]), 0)[0]
+    assert nz(z) == {0: 0x200, 1: 0x40000000, 2: 0x3F800000}
+
+
 # ----------------------------------------------------------------- figures ---
 
 def test_memory_formula_reproduces_pages_figures():
