@@ -38,7 +38,9 @@
  *    concurrently with calls that use the same context.  Exception: on the
  *    general path the appends of one context share its scratch buffer, so
  *    its tq_append_key / tq_append_value calls must be ordered (one stream,
- *    or one context per stream).
+ *    or one context per stream); tq_append_key_ws / tq_append_value_ws take
+ *    the scratch from a caller-owned workspace instead and have no such
+ *    restriction.
  *  - Shapes.  head_dim 128 with proj_dim 64 or 128 runs single-kernel
  *    compress and attention paths; every other valid shape (head_dim a
  *    multiple of 64 up to 1024, proj_dim a multiple of 32 up to 512) runs
@@ -72,7 +74,8 @@ typedef enum {
   TQ_ENOCODEBOOK = -3,  /* no codebook loaded for the bits this call needs */
   TQ_ENOMEM = -4,       /* device allocation failed (tq_create only) */
   TQ_EDEVICE = -5,      /* a HIP call or kernel launch failed */
-  TQ_EUNSUPPORTED = -6, /* valid but not built (reserved; every valid shape is built) */
+  TQ_EUNSUPPORTED = -6, /* valid but not built (a bulk general-path append into more than 256
+                           slots through the context's scratch: see tq_append_key_ws) */
   TQ_EWORKSPACE = -7    /* workspace smaller than tq_attend_workspace_bytes / tq_workspace_bytes */
 } tq_status;
 
@@ -235,6 +238,29 @@ int tq_append_key(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_
  * block are preserved.  Same arguments and errors as tq_append_key. */
 int tq_append_value(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int32_t dtype,
                     int64_t pos, int64_t n_new, void* stream);
+
+/* The appends with a caller-owned device workspace in place of the
+ * context's scratch buffer (the same results, bit for bit), so that appends
+ * of one context may run on several streams at once: each concurrent call
+ * needs a workspace of its own.  Only general-path appends of more than 16
+ * tokens per slot use it (the tiled rotation / projection kernels keep the
+ * key residual and the row norms there between launches);
+ * tq_append_workspace_bytes gives its size, 0 when the append of n_new
+ * tokens into n_seq slots uses no workspace (then workspace may be NULL)
+ * or when an argument is invalid (the append itself reports which).  The
+ * size is at most that of the context's scratch for n_seq <= 256 (4 d + 8 +
+ * 4 ceil(d/128) bytes a row, 32768 rows), and n_seq x 128 rows beyond: with
+ * a workspace, general-path appends of any slot count are built, while the
+ * context's scratch serves bulk appends into at most 256 slots
+ * (tq_append_key / tq_append_value return TQ_EUNSUPPORTED beyond).
+ * workspace: device, 16-byte aligned, owned by the caller; it is free again
+ * once the call's work on `stream` has finished.  Extra error:
+ * TQ_EWORKSPACE if workspace_bytes < tq_append_workspace_bytes. */
+size_t tq_append_workspace_bytes(const tq_ctx* ctx, int32_t n_seq, int64_t n_new);
+int tq_append_key_ws(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_t dtype, int64_t pos,
+                     int64_t n_new, void* workspace, size_t workspace_bytes, void* stream);
+int tq_append_value_ws(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int32_t dtype, int64_t pos,
+                       int64_t n_new, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Asymmetric attention scores straight from the packed keys
  * (asymmetric_attention_scores / attention_scores, nav.superapi.store

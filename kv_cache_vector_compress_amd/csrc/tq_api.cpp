@@ -3,6 +3,7 @@
 // reach the device and never leave partial writes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -327,14 +328,40 @@ static int append_common(tq_ctx* ctx, const tq_cache_view* cache, const void* x,
   return TQ_OK;
 }
 
-int tq_append_key(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_t dtype, int64_t pos,
-                  int64_t n_new, void* stream) {
-  clear_error();
-  int rc = append_common(ctx, cache, k, dtype, pos, n_new, ctx ? ctx->cfg.key_bits : 1, "tq_append_key");
-  if (rc) return rc;
-  if (n_new == 0) return TQ_OK;
+// Whether a general-path append of n_new tokens per slot runs the tiled
+// kernels, which keep the row norms and the key residual in a scratch
+// buffer between launches (the context's, or a caller's workspace).
+static bool keys_use_scratch(const tq_config& c, int64_t n_new) {
+  return !fast_keys(c) && c.key_bits > 0 && n_new > kSmallAppend;
+}
+static bool values_use_scratch(const tq_config& c, int64_t n_new) {
+  return !fast_values(c) && n_new > kSmallAppend;
+}
+
+// A caller's workspace laid out as the context's scratch: rows of
+// (norm, exponent), key residual hi / lo and residual square sums per chunk,
+// for n_seq slots x sub tokens, sub = n_new rounded up to 128 tokens and
+// capped at the context's 32768 rows (at least 128 tokens a slot).
+static int64_t ws_rows(int32_t n_seq, int64_t n_new) {
+  int64_t cap = kScratchRows / n_seq;
+  cap -= cap % kBlockTokens;
+  if (cap < kBlockTokens) cap = kBlockTokens;
+  const int64_t sub = std::min<int64_t>((n_new + kBlockTokens - 1) / kBlockTokens * kBlockTokens, cap);
+  return (int64_t)n_seq * sub;
+}
+static size_t ws_layout(int d, int64_t rows, size_t off[4]) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  off[0] = 0;
+  off[1] = up((size_t)rows * 8);
+  off[2] = off[1] + up((size_t)rows * d * 2);
+  off[3] = off[2] + up((size_t)rows * d * 2);
+  return off[3] + up((size_t)rows * key_chunks(d) * 4);
+}
+
+static int append_key_impl(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_t dtype, int64_t pos,
+                           int64_t n_new, const GenMats* scratch, void* stream, const char* fn) {
   AppendShape s{k, dtype, n_new, pos, cache->capacity, cache->n_seq};
-  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_append_key: hipSetDevice failed");
+  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "%s: hipSetDevice failed", fn);
   // A decode step on the general path takes one launch of the small kernel
   // instead of the tiled norm / rotation / projection kernels (with head_dim
   // 128 the single matrix-core kernel is as quick for a few tokens).  0-bit
@@ -342,16 +369,68 @@ int tq_append_key(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_
   // head_dim 128 and proj_dim 64, and the small kernel otherwise.
   const tq_config& c = ctx->cfg;
   const bool zero_tiles = c.key_bits == 0 && c.head_dim == kD && c.proj_dim == 64 && dtype == TQ_F16;
+  int rc;
   if (fast_keys(c) || (zero_tiles && n_new > kSmallAppend))
     rc = launch_compress_keys(ctx->mats, ctx->cb[c.key_bits], c.key_bits, c.proj_dim, s, cache->key_records,
                               stream);
-  else if (n_new <= kSmallAppend || c.key_bits == 0)
+  else if (!keys_use_scratch(c, n_new))
     rc = launch_small_keys(ctx->mats, ctx->cb[c.key_bits], c.key_bits, c.head_dim, c.proj_dim, s,
                            cache->key_records, stream);
   else
-    rc = launch_general_keys(ctx->gen, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cfg.head_dim,
-                             ctx->cfg.proj_dim, s, cache->key_records, stream);
-  return rc ? fail(rc, "tq_append_key: launch failed (%d)", rc) : TQ_OK;
+    rc = launch_general_keys(*scratch, ctx->cb[c.key_bits], c.key_bits, c.head_dim, c.proj_dim, s,
+                             cache->key_records, stream);
+  if (rc == TQ_EUNSUPPORTED)
+    return fail(rc, "%s: a bulk append into %d slots needs more rows than the context's scratch holds "
+                    "(tq_append_key_ws takes a workspace of any size)", fn, cache->n_seq);
+  return rc ? fail(rc, "%s: launch failed (%d)", fn, rc) : TQ_OK;
+}
+
+static int append_value_impl(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int32_t dtype, int64_t pos,
+                             int64_t n_new, const GenMats* scratch, void* stream, const char* fn) {
+  AppendShape s{v, dtype, n_new, pos, cache->capacity, cache->n_seq};
+  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "%s: hipSetDevice failed", fn);
+  const tq_config& c = ctx->cfg;
+  int rc;
+  if (n_new <= kSmallAppend)  // a decode step: no tile set-up
+    rc = launch_small_values(ctx->mats, ctx->cb[c.value_bits], c.value_bits, c.head_dim, s, cache->value_blocks,
+                             stream);
+  else if (fast_values(c))
+    rc = launch_compress_values(ctx->mats, ctx->cb[c.value_bits], c.value_bits, s, cache->value_blocks, stream);
+  else
+    rc = launch_general_values(*scratch, ctx->cb[c.value_bits], c.value_bits, c.head_dim, s, cache->value_blocks,
+                               stream);
+  if (rc == TQ_EUNSUPPORTED)
+    return fail(rc, "%s: a bulk append into %d slots needs more rows than the context's scratch holds "
+                    "(tq_append_value_ws takes a workspace of any size)", fn, cache->n_seq);
+  return rc ? fail(rc, "%s: launch failed (%d)", fn, rc) : TQ_OK;
+}
+
+// The scratch view of a caller's workspace (checked against its size).
+static int ws_scratch(const tq_ctx* ctx, int32_t n_seq, int64_t n_new, void* ws, size_t ws_bytes, GenMats* g,
+                      const char* fn) {
+  *g = ctx->gen;
+  const int64_t rows = ws_rows(n_seq, n_new);
+  size_t off[4];
+  const size_t need = ws_layout(ctx->cfg.head_dim, rows, off);
+  if (!ws) return fail(TQ_EINVAL, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (!aligned16(ws)) return fail(TQ_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  char* b = (char*)ws;
+  g->nrm = (float*)(b + off[0]);
+  g->res_hi = (uint16_t*)(b + off[1]);
+  g->res_lo = (uint16_t*)(b + off[2]);
+  g->g2p = (float*)(b + off[3]);
+  g->scratch_rows = rows;
+  return TQ_OK;
+}
+
+int tq_append_key(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_t dtype, int64_t pos,
+                  int64_t n_new, void* stream) {
+  clear_error();
+  int rc = append_common(ctx, cache, k, dtype, pos, n_new, ctx ? ctx->cfg.key_bits : 1, "tq_append_key");
+  if (rc) return rc;
+  if (n_new == 0) return TQ_OK;
+  return append_key_impl(ctx, cache, k, dtype, pos, n_new, &ctx->gen, stream, "tq_append_key");
 }
 
 int tq_append_value(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int32_t dtype, int64_t pos,
@@ -360,18 +439,42 @@ int tq_append_value(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int3
   int rc = append_common(ctx, cache, v, dtype, pos, n_new, ctx ? ctx->cfg.value_bits : 1, "tq_append_value");
   if (rc) return rc;
   if (n_new == 0) return TQ_OK;
-  AppendShape s{v, dtype, n_new, pos, cache->capacity, cache->n_seq};
-  if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_append_value: hipSetDevice failed");
-  if (n_new <= kSmallAppend)  // a decode step: no tile set-up
-    rc = launch_small_values(ctx->mats, ctx->cb[ctx->cfg.value_bits], ctx->cfg.value_bits, ctx->cfg.head_dim, s,
-                             cache->value_blocks, stream);
-  else if (fast_values(ctx->cfg))
-    rc = launch_compress_values(ctx->mats, ctx->cb[ctx->cfg.value_bits], ctx->cfg.value_bits, s,
-                                cache->value_blocks, stream);
-  else
-    rc = launch_general_values(ctx->gen, ctx->cb[ctx->cfg.value_bits], ctx->cfg.value_bits, ctx->cfg.head_dim, s,
-                               cache->value_blocks, stream);
-  return rc ? fail(rc, "tq_append_value: launch failed (%d)", rc) : TQ_OK;
+  return append_value_impl(ctx, cache, v, dtype, pos, n_new, &ctx->gen, stream, "tq_append_value");
+}
+
+size_t tq_append_workspace_bytes(const tq_ctx* ctx, int32_t n_seq, int64_t n_new) {
+  if (!ctx || n_seq < 1 || n_new < 1) return 0;
+  if (!keys_use_scratch(ctx->cfg, n_new) && !values_use_scratch(ctx->cfg, n_new)) return 0;
+  size_t off[4];
+  return ws_layout(ctx->cfg.head_dim, ws_rows(n_seq, n_new), off);
+}
+
+int tq_append_key_ws(tq_ctx* ctx, const tq_cache_view* cache, const void* k, int32_t dtype, int64_t pos,
+                     int64_t n_new, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int rc = append_common(ctx, cache, k, dtype, pos, n_new, ctx ? ctx->cfg.key_bits : 1, "tq_append_key_ws");
+  if (rc) return rc;
+  if (n_new == 0) return TQ_OK;
+  GenMats g;
+  if (keys_use_scratch(ctx->cfg, n_new)) {
+    rc = ws_scratch(ctx, cache->n_seq, n_new, workspace, workspace_bytes, &g, "tq_append_key_ws");
+    if (rc) return rc;
+  }
+  return append_key_impl(ctx, cache, k, dtype, pos, n_new, &g, stream, "tq_append_key_ws");
+}
+
+int tq_append_value_ws(tq_ctx* ctx, const tq_cache_view* cache, const void* v, int32_t dtype, int64_t pos,
+                       int64_t n_new, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int rc = append_common(ctx, cache, v, dtype, pos, n_new, ctx ? ctx->cfg.value_bits : 1, "tq_append_value_ws");
+  if (rc) return rc;
+  if (n_new == 0) return TQ_OK;
+  GenMats g;
+  if (values_use_scratch(ctx->cfg, n_new)) {
+    rc = ws_scratch(ctx, cache->n_seq, n_new, workspace, workspace_bytes, &g, "tq_append_value_ws");
+    if (rc) return rc;
+  }
+  return append_value_impl(ctx, cache, v, dtype, pos, n_new, &g, stream, "tq_append_value_ws");
 }
 
 static int attn_common(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dtype, int32_t G,

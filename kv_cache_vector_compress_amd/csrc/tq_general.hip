@@ -1048,6 +1048,7 @@ int launch_general_values(const GenMats& g, const CodebookDev& cb, int bits, int
                           void* value_blocks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int64_t sub = gen_sub_tokens(g, s.n_seq);
+  if (sub * s.n_seq > g.scratch_rows) return TQ_EUNSUPPORTED;  // (the row norms live in the scratch)
   // launch boundaries at absolute multiples of sub (a multiple of 128): no
   // value block is touched by two launches
   int64_t off = 0;

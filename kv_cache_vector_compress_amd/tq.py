@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
         "tq_codebook_load": (ctypes.c_int, [P, I32, D, D]),
         "tq_append_key": (ctypes.c_int, [P, VIEW, P, I32, I64, I64, P]),
         "tq_append_value": (ctypes.c_int, [P, VIEW, P, I32, I64, I64, P]),
+        "tq_append_workspace_bytes": (SZ, [P, I32, I64]),
+        "tq_append_key_ws": (ctypes.c_int, [P, VIEW, P, I32, I64, I64, P, SZ, P]),
+        "tq_append_value_ws": (ctypes.c_int, [P, VIEW, P, I32, I64, I64, P, SZ, P]),
         "tq_attention_scores": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, P, P, SZ, P]),
         "tq_attend": (ctypes.c_int, [P, VIEW, P, I32, I32, I64, ctypes.c_float, P, P, SZ, P]),
         "tq_topk_workspace_bytes": (SZ, [CFG, I32, I32, I64, I32]),
@@ -201,6 +204,11 @@ class Context:
         """tq_attend_workspace_bytes: workspace of the score / attend calls."""
         return lib().tq_attend_workspace_bytes(self._h, n_seq, G, n_tokens)
 
+    def append_workspace_bytes(self, n_seq: int, n_new: int) -> int:
+        """tq_append_workspace_bytes: workspace of tq_append_key_ws /
+        tq_append_value_ws (0: the append uses none)."""
+        return lib().tq_append_workspace_bytes(self._h, n_seq, n_new)
+
     def codebook_load(self, bits: int, centroids: Optional[np.ndarray] = None,
                       boundaries: Optional[np.ndarray] = None) -> None:
         """Load a codebook; by default the library's own Lloyd-Max codebook."""
@@ -239,7 +247,8 @@ class KVCache:
         self.key_records = torch.zeros(kb // 4, dtype=torch.int32, device=device)
         self.value_blocks = torch.zeros(vb // 4, dtype=torch.int32, device=device)
         self.view = CacheView(self.key_records.data_ptr(), self.value_blocks.data_ptr(), capacity, n_seq)
-        self._ws = {}  # one workspace per stream: calls on different streams never share one
+        self._ws = {}   # one attention workspace per stream: calls on different streams never share one
+        self._aws = {}  # the same for the appends' workspace (general-path bulk appends)
 
     def workspace(self, G: int, n_tokens: int, stream=None):
         """The attention workspace of the given stream (torch's current
@@ -277,14 +286,47 @@ class KVCache:
             raise ValueError(f"{name} is on {out.device}, the cache on {self.key_records.device}")
         return out
 
+    def append_workspace(self, n_new: int, stream=None):
+        """The appends' workspace of the given stream, grown to
+        tq_append_workspace_bytes, or None when the append uses none."""
+        torch = _torch()
+        need = self.ctx.append_workspace_bytes(self.n_seq, n_new)
+        if need == 0:
+            return None
+        key = _stream_ptr(stream).value
+        ws = self._aws.get(key)
+        if ws is None or ws.numel() < need:
+            ws = self._aws[key] = torch.empty(need, dtype=torch.uint8, device=self.key_records.device)
+        return ws
+
     # hot path ---------------------------------------------------------------
+    # The appends go through tq_append_key_ws / tq_append_value_ws with a
+    # workspace per stream, so that appends on different streams never share
+    # the context's scratch.
     def append_key(self, k, pos: int, stream=None) -> None:
         """k: (n_seq, n_new, d) fp16/fp32 device tensor."""
+        n_new = self._rows(k, "k")
+        ws = self.append_workspace(n_new, stream)
+        _check(lib().tq_append_key_ws(self.ctx.handle, ctypes.byref(self.view), _dev(k, "k"), _dtype_code(k),
+                                      pos, n_new, ctypes.c_void_p(ws.data_ptr() if ws is not None else None),
+                                      ws.numel() if ws is not None else 0, _stream_ptr(stream)))
+
+    def append_value(self, v, pos: int, stream=None) -> None:
+        n_new = self._rows(v, "v")
+        ws = self.append_workspace(n_new, stream)
+        _check(lib().tq_append_value_ws(self.ctx.handle, ctypes.byref(self.view), _dev(v, "v"), _dtype_code(v),
+                                        pos, n_new, ctypes.c_void_p(ws.data_ptr() if ws is not None else None),
+                                        ws.numel() if ws is not None else 0, _stream_ptr(stream)))
+
+    def append_key_ctx_scratch(self, k, pos: int, stream=None) -> None:
+        """tq_append_key: the same append with the context's scratch buffer
+        (calls of one context must then be ordered)."""
         n_new = self._rows(k, "k")
         _check(lib().tq_append_key(self.ctx.handle, ctypes.byref(self.view), _dev(k, "k"), _dtype_code(k),
                                    pos, n_new, _stream_ptr(stream)))
 
-    def append_value(self, v, pos: int, stream=None) -> None:
+    def append_value_ctx_scratch(self, v, pos: int, stream=None) -> None:
+        """tq_append_value with the context's scratch buffer."""
         n_new = self._rows(v, "v")
         _check(lib().tq_append_value(self.ctx.handle, ctypes.byref(self.view), _dev(v, "v"), _dtype_code(v),
                                      pos, n_new, _stream_ptr(stream)))

@@ -134,6 +134,11 @@ def test_hot_path_entry_points_reject_null_context():
     view = tq.CacheView(16, 16, 128, 1)
     assert lib.tq_append_key(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 0, 1, None) == -1
     assert lib.tq_append_value(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 0, 1, None) == -1
+    assert lib.tq_append_key_ws(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 0, 1, ctypes.c_void_p(16),
+                                1 << 20, None) == -1
+    assert lib.tq_append_value_ws(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 0, 1, ctypes.c_void_p(16),
+                                  1 << 20, None) == -1
+    assert lib.tq_append_workspace_bytes(None, 4, 1000) == 0
     assert lib.tq_attention_scores(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 4, 1,
                                    ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 20, None) == -1
     assert lib.tq_attend(None, ctypes.byref(view), ctypes.c_void_p(16), 1, 4, 1, 0.0,
