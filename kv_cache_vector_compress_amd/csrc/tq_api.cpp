@@ -1,7 +1,7 @@
 // C ABI of libtq.so: argument checking, context set-up and launch dispatch.
 // Every argument is checked on the host before any HIP call, so errors never
 // reach the device and never leave partial writes.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cmath>
