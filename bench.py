@@ -65,7 +65,7 @@ def algorithmic_bytes(w):
 
 # Sources the long-context step's kernels are built from (the counter record
 # in profiles/ is valid only for these exact files).
-STEP_SOURCES = ("tq_attention.hip", "tq_compress.hip", "tq_device.h", "tq_internal.h")
+STEP_SOURCES = ("tq_attend.h", "tq_attention.hip", "tq_compress.hip", "tq_device.h", "tq_internal.h")
 
 
 def kernel_source_hash() -> str:

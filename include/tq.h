@@ -318,15 +318,17 @@ int tq_attend_noalloc(tq_ctx* ctx, const tq_cache_view* cache, const void* q, in
  * for tq_attend with n_tokens = pos + n_new (workspace >=
  * tq_attend_workspace_bytes(ctx, n_seq, G, pos + n_new)).  On the
  * single-kernel shapes (head_dim 128, proj_dim 64 or 128, G <= 16) with
- * n_new <= 16 (and at most 4096 attention partials per slot, waves per slot
- * / 4 + 2 times G) the whole step is one kernel launch: appends, query
- * preparation, attention and the final merge, its workgroups synchronised
- * through flags and a count in the workspace (each tagged with a value
- * unique to the launch, so the workspace needs no clearing; a replayed
- * graph of the call works too).  A wait inside that launch is bounded: in
- * the pathological case of inputs that never become ready (about a second)
- * the output is NaN and a status word in the workspace is set.  Otherwise
- * the three calls run in order.  Calls that overlap on one workspace race.
+ * n_new <= 16 (and at most 4096 partials per slot: attention workgroups +
+ * 1, times G) the whole step is one kernel launch in which no workgroup
+ * waits for another: attention workgroups over the tokens before pos (each
+ * preparing the queries itself), one workgroup per slot that appends the
+ * new tokens and forms their share of the softmax, and the merge, done by
+ * the workgroup that completes the slot's arrival count at the start of the
+ * workspace (a tagged word that the step sets up itself, so the workspace
+ * needs no clearing; a replayed graph of the call works too).  The new
+ * tokens' scores are taken in fp32, the others' as tq_attend does, so the
+ * output equals the three calls' up to rounding.  Otherwise the three calls
+ * run in order.  Calls that overlap on one workspace race.
  * Every argument is checked before anything is launched.  Errors: TQ_EINVAL
  * (including n_new < 1), TQ_ECAPACITY, TQ_ENOCODEBOOK, TQ_EWORKSPACE,
  * TQ_EDEVICE. */

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
-SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_compress.hip", "tq_attention.hip", "tq_general.hip",
+SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_compress.hip", "tq_attention.hip", "tq_step.hip", "tq_general.hip",
            "tq_dequant.hip", "tq_topk.hip", "tq_small.hip", "tq_stream.hip"]
 ARCH = "gfx950"
 FLAGS = [
@@ -37,7 +37,8 @@ def _hipcc() -> str:
 # Per-file extra flags.  The attention kernels keep their matrix-core
 # accumulators in ordinary VGPRs (they are rescaled by VALU code), so ask for
 # the VGPR form of MFMA there instead of round-tripping through AGPRs.
-EXTRA = {"tq_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"tq_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "tq_step.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

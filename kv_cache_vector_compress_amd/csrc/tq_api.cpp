@@ -171,6 +171,25 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
       split(R[(size_t)i * d + k], rh[(size_t)i * ld + k], rl[(size_t)i * ld + k]);
       r32[(size_t)i * d + k] = (float)R[(size_t)i * d + k];
     }
+  // The fused decode step (head_dim 128 with proj_dim 64 or 128) prepares
+  // its queries and rotates its partials back on the matrix cores: R^T and
+  // P = S R (the query's projection p = S R q in one product) as the same
+  // scaled hi / lo fp16 images, P formed in fp64.
+  const bool step_imgs = fast_shape(*cfg);
+  const size_t t_img = step_imgs ? (size_t)d * ld : 0, p_img = step_imgs ? (size_t)m * ld : 0;
+  std::vector<uint16_t> rth(t_img, 0), rtl(t_img, 0), ph(p_img, 0), pl(p_img, 0);
+  if (step_imgs) {
+    for (int i = 0; i < d; ++i)
+      for (int k = 0; k < d; ++k) split(R[(size_t)k * d + i], rth[(size_t)i * ld + k], rtl[(size_t)i * ld + k]);
+    std::vector<double> P((size_t)m * d, 0.0);
+    for (int i = 0; i < m; ++i)
+      for (int j = 0; j < d; ++j) {
+        const double sij = S[(size_t)i * d + j];
+        for (int k = 0; k < d; ++k) P[(size_t)i * d + k] += sij * R[(size_t)j * d + k];
+      }
+    for (int i = 0; i < m; ++i)
+      for (int k = 0; k < d; ++k) split(P[(size_t)i * d + k], ph[(size_t)i * ld + k], pl[(size_t)i * ld + k]);
+  }
   for (int i = 0; i < m; ++i) {
     for (int col = 0; col < d; ++col) {
       const int u = col / 128, c = col % 128, kb = c / 32, q = (c % 32) / 8, e = c % 8;
@@ -202,7 +221,9 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   const size_t b_rimg = r_img * 2, b_simg = s_img * 2;
   const size_t off_rl = b_rimg, off_sh = 2 * b_rimg, off_sl = off_sh + b_simg, off_sh32 = off_sl + b_simg;
   const size_t off_sl32 = off_sh32 + b_simg, off_r32 = off_sl32 + b_simg;
-  const size_t off_s32 = off_r32 + r32.size() * 4, end_imgs = off_s32 + s32.size() * 4;
+  const size_t off_s32 = off_r32 + r32.size() * 4, off_rth = off_s32 + s32.size() * 4;
+  const size_t off_rtl = off_rth + t_img * 2, off_ph = off_rtl + t_img * 2, off_pl = off_ph + p_img * 2;
+  const size_t end_imgs = off_pl + p_img * 2;
   // general-path scratch (row norms, key residual hi/lo, residual square sums)
   const bool gen = (!fast_keys(*cfg) && cfg->key_bits > 0) || !fast_values(*cfg);
   const int64_t srows = gen ? kScratchRows : 0;
@@ -222,7 +243,12 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
             hipMemcpy(base + off_sh32, sh32.data(), b_simg, hipMemcpyHostToDevice) == hipSuccess &&
             hipMemcpy(base + off_sl32, sl32.data(), b_simg, hipMemcpyHostToDevice) == hipSuccess &&
             hipMemcpy(base + off_r32, r32.data(), r32.size() * 4, hipMemcpyHostToDevice) == hipSuccess &&
-            hipMemcpy(base + off_s32, s32.data(), s32.size() * 4, hipMemcpyHostToDevice) == hipSuccess;
+            hipMemcpy(base + off_s32, s32.data(), s32.size() * 4, hipMemcpyHostToDevice) == hipSuccess &&
+            (!step_imgs ||
+             (hipMemcpy(base + off_rth, rth.data(), t_img * 2, hipMemcpyHostToDevice) == hipSuccess &&
+              hipMemcpy(base + off_rtl, rtl.data(), t_img * 2, hipMemcpyHostToDevice) == hipSuccess &&
+              hipMemcpy(base + off_ph, ph.data(), p_img * 2, hipMemcpyHostToDevice) == hipSuccess &&
+              hipMemcpy(base + off_pl, pl.data(), p_img * 2, hipMemcpyHostToDevice) == hipSuccess));
   if (!ok) {
     (void)hipFree(c->dev_mem);
     delete c;
@@ -236,6 +262,10 @@ int tq_create(const tq_config* cfg, const double* R, const double* S, tq_ctx** o
   c->mats.s_lo32 = (const uint16_t*)(base + off_sl32);
   c->mats.r32 = (const float*)(base + off_r32);
   c->mats.s32 = (const float*)(base + off_s32);
+  c->mats.rt_hi = step_imgs ? (const uint16_t*)(base + off_rth) : nullptr;
+  c->mats.rt_lo = step_imgs ? (const uint16_t*)(base + off_rtl) : nullptr;
+  c->mats.p_hi = step_imgs ? (const uint16_t*)(base + off_ph) : nullptr;
+  c->mats.p_lo = step_imgs ? (const uint16_t*)(base + off_pl) : nullptr;
   c->gen.mats = c->mats;
   c->gen.ld = ld;
   c->gen.scratch_rows = srows;

@@ -38,6 +38,10 @@ struct Matrices {
   const uint16_t* s_lo32;
   const float* r32;      // [d][d] fp32 R
   const float* s32;      // [m][d] fp32 S (natural column order)
+  const uint16_t* rt_hi;  // [d][kLdsStride] R^T * 2^8 hi / lo (d = 128, m in {64, 128}: the fused decode step)
+  const uint16_t* rt_lo;
+  const uint16_t* p_hi;   // [m][kLdsStride] (S R) * 2^8 hi / lo (the same shapes)
+  const uint16_t* p_lo;
 };
 
 // ---- launchers (defined in the .hip files) -----------------------------------
@@ -132,13 +136,14 @@ int launch_small_keys(const Matrices& mats, const CodebookDev& cb, int bits, int
 int launch_small_values(const Matrices& mats, const CodebookDev& cb, int bits, int d, const AppendShape& s,
                         void* value_blocks, void* stream);
 
-// The whole decode step in one launch (tq_attention.hip) serves shapes whose
-// workgroup partials per slot (waves per slot / 4 + 2, x G) are at most this
-// many (its combine keeps their weights in LDS).
+// The whole decode step in one launch (tq_step.hip) serves shapes whose
+// workgroup partials per slot (attend workgroups + 1, x G) are at most this
+// many (its merge keeps their weights in LDS).
 constexpr int kStepMaxPartials = 4096;
-// The whole decode step in one launch (tq_attention.hip): key and value
-// appends and query preparation (tq_small.h, tq_prep.h), attend and combine,
-// synchronised through flags and a count in the workspace.
+int decode_step_device_init();  // (tq_step.hip; called by attention_device_init)
+// The whole decode step in one launch (tq_step.hip): the appends, the query
+// preparation, the attention over the cache and the merge of the partials,
+// ordered by one arrival count per slot in the workspace.
 int launch_decode_step(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
                        int d, int m, const AppendShape& ks, const AppendShape& vs, const AttnShape& s,
                        void* key_records, void* value_blocks, float scale, float* out, void* ws, const AttnPlan& p,

@@ -318,16 +318,6 @@ __device__ __forceinline__ void small_values_block(const SmallArgs& a, int64_t b
   if (threadIdx.x < nt) vnorm[tau_of[threadIdx.x]] = nrm[threadIdx.x];
 }
 
-// The producers of a decode step (tq_decode_step's single launch): the key
-// appends (workgroups [0, nk)), the value appends ([nk, nk + nv)) and the
-// query preparation of the attention that follows ([nk + nv, ...)).  The
-// role is uniform over a workgroup, so each branch keeps its own barriers.
-struct DecodeArgs {
-  SmallArgs k, v;
-  GenPrepArgs p;
-  int nk, nv;
-};
-
 // Host: the arguments of a small append.
 inline SmallArgs small_args(const Matrices& mats, const CodebookDev& cb, int bits, int d, int m, const AppendShape& s,
                             void* out) {
@@ -354,34 +344,5 @@ inline SmallArgs small_args(const Matrices& mats, const CodebookDev& cb, int bit
   return a;
 }
 
-
-// Host: the arguments of the decode step's producers (key appends, value
-// appends, query preparation), and their dynamic LDS.
-inline DecodeArgs decode_args(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv,
-                              int vbits, int d, int m, const AppendShape& ks, const AppendShape& vs,
-                              const AttnShape& qs, void* key_records, void* value_blocks, uint16_t* wq, float* wqn) {
-  DecodeArgs a;
-  a.k = small_args(mats, cbk, kbits, d, m, ks, key_records);
-  a.v = small_args(mats, cbv, vbits, d, m, vs, value_blocks);
-  const int64_t nblk = (vs.pos + vs.n_new - 1) / kBlockTokens - vs.pos / kBlockTokens + 1;
-  a.nk = (int)(ks.n_seq * ks.n_new);
-  a.nv = (int)(vs.n_seq * nblk);
-  a.p.q = qs.q;
-  a.p.dtype = qs.dtype;
-  a.p.G = qs.G;
-  a.p.HG = 1;
-  a.p.n_seq = qs.n_seq;
-  a.p.d = d;
-  a.p.m = m;
-  a.p.n_oct = (d + 127) / 128;
-  a.p.r32 = mats.r32;
-  a.p.s32 = mats.s32;
-  a.p.wq = wq;
-  a.p.wqn = wqn;
-  return a;
-}
-inline size_t decode_lds_bytes(int d, int m) {
-  return sizeof(float) * (size_t)std::max(std::max(4 * d + m, 2 * d + kSmallAppend * d), 2 * d + m);
-}
 
 }  // namespace tq

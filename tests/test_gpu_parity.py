@@ -919,21 +919,21 @@ def test_binding_rejects_mismatched_tensor_shapes():
     ctx.close()
 
 
-def test_decode_step_single_launch_slot_spanning_and_graph_replay():
-    """The single-launch decode step with attend workgroups that span slots
-    (6 waves per slot at 700 tokens, so 4-wave workgroups straddle two
-    slots), step by step against the oracle on the GPU's codes; then the
-    same step captured in a HIP graph and replayed several times (the launch
-    keeps its tag on replay, so its flags must be cleared by each replay's
-    last workgroup), every replay equal to the eager output, with eager work
-    and synchronisations between replays."""
+def test_decode_step_single_launch_workgroups_and_graph_replay():
+    """The single-launch decode step with two attention workgroups and the
+    append workgroup per slot (6 blocks per slot at 700 tokens, 5 slots),
+    step by step against the oracle on the GPU's codes; then the same step
+    captured in a HIP graph and replayed several times (each replay finds
+    the slots' arrival counts back at their start), every replay equal to
+    the eager output, with eager work and synchronisations between
+    replays."""
     d, m, G, n_seq, prefill = 128, 64, 8, 5, 690
     steps = [1, 3, 1, 5]
     T = prefill + sum(steps)
     K = np.stack([synth.kv_slot(230, s, s, T, d) for s in range(n_seq)])
     V = np.stack([synth.kv_slot(231, s, s, T, d) for s in range(n_seq)])
     Qs = [np.stack([synth.kv_slot(232 + i, s, s, G, d) for s in range(n_seq)]) for i in range(len(steps))]
-    _say("decode step, slot-spanning workgroups", (n_seq, T, G))
+    _say("decode step, several workgroups per slot", (n_seq, T, G))
     ctx, R, S = make_ctx(d, m, 3, 3)
     cache = tq.KVCache(ctx, n_seq, 768)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
