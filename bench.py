@@ -35,6 +35,15 @@ sys.path.insert(0, ROOT)
 METRIC = "keys compressed/s + decode score/attend HBM GB/s (fraction of peak), 3-bit d=128"
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 FP16_MFMA_PEAK_TFLOPS = 2500.0
+# Issue roofline of compress: SIMD cycles per token of the kernels'
+# instruction streams (a wave64 VALU instruction holds its SIMD 4 cycles, a
+# 32x32x16 f16 MFMA 32 and a 16x16x32 one 16), from the instruction-mix
+# counters of the long-context step (SQ_INSTS_VALU, SQ_INSTS_MFMA per
+# 16-token tile: keys 551 VALU + 56 MFMA 32x32x16, values 412 VALU + 64 MFMA
+# 16x16x32), against 256 CUs x 4 SIMDs at the 2.4 GHz peak clock.
+SIMDS, PEAK_CLOCK_HZ = 1024, 2.4e9
+COMPRESS_ISSUE_CYCLES = {"compress_keys": (551 * 4 / 16, 56 * 32 / 16),
+                         "compress_values": (412 * 4 / 16, 64 * 16 / 16)}
 WORKLOAD = dict(name="long_context_8x8x131072", n_seq=64, n_tok=131072, d=128, m=64, key_bits=3,
                 value_bits=3, G=4, heads_per_slot_cycle=8)
 
@@ -533,10 +542,24 @@ def main():
             "peak_TFLOPs": FP16_MFMA_PEAK_TFLOPS,
             "alg_frac": round(units * alg_f / sec / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
             "executed_frac": round(units * exe_f / sec / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4)}
+        # issue roofline: the VALU and MFMA cycles of the instruction stream
+        # spread over every SIMD at the peak clock, overlapped (the larger of
+        # the two) or back to back (their sum)
+        valu_c, mfma_c = COMPRESS_ISSUE_CYCLES[s_]
+        t_valu = units * valu_c / SIMDS / PEAK_CLOCK_HZ * 1e3
+        t_mfma = units * mfma_c / SIMDS / PEAK_CLOCK_HZ * 1e3
+        stage_info[s_]["issue_roofline"] = {
+            "valu_ms": round(t_valu, 4), "mfma_ms": round(t_mfma, 4),
+            "overlapped_ms": round(max(t_valu, t_mfma), 4), "additive_ms": round(t_valu + t_mfma, 4),
+            "frac_overlapped": round(max(t_valu, t_mfma) / stage_ms[s_], 4),
+            "frac_additive": round((t_valu + t_mfma) / stage_ms[s_], 4)}
     dom = max(stages, key=lambda s: stage_ms[s])
     roof = {"bound": "hbm", "kernel": dom, "achieved": stage_info[dom]["GBps"], "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": stage_info[dom]["frac_hbm_peak"], "traffic": counter_traffic(dom),
             "alg_bytes": int(alg[dom])}
+    if "issue_roofline" in stage_info[dom]:
+        # the bound that binds compress on this chip: SIMD issue, beside HBM
+        roof["issue_roofline"] = stage_info[dom]["issue_roofline"]
 
     # Practical HBM ceiling beside the theoretical peak: a plain read stream
     # over the 2 GiB key input, and the same with writes interleaved 4:1 (the
@@ -547,7 +570,8 @@ def main():
     # is an independent check of the read figure.
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     dst = torch.empty(Kd.numel() * Kd.element_size() // 16, dtype=torch.float32, device=dev)
-    stream_ms, stream_cfg = {}, {}
+    stream_ms, stream_cfg, sweep = {}, {}, []
+    nbytes_k = Kd.numel() * Kd.element_size()
     for name, d_ in (("read", None), ("read4_write1", dst)):
         for nl, nt in ((4, False), (8, True), (16, True)):
             for wpc in (8, 16, 32, 64):
@@ -561,6 +585,8 @@ def main():
                 e1.record()
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / 10
+                sweep.append({"mix": name, "loads_in_flight": nl, "nontemporal": nt, "waves_per_cu": wpc,
+                              "GBps": round((nbytes_k * (1.25 if d_ is not None else 1.0)) / (ms * 1e-3) / 1e9, 1)})
                 if name not in stream_ms or ms < stream_ms[name]:
                     stream_ms[name] = ms
                     stream_cfg[name] = {"waves_per_cu": wpc, "loads_in_flight": nl, "nontemporal": nt}
@@ -571,7 +597,7 @@ def main():
     hbm_stream = {"read_GBps": round(nbytes / (stream_ms["read"] * 1e-3) / 1e9, 1),
                   "read4_write1_GBps": round(nbytes * 1.25 / (stream_ms["read4_write1"] * 1e-3) / 1e9, 1),
                   "torch_sum_read_GBps": round(nbytes / (torch_ms * 1e-3) / 1e9, 1),
-                  "bytes_read": nbytes, "best": stream_cfg}
+                  "bytes_read": nbytes, "best": stream_cfg, "sweep": sweep}
     mix = {"compress_keys": "read4_write1_GBps", "compress_values": "read4_write1_GBps",
            "scores": "read4_write1_GBps", "attend": "read_GBps"}
     for s_ in stages:

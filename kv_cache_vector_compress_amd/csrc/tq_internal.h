@@ -138,7 +138,8 @@ int launch_small_values(const Matrices& mats, const CodebookDev& cb, int bits, i
 
 // The whole decode step in one launch (tq_step.hip) serves shapes whose
 // workgroup partials per slot (attend workgroups + 1, x G) are at most this
-// many (its merge keeps their weights in LDS).
+// many: one workgroup merges them, and beyond this the merge would take
+// longer than the separate launches of the three calls.
 constexpr int kStepMaxPartials = 4096;
 int decode_step_device_init();  // (tq_step.hip; called by attention_device_init)
 // The whole decode step in one launch (tq_step.hip): the appends, the query

@@ -56,7 +56,6 @@ constexpr int kLdsOps = kLdsQn + 64;              // attend operands [KBT <= 8][
 constexpr int kLdsPm = kLdsOps + 8 * 64 * 8 / 2;  // wave partials [4][16][kPartFloats]; append scratch
 constexpr int kLdsEnd = kLdsPm + 4 * 16 * kPartFloats;
 constexpr size_t kStepLdsBytes = sizeof(float) * kLdsEnd;
-static_assert(kLdsQs + 3 * kStepMaxPartials + 32 <= kLdsEnd, "the merge's tables fit the step's LDS");
 
 struct StepArgs {
   AttendArgs att;             // attention over tokens [0, pos): n_tokens = pos, waves_per_slot = 4 n_plain
@@ -306,67 +305,68 @@ __device__ __forceinline__ int normalise8(float (&o)[8]) {
 }
 
 // The merge of the slot's partials [gi][h][kPartFloats] (gi < n) into the
-// output, by the workgroup that completed the slot's count (its LDS from
-// kLdsQs on is free).
-__device__ __forceinline__ void step_combine(const StepArgs& a, int slot, float* L, int n) {
-  const int tid = threadIdx.x, G = a.att.G;
-  const float* gp = a.group + (int64_t)slot * a.group_stride * G * kPartFloats;
-  float* mm = L + kLdsQs;          // [n G] m, then weights
-  float* ll = mm + kStepMaxPartials;
-  float* vv = ll + kStepMaxPartials;
-  float* hL = vv + kStepMaxPartials;  // [16]
-  int* hE = (int*)(hL + 16);
-  // The partials come from other XCDs: system-coherent loads (cache policy
-  // sc0 sc1) read them past this XCD's caches, 16 bytes at a time.
+// output, by the workgroup that completed the slot's count.  Thread (h, j4)
+// owns output coordinates 4 j4 .. 4 j4 + 3 of head h and merges every
+// partial itself, 16 at a time: it issues the loads of 16 partials' headers
+// (m, l, ve) and of its 4 accumulator values before it uses any of them, so
+// a chunk costs one round trip to memory, and carries the running maximum,
+// value exponent and sums from chunk to chunk (the softmax merge in its
+// online form).  The partials come from other XCDs: system-coherent loads
+// (cache policy sc0 sc1) read them past this XCD's caches.
+__device__ __forceinline__ void step_combine(const StepArgs& a, int slot, int n) {
+  constexpr int kChunk = 16;
   constexpr int kSysCoherent = 1 | 16;
+  const int G = a.att.G;
+  const float* gp = a.group + (int64_t)slot * a.group_stride * G * kPartFloats;
   const __amdgpu_buffer_rsrc_t prs = slot_rsrc(gp, (uint32_t)(n * G * kPartFloats * 4));
   auto ld4 = [&](int c, int h, int off) {
     return __builtin_bit_cast(
         f4, __builtin_amdgcn_raw_buffer_load_b128(prs, 4u * (uint32_t)((c * G + h) * kPartFloats + off), 0,
                                                   kSysCoherent));
   };
-  for (int i = tid; i < n * G; i += blockDim.x) {
-    const f4 h4 = ld4(i / G, i % G, 0);  // m, l, ve, pad
-    mm[i] = h4[0];
-    ll[i] = h4[1];
-    vv[i] = h4[2];
-  }
-  __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY, VE = -INFINITY;
-    for (int c = 0; c < n; ++c) {
-      const float mc = mm[c * G + tid];
-      M = fmaxf(M, mc);
-      if (mc != -INFINITY) VE = fmaxf(VE, vv[c * G + tid]);
-    }
-    const int ve_max = VE == -INFINITY ? 0 : (int)VE;
-    float Lh = 0.f;
-    for (int c = 0; c < n; ++c) {
-      const float mc = mm[c * G + tid];
-      const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
-      Lh = fmaf(w, ll[c * G + tid], Lh);
-      mm[c * G + tid] = ldexpf(w, (int)vv[c * G + tid] - ve_max);
-    }
-    hL[tid] = Lh;
-    hE[tid] = ve_max;
-  }
-  __syncthreads();
-  for (int e = tid; e < G * (kD / 4); e += blockDim.x) {
+  constexpr int kNoExp = -100000;  // value exponent before any partial with weight
+  for (int e = threadIdx.x; e < G * (kD / 4); e += blockDim.x) {
     const int h = e >> 5, j4 = e & 31;
-    f4 o[4];
+    float M = -INFINITY, Lh = 0.f;
+    int VE = kNoExp;
+    f4 o = {0.f, 0.f, 0.f, 0.f};  // sum of weight x acc, in the scale 2^-VE
+    for (int c0 = 0; c0 < n; c0 += kChunk) {
+      f4 hd[kChunk], av[kChunk];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = f4{0.f, 0.f, 0.f, 0.f};
-    int c = 0;
-    for (; c + 4 <= n; c += 4) {
+      for (int u = 0; u < kChunk; ++u) {
+        if (c0 + u < n) {
+          hd[u] = ld4(c0 + u, h, 0);
+          av[u] = ld4(c0 + u, h, 4 + 4 * j4);
+        } else {
+          hd[u] = f4{-INFINITY, 0.f, 0.f, 0.f};
+          av[u] = f4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      float Mc = M;
+      int Vc = VE;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) o[u] += mm[(c + u) * G + h] * ld4(c + u, h, 4 + 4 * j4);
+      for (int u = 0; u < kChunk; ++u) {
+        Mc = fmaxf(Mc, hd[u][0]);
+        if (hd[u][0] != -INFINITY) Vc = max(Vc, (int)hd[u][2]);
+      }
+      if (Mc == -INFINITY) continue;  // no partial with weight yet
+      // the running sums move to the chunk's maximum and exponent
+      const float f = M == -INFINITY ? 0.f : exp2f(M - Mc);
+      Lh *= f;
+      o *= ldexpf(f, max(VE - Vc, -1000));
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const float w = hd[u][0] == -INFINITY ? 0.f : exp2f(hd[u][0] - Mc);
+        Lh = fmaf(w, hd[u][1], Lh);
+        o += ldexpf(w, (int)hd[u][2] - Vc) * av[u];
+      }
+      M = Mc;
+      VE = Vc;
     }
-    for (; c < n; ++c) o[0] += mm[c * G + h] * ld4(c, h, 4 + 4 * j4);
-    const f4 t = (o[0] + o[1]) + (o[2] + o[3]);
-    const float inv = hL[h] > 0.f ? 1.f / hL[h] : 0.f;
+    const float inv = Lh > 0.f ? 1.f / Lh : 0.f;
     f4 r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = ldexpf(t[i] * inv, hE[h]);
+    for (int i = 0; i < 4; ++i) r[i] = VE == kNoExp ? 0.f : ldexpf(o[i] * inv, VE);
     *(f4*)(a.out + ((int64_t)slot * G + h) * kD + 4 * j4) = r;
   }
 }
@@ -731,7 +731,7 @@ __global__ __launch_bounds__(256, 1) void decode_step_kernel(const StepArgs a) {
     __syncthreads();
     step_emit(a, slot, r, acc, hm, hl, hv, rt);
   }
-  if (step_arrive(a, slot, &flag)) step_combine(a, slot, L, per);
+  if (step_arrive(a, slot, &flag)) step_combine(a, slot, per);
 }
 
 int launch_decode_step(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
