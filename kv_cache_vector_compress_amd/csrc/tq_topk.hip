@@ -34,7 +34,8 @@ struct TopkArgs {
   int32_t* ci;
   int64_t n_tokens, capacity;
   int n_seq, G, HG, d, m, n_oct, rec_words, k, n_qblk, n_ranges;
-  int64_t tiles_per_range;
+  int64_t tiles_per_range, range_stride;  // range r: tiles [r range_stride, + tiles_per_range)
+  const float* tau;  // nullable: [n_seq][G][k] a sample's top-k scores; its k-th entry starts the threshold
   float kappa;
   uint32_t tlo[4], thi[4];
 };
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
   uint16_t* qop = tsm;                                      // [2][KBT][64][8]
   float* ls = (float*)(tsm + 2 * KBT * 512);                // [waves][32][k]
   int32_t* li = (int32_t*)(ls + kTkWaves * 32 * a.k);
+  float* thr_wg = (float*)(li + kTkWaves * 32 * a.k);  // [32]: the best k-th score of any wave's list
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q = lane >> 4;
   const int qblk = blockIdx.x % a.n_qblk;
@@ -92,6 +94,12 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
     for (int i = tid; i < kTkWaves * 32 * a.k; i += blockDim.x) {
       ls[i] = -INFINITY;
       li[i] = -1;
+    }
+    if (tid < 32) {
+      // a sample's k-th best score: k tokens reach it, so no token below it
+      // is in the top k
+      const int h = 32 * qblk + tid;
+      thr_wg[tid] = a.tau && h < a.G ? a.tau[((int64_t)slot * a.G + h) * a.k + a.k - 1] : -INFINITY;
     }
   }
   __syncthreads();
@@ -110,7 +118,7 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
   for (int i = 0; i < 4; ++i) { tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; }
   const int n_tok = (int)a.n_tokens;
   const int64_t ntile = (a.n_tokens + 15) / 16;
-  const int64_t t_lo = (int64_t)range * a.tiles_per_range;
+  const int64_t t_lo = (int64_t)range * a.range_stride;
   const int64_t t_hi = min(ntile, t_lo + a.tiles_per_range);
   const int sh0 = 15 - 8 * (q & 1);
   const int sw0 = B * a.d / 32;
@@ -249,12 +257,18 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       if (g >= ng) break;
+      // A candidate must beat this wave's own k-th entry and reach the best
+      // k-th entry of any wave of the workgroup (or the sample's k-th best
+      // score it started from): k tokens rank at least as high as that one,
+      // so a token below it is in no top k (one equal to it may still rank
+      // before by its index, so it goes on to the list).
+      const float thw = thr_wg[16 * g + r16];
       float est[4];
       bool pass[4], any = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         est[i] = acc[g][i] * nk[i] * qn[g];
-        pass[i] = live[g] && t0 + i < n_tok && est[i] > thr[g];
+        pass[i] = live[g] && t0 + i < n_tok && est[i] > thr[g] && est[i] >= thw;
         any |= pass[i];
       }
       if (__any(any)) {  // rare once the lists are full
@@ -271,6 +285,8 @@ __global__ __launch_bounds__(512) void topk_scores_kernel(const TopkArgs a) {
             }
           }
         thr[g] = cls[a.k - 1];
+        if (q == 0 && thr[g] != -INFINITY)
+          (void)__hip_atomic_fetch_max(thr_wg + 16 * g + r16, thr[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
   };
@@ -393,7 +409,7 @@ TopkPlan topk_plan(int d, int m, int n_seq, int G, int64_t n_tokens, int k) {
 }
 
 static size_t topk_lds(int d, int m, int k) {
-  return (size_t)2 * (d / 32 + m / 32) * 512 * 2 + (size_t)kTkWaves * 32 * k * 8;
+  return (size_t)2 * (d / 32 + m / 32) * 512 * 2 + (size_t)kTkWaves * 32 * k * 8 + 32 * 4;
 }
 
 int topk_device_init() {
@@ -443,16 +459,19 @@ int launch_topk(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, 
   a.n_qblk = p.n_qblk;
   a.n_ranges = p.n_ranges;
   a.tiles_per_range = p.tiles_per_range;
+  a.range_stride = p.tiles_per_range;
+  a.tau = nullptr;
   a.kappa = (float)(1.2533141373155002512 / m);  // sqrt(pi/2) / m
   for (int i = 0; i < 4; ++i) { a.tlo[i] = cbk.tlo[i]; a.thi[i] = cbk.thi[i]; }
   const dim3 grid((unsigned)((int64_t)s.n_seq * p.n_ranges * p.n_qblk)), block(64 * kTkWaves);
   const size_t lds = topk_lds(d, m, k);
-  bool launched = false;
   const int n_full = d / 128;
   const bool half = d % 128 != 0;
+  auto search = [&](const TopkArgs& x) -> int {
+    bool launched = false;
 #define TQ_TK(B, N, H) \
   if (!launched && kbits == B && n_full == N && half == H) { \
-    hipLaunchKernelGGL((topk_scores_kernel<B, N, H>), grid, block, lds, st, a); \
+    hipLaunchKernelGGL((topk_scores_kernel<B, N, H>), grid, block, lds, st, x); \
     launched = true; \
   }
 #define TQ_TK_B(B)                                                                                   \
@@ -460,24 +479,39 @@ int launch_topk(const Matrices& mats, const CodebookDev& cbk, int kbits, int d, 
   TQ_TK(B, 6, false) TQ_TK(B, 7, false) TQ_TK(B, 8, false) TQ_TK(B, 0, true) TQ_TK(B, 1, true)       \
   TQ_TK(B, 2, true) TQ_TK(B, 3, true) TQ_TK(B, 4, true) TQ_TK(B, 5, true) TQ_TK(B, 6, true)          \
   TQ_TK(B, 7, true)
-  if (kbits == 0) {  // 0-bit keys: no code chunks, one instance for every head_dim
-    hipLaunchKernelGGL((topk_scores_kernel<0, 1, false>), grid, block, lds, st, a);
-    launched = true;
-  }
-  TQ_TK_B(1) TQ_TK_B(2) TQ_TK_B(3) TQ_TK_B(4)
+    if (kbits == 0) {  // 0-bit keys: no code chunks, one instance for every head_dim
+      hipLaunchKernelGGL((topk_scores_kernel<0, 1, false>), grid, block, lds, st, x);
+      launched = true;
+    }
+    TQ_TK_B(1) TQ_TK_B(2) TQ_TK_B(3) TQ_TK_B(4)
 #undef TQ_TK_B
 #undef TQ_TK
-  if (!launched) return TQ_EUNSUPPORTED;
-  if (hipGetLastError() != hipSuccess) return TQ_EDEVICE;
-  TopkMergeArgs b;
-  b.cs = cs;
-  b.ci = ci;
-  b.out_s = top_s;
-  b.out_i = top_i;
-  b.n_cand = p.n_lists * k;
-  b.k = k;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)(s.n_seq * s.G)), dim3(256), 0, st, b);
-  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+    if (!launched) return TQ_EUNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return TQ_EDEVICE;
+    TopkMergeArgs b;
+    b.cs = cs;
+    b.ci = ci;
+    b.out_s = top_s;
+    b.out_i = top_i;
+    b.n_cand = p.n_lists * k;
+    b.k = k;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)(s.n_seq * s.G)), dim3(256), 0, st, b);
+    return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+  };
+  // A sample first, when the ranges are long: the first 32 tiles of every
+  // range's stretch of the token axis (4 tiles per wave), spread over the
+  // whole axis, searched the same way into the outputs.  Its k-th best score
+  // per query is reached by k tokens, so the full search starts every
+  // workgroup's threshold there: only tokens at or above it become
+  // candidates, and the lists are not filled from -inf.
+  if (p.tiles_per_range >= 8 * 4 * kTkWaves) {  // (the sample is at most 1/8 of the work)
+    TopkArgs smp = a;
+    smp.tiles_per_range = 4 * kTkWaves;  // range r: tiles [r range_stride, + 32), clipped to the axis
+    const int rc = search(smp);
+    if (rc) return rc;
+    a.tau = top_s;
+  }
+  return search(a);
 }
 
 }  // namespace tq
