@@ -249,12 +249,18 @@ class KVCache:
         self.view = CacheView(self.key_records.data_ptr(), self.value_blocks.data_ptr(), capacity, n_seq)
         self._ws = {}   # one attention workspace per stream: calls on different streams never share one
         self._aws = {}  # the same for the appends' workspace (general-path bulk appends)
+        self._aws_need = {}  # its size per append length (n_seq is fixed)
+        self._ws_need = (None, 0)  # the last attention workspace size query and its answer
 
     def workspace(self, G: int, n_tokens: int, stream=None):
         """The attention workspace of the given stream (torch's current
         stream by default), grown to tq_attend_workspace_bytes."""
         torch = _torch()
-        need = self.ctx.attend_workspace_bytes(self.n_seq, G, n_tokens)
+        if self._ws_need[0] == (G, n_tokens):  # (the last size query, kept: decode loops repeat it)
+            need = self._ws_need[1]
+        else:
+            need = self.ctx.attend_workspace_bytes(self.n_seq, G, n_tokens)
+            self._ws_need = ((G, n_tokens), need)
         if need == 0:
             raise TQError(-1, f"tq_attend_workspace_bytes: invalid arguments (n_seq {self.n_seq}, G {G}, "
                               f"n_tokens {n_tokens})")
@@ -290,7 +296,9 @@ class KVCache:
         """The appends' workspace of the given stream, grown to
         tq_append_workspace_bytes, or None when the append uses none."""
         torch = _torch()
-        need = self.ctx.append_workspace_bytes(self.n_seq, n_new)
+        need = self._aws_need.get(n_new)
+        if need is None:  # (a host-only size query, remembered per append length)
+            need = self._aws_need[n_new] = self.ctx.append_workspace_bytes(self.n_seq, n_new)
         if need == 0:
             return None
         key = _stream_ptr(stream).value
