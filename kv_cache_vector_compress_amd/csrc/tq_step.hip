@@ -56,6 +56,7 @@ constexpr int kLdsOps = kLdsQn + 64;              // attend operands [KBT <= 8][
 constexpr int kLdsPm = kLdsOps + 8 * 64 * 8 / 2;  // wave partials [4][16][kPartFloats]; append scratch
 constexpr int kLdsEnd = kLdsPm + 4 * 16 * kPartFloats;
 constexpr size_t kStepLdsBytes = sizeof(float) * kLdsEnd;
+static_assert(4 * kStepMaxPartials <= kLdsEnd, "the merge keeps every partial's header in LDS");
 
 struct StepArgs {
   AttendArgs att;             // attention over tokens [0, pos): n_tokens = pos, waves_per_slot = 4 n_plain
@@ -125,8 +126,8 @@ __device__ __forceinline__ void load_tile_ops(TileOps& o, const uint16_t* hi, co
 
 // The slot's query preparation by the whole workgroup on the matrix cores:
 // per-head norms with a power-of-two shift (any finite query), then
-// q~ = R q_shifted and p = (S R) q_shifted as split-fp16 products (images hi
-// + lo times q hi (+ lo for fp32 queries)), wave w forming rows 32 w .. +31
+// q~ = R q_shifted and p = (S R) q_shifted on the matrix cores (the fp16 hi
+// images times q hi, + lo for fp32 queries), wave w forming rows 32 w .. +31
 // of q~ and rows 16 (w + 4 u) .. of p for all 16 head lanes.  q~ and p go to
 // LDS in fp32; with `plain` also the fp16 attend operands, the centroid
 // part straight from the q~ tiles (their lane layout is the operand's).
@@ -142,18 +143,23 @@ __device__ __forceinline__ void step_prep(const StepArgs& a, int slot, float* L,
   float* qsn = qn + 16;       // norm of the shifted query
   int* qe = (int*)(qn + 32);  // its exponent
   uint16_t* ops = (uint16_t*)(L + kLdsOps);
-  // image operands in flight first (L2-resident: every workgroup reads them)
-  TileOps ra;
-  load_tile_ops(ra, a.r_hi, a.r_lo, wave, lane);
-  h8 pa[NP][4][2];
+  // image operands in flight first: the hi images only.  The query operands
+  // are rounded to fp16 for the score products anyway, and R_hi q is within
+  // ~2^-12 of R q, far inside the score tolerance (2e-3 of ||q|| ||k||);
+  // the lo halves would double the bytes every workgroup loads before it
+  // can start.
+  h8 ra[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      ra[t][ks] = *(const h8*)(a.r_hi + (16 * (2 * wave + t) + r16) * kLdsStride + 32 * ks + 8 * q);
+  h8 pa[NP][4];
 #pragma unroll
   for (int u = 0; u < NP; ++u)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int off = (16 * (wave + 4 * u) + r16) * kLdsStride + 32 * ks + 8 * q;
-      pa[u][ks][0] = *(const h8*)(a.p_hi + off);
-      pa[u][ks][1] = *(const h8*)(a.p_lo + off);
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      pa[u][ks] = *(const h8*)(a.p_hi + (16 * (wave + 4 * u) + r16) * kLdsStride + 32 * ks + 8 * q);
   // norms: thread (head h, seg) holds coordinates 8 seg .. + 7
   {
     const int h = tid >> 4, seg = tid & 15;
@@ -200,15 +206,13 @@ __device__ __forceinline__ void step_prep(const StepArgs& a, int slot, float* L,
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      tq[t] = mfma(ra.a[t][ks][0], bh[ks], tq[t]);
-      tq[t] = mfma(ra.a[t][ks][1], bh[ks], tq[t]);
-      if (f32) tq[t] = mfma(ra.a[t][ks][0], bl[ks], tq[t]);
+      tq[t] = mfma(ra[t][ks], bh[ks], tq[t]);
+      if (f32) tq[t] = mfma(ra[t][ks], bl[ks], tq[t]);
     }
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
-      tp[u] = mfma(pa[u][ks][0], bh[ks], tp[u]);
-      tp[u] = mfma(pa[u][ks][1], bh[ks], tp[u]);
-      if (f32) tp[u] = mfma(pa[u][ks][0], bl[ks], tp[u]);
+      tp[u] = mfma(pa[u][ks], bh[ks], tp[u]);
+      if (f32) tp[u] = mfma(pa[u][ks], bl[ks], tp[u]);
     }
   }
   const bool live = r16 < G;
@@ -276,14 +280,21 @@ __device__ __forceinline__ void step_emit(const StepArgs& a, int slot, int gi, c
     }
   }
   if (r16 < G) {
-    float* pr = a.group + (((int64_t)slot * a.group_stride + gi) * G + r16) * kPartFloats;
+    // written through to memory (cache policy sc0 sc1): the workgroup that
+    // merges the slot may run on another XCD, and step_arrive then only
+    // waits for these stores instead of writing back this XCD's L2
+    // (the descriptor spans the partial's G heads: wave-uniform)
+    constexpr int kSysCoherent = 1 | 16;
+    const float* pg = a.group + ((int64_t)slot * a.group_stride + gi) * G * kPartFloats;
+    const __amdgpu_buffer_rsrc_t prs = slot_rsrc(pg, 4u * (uint32_t)(G * kPartFloats));
+    const uint32_t ph = 4u * (uint32_t)(r16 * kPartFloats);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) *(f4*)(pr + 4 + 16 * (2 * wave + t) + 4 * q) = o[t] * (1.f / kRotScale);
-    if (wave == 0 && q == 0) {
-      pr[0] = hm[r16];
-      pr[1] = hl[r16];
-      pr[2] = (float)hv[r16];
-    }
+    for (int t = 0; t < 2; ++t)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, o[t] * (1.f / kRotScale)), prs,
+                                             ph + 4u * (uint32_t)(4 + 16 * (2 * wave + t) + 4 * q), 0, kSysCoherent);
+    if (wave == 0 && q == 0)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u4, f4{hm[r16], hl[r16], (float)hv[r16], 0.f}), prs, ph, 0, kSysCoherent);
   }
 }
 
@@ -307,16 +318,17 @@ __device__ __forceinline__ int normalise8(float (&o)[8]) {
 // The merge of the slot's partials [gi][h][kPartFloats] (gi < n) into the
 // output, by the workgroup that completed the slot's count.  Thread (h, j4)
 // owns output coordinates 4 j4 .. 4 j4 + 3 of head h and merges every
-// partial itself, 16 at a time: it issues the loads of 16 partials' headers
-// (m, l, ve) and of its 4 accumulator values before it uses any of them, so
-// a chunk costs one round trip to memory, and carries the running maximum,
-// value exponent and sums from chunk to chunk (the softmax merge in its
-// online form).  The partials come from other XCDs: system-coherent loads
-// (cache policy sc0 sc1) read them past this XCD's caches.
-__device__ __forceinline__ void step_combine(const StepArgs& a, int slot, int n) {
-  constexpr int kChunk = 16;
+// partial itself, kChunk at a time, carrying the running maximum, value
+// exponent and sums from chunk to chunk (the softmax merge in its online
+// form).  The partials' headers (m, l, ve) go to LDS once, and the loads of
+// the first chunk's accumulator values are issued before them, so a slot of
+// up to kChunk partials costs one round trip to memory.  The partials come
+// from other XCDs: system-coherent loads (cache policy sc0 sc1) read them
+// past this XCD's caches.
+__device__ __forceinline__ void step_combine(const StepArgs& a, int slot, int n, float* L) {
+  constexpr int kChunk = 24;
   constexpr int kSysCoherent = 1 | 16;
-  const int G = a.att.G;
+  const int G = a.att.G, tid = threadIdx.x;
   const float* gp = a.group + (int64_t)slot * a.group_stride * G * kPartFloats;
   const __amdgpu_buffer_rsrc_t prs = slot_rsrc(gp, (uint32_t)(n * G * kPartFloats * 4));
   auto ld4 = [&](int c, int h, int off) {
@@ -324,30 +336,36 @@ __device__ __forceinline__ void step_combine(const StepArgs& a, int slot, int n)
         f4, __builtin_amdgcn_raw_buffer_load_b128(prs, 4u * (uint32_t)((c * G + h) * kPartFloats + off), 0,
                                                   kSysCoherent));
   };
+  f4* hdr = (f4*)L;  // [n][G] headers (n G <= kStepMaxPartials fits the step's LDS)
+  const bool own0 = tid < G * (kD / 4);
+  f4 av0[kChunk];    // this thread's first element, first chunk: in flight with the headers
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u)
+    av0[u] = own0 && u < n ? ld4(u, tid >> 5, 4 + 4 * (tid & 31)) : f4{0.f, 0.f, 0.f, 0.f};
+  for (int i = tid; i < n * G; i += blockDim.x) hdr[i] = ld4(i / G, i % G, 0);
+  __syncthreads();
   constexpr int kNoExp = -100000;  // value exponent before any partial with weight
-  for (int e = threadIdx.x; e < G * (kD / 4); e += blockDim.x) {
+  for (int e = tid; e < G * (kD / 4); e += blockDim.x) {
     const int h = e >> 5, j4 = e & 31;
     float M = -INFINITY, Lh = 0.f;
     int VE = kNoExp;
     f4 o = {0.f, 0.f, 0.f, 0.f};  // sum of weight x acc, in the scale 2^-VE
     for (int c0 = 0; c0 < n; c0 += kChunk) {
-      f4 hd[kChunk], av[kChunk];
+      f4 av[kChunk];
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u) {
-        if (c0 + u < n) {
-          hd[u] = ld4(c0 + u, h, 0);
-          av[u] = ld4(c0 + u, h, 4 + 4 * j4);
-        } else {
-          hd[u] = f4{-INFINITY, 0.f, 0.f, 0.f};
-          av[u] = f4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
+      for (int u = 0; u < kChunk; ++u)
+        av[u] = e == tid && c0 == 0 ? av0[u]
+                : c0 + u < n        ? ld4(c0 + u, h, 4 + 4 * j4)
+                                    : f4{0.f, 0.f, 0.f, 0.f};
       float Mc = M;
       int Vc = VE;
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
-        Mc = fmaxf(Mc, hd[u][0]);
-        if (hd[u][0] != -INFINITY) Vc = max(Vc, (int)hd[u][2]);
+        if (c0 + u < n) {
+          const f4 hd = hdr[(c0 + u) * G + h];
+          Mc = fmaxf(Mc, hd[0]);
+          if (hd[0] != -INFINITY) Vc = max(Vc, (int)hd[2]);
+        }
       }
       if (Mc == -INFINITY) continue;  // no partial with weight yet
       // the running sums move to the chunk's maximum and exponent
@@ -356,9 +374,12 @@ __device__ __forceinline__ void step_combine(const StepArgs& a, int slot, int n)
       o *= ldexpf(f, max(VE - Vc, -1000));
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
-        const float w = hd[u][0] == -INFINITY ? 0.f : exp2f(hd[u][0] - Mc);
-        Lh = fmaf(w, hd[u][1], Lh);
-        o += ldexpf(w, (int)hd[u][2] - Vc) * av[u];
+        if (c0 + u < n) {
+          const f4 hd = hdr[(c0 + u) * G + h];
+          const float w = hd[0] == -INFINITY ? 0.f : exp2f(hd[0] - Mc);
+          Lh = fmaf(w, hd[1], Lh);
+          o += ldexpf(w, (int)hd[2] - Vc) * av[u];
+        }
       }
       M = Mc;
       VE = Vc;
@@ -377,13 +398,16 @@ __device__ __forceinline__ void step_combine(const StepArgs& a, int slot, int n)
 // used by a decode step) is first set to (tag, 0) by compare-and-swap and
 // the arrival repeated.
 __device__ __forceinline__ bool step_arrive(const StepArgs& a, int slot, int* flag) {
-  // Every wave makes its own partial stores visible to every XCD (a release
-  // fence waits for the wave's stores and writes its L2 back) before the
-  // barrier: a fence in one wave does not cover the stores of the others.
-  // The workgroups of a slot run on different XCDs, each with an L2 of its
-  // own: the counts are only ever read by atomics, and the merge reads the
-  // partials with system-coherent loads, which bypass this XCD's caches.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // Every wave waits for its own partial stores (written through to memory
+  // by step_emit) to complete before the barrier: a wait in one wave does
+  // not cover the stores of the others.  The workgroups of a slot run on
+  // different XCDs, each with an L2 of its own: the counts are only ever
+  // read by atomics, and the merge reads the partials with system-coherent
+  // loads, which bypass this XCD's caches.  Nothing else this launch writes
+  // is read by another workgroup of it, so no L2 write-back is needed.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned long long* cnt = a.count + slot;
@@ -731,7 +755,7 @@ __global__ __launch_bounds__(256, 1) void decode_step_kernel(const StepArgs a) {
     __syncthreads();
     step_emit(a, slot, r, acc, hm, hl, hv, rt);
   }
-  if (step_arrive(a, slot, &flag)) step_combine(a, slot, per);
+  if (step_arrive(a, slot, &flag)) step_combine(a, slot, per, L);
 }
 
 int launch_decode_step(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
