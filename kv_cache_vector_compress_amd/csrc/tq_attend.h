@@ -145,10 +145,13 @@ struct KeyStage {
   u4 v[NL];
 };
 
-// Cache policy of the score kernel's record loads and score stores: each
-// byte is touched once, and nontemporal accesses measured a few percent
-// faster on this stream (the attend kernel, whose lanes read scattered words
-// of lines other lanes also read, keeps the default policy).
+// Cache policy of the score kernel's record loads: each byte is read once,
+// and nontemporal loads measured a few percent faster on this stream (the
+// attend kernel, whose lanes read scattered words of lines other lanes also
+// read, keeps the default policy).  The score stores keep the default
+// policy: a wave writes 64-byte pieces of 16 head rows, and nontemporal
+// stores of those moved 17% more bytes than they carry (WRITE_SIZE) for no
+// gain in time.
 constexpr int kNonTemporal = 2;
 
 template <int RW, int U>
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const ScoreArgs a) {
         const f4 v = acc[u] * nk * qn;
         const uint32_t ob = (orow + (uint32_t)t0) * 4u;
         if (t0 + 4 <= n_tok) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), ors, ob, 0, kNonTemporal);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), ors, ob, 0, 0);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
