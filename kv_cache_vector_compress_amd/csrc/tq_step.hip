@@ -758,6 +758,40 @@ __global__ __launch_bounds__(256, 1) void decode_step_kernel(const StepArgs a) {
   if (step_arrive(a, slot, &flag)) step_combine(a, slot, per, L);
 }
 
+// Query preparation for the attend kernel on the single-kernel shapes: one
+// workgroup per slot runs the decode step's preparation (the fp16 hi images
+// on the matrix cores; the attend operands are fp16, so R_hi q, within
+// ~2^-12 of R q, loses nothing they keep) and writes the operands and norms
+// where the attend kernel reads them ([n_seq][KBT][64][8] fp16, [n_seq][16]).
+template <int M>
+__global__ __launch_bounds__(256) void prep_step_kernel(const StepArgs a, uint16_t* wq, float* wqn) {
+  extern __shared__ __align__(16) float L[];
+  constexpr int KBT = 4 + M / 32;
+  const int slot = blockIdx.x;
+  step_prep<M>(a, slot, L, true);  // (ends with a barrier: operands and norms complete)
+  const u4* ops = (const u4*)(L + kLdsOps);
+  u4* dst = (u4*)(wq + (int64_t)slot * KBT * 64 * 8);
+  for (int i = threadIdx.x; i < KBT * 64; i += blockDim.x) dst[i] = ops[i];
+  if (threadIdx.x < 16) wqn[(int64_t)slot * 16 + threadIdx.x] = L[kLdsQn + threadIdx.x];
+}
+
+int launch_prep_step(const Matrices& mats, int m, const AttnShape& s, uint16_t* wq, float* wqn, void* stream) {
+  StepArgs a{};
+  a.att.G = s.G;
+  a.q = s.q;
+  a.dtype = s.dtype;
+  a.r_hi = mats.r_hi;
+  a.p_hi = mats.p_hi;
+  if (!a.r_hi || !a.p_hi) return TQ_EUNSUPPORTED;
+  const dim3 grid((unsigned)s.n_seq), block(256);
+  const size_t lds = sizeof(float) * kLdsPm;  // query, q~, p, norms, operands
+  hipStream_t st = (hipStream_t)stream;
+  if (m == 64) hipLaunchKernelGGL(prep_step_kernel<64>, grid, block, lds, st, a, wq, wqn);
+  else if (m == 128) hipLaunchKernelGGL(prep_step_kernel<128>, grid, block, lds, st, a, wq, wqn);
+  else return TQ_EUNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? 0 : TQ_EDEVICE;
+}
+
 int launch_decode_step(const Matrices& mats, const CodebookDev& cbk, int kbits, const CodebookDev& cbv, int vbits,
                        int d, int m, const AppendShape& ks, const AppendShape& vs, const AttnShape& s,
                        void* key_records, void* value_blocks, float scale, float* out, void* ws, const AttnPlan& p,
