@@ -568,7 +568,7 @@ int tq_attend(tq_ctx* ctx, const tq_cache_view* cache, const void* q, int32_t dt
   if (hipSetDevice(ctx->device) != hipSuccess) return fail(TQ_EDEVICE, "tq_attend: hipSetDevice");
   AttnShape s{q, dtype, G, n_tokens, cache->capacity, cache->n_seq};
   if (fast_attn(ctx->cfg, G)) {
-    rc = launch_prep_queries_attend(ctx->mats, ctx->cfg.proj_dim, s, workspace, plan, stream);
+    rc = launch_prep_queries(ctx->mats, ctx->cfg.proj_dim, s, workspace, plan, stream);
     if (!rc)
       rc = launch_attend(ctx->mats, ctx->cb[ctx->cfg.key_bits], ctx->cfg.key_bits, ctx->cb[ctx->cfg.value_bits],
                          ctx->cfg.value_bits, ctx->cfg.proj_dim, s, cache->key_records, cache->value_blocks, scale,

@@ -225,12 +225,6 @@ int launch_prep_queries(const Matrices& mats, int m, const AttnShape& s, void* w
   return launch_gen_prep(mats, kD, m, s, 1, w.wq, w.wqn, stream);
 }
 
-int launch_prep_queries_attend(const Matrices& mats, int m, const AttnShape& s, void* ws, const AttnPlan& p,
-                               void* stream) {
-  const WsPtrs w = ws_ptrs(ws, p);
-  return launch_prep_step(mats, m, s, w.wq, w.wqn, stream);
-}
-
 int launch_scores(const CodebookDev& cbk, int kbits, int m, const AttnShape& s, const void* key_records,
                   float* scores, void* ws, const AttnPlan& p, void* stream) {
   ScoreArgs a;

@@ -1092,6 +1092,11 @@ size_t general_scores_workspace(int d, int m, int n_seq, int G) {
 
 int launch_gen_prep(const Matrices& mats, int d, int m, const AttnShape& s, int HG, uint16_t* wq, float* wqn,
                     void* stream) {
+  // one head group at head_dim 128: the decode step's preparation on the
+  // matrix cores, one workgroup per slot (tq_step.hip); the score kernels,
+  // attend and top-k of these shapes all read its operands
+  if (d == 128 && HG == 1 && (m == 64 || m == 128) && mats.r_hi && mats.p_hi)
+    return launch_prep_step(mats, m, s, wq, wqn, stream);
   GenPrepArgs p;
   p.q = s.q;
   p.dtype = s.dtype;

@@ -86,11 +86,8 @@ int attention_device_init();
 
 int launch_prep_queries(const Matrices& mats, int m, const AttnShape& s, void* ws, const AttnPlan& p,
                         void* stream);
-// The attend path's query preparation: the decode step's preparation on the
-// matrix cores, one workgroup per slot (tq_step.hip); the score path keeps
-// launch_prep_queries, whose operands the top-k search shares.
-int launch_prep_queries_attend(const Matrices& mats, int m, const AttnShape& s, void* ws, const AttnPlan& p,
-                               void* stream);
+// Query preparation on the matrix cores for one head group at head_dim 128
+// (the decode step's preparation, one workgroup per slot; tq_step.hip).
 int launch_prep_step(const Matrices& mats, int m, const AttnShape& s, uint16_t* wq, float* wqn, void* stream);
 int launch_scores(const CodebookDev& cbk, int kbits, int m, const AttnShape& s, const void* key_records,
                   float* scores, void* ws, const AttnPlan& p, void* stream);
