@@ -750,15 +750,22 @@ __global__ __launch_bounds__(256) void gen_scores(const GenScoreArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) nk[i] = __shfl(kn, 4 * q + i, 64);
   const int t0 = (int)(tile * 16) + 4 * q;
+  // a lane's 4 tokens of a head row are one 16-byte store when rows start
+  // 16-byte aligned (the score buffer aligned and n_tokens a multiple of 4)
+  const bool vec = (n_tok & 3) == 0 && ((uintptr_t)a.scores & 15) == 0 && t0 + 4 <= n_tok;
 #pragma unroll
   for (int g = 0; g < HG; ++g) {
     const int h = 16 * g + r16;
     if (h >= a.G) continue;
     const float qn = a.wqn[(int64_t)slot * 16 * HG + h];
     float* out = a.scores + ((int64_t)slot * a.G + h) * (int64_t)n_tok;
+    if (vec) {
+      *(f4*)(out + t0) = acc[g] * nk * qn;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (t0 + i < n_tok) out[t0 + i] = acc[g][i] * nk[i] * qn;
+      for (int i = 0; i < 4; ++i)
+        if (t0 + i < n_tok) out[t0 + i] = acc[g][i] * nk[i] * qn;
+    }
   }
 }
 
