@@ -769,6 +769,136 @@ __global__ __launch_bounds__(256) void gen_scores(const GenScoreArgs a) {
   }
 }
 
+// Scores for many head groups (HG >= 8, e.g. 512 queries against one slot):
+// a wave takes NT consecutive tiles and the head groups CG at a time, so
+// each query operand read from L2 feeds NT tiles' products (gen_scores reads
+// every operand once per tile).  The key words are decoded once per group
+// chunk.  Each accumulator (tile, head group) takes its products in
+// gen_scores' order (chunks, half chunk, sign blocks; K blocks in order), so
+// the estimates are the same bits.
+template <int B, int NT, int CG>
+__global__ __launch_bounds__(256) void gen_scores_blk(const GenScoreArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t wps = (a.tiles_per_slot + NT - 1) / NT;  // waves per slot
+  const int64_t gw = a.gw0 + (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (gw >= wps * a.n_seq) return;
+  const int slot = (int)(gw / wps);
+  const int64_t tile0 = (gw - (int64_t)slot * wps) * NT;
+  const int n_tok = (int)a.n_tokens;
+  const uint32_t* rp[NT];
+  float gkf[NT];
+  f4 nk[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tok = min((int)((tile0 + t) * 16) + r16, n_tok - 1);
+    rp[t] = a.rec + ((int64_t)slot * a.capacity + tok) * a.rec_words;
+    gkf[t] = __uint_as_float(rp[t][a.rec_words - 1]) * a.kappa;
+    const float kn = __uint_as_float(rp[t][a.rec_words - 2]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nk[t][i] = __shfl(kn, 4 * q + i, 64);
+  }
+  const int KBT = a.d / 32 + a.m / 32;
+  const uint16_t* wq = a.wq + (int64_t)slot * a.HG * KBT * 64 * 8 + lane * 8;
+  uint32_t tlo[4], thi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { tlo[i] = a.tlo[i]; thi[i] = a.thi[i]; }
+  const int sh0 = 15 - 8 * (q & 1);
+  const int sw0 = B * a.d / 32;
+  const bool vec = (n_tok & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;
+  for (int g0 = 0; g0 < a.HG; g0 += CG) {
+    f4 acc[NT][CG];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < CG; ++g) acc[t][g] = f4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* wg0 = wq + (int64_t)g0 * KBT * 64 * 8;
+    if constexpr (B > 0) {
+      const int n_full = key_full_chunks(a.d);
+      auto kblock = [&](const uint32_t (&cw)[NT][B], int kb, auto kk_tag) {
+        constexpr int KK = decltype(kk_tag)::value;
+        h8 A[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) A[t] = decode_pair<B, 2 * KK>(cw[t], tlo, thi);
+#pragma unroll
+        for (int g = 0; g < CG; ++g) {
+          const h8 b = *(const h8*)(wg0 + ((int64_t)g * KBT + kb) * 64 * 8);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t][g] = mfma(A[t], b, acc[t][g]);
+        }
+      };
+      for (int c = 0; c < n_full; ++c) {
+        uint32_t cw[NT][B];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int w = 0; w < B; ++w) cw[t][w] = rp[t][(q * n_full + c) * B + w];
+        kblock(cw, 4 * c, std::integral_constant<int, 0>{});
+        kblock(cw, 4 * c + 1, std::integral_constant<int, 1>{});
+        kblock(cw, 4 * c + 2, std::integral_constant<int, 2>{});
+        kblock(cw, 4 * c + 3, std::integral_constant<int, 3>{});
+      }
+      if (a.d % 128) {  // the half chunk: this lane group's slots 0..3 (two K blocks)
+        uint32_t cw[NT][B];
+        const int w0 = key_group_word(q, n_full, n_full, B);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          uint32_t cl[B];
+#pragma unroll
+          for (int w = 0; w < B; ++w) cw[t][w] = cl[w] = rp[t][w0 + w];
+          lower_half<B>(cl);
+#pragma unroll
+          for (int w = 0; w < B; ++w) cw[t][w] = q >= 2 ? cl[w] : cw[t][w];
+        }
+        kblock(cw, 4 * n_full, std::integral_constant<int, 0>{});
+        kblock(cw, 4 * n_full + 1, std::integral_constant<int, 1>{});
+      }
+    }
+    for (int kbp = 0; kbp < a.m / 32; ++kbp) {
+      const bool hb = 32 * kbp + 64 > a.m && (kbp % 2) == 0;
+      const int sh1 = hb ? 15 - 4 * q : sh0 - 4 * (kbp % 2);
+      h8 A[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t w = ~rp[t][sw0 + 2 * (kbp / 2) + (hb ? 0 : (q >> 1))];
+        const _Float16 gk = (_Float16)gkf[t];
+        const uint32_t gk2 = (uint32_t)__builtin_bit_cast(uint16_t, gk) * 0x00010001u;
+        u4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t sh = w << (sh1 - e);  // bits p, p+16 -> 15, 31
+          v[e] = (sh & 0x80008000u) | (gk2 & 0x7FFF7FFFu);
+        }
+        A[t] = as_h8(v);
+      }
+#pragma unroll
+      for (int g = 0; g < CG; ++g) {
+        const h8 b = *(const h8*)(wg0 + ((int64_t)g * KBT + a.d / 32 + kbp) * 64 * 8);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][g] = mfma(A[t], b, acc[t][g]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < CG; ++g) {
+      const int h = 16 * (g0 + g) + r16;
+      if (h >= a.G) continue;
+      const float qn = a.wqn[(int64_t)slot * 16 * a.HG + h];
+      float* out = a.scores + ((int64_t)slot * a.G + h) * (int64_t)n_tok;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int t0 = (int)((tile0 + t) * 16) + 4 * q;
+        if (vec && t0 + 4 <= n_tok) {
+          *(f4*)(out + t0) = acc[t][g] * nk[t] * qn;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + i < n_tok) out[t0 + i] = acc[t][g][i] * nk[t][i] * qn;
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // attend (general shapes): the scores come from gen_scores (materialised in
 // the workspace); each wave runs the online softmax over a range of 128-token
@@ -1155,6 +1285,21 @@ int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbit
   a.tiles_per_slot = (s.n_tokens + 15) / 16;
   a.kappa = (float)(1.2533141373155002512 / m);  // sqrt(pi/2) / m
   for (int i = 0; i < 4; ++i) { a.tlo[i] = cbk.tlo[i]; a.thi[i] = cbk.thi[i]; }
+  // many head groups: the blocked kernel (4 tiles a wave, 8 groups at a time)
+  constexpr int kBlkTiles = 4, kBlkGroups = 8;
+  if (HG >= kBlkGroups) {
+    const int64_t waves = (a.tiles_per_slot + kBlkTiles - 1) / kBlkTiles * s.n_seq, chunk = (int64_t)4 << 22;
+    for (a.gw0 = 0; a.gw0 < waves; a.gw0 += chunk) {
+      const int64_t nw = std::min(chunk, waves - a.gw0);
+      const dim3 grid((unsigned)((nw + 3) / 4)), block(256);
+#define TQ_GSK(B) \
+  if (kbits == B) hipLaunchKernelGGL((gen_scores_blk<B, kBlkTiles, kBlkGroups>), grid, block, 0, st, a);
+      TQ_GSK(0) TQ_GSK(1) TQ_GSK(2) TQ_GSK(3) TQ_GSK(4)
+#undef TQ_GSK
+      if (hipGetLastError() != hipSuccess) return TQ_EDEVICE;
+    }
+    return 0;
+  }
   // one wave per (slot, 16-token tile), in launches of at most 2^22
   // workgroups so that a grid's thread count stays within 32 bits
   const int64_t waves = a.tiles_per_slot * s.n_seq, chunk = (int64_t)4 << 22;

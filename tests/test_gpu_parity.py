@@ -263,6 +263,9 @@ def test_long_context_full_size_sampled():
     (320, 160, 2, 4, np.float32, 12),
     (128, 32, 3, 3, np.float16, 8),    # head_dim 128 with a single half sign block
     (960, 480, 4, 1, np.float32, 3),
+    # many head groups (the blocked score kernel: 4 tiles a wave, 8 groups at a time)
+    (192, 96, 3, 3, np.float16, 130),  # 9 live groups of a 16-group bucket, half chunk, half sign block
+    (128, 64, 2, 2, np.float32, 100),  # head_dim 128 beyond 16 query heads
 ])
 def test_general_shapes_ragged_chunks(d, m, kb, vb, dtype, G):
     """Codes, signs, norms, gamma of keys and values, scores and (G <= 16)
@@ -274,6 +277,19 @@ def test_general_shapes_ragged_chunks(d, m, kb, vb, dtype, G):
     Q = np.stack([synth.kv_slot(62 + d, s, s, G, d, dtype=dtype) for s in range(n_seq)])
     _say("general", (d, m, kb, vb, dtype.__name__, G))
     _say(run_case(K, V, Q, kb=kb, vb=vb, m=m, chunks=[130, 1, 300, 269], check_attend=G <= 16))
+
+
+@pytest.mark.parametrize("T,G", [(333, 136), (18, 129)])
+def test_many_head_scores_ragged_tokens(T, G):
+    """The blocked score kernel with a token count that is not a multiple of
+    4 (per-score stores) and a last wave holding fewer than 4 tiles; scores
+    against the oracle."""
+    d, m, kb, n_seq = 256, 128, 4, 2
+    K = np.stack([synth.kv_slot(140, s, s, T, d, dtype=np.float16) for s in range(n_seq)])
+    V = np.stack([synth.kv_slot(141, s, s, T, d, dtype=np.float16) for s in range(n_seq)])
+    Q = np.stack([synth.kv_slot(142, s, s, G, d, dtype=np.float16) for s in range(n_seq)])
+    _say("many heads, ragged tokens", (T, G))
+    _say(run_case(K, V, Q, kb=kb, vb=2, m=m, chunks=[T], check_attend=False))
 
 
 def test_vector_search_shape():
