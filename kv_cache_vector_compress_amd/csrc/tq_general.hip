@@ -769,13 +769,16 @@ __global__ __launch_bounds__(256) void gen_scores(const GenScoreArgs a) {
   }
 }
 
-// Scores for many head groups (HG >= 8, e.g. 512 queries against one slot):
-// a wave takes NT consecutive tiles and the head groups CG at a time, so
-// each query operand read from L2 feeds NT tiles' products (gen_scores reads
-// every operand once per tile).  The key words are decoded once per group
-// chunk.  Each accumulator (tile, head group) takes its products in
-// gen_scores' order (chunks, half chunk, sign blocks; K blocks in order), so
-// the estimates are the same bits.
+// Scores for many head groups (HG >= 4, e.g. 512 queries against one slot):
+// a wave takes NT consecutive tiles and the head groups CG at a time.  Only
+// CG groups' accumulators are live, so the kernel holds ~100 registers a
+// lane (gen_scores<4, 32> holds ~330, one wave per SIMD) and runs several
+// waves per SIMD; the key words are decoded again for every group chunk.
+// With NT > 1 each query operand read from L2 would feed NT tiles' products,
+// but the registers that costs measured slower than the waves it loses.
+// Each accumulator (tile, head group) takes its products in gen_scores'
+// order (chunks, half chunk, sign blocks; K blocks in order), so the
+// estimates are the same bits.
 template <int B, int NT, int CG>
 __global__ __launch_bounds__(256) void gen_scores_blk(const GenScoreArgs a) {
   const int lane = threadIdx.x & 63;
@@ -1285,8 +1288,9 @@ int launch_general_scores(const Matrices& mats, const CodebookDev& cbk, int kbit
   a.tiles_per_slot = (s.n_tokens + 15) / 16;
   a.kappa = (float)(1.2533141373155002512 / m);  // sqrt(pi/2) / m
   for (int i = 0; i < 4; ++i) { a.tlo[i] = cbk.tlo[i]; a.thi[i] = cbk.thi[i]; }
-  // many head groups: the blocked kernel (4 tiles a wave, 8 groups at a time)
-  constexpr int kBlkTiles = 4, kBlkGroups = 8;
+  // many head groups: the blocked kernel (one tile a wave, 4 groups at a time;
+  // of 1-8 tiles and 1-16 groups, measured best on 512 queries x 2M keys)
+  constexpr int kBlkTiles = 1, kBlkGroups = 4;
   if (HG >= kBlkGroups) {
     const int64_t waves = (a.tiles_per_slot + kBlkTiles - 1) / kBlkTiles * s.n_seq, chunk = (int64_t)4 << 22;
     for (a.gw0 = 0; a.gw0 < waves; a.gw0 += chunk) {

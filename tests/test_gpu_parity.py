@@ -263,7 +263,7 @@ def test_long_context_full_size_sampled():
     (320, 160, 2, 4, np.float32, 12),
     (128, 32, 3, 3, np.float16, 8),    # head_dim 128 with a single half sign block
     (960, 480, 4, 1, np.float32, 3),
-    # many head groups (the blocked score kernel: 4 tiles a wave, 8 groups at a time)
+    # many head groups (the blocked score kernel: head groups 4 at a time)
     (192, 96, 3, 3, np.float16, 130),  # 9 live groups of a 16-group bucket, half chunk, half sign block
     (128, 64, 2, 2, np.float32, 100),  # head_dim 128 beyond 16 query heads
 ])
