@@ -157,12 +157,15 @@ __device__ __forceinline__ void decode4(uint32_t sel, const uint32_t (&tlo)[4], 
     lo = perm(tlo[1], tlo[0], sel);
     hi = perm(thi[1], thi[0], sel);
   } else {
-    const uint32_t s7 = sel & 0x07070707u;
-    const uint32_t upper = ((sel >> 3) & 0x01010101u) * 0xFFu;  // byte mask: code >= 8
-    const uint32_t lo_a = perm(tlo[1], tlo[0], s7), lo_b = perm(tlo[3], tlo[2], s7);
-    const uint32_t hi_a = perm(thi[1], thi[0], s7), hi_b = perm(thi[3], thi[2], s7);
-    lo = (lo_b & upper) | (lo_a & ~upper);
-    hi = (hi_b & upper) | (hi_a & ~upper);
+    // The codebook is symmetric (c[v] = -c[15 - v], exactly: the loaded
+    // centroids are symmetrised), so only its positive half (entries 8..15,
+    // tlo/thi[2..3]) is read: code v >= 8 is c[v], code v < 8 is -c[15 - v],
+    // whose magnitude index 7 - v is (v & 7) ^ 7 and whose sign is the top
+    // bit of the high byte.
+    const uint32_t neg = (~sel >> 3) & 0x01010101u;  // 1 in the bytes of codes < 8
+    const uint32_t mag = (sel & 0x07070707u) ^ (neg * 7u);
+    lo = perm(tlo[3], tlo[2], mag);
+    hi = perm(thi[3], thi[2], mag) | (neg << 7);
   }
   p01 = perm(hi, lo, 0x05010400u);
   p23 = perm(hi, lo, 0x07030602u);
